@@ -1,0 +1,179 @@
+"""fp64 CPU oracle for sparse multi-head graph attention (ctypes wrapper of oracle.c).
+
+TEST INFRASTRUCTURE.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+benchmark's ``cpu_baseline`` leg may import this package.  The GPU library
+never does, and shares no code with it.
+
+What it computes, and the passages it follows, is stated in ``oracle.c``:
+per destination v and head h, scores s_e = <q_v, k_u>/sqrt(D) over the
+in-edges u->v (SDDMM), a softmax over those scores, and the weighted sum of
+the source V rows (SpMM); zero for a destination with no in-edges.
+
+Every function here is pinned by ``tests/test_oracle_pins.py`` against
+things other than itself (library masked attention, closed forms, hand-worked
+golden examples, invariants); ``tests/test_oracle_mutants.py`` shows that
+plausible mistakes planted in a copy of oracle.c fail those pins.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import _build
+
+F32, BF16, F64 = 0, 1, 2
+
+_LIBS = {}
+_i64 = ctypes.c_int64
+_int = ctypes.c_int
+_p = ctypes.c_void_p
+
+
+def load(path=None):
+    """Load liboracle.so (built on first use), or another build of oracle.c at path."""
+    path = path or _build.LIB
+    if path not in _LIBS:
+        if path == _build.LIB and not os.path.exists(path):
+            _build.build()
+        L = ctypes.CDLL(path)
+        L.oracle_sddmm.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _int]
+        L.oracle_edge_softmax.argtypes = [_i64, _i64, _int, _p, _p, _p, _int]
+        L.oracle_spmm.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _int]
+        L.oracle_fwd_rows.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _p, _i64, _p, _p, _p, _int]
+        L.oracle_fwd.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _p, _p, _p, _int]
+        L.oracle_max_threads.restype = _int
+        _LIBS[path] = L
+    return _LIBS[path]
+
+
+def _p_(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _dtype_of(x):
+    if x.dtype == np.float32:
+        return F32
+    if x.dtype == np.uint16:
+        return BF16
+    if x.dtype == np.float64:
+        return F64
+    raise TypeError("features must be float32, float64 or uint16 (bf16 bits), got %s" % x.dtype)
+
+
+def _csr(indptr, indices):
+    return (np.ascontiguousarray(indptr, dtype=np.int64), np.ascontiguousarray(indices, dtype=np.int32))
+
+
+def _shape(Q):
+    if Q.ndim != 3:
+        raise ValueError("features are [N][H][D]")
+    return Q.shape
+
+
+class Oracle:
+    """Bound to one build of oracle.c (the default, or a test's variant)."""
+
+    def __init__(self, path=None):
+        self.L = load(path)
+
+    def max_threads(self):
+        return self.L.oracle_max_threads()
+
+    def fwd(self, indptr, indices, Q, K, V, want_edges=False, nthreads=0):
+        """Whole forward: out [N][H][D] (fp64); with want_edges also scores and alpha [E][H]."""
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        E = len(indices)
+        dt = _dtype_of(Q)
+        Q, K, V = (np.ascontiguousarray(x) for x in (Q, K, V))
+        out = np.empty((N, H, D), dtype=np.float64)
+        s = np.empty((E, H), dtype=np.float64) if want_edges else None
+        a = np.empty((E, H), dtype=np.float64) if want_edges else None
+        rc = self.L.oracle_fwd(N, E, H, D, dt, _p_(indptr), _p_(indices), _p_(Q), _p_(K), _p_(V),
+                               _p_(out), _p_(s), _p_(a), nthreads)
+        if rc:
+            raise ValueError("oracle_fwd rejected its arguments")
+        return (out, s, a) if want_edges else out
+
+    def fwd_rows(self, indptr, indices, Q, K, V, rows, nthreads=0, want_edges=False):
+        """Forward for the listed destination rows only: out [len(rows)][H][D]."""
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        E = len(indices)
+        dt = _dtype_of(Q)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        out = np.empty((len(rows), H, D), dtype=np.float64)
+        ne = int((indptr[rows + 1] - indptr[rows]).sum()) if len(rows) else 0
+        s = np.empty((ne, H), dtype=np.float64) if want_edges else None
+        a = np.empty((ne, H), dtype=np.float64) if want_edges else None
+        rc = self.L.oracle_fwd_rows(N, E, H, D, dt, _p_(indptr), _p_(indices), _p_(Q), _p_(K), _p_(V),
+                                    _p_(rows), len(rows), _p_(out), _p_(s), _p_(a), nthreads)
+        if rc:
+            raise ValueError("oracle_fwd_rows rejected its arguments")
+        return (out, s, a) if want_edges else out
+
+    def sddmm(self, indptr, indices, Q, K, nthreads=0):
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        E = len(indices)
+        Q, K = np.ascontiguousarray(Q), np.ascontiguousarray(K)
+        s = np.empty((E, H), dtype=np.float64)
+        rc = self.L.oracle_sddmm(N, E, H, D, _dtype_of(Q), _p_(indptr), _p_(indices), _p_(Q), _p_(K), _p_(s),
+                                 nthreads)
+        if rc:
+            raise ValueError("oracle_sddmm rejected its arguments")
+        return s
+
+    def edge_softmax(self, indptr, scores, nthreads=0):
+        indptr = np.ascontiguousarray(indptr, dtype=np.int64)
+        scores = np.ascontiguousarray(scores, dtype=np.float64)
+        E, H = scores.shape
+        N = len(indptr) - 1
+        a = np.empty((E, H), dtype=np.float64)
+        rc = self.L.oracle_edge_softmax(N, E, H, _p_(indptr), _p_(scores), _p_(a), nthreads)
+        if rc:
+            raise ValueError("oracle_edge_softmax rejected its arguments")
+        return a
+
+    def spmm(self, indptr, indices, alpha, V, nthreads=0):
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(V)
+        E = len(indices)
+        alpha = np.ascontiguousarray(alpha, dtype=np.float64)
+        V = np.ascontiguousarray(V)
+        out = np.empty((N, H, D), dtype=np.float64)
+        rc = self.L.oracle_spmm(N, E, H, D, _dtype_of(V), _p_(indptr), _p_(indices), _p_(alpha), _p_(V),
+                                _p_(out), nthreads)
+        if rc:
+            raise ValueError("oracle_spmm rejected its arguments")
+        return out
+
+
+_default = None
+
+
+def default():
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def fwd(*a, **k):
+    return default().fwd(*a, **k)
+
+
+def fwd_rows(*a, **k):
+    return default().fwd_rows(*a, **k)
+
+
+def sddmm(*a, **k):
+    return default().sddmm(*a, **k)
+
+
+def edge_softmax(*a, **k):
+    return default().edge_softmax(*a, **k)
+
+
+def spmm(*a, **k):
+    return default().spmm(*a, **k)

@@ -1,0 +1,226 @@
+/*
+ * oracle.c -- plain fp64 CPU oracle for sparse multi-head graph attention.
+ *
+ * TEST INFRASTRUCTURE.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this code.  It shares nothing with
+ * the GPU library: no headers, helpers, tables or kernels.
+ *
+ * What it computes (destination-sorted CSR: row v lists the sources u of its
+ * in-edges u->v; Q, K, V are [N][H][D] with D contiguous):
+ *
+ *   s_e      = <Q[v,h,:], K[u_e,h,:]> / sqrt(D)            for e in row v
+ *   alpha_e  = exp(s_e - m) / sum_e' exp(s_e' - m),  m = max_e s_e
+ *   out[v,h] = sum_e alpha_e * V[u_e,h,:]    (0 when v has no in-edges)
+ *
+ * Sources:
+ *  - "Graph Transformer in a Nutshell" (DGL sparse tutorial), section "Sparse
+ *    Multi-head Attention": SparseAttn(Q,K,V,A) = softmax((QK^T) o A / sqrt(d)) V,
+ *    scores only where A is nonzero (SDDMM), a sparse softmax, then an SpMM.
+ *  - "Efficient Sparse Transformer implementation with DGL's builtin
+ *    operators", TransLayer.forward: u_dot_v (source key . destination
+ *    query), edge_softmax of the scores divided by sqrt(d_qkv), u_mul_e_sum.
+ *  - "Graph Transformer theory, derivation and implementation" (Japanese blog),
+ *    section reviewing scaled dot-product attention: e_ij = q_i.k_j / sqrt(d_k),
+ *    alpha_ij = exp(e_ij) / sum_j' exp(e_ij'), h_i = sum_j alpha_ij v_j; here j
+ *    ranges over the in-edges of i only.
+ *
+ * Readings where the pages are silent:
+ *  - the softmax of each destination runs over its in-edges (the tutorial's
+ *    Hadamard form read as a logit of -inf, not 0, off the graph);
+ *  - each stored edge is its own term (duplicates count twice);
+ *  - a destination with no in-edges gets the empty sum, 0;
+ *  - the max is subtracted before exp (mathematically a no-op).
+ *
+ * The algorithm is deliberately plain: per row and head, one pass for all
+ * scores and their max, one for the exponentials and their sum, one for the
+ * weights and the weighted sum of V rows, all in double.  Inputs are widened
+ * to double exactly (fp32 and bf16 values are representable in fp64).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_F32 = 0, OR_BF16 = 1, OR_F64 = 2 };
+
+/* element i of a feature array, widened exactly to double */
+static double elem(const void* base, int dtype, int64_t i) {
+    if (dtype == OR_F32) return (double)((const float*)base)[i];
+    if (dtype == OR_F64) return ((const double*)base)[i];
+    /* bf16: the upper 16 bits of an IEEE binary32 */
+    uint32_t bits = (uint32_t)((const uint16_t*)base)[i] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+static int bad_dtype(int dtype) { return dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F64; }
+
+static void set_threads(int nthreads) {
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#else
+    (void)nthreads;
+#endif
+}
+
+int oracle_max_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/* score of edge e (source u) for destination v, head h: dot product over D, then / sqrt(D) */
+static double edge_score(const void* Q, const void* K, int dtype, int H, int D, int64_t v, int64_t u, int h) {
+    int64_t qo = (v * H + h) * (int64_t)D, ko = (u * H + h) * (int64_t)D;
+    double dot = 0.0;
+    for (int d = 0; d < D; ++d) dot += elem(Q, dtype, qo + d) * elem(K, dtype, ko + d);
+    return dot / sqrt((double)D);
+}
+
+/*
+ * Softmax over the in-edges of one destination for one head, two-pass:
+ * s[0..deg) in, a[0..deg) out (a may alias s).
+ */
+static void row_softmax(const double* s, double* a, int64_t deg) {
+    double m = -INFINITY;
+    for (int64_t i = 0; i < deg; ++i)
+        if (s[i] > m) m = s[i];
+    double z = 0.0;
+    for (int64_t i = 0; i < deg; ++i) {
+        a[i] = exp(s[i] - m);
+        z += a[i];
+    }
+    for (int64_t i = 0; i < deg; ++i) a[i] /= z;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 1: SDDMM.  scores[e*H + h] = s_e for head h.                        */
+/* ------------------------------------------------------------------------ */
+int oracle_sddmm(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                 const void* Q, const void* K, double* scores, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || bad_dtype(dtype)) return 1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t v = 0; v < N; ++v)
+        for (int64_t e = indptr[v]; e < indptr[v + 1]; ++e)
+            for (int h = 0; h < H; ++h) scores[e * H + h] = edge_score(Q, K, dtype, H, D, v, indices[e], h);
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 2: edge softmax per (destination, head).  alpha may alias scores.   */
+/* ------------------------------------------------------------------------ */
+int oracle_edge_softmax(int64_t N, int64_t E, int H, const int64_t* indptr, const double* scores, double* alpha,
+                        int nthreads) {
+    if (N < 0 || E < 0 || H < 1) return 1;
+    int64_t maxdeg = 0;
+    for (int64_t v = 0; v < N; ++v)
+        if (indptr[v + 1] - indptr[v] > maxdeg) maxdeg = indptr[v + 1] - indptr[v];
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* buf = (double*)malloc(sizeof(double) * (size_t)(maxdeg > 0 ? maxdeg : 1));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t v = 0; v < N; ++v) {
+            int64_t b = indptr[v], deg = indptr[v + 1] - b;
+            for (int h = 0; h < H; ++h) {
+                for (int64_t i = 0; i < deg; ++i) buf[i] = scores[(b + i) * H + h];
+                row_softmax(buf, buf, deg);
+                for (int64_t i = 0; i < deg; ++i) alpha[(b + i) * H + h] = buf[i];
+            }
+        }
+        free(buf);
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Stage 3: SpMM.  out[v,h,:] = sum_e alpha[e*H+h] * V[u_e,h,:].             */
+/* ------------------------------------------------------------------------ */
+int oracle_spmm(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                const double* alpha, const void* V, double* out, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || bad_dtype(dtype)) return 1;
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 64)
+    for (int64_t v = 0; v < N; ++v)
+        for (int h = 0; h < H; ++h) {
+            double* o = out + (v * H + h) * (int64_t)D;
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            for (int64_t e = indptr[v]; e < indptr[v + 1]; ++e) {
+                double a = alpha[e * H + h];
+                int64_t vo = ((int64_t)indices[e] * H + h) * (int64_t)D;
+                for (int d = 0; d < D; ++d) o[d] += a * elem(V, dtype, vo + d);
+            }
+        }
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Whole forward for a list of destination rows: the three stages above,    */
+/* applied row by row.  out_rows is [nrows][H][D]; scores_rows and           */
+/* alpha_rows (optional) receive the row's edges in CSR order, packed in     */
+/* the order the rows are listed: [sum of degrees][H].                       */
+/* ------------------------------------------------------------------------ */
+int oracle_fwd_rows(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                    const void* Q, const void* K, const void* V, const int64_t* rows, int64_t nrows,
+                    double* out_rows, double* scores_rows, double* alpha_rows, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || nrows < 0 || bad_dtype(dtype)) return 1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return 1;
+    /* packed offset of each listed row's edges */
+    int64_t* pos = (int64_t*)malloc(sizeof(int64_t) * (size_t)(nrows + 1));
+    int64_t maxdeg = 0;
+    pos[0] = 0;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t deg = indptr[rows[r] + 1] - indptr[rows[r]];
+        pos[r + 1] = pos[r] + deg;
+        if (deg > maxdeg) maxdeg = deg;
+    }
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(maxdeg > 0 ? maxdeg : 1));
+        double* a = (double*)malloc(sizeof(double) * (size_t)(maxdeg > 0 ? maxdeg : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t v = rows[r], b = indptr[v], deg = indptr[v + 1] - b;
+            for (int h = 0; h < H; ++h) {
+                double* o = out_rows + (r * H + h) * (int64_t)D;
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                /* pass 1: scores (and their max, inside row_softmax) */
+                for (int64_t i = 0; i < deg; ++i) s[i] = edge_score(Q, K, dtype, H, D, v, indices[b + i], h);
+                /* pass 2: exponentials, their sum, the weights */
+                row_softmax(s, a, deg);
+                /* pass 3: weighted sum of the source V rows */
+                for (int64_t i = 0; i < deg; ++i) {
+                    int64_t vo = ((int64_t)indices[b + i] * H + h) * (int64_t)D;
+                    for (int d = 0; d < D; ++d) o[d] += a[i] * elem(V, dtype, vo + d);
+                    if (scores_rows) scores_rows[(pos[r] + i) * H + h] = s[i];
+                    if (alpha_rows) alpha_rows[(pos[r] + i) * H + h] = a[i];
+                }
+            }
+        }
+        free(a);
+        free(s);
+    }
+    free(pos);
+    return 0;
+}
+
+/* Whole forward over every row: out is [N][H][D]; scores/alpha optional [E][H]. */
+int oracle_fwd(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+               const void* Q, const void* K, const void* V, double* out, double* scores, double* alpha,
+               int nthreads) {
+    if (N < 0) return 1;
+    int64_t* rows = (int64_t*)malloc(sizeof(int64_t) * (size_t)(N > 0 ? N : 1));
+    for (int64_t v = 0; v < N; ++v) rows[v] = v;
+    int rc = oracle_fwd_rows(N, E, H, D, dtype, indptr, indices, Q, K, V, rows, N, out, scores, alpha, nthreads);
+    free(rows);
+    return rc;
+}
