@@ -1,0 +1,220 @@
+"""Benchmark of the fused sparse multi-head attention forward on one MI355X.
+
+One step = one gt_sparse_mha_fwd call (plan, fused attention kernel, merge of
+split rows) over the power-law workload: N=1,000,000 nodes, E=16,000,000
+edges, in-degrees Zipf(1.8) clipped at 50,000, uniform sources, H=8 heads of
+D=64, fp32; inputs resident in HBM before timing starts.
+
+Prints one JSON line: edge-heads/s of the whole call, the roofline of the
+dominant kernel (the fused attention kernel, timed with HIP events on its own
+stream over the timed region) against MI355X's 8 TB/s HBM peak, the HBM
+traffic counted by rocprofv3 (from the committed counter summary, when it
+matches the current kernel source), and the CPU oracle timed on a bounded
+sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                  [--no-cpu-baseline] [--calib-copy]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "edge-heads/sec + achieved HBM GB/s (% of peak), fused sparse MHA fwd"
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_fwd_powerlaw_1M.traffic.txt")
+KERNEL_SOURCES = ["sparse_graph_attention_amd/csrc/fused.hip", "sparse_graph_attention_amd/csrc/common.hpp",
+                  "sparse_graph_attention_amd/csrc/kernels.hpp"]
+
+DESCRIPTIONS = {
+    "powerlaw": "power-law graph: N=1,000,000, E=16,000,000, in-degree Zipf(1.8) clipped at 50,000, "
+                "uniform sources, H=8, D=64, fp32",
+    "lognormal": "log-normal graph: N=2,400,000, E=60,000,000, in-degree log-normal (mean 25, sigma 1.2), "
+                 "uniform sources, H=8, D=32, bf16 in/out, fp32 accumulation",
+    "regular16": "in-degree-16 graph: N=100,000, E=1,600,000, uniform sources, H=8, D=64, fp32",
+}
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
+def load_traffic():
+    """HBM bytes per launch of the fused kernel from the committed counter summary, or None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line and not line.startswith("#") and "=" in line:
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_sha():
+        return None, "kernel changed since the counters were taken"
+    fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_scale"])
+    write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_scale"])
+    return fetch + write, "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy"
+
+
+def algorithmic_bytes(w):
+    """Bytes the method must move: each edge gathers one K and one V row, Q is read
+    once per row with in-edges, out is written once per row, plus the CSR."""
+    import numpy as np
+
+    b = 4 if w["dtype"] == 0 else 2
+    HD = w["H"] * w["D"]
+    nnz = int((np.diff(w["indptr"]) > 0).sum())
+    return nnz * HD * b + 2 * w["E"] * HD * b + w["N"] * HD * b + 4 * w["E"] + 8 * (w["N"] + 1)
+
+
+def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
+    """The oracle as it stands on a fixed random sample of destination rows."""
+    import numpy as np
+
+    import oracle
+
+    N = w["N"]
+    rng = np.random.default_rng(seed)
+    rows = np.sort(rng.choice(N, size=max(1, int(N * fraction)), replace=False)).astype(np.int64)
+    ip = w["indptr"]
+    edges = int((ip[rows + 1] - ip[rows]).sum())
+    threads = oracle.default().max_threads()
+    log("cpu baseline: oracle on %d rows (%d edges) with %d threads" % (len(rows), edges, threads))
+    t0 = time.perf_counter()
+    ref = oracle.fwd_rows(w["indptr"], w["indices"], w["Q"], w["K"], w["V"], rows)
+    dt = time.perf_counter() - t0
+    g = out_gpu[rows].astype(np.float64)
+    log("cpu baseline: %.2f s; GPU vs oracle on the sample: max abs err %.3e" % (dt, float(np.abs(g - ref).max())))
+    return {
+        "value": edges * w["H"] / dt,
+        "unit": "edge-heads/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": "%d%% of destination rows drawn uniformly (seed %d): %d rows, %d edges, %.1f s wall" % (
+            round(fraction * 100), seed, len(rows), edges, dt),
+    }
+
+
+def calib_copy(gib=1.0, reps=5):
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+
+    n = int(gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "reps": reps}), flush=True)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="powerlaw", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr, flush=True)
+        sys.exit(2)
+    if args.calib_copy:
+        calib_copy()
+        return
+
+    import numpy as np
+    import torch
+
+    import gtgen
+    import sparse_graph_attention_amd as gt
+
+    log("generating %s" % args.workload)
+    t0 = time.perf_counter()
+    w = gtgen.make_workload(args.workload)
+    log("generated N=%d E=%d in %.1f s" % (w["N"], w["E"], time.perf_counter() - t0))
+    dev = torch.device("cuda:0")
+    t = {k: torch.from_numpy(w[k]).to(dev) for k in ("indptr", "indices")}
+    for k in ("Q", "K", "V"):
+        x = w[k]
+        t[k] = (torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16) if x.dtype == np.uint16
+                else torch.from_numpy(x).to(dev))
+    out = torch.empty_like(t["Q"])
+    torch.cuda.synchronize()
+
+    def step():
+        gt.gt_sparse_mha_fwd(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], out=out)
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timing %d steps" % args.steps)
+    gt.gt_profile_begin(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kern_ms, call_ms, calls = gt.gt_profile_end()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_avg_ms = kern_ms / calls
+    E, H = w["E"], w["H"]
+    alg = algorithmic_bytes(w)
+    achieved = alg / (kern_avg_ms * 1e-3) / 1e9
+    traffic, traffic_note = load_traffic() if args.workload == "powerlaw" else (None, "counters are for powerlaw")
+    log("ms/step %.3f (event-timed call %.3f ms, fused kernel %.3f ms); algorithmic %.2f GB -> %.0f GB/s"
+        % (ms_per_step, call_ms / calls, kern_avg_ms, alg / 1e9, achieved))
+    log("traffic: %s" % traffic_note)
+
+    line = {
+        "metric": METRIC,
+        "value": E * H / (ms_per_step * 1e-3),
+        "unit": "edge-heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32" if w["dtype"] == 0 else "bf16",
+        "data": "synthetic",
+        "config": {"workload": DESCRIPTIONS[args.workload], "N": w["N"], "E": E, "H": H, "D": w["D"]},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": achieved,
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS,
+            "traffic": traffic,
+            "kernel": "fused attention kernel",
+            "kernel_ms": kern_avg_ms,
+            "algorithmic_bytes": alg,
+        },
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, out.float().cpu().numpy() if out.dtype == torch.bfloat16
+                                            else out.cpu().numpy())
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

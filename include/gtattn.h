@@ -1,0 +1,159 @@
+/*
+ * gtattn.h -- C ABI of libgtattn: sparse multi-head graph attention forward
+ * on one AMD Instinct MI355X (gfx950).
+ *
+ * The operation.  For a directed graph stored as a destination-sorted CSR and
+ * per-node features Q, K, V of H heads x D dims, every edge u->v and head h
+ * gets the score
+ *
+ *     s = <Q[v,h,:], K[u,h,:]> / sqrt(D)
+ *
+ * (an SDDMM: scores are computed only where the adjacency matrix is nonzero);
+ * the scores of each destination's in-edges are normalised by a softmax,
+ *
+ *     alpha = exp(s - m) / sum exp(s' - m),   m = max over the in-edges of v,
+ *
+ * and the output is the alpha-weighted sum of the source rows of V (an SpMM):
+ *
+ *     out[v,h,:] = sum over in-edges u->v of alpha * V[u,h,:].
+ *
+ * Sources: "Graph Transformer in a Nutshell" (DGL sparse-matrix tutorial),
+ * section "Sparse Multi-head Attention" (SparseAttn equation; batched SDDMM,
+ * sparse softmax and SpMM over heads); the gist "Efficient Sparse Transformer
+ * implementation with DGL's builtin operators", TransLayer.forward (u_dot_v,
+ * edge_softmax of e / sqrt(d_qkv), u_mul_e_sum, features viewed as (N, h, d));
+ * the blog "Graph Transformer theory, derivation and implementation",
+ * scaled dot-product attention review (per-node e_ij, alpha_ij, h_i).
+ *
+ * Conventions fixed here where the pages leave them open:
+ *  - the softmax of a destination runs over its in-edges only (off-graph
+ *    pairs take no part: a logit of -inf, not 0);
+ *  - every stored edge is its own term, so a duplicated edge counts twice;
+ *  - a destination with no in-edges gets out = 0 (the empty sum);
+ *  - the d under the square root is the per-head dimension D.
+ *
+ * Layouts (all arrays dense, row-major, no padding):
+ *  - indptr  int64[N+1], indptr[0] = 0, indptr[N] = E, non-decreasing;
+ *  - indices int32[E]: indices[e] in [0, N) is the SOURCE of edge e, whose
+ *    destination is the row v with indptr[v] <= e < indptr[v+1];
+ *  - Q, K, V, out: [N][H][D], D contiguous, element type given by dtype;
+ *  - scores, alpha: float32 [E][H], in CSR edge order.
+ *
+ * Pointers.  Every array pointer is a DEVICE pointer on the current HIP
+ * device, allocated and owned by the caller, who keeps it alive until the
+ * work enqueued on `stream` has finished.  The library keeps no caller
+ * pointer after a call returns.  It owns its internal scratch (work lists
+ * and the partial results of split rows): one buffer per (device, stream),
+ * grown on demand; growing it synchronises that stream once.
+ *
+ * Execution.  Calls enqueue kernels on `stream` (NULL = the null stream) and
+ * return without waiting for them; gt_validate_csr is the exception.  Every
+ * element of every output is written, including the zeros of destinations
+ * without in-edges, so outputs need no clearing.  Results are deterministic:
+ * two calls on the same inputs give bit-identical outputs.  Calls on
+ * different streams may run concurrently.
+ *
+ * Errors.  Arguments are checked before anything is enqueued; on a non-OK
+ * status nothing was launched.  No exception or abort crosses the ABI.
+ *  GT_EINVAL       a NULL array with N > 0 (or E > 0 for indices/scores/
+ *                  alpha), N < 0, E < 0, H < 1, D < 1, N >= 2^31, or an
+ *                  invalid configuration value;
+ *  GT_EUNSUPPORTED an unknown dtype, H > 64 or D > 256;
+ *  GT_ENOMEM       the scratch buffer could not be allocated;
+ *  GT_EHIP         a HIP runtime or launch error (gt_last_error() has it).
+ * Special sizes: N = 0 is a no-op returning GT_OK; E = 0 writes zeros.
+ * The CSR's contents are not checked on the hot path (a malformed CSR is
+ * undefined behaviour); gt_validate_csr checks them for tests and debugging.
+ * Non-finite inputs are outside the contract.
+ */
+#ifndef GTATTN_H
+#define GTATTN_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of Q, K, V and out.  bf16 inputs are accumulated in fp32 and
+ * the bf16 output is rounded to nearest-even.  scores/alpha are always fp32. */
+typedef enum { GT_F32 = 0, GT_BF16 = 1 } gt_dtype;
+
+typedef enum { GT_OK = 0, GT_EINVAL = 1, GT_EUNSUPPORTED = 2, GT_ENOMEM = 3, GT_EHIP = 4 } gt_status;
+
+/*
+ * Fused forward: out = SpMM(edge_softmax(SDDMM(Q, K))) in one pass over the
+ * edges; the E x H score and weight arrays never reach memory.  Follows the
+ * SparseMHA forward of "Graph Transformer in a Nutshell" (bsddmm, softmax,
+ * bspmm) and TransLayer.forward of the DGL builtin-operator gist.
+ */
+int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
+                      void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
+
+/*
+ * SDDMM stage: scores[e][h] = <Q[v,h,:], K[u_e,h,:]> / sqrt(D) for every edge
+ * e = (u_e -> v).  The DGL gist's u_dot_v (source key with destination query)
+ * followed by its division by sqrt(d_qkv); the tutorial's bsddmm.
+ */
+int gt_sddmm(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, float* scores, int64_t N,
+             int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
+
+/*
+ * Edge-softmax stage: alpha[e][h] = exp(scores[e][h] - m) / sum exp(scores[e'][h] - m)
+ * over the in-edges e' of e's destination, m their maximum.  The gist's
+ * edge_softmax, normalised per destination; the tutorial's sparse softmax.
+ * alpha may equal scores (in place).
+ */
+int gt_edge_softmax(const int64_t* indptr, const float* scores, float* alpha, int64_t N, int64_t E, int32_t H,
+                    hipStream_t stream);
+
+/*
+ * SpMM stage: out[v,h,:] = sum over in-edges e of v of alpha[e][h] * V[u_e,h,:],
+ * zero for destinations without in-edges.  The gist's u_mul_e_sum; the
+ * tutorial's bspmm.  alpha need not be normalised.
+ */
+int gt_spmm(const int64_t* indptr, const int32_t* indices, const float* alpha, const void* V, void* out, int64_t N,
+            int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
+
+/*
+ * Checks a CSR on the device: indptr[0] == 0, indptr[N] == E, indptr
+ * non-decreasing, every index in [0, N).  Synchronises `stream`.  Returns
+ * GT_OK for a valid graph, GT_EINVAL otherwise (gt_last_error() says what).
+ */
+int gt_validate_csr(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* gt_status_string(int status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* gt_last_error(void);
+
+/*
+ * Tuning and testing knobs, process-wide, read at each call.
+ *  GT_CFG_CHUNK_EDGES  rows with more in-edges than this are split into
+ *                      chunks of this many edges, processed in parallel and
+ *                      merged exactly (default 1024; valid 1 .. 2^30).
+ * gt_config_set returns GT_EINVAL for an unknown key or an invalid value.
+ */
+typedef enum { GT_CFG_CHUNK_EDGES = 0 } gt_config_key;
+int gt_config_set(int32_t key, int64_t value);
+int64_t gt_config_get(int32_t key);
+
+/*
+ * Kernel timing for measurement.  gt_profile_begin(capacity) makes the next
+ * `capacity` calls of gt_sparse_mha_fwd record HIP events, on the stream they
+ * launch on, around their attention kernel and around the whole call.
+ * gt_profile_end waits for those events and returns the summed kernel time,
+ * the summed call time (milliseconds) and the number of calls recorded, then
+ * stops recording.  Not for concurrent use from several threads.
+ */
+int gt_profile_begin(int32_t capacity);
+int gt_profile_end(double* kernel_ms, double* call_ms, int64_t* calls);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GTATTN_H */

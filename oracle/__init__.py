@@ -136,8 +136,10 @@ class Oracle:
         return a
 
     def spmm(self, indptr, indices, alpha, V, nthreads=0):
+        """out [len(indptr)-1][H][D]; V may hold more rows than indptr has (sources index V)."""
         indptr, indices = _csr(indptr, indices)
-        N, H, D = _shape(V)
+        _, H, D = _shape(V)
+        N = len(indptr) - 1
         E = len(indices)
         alpha = np.ascontiguousarray(alpha, dtype=np.float64)
         V = np.ascontiguousarray(V)

@@ -1,0 +1,227 @@
+"""Python binding of libgtattn: sparse multi-head graph attention forward on MI355X.
+
+Argument marshalling only.  Every step of the computation runs in the HIP
+kernels of ``libgtattn.so`` (built from ``csrc/`` for gfx950); PyTorch
+supplies device memory and the current stream.  There is no CPU fallback: if
+the library is missing or the tensors are not on the GPU, calls fail.
+
+The functions have the names of the C entry points declared in
+``include/gtattn.h`` and follow their contracts:
+
+* ``gt_sparse_mha_fwd(indptr, indices, Q, K, V, out=None)`` -- fused forward;
+* ``gt_sddmm(indptr, indices, Q, K, scores=None)`` -- scores [E][H] (fp32);
+* ``gt_edge_softmax(indptr, scores, alpha=None)`` -- alpha [E][H] (fp32);
+* ``gt_spmm(indptr, indices, alpha, V, out=None)`` -- out [N][H][D];
+* ``gt_validate_csr(indptr, indices, N)`` -- device-side CSR check.
+
+Graphs are destination-sorted CSR: ``indptr`` int64 [N+1], ``indices`` int32
+[E] holding the source of each in-edge.  Features are [N][H][D] tensors of
+dtype float32 or bfloat16.
+"""
+import ctypes
+import os
+
+import torch  # loaded first: libgtattn then binds to the HIP runtime torch already holds
+
+from . import _build
+
+GT_F32, GT_BF16 = 0, 1
+GT_OK, GT_EINVAL, GT_EUNSUPPORTED, GT_ENOMEM, GT_EHIP = 0, 1, 2, 3, 4
+GT_CFG_CHUNK_EDGES = 0
+
+EXPORTS = (
+    "gt_sparse_mha_fwd",
+    "gt_sddmm",
+    "gt_edge_softmax",
+    "gt_spmm",
+    "gt_validate_csr",
+    "gt_status_string",
+    "gt_last_error",
+    "gt_config_set",
+    "gt_config_get",
+    "gt_profile_begin",
+    "gt_profile_end",
+)
+
+_lib = None
+_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_i32 = ctypes.c_int32
+
+
+class GtError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s (%d): %s" % (where, lib().gt_status_string(status).decode(), status,
+                                             lib().gt_last_error().decode()))
+
+
+def lib():
+    """The loaded libgtattn.so (compiled on first use if it is not built yet)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_build.LIB):
+            _build.build()
+        L = ctypes.CDLL(_build.LIB)
+        L.gt_sparse_mha_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
+        L.gt_sddmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
+        L.gt_edge_softmax.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
+        L.gt_spmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
+        L.gt_validate_csr.argtypes = [_p, _p, _i64, _i64, _p]
+        L.gt_status_string.restype = ctypes.c_char_p
+        L.gt_status_string.argtypes = [ctypes.c_int]
+        L.gt_last_error.restype = ctypes.c_char_p
+        L.gt_last_error.argtypes = []
+        L.gt_config_set.argtypes = [_i32, _i64]
+        L.gt_config_get.restype = _i64
+        L.gt_config_get.argtypes = [_i32]
+        L.gt_profile_begin.argtypes = [_i32]
+        L.gt_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
+                                     ctypes.POINTER(_i64)]
+        for name in ("gt_sparse_mha_fwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
+                     "gt_config_set", "gt_profile_begin", "gt_profile_end"):
+            getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc, where):
+    if rc != GT_OK:
+        raise GtError(rc, where)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return GT_F32
+    if t.dtype == torch.bfloat16:
+        return GT_BF16
+    raise TypeError("features must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libgtattn works on GPU tensors only; got a %s tensor" % t.device)
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _csr(indptr, indices):
+    if indptr.dtype != torch.int64 or indices.dtype != torch.int32:
+        raise TypeError("indptr must be int64 and indices int32")
+    return indptr.numel() - 1, indices.numel()
+
+
+def gt_sparse_mha_fwd(indptr, indices, Q, K, V, out=None, stream=None):
+    N, E = _csr(indptr, indices)
+    if Q.dim() != 3 or Q.shape[0] != N or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must all be [N][H][D] with N = len(indptr) - 1")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    if out is None:
+        out = torch.empty_like(Q)
+    elif out.shape != Q.shape or out.dtype != Q.dtype:
+        raise ValueError("out must match Q in shape and dtype")
+    _need_gpu(indptr, indices, Q, K, V, out)
+    H, D = Q.shape[1], Q.shape[2]
+    _check(lib().gt_sparse_mha_fwd(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), N, E, H, D,
+                                   _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd")
+    return out
+
+
+def gt_sddmm(indptr, indices, Q, K, scores=None, stream=None):
+    N, E = _csr(indptr, indices)
+    if Q.dim() != 3 or Q.shape[0] != N or K.shape != Q.shape or Q.dtype != K.dtype:
+        raise ValueError("Q and K must both be [N][H][D] of one dtype")
+    H, D = Q.shape[1], Q.shape[2]
+    if scores is None:
+        scores = torch.empty((E, H), dtype=torch.float32, device=Q.device)
+    elif scores.shape != (E, H) or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [E][H]")
+    _need_gpu(indptr, indices, Q, K, scores)
+    _check(lib().gt_sddmm(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(scores), N, E, H, D, _dtype_code(Q),
+                          _stream(stream)), "gt_sddmm")
+    return scores
+
+
+def gt_edge_softmax(indptr, scores, alpha=None, stream=None):
+    if indptr.dtype != torch.int64:
+        raise TypeError("indptr must be int64")
+    N = indptr.numel() - 1
+    if scores.dim() != 2 or scores.dtype != torch.float32:
+        raise ValueError("scores must be float32 [E][H]")
+    E, H = scores.shape
+    if alpha is None:
+        alpha = torch.empty_like(scores)
+    elif alpha.shape != scores.shape or alpha.dtype != torch.float32:
+        raise ValueError("alpha must be float32 [E][H]")
+    _need_gpu(indptr, scores, alpha)
+    _check(lib().gt_edge_softmax(_ptr(indptr), _ptr(scores), _ptr(alpha), N, E, H, _stream(stream)),
+           "gt_edge_softmax")
+    return alpha
+
+
+def gt_spmm(indptr, indices, alpha, V, out=None, stream=None):
+    N, E = _csr(indptr, indices)
+    if V.dim() != 3 or V.shape[0] != N:
+        raise ValueError("V must be [N][H][D] with N = len(indptr) - 1")
+    H, D = V.shape[1], V.shape[2]
+    if alpha.shape != (E, H) or alpha.dtype != torch.float32:
+        raise ValueError("alpha must be float32 [E][H]")
+    if out is None:
+        out = torch.empty_like(V)
+    elif out.shape != V.shape or out.dtype != V.dtype:
+        raise ValueError("out must match V in shape and dtype")
+    _need_gpu(indptr, indices, alpha, V, out)
+    _check(lib().gt_spmm(_ptr(indptr), _ptr(indices), _ptr(alpha), _ptr(V), _ptr(out), N, E, H, D, _dtype_code(V),
+                         _stream(stream)), "gt_spmm")
+    return out
+
+
+def gt_validate_csr(indptr, indices, N=None, stream=None):
+    """True for a valid destination-sorted CSR; False (with the reason in gt_last_error) otherwise."""
+    n, E = _csr(indptr, indices)
+    N = n if N is None else N
+    _need_gpu(indptr, indices)
+    rc = lib().gt_validate_csr(_ptr(indptr), _ptr(indices), N, E, _stream(stream))
+    if rc == GT_EINVAL:
+        return False
+    _check(rc, "gt_validate_csr")
+    return True
+
+
+def gt_config_set(key, value):
+    _check(lib().gt_config_set(key, value), "gt_config_set")
+
+
+def gt_config_get(key):
+    return lib().gt_config_get(key)
+
+
+def gt_profile_begin(capacity):
+    _check(lib().gt_profile_begin(capacity), "gt_profile_begin")
+
+
+def gt_profile_end():
+    """(summed attention-kernel ms, summed whole-call ms, calls recorded)."""
+    k, c, n = ctypes.c_double(), ctypes.c_double(), _i64()
+    _check(lib().gt_profile_end(ctypes.byref(k), ctypes.byref(c), ctypes.byref(n)), "gt_profile_end")
+    return k.value, c.value, n.value
+
+
+def gt_last_error():
+    return lib().gt_last_error().decode()
+
+
+def gt_status_string(status):
+    return lib().gt_status_string(status).decode()

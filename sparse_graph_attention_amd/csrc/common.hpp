@@ -1,0 +1,230 @@
+// common.hpp -- device helpers and the work plan shared by the gfx950 kernels.
+//
+// Work decomposition.  A destination row with at most `chunk` in-edges is one
+// work item, handled by one wavefront.  A heavier row (power-law hubs) is cut
+// into chunks of `chunk` consecutive edges; each chunk is its own item and
+// leaves a partial result in scratch, and a merge kernel combines the chunks
+// of a row in chunk order, so results do not depend on scheduling.  The list
+// of heavy rows and of their chunks is built on the device by the plan kernel
+// (no host synchronisation); kernels are launched over an upper bound of the
+// item count and surplus waves exit at once.  Item ids [0, max_chunks) are
+// chunks, dispatched first so the longest work starts first; item ids
+// [max_chunks, max_chunks + N) are rows.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gt {
+
+constexpr int kWave = 64;
+constexpr int kWavesPerBlock = 4;
+constexpr int kBlock = kWave * kWavesPerBlock;
+
+enum : int { kF32 = 0, kBF16 = 1 };
+
+struct PlanCounters {
+    uint32_t nheavy;   // heavy rows listed
+    uint32_t nchunks;  // chunk items listed
+    uint32_t pad[62];  // keep the following arrays 256-byte aligned
+};
+
+struct HeavyRow {
+    int32_t row;
+    int32_t nch;   // number of chunks
+    int64_t base;  // first chunk item id; the row's chunks are base .. base+nch-1
+};
+
+struct ChunkRef {
+    int32_t row;
+    int32_t idx;    // chunk index within the row
+    int32_t hslot;  // index of the row in the heavy-row list
+    int32_t pad;
+};
+
+// Device view of the scratch buffer of one call.
+struct Plan {
+    PlanCounters* counters;
+    HeavyRow* heavy;     // [max_heavy]
+    ChunkRef* chunks;    // [max_chunks]
+    float* pm;           // [max_chunks][H] running max of a chunk (log2 domain)
+    float* pl;           // [max_chunks][H] sum of exponentials of a chunk
+    float* pacc;         // [max_chunks][H*D] unnormalised weighted sum of a chunk
+    float* hstat;        // [max_heavy][H][2] merged (max, sum) of a heavy row
+    int64_t max_heavy;
+    int64_t max_chunks;
+    int64_t chunk;       // edges per chunk; rows with more edges are split
+};
+
+// What one wavefront works on.
+struct Item {
+    int64_t row;
+    int64_t e0, e1;  // edge range [e0, e1)
+    int64_t slot;    // chunk item id (partial results) or -1 for a whole row
+    int32_t hslot;   // heavy-row index for chunks
+};
+
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)x);
+    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)x >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// The item of the calling wave; false when the wave has nothing to do.
+__device__ __forceinline__ bool resolve_item(const Plan& p, const int64_t* __restrict__ indptr, int64_t N,
+                                             int64_t item, Item& it) {
+    if (item < p.max_chunks) {
+        int64_t n = (int64_t)__atomic_load_n(&p.counters->nchunks, __ATOMIC_RELAXED);
+        if (item >= n) return false;
+        ChunkRef c = p.chunks[item];
+        int64_t b = indptr[c.row], e = indptr[c.row + 1];
+        it.row = c.row;
+        it.e0 = b + (int64_t)c.idx * p.chunk;
+        it.e1 = it.e0 + p.chunk < e ? it.e0 + p.chunk : e;
+        it.slot = item;
+        it.hslot = c.hslot;
+        return true;
+    }
+    int64_t row = item - p.max_chunks;
+    if (row >= N) return false;
+    it.row = row;
+    it.e0 = indptr[row];
+    it.e1 = indptr[row + 1];
+    if (it.e1 - it.e0 > p.chunk) return false;  // heavy: its chunks do the work
+    it.slot = -1;
+    it.hslot = -1;
+    return true;
+}
+
+// ---------------------------------------------------------------- numerics
+
+__device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// exp2(a - b) with exp2(-inf - x) = 0 also when b is -inf
+__device__ __forceinline__ float rescale(float a, float b) { return a == -INFINITY ? 0.0f : exp2_(a - b); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even; NaN stays NaN
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------- cross-lane
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+constexpr int kQuadXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kQuadXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;  // lane i <- lane 7-i within 8
+constexpr int kRowMirror = 0x140;      // lane i <- lane 15-i within 16
+
+// Sum over aligned segments of `seg` lanes (a power of two <= 64); every lane
+// of a segment ends with the same bits (each step adds a commutative pair).
+__device__ __forceinline__ float seg_sum(float x, int seg) {
+    if (seg >= 2) x += dpp<kQuadXor1>(x);
+    if (seg >= 4) x += dpp<kQuadXor2>(x);
+    if (seg >= 8) x += dpp<kRowHalfMirror>(x);
+    if (seg >= 16) x += dpp<kRowMirror>(x);
+    if (seg >= 32) x += __shfl_xor(x, 16, 64);
+    if (seg >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+template <int SEG>
+__device__ __forceinline__ float seg_sum_c(float x) {
+    if constexpr (SEG >= 2) x += dpp<kQuadXor1>(x);
+    if constexpr (SEG >= 4) x += dpp<kQuadXor2>(x);
+    if constexpr (SEG >= 8) x += dpp<kRowHalfMirror>(x);
+    if constexpr (SEG >= 16) x += dpp<kRowMirror>(x);
+    if constexpr (SEG >= 32) x += __shfl_xor(x, 16, 64);
+    if constexpr (SEG >= 64) x += __shfl_xor(x, 32, 64);
+    return x;
+}
+
+// ---------------------------------------------------------------- 16-byte vectors
+
+struct alignas(16) U4 {
+    uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 ld16(const void* p) {
+    const uint4 v = *reinterpret_cast<const uint4*>(p);
+    return U4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ void st16(void* p, U4 v) {
+    *reinterpret_cast<uint4*>(p) = make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Elements held by one lane per 16-byte vector.
+template <int DT>
+struct Vec;
+
+template <>
+struct Vec<kF32> {
+    static constexpr int n = 4;
+    static constexpr int bytes = 4;
+    __device__ static __forceinline__ void unpack(const U4& r, float* f) {
+        f[0] = __uint_as_float(r.x);
+        f[1] = __uint_as_float(r.y);
+        f[2] = __uint_as_float(r.z);
+        f[3] = __uint_as_float(r.w);
+    }
+    __device__ static __forceinline__ U4 pack(const float* f) {
+        return U4{__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]), __float_as_uint(f[3])};
+    }
+    __device__ static __forceinline__ float scalar(const void* base, int64_t i) {
+        return reinterpret_cast<const float*>(base)[i];
+    }
+    __device__ static __forceinline__ void store_scalar(void* base, int64_t i, float f) {
+        reinterpret_cast<float*>(base)[i] = f;
+    }
+};
+
+template <>
+struct Vec<kBF16> {
+    static constexpr int n = 8;
+    static constexpr int bytes = 2;
+    __device__ static __forceinline__ void unpack(const U4& r, float* f) {
+        f[0] = bf16_lo(r.x); f[1] = bf16_hi(r.x);
+        f[2] = bf16_lo(r.y); f[3] = bf16_hi(r.y);
+        f[4] = bf16_lo(r.z); f[5] = bf16_hi(r.z);
+        f[6] = bf16_lo(r.w); f[7] = bf16_hi(r.w);
+    }
+    __device__ static __forceinline__ U4 pack(const float* f) {
+        return U4{bf16_bits(f[0]) | (bf16_bits(f[1]) << 16), bf16_bits(f[2]) | (bf16_bits(f[3]) << 16),
+                  bf16_bits(f[4]) | (bf16_bits(f[5]) << 16), bf16_bits(f[6]) | (bf16_bits(f[7]) << 16)};
+    }
+    __device__ static __forceinline__ float scalar(const void* base, int64_t i) {
+        return __uint_as_float((uint32_t)reinterpret_cast<const uint16_t*>(base)[i] << 16);
+    }
+    __device__ static __forceinline__ void store_scalar(void* base, int64_t i, float f) {
+        reinterpret_cast<uint16_t*>(base)[i] = (uint16_t)bf16_bits(f);
+    }
+};
+
+// ---------------------------------------------------------------- lane layouts
+//
+// Vector layout: a node row of H*D elements is R = H*D*bytes/16 vectors of
+// 16 bytes.  Lanes per head LPH = D*bytes/16 (a power of two), so a vector
+// never straddles two heads.  A group of G lanes (power of two) covers one
+// edge's row in NC vectors per lane, lane j of the group holding vectors
+// c*G + j, c < NC; a wave runs 64/G groups, each on its own edges.
+//
+// Scalar layout (any D, one head per wave): a group of G = pow2ceil(D)
+// lanes (at most 64) covers one head of one edge, lane j holding elements
+// j + k*G, k < KD; a wave runs 64/G groups.
+struct VecShape {
+    int G;     // lanes per edge group
+    int lph;   // lanes per head
+    int R;     // 16-byte vectors per node row
+};
+
+}  // namespace gt

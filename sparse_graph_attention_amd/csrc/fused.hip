@@ -1,0 +1,369 @@
+// fused.hip -- fused sparse multi-head attention forward on gfx950.
+//
+// One wavefront per work item (a destination row, or a chunk of a heavy
+// row).  For every in-edge u->v it gathers the source's K row, forms the
+// per-head score <q_v, k_u>/sqrt(D) with a segmented cross-lane sum, keeps a
+// running maximum m and a running sum l of exp(s - m) per head (rescaling l
+// and the accumulator when m grows), gathers the source's V row and adds
+// p * v to the accumulator.  The E x H scores and weights live only in
+// registers.  At the end out = acc / l, or, for a chunk of a split row, the
+// triple (m, l, acc) goes to scratch for the merge kernel below.
+//
+// The method: "Graph Transformer in a Nutshell", section "Sparse Multi-head
+// Attention" (SDDMM, sparse softmax, SpMM); the DGL builtin-operator gist,
+// TransLayer.forward (u_dot_v, edge_softmax, u_mul_e_sum).  Computing the
+// softmax with a running maximum instead of a separate max pass gives the
+// same weights: exp(s - m_old) * exp(m_old - m_new) = exp(s - m_new).
+//
+// Scores are kept in the log2 domain (q is pre-scaled by log2(e)/sqrt(D)) so
+// each exponential is one v_exp_f32.  Partial maxima in scratch are also in
+// the log2 domain; only this file reads them.
+#include "kernels.hpp"
+
+namespace gt {
+
+// ------------------------------------------------------------ vector layout
+//
+// G_ and LPH_ are compile-time lane-group and lanes-per-head sizes when
+// nonzero, else read from the arguments.  U edges per group are in flight.
+template <int DT, int NC, int U, int G_, int LPH_>
+__global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    it.row = uniform64(it.row);
+    it.e0 = uniform64(it.e0);
+    it.e1 = uniform64(it.e1);
+
+    const int G = G_ ? G_ : a.G;
+    const int lph = LPH_ ? LPH_ : a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+
+    float q[NC][VN];
+    bool act[NC];
+    const char* qrow = (const char*)a.Q + it.row * rowbytes;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int vi = c * G + gl;
+        act[c] = vi < a.R;
+        if (act[c]) {
+            VT::unpack(ld16(qrow + vi * 16), q[c]);
+#pragma unroll
+            for (int k = 0; k < VN; ++k) q[c][k] *= a.qscale;
+        } else {
+#pragma unroll
+            for (int k = 0; k < VN; ++k) q[c][k] = 0.0f;
+        }
+    }
+
+    float m[NC], l[NC], acc[NC][VN];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        m[c] = -INFINITY;
+        l[c] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VN; ++k) acc[c][k] = 0.0f;
+    }
+
+    const char* Kb = (const char*)a.K;
+    const char* Vb = (const char*)a.V;
+    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t ee = e + (int64_t)j * epw;
+            ok[j] = ee < it.e1;
+            u[j] = ok[j] ? a.indices[ee] : 0;
+        }
+        U4 kr[U][NC], vr[U][NC];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+
+        float s[U][NC];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float kf[VN];
+                VT::unpack(kr[j][c], kf);
+                float d = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VN; ++k) d = __builtin_fmaf(q[c][k], kf[k], d);
+                d = LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph);
+                s[j][c] = ok[j] ? d : -INFINITY;
+            }
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            float mb = s[0][c];
+#pragma unroll
+            for (int j = 1; j < U; ++j) mb = fmaxf(mb, s[j][c]);
+            const float mn = fmaxf(m[c], mb);
+            const float sc = rescale(m[c], mn);
+            l[c] *= sc;
+#pragma unroll
+            for (int k = 0; k < VN; ++k) acc[c][k] *= sc;
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                const float p = exp2_(s[j][c] - mn);
+                l[c] += p;
+                float vf[VN];
+                VT::unpack(vr[j][c], vf);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(p, vf[k], acc[c][k]);
+            }
+            m[c] = mn;
+        }
+    }
+
+    // fold the edge groups of the wave together (lanes gl, gl+G, ... hold the same vectors)
+    for (int off = G; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float mo = __shfl_xor(m[c], off, kWave);
+            const float lo = __shfl_xor(l[c], off, kWave);
+            const float mn = fmaxf(m[c], mo);
+            const float sa = rescale(m[c], mn), sb = rescale(mo, mn);
+            l[c] = l[c] * sa + lo * sb;
+#pragma unroll
+            for (int k = 0; k < VN; ++k) {
+                const float ao = __shfl_xor(acc[c][k], off, kWave);
+                acc[c][k] = acc[c][k] * sa + ao * sb;
+            }
+            m[c] = mn;
+        }
+    }
+    if (grp != 0) return;
+
+    if (it.slot < 0) {
+        char* orow = (char*)a.out + it.row * rowbytes;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (!act[c]) continue;
+            const float inv = l[c] > 0.0f ? 1.0f / l[c] : 0.0f;
+            float o[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * inv;
+            st16(orow + (c * G + gl) * 16, VT::pack(o));
+        }
+    } else {
+        const int64_t HD = (int64_t)a.H * a.D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (!act[c]) continue;
+            const int vi = c * G + gl;
+            if ((vi & (lph - 1)) == 0) {
+                const int64_t h = it.slot * a.H + vi / lph;
+                a.plan.pm[h] = m[c];
+                a.plan.pl[h] = l[c];
+            }
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)vi * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
+        }
+    }
+}
+
+// ------------------------------------------------------------ scalar layout
+//
+// One wave per (item, head); a group of G = pow2ceil(D) lanes (<= 64) covers
+// one edge's head, lane j holding elements j + k*G, k < KD.
+template <int DT, int KD, int U>
+__global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y;
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    it.row = uniform64(it.row);
+    it.e0 = uniform64(it.e0);
+    it.e1 = uniform64(it.e1);
+
+    const int G = a.G, D = a.D;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t HD = (int64_t)a.H * D;
+    const int64_t hoff = (int64_t)h * D;
+
+    float q[KD];
+    bool act[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        const int d = gl + k * G;
+        act[k] = d < D;
+        q[k] = act[k] ? VT::scalar(a.Q, it.row * HD + hoff + d) * a.qscale : 0.0f;
+    }
+    float m = -INFINITY, l = 0.0f, acc[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) acc[k] = 0.0f;
+
+    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t ee = e + (int64_t)j * epw;
+            ok[j] = ee < it.e1;
+            u[j] = ok[j] ? a.indices[ee] : 0;
+        }
+        float kv[U][KD], vv[U][KD];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k)
+                kv[j][k] = (ok[j] && act[k]) ? VT::scalar(a.K, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k)
+                vv[j][k] = (ok[j] && act[k]) ? VT::scalar(a.V, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+        float s[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float d = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KD; ++k) d = __builtin_fmaf(q[k], kv[j][k], d);
+            d = seg_sum(d, G);
+            s[j] = ok[j] ? d : -INFINITY;
+        }
+        float mb = s[0];
+#pragma unroll
+        for (int j = 1; j < U; ++j) mb = fmaxf(mb, s[j]);
+        const float mn = fmaxf(m, mb);
+        const float sc = rescale(m, mn);
+        l *= sc;
+#pragma unroll
+        for (int k = 0; k < KD; ++k) acc[k] *= sc;
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const float p = exp2_(s[j] - mn);
+            l += p;
+#pragma unroll
+            for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(p, vv[j][k], acc[k]);
+        }
+        m = mn;
+    }
+    for (int off = G; off < kWave; off <<= 1) {
+        const float mo = __shfl_xor(m, off, kWave);
+        const float lo = __shfl_xor(l, off, kWave);
+        const float mn = fmaxf(m, mo);
+        const float sa = rescale(m, mn), sb = rescale(mo, mn);
+        l = l * sa + lo * sb;
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            const float ao = __shfl_xor(acc[k], off, kWave);
+            acc[k] = acc[k] * sa + ao * sb;
+        }
+        m = mn;
+    }
+    if (grp != 0) return;
+    if (it.slot < 0) {
+        const float inv = l > 0.0f ? 1.0f / l : 0.0f;
+#pragma unroll
+        for (int k = 0; k < KD; ++k)
+            if (act[k]) VT::store_scalar(a.out, it.row * HD + hoff + gl + k * G, acc[k] * inv);
+    } else {
+        if (gl == 0) {
+            a.plan.pm[it.slot * a.H + h] = m;
+            a.plan.pl[it.slot * a.H + h] = l;
+        }
+#pragma unroll
+        for (int k = 0; k < KD; ++k)
+            if (act[k]) a.plan.pacc[it.slot * HD + hoff + gl + k * G] = acc[k];
+    }
+}
+
+// ------------------------------------------------------------ merge of split rows
+//
+// One wave per heavy row: for each element (h, d) combine the row's chunks
+// in chunk order: M = max m_i, L = sum l_i 2^(m_i - M), A = sum acc_i 2^(m_i - M),
+// out = A / L.  The same associative form of the softmax the running-max loop uses.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
+    const HeavyRow hr = a.plan.heavy[hs];
+    const int64_t HD = (int64_t)a.H * a.D;
+    for (int64_t j = lane; j < HD; j += kWave) {
+        const int h = (int)(j / a.D);
+        float M = -INFINITY;
+        for (int i = 0; i < hr.nch; ++i) M = fmaxf(M, a.plan.pm[(hr.base + i) * a.H + h]);
+        float L = 0.0f, A = 0.0f;
+        for (int i = 0; i < hr.nch; ++i) {
+            const float w = exp2_(a.plan.pm[(hr.base + i) * a.H + h] - M);
+            L = __builtin_fmaf(a.plan.pl[(hr.base + i) * a.H + h], w, L);
+            A = __builtin_fmaf(a.plan.pacc[(hr.base + i) * HD + j], w, A);
+        }
+        VT::store_scalar(a.out, (int64_t)hr.row * HD + j, A / L);
+    }
+}
+
+// ------------------------------------------------------------ launchers
+
+template <int DT>
+static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
+    const dim3 block(kBlock);
+    if (a0.vec) {
+        return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx);
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16)
+                fused_vec_kernel<DT, 2, 4, 64, 16><<<grid, block, 0, s>>>(a);
+            else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4)
+                fused_vec_kernel<DT, 1, 8, 32, 4><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 1)
+                fused_vec_kernel<DT, 1, 8, 0, 0><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 2)
+                fused_vec_kernel<DT, 2, 4, 0, 0><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 3)
+                fused_vec_kernel<DT, 3, 2, 0, 0><<<grid, block, 0, s>>>(a);
+            else
+                fused_vec_kernel<DT, 4, 2, 0, 0><<<grid, block, 0, s>>>(a);
+        });
+    }
+    return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+        const dim3 grid(gx, a.H);
+        switch (a.KD) {
+            case 1: fused_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
+            case 2: fused_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
+            case 3: fused_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
+            default: fused_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+        }
+    });
+}
+
+hipError_t launch_fused(const Args& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (ev0) (void)hipEventRecord(ev0, s);
+    const hipError_t err = a.dtype == kF32 ? launch_fused_dt<kF32>(a, s) : launch_fused_dt<kBF16>(a, s);
+    if (ev1) (void)hipEventRecord(ev1, s);
+    return err;
+}
+
+hipError_t launch_fused_merge(const Args& a, hipStream_t s) {
+    const dim3 block(kBlock);
+    return for_slices(a, a.plan.max_heavy, [&](const Args& as, unsigned gx) {
+        if (a.dtype == kF32)
+            fused_merge_kernel<kF32><<<gx, block, 0, s>>>(as);
+        else
+            fused_merge_kernel<kBF16><<<gx, block, 0, s>>>(as);
+    });
+}
+
+}  // namespace gt

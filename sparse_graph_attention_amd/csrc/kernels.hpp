@@ -1,0 +1,70 @@
+// kernels.hpp -- host-side launchers of the gfx950 kernels (one translation
+// unit per stage) and the argument block they share.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace gt {
+
+struct Args {
+    const int64_t* indptr;
+    const int32_t* indices;
+    const void* Q;
+    const void* K;
+    const void* V;
+    void* out;
+    const float* scores_in;
+    float* scores_out;
+    const float* alpha_in;
+    float* alpha_out;
+    int64_t N, E;
+    int H, D, dtype;
+    float qscale;  // fused: log2(e)/sqrt(D); SDDMM: 1/sqrt(D)
+    Plan plan;
+    // lane layout (chosen on the host)
+    int vec;       // 1: 16-byte vector layout, 0: scalar layout
+    int G;         // lanes per edge group
+    int lph;       // vector layout: lanes per head
+    int R;         // vector layout: 16-byte vectors per node row
+    int NC;        // vector layout: vectors per lane
+    int KD;        // scalar layout: elements per lane
+    // grid
+    int64_t items;      // max_chunks + N
+    int64_t item_base;  // first item of the current launch slice
+};
+
+// Items per launch slice: keeps gridDim.x * blockDim.x below 2^32.
+constexpr int64_t kSliceItems = (int64_t)1 << 24;
+
+// Launches `fn(args_with_item_base, grid_x)` over [0, items) in slices.
+template <typename F>
+inline hipError_t for_slices(Args a, int64_t items, F fn) {
+    for (int64_t b = 0; b < items; b += kSliceItems) {
+        a.item_base = b;
+        const int64_t n = items - b < kSliceItems ? items - b : kSliceItems;
+        fn(a, (unsigned)((n + kWavesPerBlock - 1) / kWavesPerBlock));
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
+    return hipSuccess;
+}
+
+// Plan: clears the counters and lists heavy rows and their chunks.
+hipError_t launch_plan(const Args& a, hipStream_t s);
+// Fused forward over all items, then the merge of split rows.
+hipError_t launch_fused(const Args& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+hipError_t launch_fused_merge(const Args& a, hipStream_t s);
+// Unfused stages.
+hipError_t launch_sddmm(const Args& a, hipStream_t s);
+hipError_t launch_softmax(const Args& a, hipStream_t s);
+hipError_t launch_spmm(const Args& a, hipStream_t s);
+// CSR check: writes error flags into *flags (device memory, cleared first).
+hipError_t launch_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, uint32_t* flags,
+                           hipStream_t s);
+
+inline unsigned blocks_for(int64_t waves) { return (unsigned)((waves + kWavesPerBlock - 1) / kWavesPerBlock); }
+
+}  // namespace gt

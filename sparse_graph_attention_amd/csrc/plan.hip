@@ -1,0 +1,77 @@
+// plan.hip -- device-side work list (heavy rows and their chunks) and the
+// CSR validity check.
+#include "kernels.hpp"
+
+namespace gt {
+
+__global__ void reset_kernel(PlanCounters* c) {
+    if (threadIdx.x == 0) {
+        c->nheavy = 0;
+        c->nchunks = 0;
+    }
+}
+
+// One thread per row.  A row with more than `chunk` in-edges gets a slot in
+// the heavy-row list and a contiguous range of chunk item ids; the chunk
+// table maps each id back to (row, chunk index, heavy slot).  Slot order
+// depends on scheduling, but each chunk's result does not, and the merges
+// read a row's chunks in chunk order, so outputs are deterministic.
+__global__ __launch_bounds__(256) void plan_kernel(const int64_t* __restrict__ indptr, int64_t N, Plan p) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v >= N) return;
+    const int64_t deg = indptr[v + 1] - indptr[v];
+    if (deg <= p.chunk) return;
+    const int64_t nch = (deg + p.chunk - 1) / p.chunk;
+    const uint32_t hs = atomicAdd(&p.counters->nheavy, 1u);
+    const uint32_t base = atomicAdd(&p.counters->nchunks, (uint32_t)nch);
+    // a valid CSR never trips these (the host sizes both tables for it); a
+    // malformed one must not write past them
+    if ((int64_t)hs >= p.max_heavy || (int64_t)base + nch > p.max_chunks) return;
+    p.heavy[hs] = HeavyRow{(int32_t)v, (int32_t)nch, (int64_t)base};
+    for (int64_t i = 0; i < nch; ++i) p.chunks[base + i] = ChunkRef{(int32_t)v, (int32_t)i, (int32_t)hs, 0};
+}
+
+hipError_t launch_plan(const Args& a, hipStream_t s) {
+    reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    plan_kernel<<<(unsigned)((a.N + 255) / 256), 256, 0, s>>>(a.indptr, a.N, a.plan);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------ validation
+enum : uint32_t { kBadFirst = 1, kBadLast = 2, kDecreasing = 4, kIndexRange = 8 };
+
+__global__ void clear_flags_kernel(uint32_t* flags) {
+    if (threadIdx.x == 0) *flags = 0;
+}
+
+__global__ __launch_bounds__(256) void validate_kernel(const int64_t* __restrict__ indptr,
+                                                       const int32_t* __restrict__ indices, int64_t N, int64_t E,
+                                                       uint32_t* flags) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t f = 0;
+    if (t0 == 0) {
+        if (indptr[0] != 0) f |= kBadFirst;
+        if (indptr[N] != E) f |= kBadLast;
+    }
+    for (int64_t v = t0; v < N; v += stride)
+        if (indptr[v + 1] < indptr[v]) f |= kDecreasing;
+    for (int64_t e = t0; e < E; e += stride) {
+        const int32_t u = indices[e];
+        if (u < 0 || (int64_t)u >= N) f |= kIndexRange;
+    }
+    if (f) atomicOr(flags, f);
+}
+
+hipError_t launch_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, uint32_t* flags,
+                           hipStream_t s) {
+    clear_flags_kernel<<<1, 64, 0, s>>>(flags);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    validate_kernel<<<1024, 256, 0, s>>>(indptr, indices, N, E, flags);
+    return hipGetLastError();
+}
+
+}  // namespace gt

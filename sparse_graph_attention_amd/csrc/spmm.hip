@@ -1,0 +1,205 @@
+// spmm.hip -- SpMM stage: out[v,h,:] = sum over in-edges e of v of alpha[e][h] * V[u_e,h,:].
+//
+// "Graph Transformer in a Nutshell", section "Sparse Multi-head Attention"
+// (bspmm of the sparse attention matrix with V); the DGL builtin-operator
+// gist's u_mul_e_sum.  Same lane layouts and work items as the fused kernel.
+// Chunks of heavy rows leave partial sums; the merge adds them in chunk order.
+#include "kernels.hpp"
+
+namespace gt {
+
+template <int DT, int NC, int U>
+__global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    it.row = uniform64(it.row);
+    it.e0 = uniform64(it.e0);
+    it.e1 = uniform64(it.e1);
+
+    const int G = a.G, lph = a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+
+    bool act[NC];
+    int head[NC];
+    float acc[NC][VN];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int vi = c * G + gl;
+        act[c] = vi < a.R;
+        head[c] = act[c] ? vi / lph : 0;
+#pragma unroll
+        for (int k = 0; k < VN; ++k) acc[c][k] = 0.0f;
+    }
+    const char* Vb = (const char*)a.V;
+    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t ee = e + (int64_t)j * epw;
+            ok[j] = ee < it.e1;
+            u[j] = ok[j] ? a.indices[ee] : 0;
+        }
+        U4 vr[U][NC];
+        float al[U][NC];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bool go = ok[j] && act[c];
+                vr[j][c] = go ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                al[j][c] = go ? a.alpha_in[(e + (int64_t)j * epw) * a.H + head[c]] : 0.0f;
+            }
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float vf[VN];
+                VT::unpack(vr[j][c], vf);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(al[j][c], vf[k], acc[c][k]);
+            }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int k = 0; k < VN; ++k) acc[c][k] += __shfl_xor(acc[c][k], off, kWave);
+    if (grp != 0) return;
+    if (it.slot < 0) {
+        char* orow = (char*)a.out + it.row * rowbytes;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (act[c]) st16(orow + (c * G + gl) * 16, VT::pack(acc[c]));
+    } else {
+        const int64_t HD = (int64_t)a.H * a.D;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            if (!act[c]) continue;
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)(c * G + gl) * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
+        }
+    }
+}
+
+template <int DT, int KD, int U>
+__global__ __launch_bounds__(kBlock) void spmm_scalar_kernel(const Args a) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y;
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    it.row = uniform64(it.row);
+    it.e0 = uniform64(it.e0);
+    it.e1 = uniform64(it.e1);
+
+    const int G = a.G, D = a.D;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t HD = (int64_t)a.H * D;
+    const int64_t hoff = (int64_t)h * D;
+    bool act[KD];
+    float acc[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        act[k] = gl + k * G < D;
+        acc[k] = 0.0f;
+    }
+    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+        float al[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const int64_t ee = e + (int64_t)j * epw;
+            ok[j] = ee < it.e1;
+            u[j] = ok[j] ? a.indices[ee] : 0;
+            al[j] = ok[j] ? a.alpha_in[ee * a.H + h] : 0.0f;
+        }
+        float vv[U][KD];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k)
+                vv[j][k] = (ok[j] && act[k]) ? VT::scalar(a.V, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(al[j], vv[j][k], acc[k]);
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < KD; ++k) acc[k] += __shfl_xor(acc[k], off, kWave);
+    if (grp != 0) return;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        if (!act[k]) continue;
+        if (it.slot < 0)
+            VT::store_scalar(a.out, it.row * HD + hoff + gl + k * G, acc[k]);
+        else
+            a.plan.pacc[it.slot * HD + hoff + gl + k * G] = acc[k];
+    }
+}
+
+// One wave per heavy row: out = sum of the chunks' partial sums, in chunk order.
+template <int DT>
+__global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const Args a) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
+    const HeavyRow hr = a.plan.heavy[hs];
+    const int64_t HD = (int64_t)a.H * a.D;
+    for (int64_t j = lane; j < HD; j += kWave) {
+        float A = 0.0f;
+        for (int i = 0; i < hr.nch; ++i) A += a.plan.pacc[(hr.base + i) * HD + j];
+        VT::store_scalar(a.out, (int64_t)hr.row * HD + j, A);
+    }
+}
+
+template <int DT>
+static hipError_t launch_spmm_dt(const Args& a0, hipStream_t s) {
+    const dim3 block(kBlock);
+    hipError_t err;
+    if (a0.vec) {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx);
+            switch (a.NC) {
+                case 1: spmm_vec_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
+                case 2: spmm_vec_kernel<DT, 2, 4><<<grid, block, 0, s>>>(a); break;
+                case 3: spmm_vec_kernel<DT, 3, 2><<<grid, block, 0, s>>>(a); break;
+                default: spmm_vec_kernel<DT, 4, 2><<<grid, block, 0, s>>>(a); break;
+            }
+        });
+    } else {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx, a.H);
+            switch (a.KD) {
+                case 1: spmm_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
+                case 2: spmm_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
+                case 3: spmm_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
+                default: spmm_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+            }
+        });
+    }
+    if (err != hipSuccess || a0.plan.max_heavy == 0) return err;
+    return for_slices(a0, a0.plan.max_heavy, [&](const Args& a, unsigned gx) {
+        spmm_merge_kernel<DT><<<gx, block, 0, s>>>(a);
+    });
+}
+
+hipError_t launch_spmm(const Args& a, hipStream_t s) {
+    return a.dtype == kF32 ? launch_spmm_dt<kF32>(a, s) : launch_spmm_dt<kBF16>(a, s);
+}
+
+}  // namespace gt

@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports what include/gtattn.h declares, and rejects
+bad arguments before touching the GPU (CPU only: no compute call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_graph_attention_amd as gt
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "gtattn.h")
+
+NULL = None
+S = None  # null stream; never reached by these calls
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gt_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_exports_agree():
+    names = declared_functions()
+    assert set(names) == set(gt.EXPORTS), names
+    L = gt.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_library_is_the_in_tree_build():
+    assert os.path.dirname(gt._build.LIB) == os.path.dirname(os.path.abspath(gt.__file__))
+    assert os.path.exists(gt._build.LIB)
+
+
+def test_status_strings():
+    assert gt.gt_status_string(0) == "ok"
+    assert "invalid" in gt.gt_status_string(1)
+    assert "unsupported" in gt.gt_status_string(2)
+    assert gt.gt_status_string(99) == "unknown status"
+
+
+def fwd(N=4, E=4, H=8, D=64, dtype=0, ptr=1):
+    p = ctypes.c_void_p(ptr) if ptr else None
+    return gt.lib().gt_sparse_mha_fwd(p, p, p, p, p, p, N, E, H, D, dtype, S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=-1), gt.GT_EINVAL),
+    (dict(E=-1), gt.GT_EINVAL),
+    (dict(H=0), gt.GT_EINVAL),
+    (dict(D=0), gt.GT_EINVAL),
+    (dict(N=1 << 31), gt.GT_EINVAL),
+    (dict(ptr=0), gt.GT_EINVAL),
+    (dict(dtype=7), gt.GT_EUNSUPPORTED),
+    (dict(H=65), gt.GT_EUNSUPPORTED),
+    (dict(D=257), gt.GT_EUNSUPPORTED),
+])
+def test_fused_rejects(kw, status):
+    assert fwd(**kw) == status
+    assert gt.gt_last_error() != ""
+
+
+def test_zero_nodes_is_a_noop():
+    assert fwd(N=0, E=0, ptr=0) == gt.GT_OK
+
+
+def test_unfused_reject():
+    L = gt.lib()
+    p = ctypes.c_void_p(1)
+    assert L.gt_sddmm(None, p, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_EINVAL
+    assert L.gt_sddmm(p, p, p, p, p, 4, 4, 8, 300, 0, S) == gt.GT_EUNSUPPORTED
+    assert L.gt_edge_softmax(p, None, p, 4, 4, 8, S) == gt.GT_EINVAL
+    assert L.gt_edge_softmax(p, p, p, 4, 4, 0, S) == gt.GT_EINVAL
+    assert L.gt_spmm(p, None, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_EINVAL
+    assert L.gt_spmm(p, p, p, p, p, 4, 4, 8, 64, 5, S) == gt.GT_EUNSUPPORTED
+    assert L.gt_validate_csr(None, p, 4, 4, S) == gt.GT_EINVAL
+    assert L.gt_validate_csr(p, p, -1, 4, S) == gt.GT_EINVAL
+    # nothing to do: zero edges for the unfused stages that only touch edges
+    assert L.gt_sddmm(p, p, p, p, p, 4, 0, 8, 64, 0, S) == gt.GT_OK
+    assert L.gt_edge_softmax(p, p, p, 4, 0, 8, S) == gt.GT_OK
+
+
+def test_config():
+    old = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    assert old == 1024
+    try:
+        gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 7)
+        assert gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES) == 7
+        with pytest.raises(gt.GtError):
+            gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 0)
+        with pytest.raises(gt.GtError):
+            gt.gt_config_set(99, 5)
+        assert gt.gt_config_get(99) == -1
+    finally:
+        gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, old)
+    assert gt.lib().gt_profile_begin(0) == gt.GT_EINVAL
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    indptr = torch.zeros(2, dtype=torch.int64)
+    indices = torch.zeros(0, dtype=torch.int32)
+    Q = torch.zeros(1, 8, 64)
+    with pytest.raises(ValueError):
+        gt.gt_sparse_mha_fwd(indptr, indices, Q, Q, Q)
