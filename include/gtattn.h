@@ -134,7 +134,7 @@ const char* gt_last_error(void);
  * Tuning and testing knobs, process-wide, read at each call.
  *  GT_CFG_CHUNK_EDGES  rows with more in-edges than this are split into
  *                      chunks of this many edges, processed in parallel and
- *                      merged exactly (default 1024; valid 1 .. 2^30).
+ *                      merged exactly (default 512; valid 1 .. 2^30).
  * gt_config_set returns GT_EINVAL for an unknown key or an invalid value.
  */
 typedef enum { GT_CFG_CHUNK_EDGES = 0 } gt_config_key;

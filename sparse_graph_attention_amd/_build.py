@@ -25,9 +25,9 @@ FLAGS = [
 ]
 
 
-def _compile(src, verbose):
-    obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src, verbose, objdir, extra):
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -36,22 +36,23 @@ def _compile(src, verbose):
     return obj, r.stderr
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OBJDIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, extra_flags=(), objdir: str = OBJDIR) -> str:
+    """Compile every source; extra_flags (e.g. -DGT_F32_D64_U=8) build a tuning variant at `out`."""
+    os.makedirs(objdir, exist_ok=True)
     with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        results = list(ex.map(lambda s: _compile(s, verbose, objdir, list(extra_flags)), SOURCES))
     if verbose:
         for _, err in results:
             lines = [l for l in err.splitlines() if "packed-fp32-ops" not in l and l.strip()]
             if lines:
                 print("\n".join(lines))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

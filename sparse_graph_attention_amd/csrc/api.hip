@@ -19,7 +19,7 @@ using namespace gt;
 namespace {
 
 thread_local std::string g_err;
-std::atomic<int64_t> g_chunk{1024};
+std::atomic<int64_t> g_chunk{512};
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -85,13 +85,8 @@ int make_plan(const int64_t* indptr, int64_t N, int64_t E, int H, int D, hipStre
     if (p.max_chunks >= ((int64_t)1 << 31))
         return fail(GT_EUNSUPPORTED, "too many chunks (%lld); raise GT_CFG_CHUNK_EDGES", (long long)p.max_chunks);
     a.items = p.max_chunks + N;
-    if (p.max_heavy == 0) {
-        p.counters = nullptr;
-        p.heavy = nullptr;
-        p.chunks = nullptr;
-        p.pm = p.pl = p.pacc = p.hstat = nullptr;
-        return GT_OK;
-    }
+    // with max_heavy == 0 only the (unused) counters are carved out and no
+    // plan kernel runs: every row is a single item
     const size_t HD = (size_t)H * D;
     size_t off = 0;
     const size_t o_cnt = off;   off += align256(sizeof(PlanCounters));

@@ -15,18 +15,29 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Build-time tuning knobs (defaults are the measured best on MI355X).
+#ifndef GT_WAVES_PER_BLOCK
+#define GT_WAVES_PER_BLOCK 4
+#endif
+#ifndef GT_F32_D64_U
+#define GT_F32_D64_U 4  // edges in flight per wave, fp32 rows of 8 heads x 64
+#endif
+#ifndef GT_BF16_D32_U
+#define GT_BF16_D32_U 8  // edges in flight per half-wave, bf16 rows of 8 heads x 32
+#endif
+
 namespace gt {
 
 constexpr int kWave = 64;
-constexpr int kWavesPerBlock = 4;
+constexpr int kWavesPerBlock = GT_WAVES_PER_BLOCK;
 constexpr int kBlock = kWave * kWavesPerBlock;
 
 enum : int { kF32 = 0, kBF16 = 1 };
 
 struct PlanCounters {
-    uint32_t nheavy;   // heavy rows listed
-    uint32_t nchunks;  // chunk items listed
-    uint32_t pad[62];  // keep the following arrays 256-byte aligned
+    uint32_t nheavy;     // heavy rows listed
+    uint32_t nchunks;    // chunk items listed
+    uint32_t pad[62];    // keep the following arrays 256-byte aligned
 };
 
 struct HeavyRow {
@@ -74,7 +85,7 @@ __device__ __forceinline__ int64_t uniform64(int64_t x) {
 __device__ __forceinline__ bool resolve_item(const Plan& p, const int64_t* __restrict__ indptr, int64_t N,
                                              int64_t item, Item& it) {
     if (item < p.max_chunks) {
-        int64_t n = (int64_t)__atomic_load_n(&p.counters->nchunks, __ATOMIC_RELAXED);
+        const int64_t n = (int64_t)p.counters->nchunks;  // written by the plan kernel, an earlier launch
         if (item >= n) return false;
         ChunkRef c = p.chunks[item];
         int64_t b = indptr[c.row], e = indptr[c.row + 1];
@@ -161,6 +172,19 @@ __device__ __forceinline__ U4 ld16(const void* p) {
 
 __device__ __forceinline__ void st16(void* p, U4 v) {
     *reinterpret_cast<uint4*>(p) = make_uint4(v.x, v.y, v.z, v.w);
+}
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Streaming variants: the non-temporal hint marks data that will not be reused soon.
+__device__ __forceinline__ U4 ld16_nt(const void* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return U4{v.x, v.y, v.z, v.w};
+}
+
+__device__ __forceinline__ void st16_nt(void* p, U4 v) {
+    u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
 
 // Elements held by one lane per 16-byte vector.

@@ -15,18 +15,39 @@
 // softmax with a running maximum instead of a separate max pass gives the
 // same weights: exp(s - m_old) * exp(m_old - m_new) = exp(s - m_new).
 //
-// Scores are kept in the log2 domain (q is pre-scaled by log2(e)/sqrt(D)) so
-// each exponential is one v_exp_f32.  Partial maxima in scratch are also in
-// the log2 domain; only this file reads them.
+// Scores are kept in the log2 domain (each reduced dot product is scaled by
+// log2(e)/sqrt(D)) so each exponential is one v_exp_f32.  Partial maxima in
+// scratch are also in the log2 domain; only this file reads them.
+//
+// Memory-level parallelism: each batch of U edges per group issues all its K
+// and V gathers at once, and the source ids of the next batch are loaded
+// right behind them (unconditional, clamped loads; scalar loads when one
+// group spans the wave), so no gather waits on an index load.  Output rows
+// are written with the non-temporal hint (never re-read); the fp32 8x64
+// instance also gathers K/V that way (measured faster there, slower for the
+// 512-byte bf16 rows).
 #include "kernels.hpp"
 
 namespace gt {
 
+// Source ids of the U edges a group takes from the batch starting at eb:
+// edges eb + grp + j*epw, clamped into the item so that every load is valid.
+template <int U>
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int64_t eb, int grp, int epw, int64_t e1,
+                                         int32_t (&u)[U]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int64_t ee = eb + grp + (int64_t)j * epw;
+        u[j] = idx[ee < e1 ? ee : e1 - 1];
+    }
+}
+
 // ------------------------------------------------------------ vector layout
 //
 // G_ and LPH_ are compile-time lane-group and lanes-per-head sizes when
-// nonzero, else read from the arguments.  U edges per group are in flight.
-template <int DT, int NC, int U, int G_, int LPH_>
+// nonzero, else read from the arguments.  FULL: the row is exactly NC*G
+// vectors (no idle lanes).  U edges per group are in flight.
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool NTL>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -34,9 +55,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Item it;
     if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
-    it.row = uniform64(it.row);
-    it.e0 = uniform64(it.e0);
-    it.e1 = uniform64(it.e1);
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
 
     const int G = G_ ? G_ : a.G;
     const int lph = LPH_ ? LPH_ : a.lph;
@@ -44,22 +63,22 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     const int grp = lane / G;
     const int gl = lane & (G - 1);
     const int64_t rowbytes = (int64_t)a.R * 16;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
 
     float q[NC][VN];
     bool act[NC];
-    const char* qrow = (const char*)a.Q + it.row * rowbytes;
+    const char* qrow = (const char*)a.Q + row * rowbytes;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = vi < a.R;
-        if (act[c]) {
-            VT::unpack(ld16(qrow + vi * 16), q[c]);
-#pragma unroll
-            for (int k = 0; k < VN; ++k) q[c][k] *= a.qscale;
-        } else {
-#pragma unroll
-            for (int k = 0; k < VN; ++k) q[c][k] = 0.0f;
-        }
+        act[c] = FULL || vi < a.R;
+        // unscaled: the scale goes on the reduced score, so nothing waits for Q
+        // before the first gathers are issued
+        const U4 r = act[c] ? ld16(qrow + vi * 16) : U4{0, 0, 0, 0};
+        VT::unpack(r, q[c]);
     }
 
     float m[NC], l[NC], acc[NC][VN];
@@ -73,26 +92,27 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 
     const char* Kb = (const char*)a.K;
     const char* Vb = (const char*)a.V;
-    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
         int32_t u[U];
         bool ok[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int64_t ee = e + (int64_t)j * epw;
-            ok[j] = ee < it.e1;
-            u[j] = ok[j] ? a.indices[ee] : 0;
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
         U4 kr[U][NC], vr[U][NC];
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
 
         float s[U][NC];
 #pragma unroll
@@ -104,7 +124,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 float d = 0.0f;
 #pragma unroll
                 for (int k = 0; k < VN; ++k) d = __builtin_fmaf(q[c][k], kf[k], d);
-                d = LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph);
+                d = (LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph)) * a.qscale;
                 s[j][c] = ok[j] ? d : -INFINITY;
             }
 #pragma unroll
@@ -119,7 +139,8 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
             for (int k = 0; k < VN; ++k) acc[c][k] *= sc;
 #pragma unroll
             for (int j = 0; j < U; ++j) {
-                const float p = exp2_(s[j][c] - mn);
+                // a group with no edge left in this batch has mn = -inf: keep p at 0
+                const float p = ok[j] ? exp2_(s[j][c] - mn) : 0.0f;
                 l[c] += p;
                 float vf[VN];
                 VT::unpack(vr[j][c], vf);
@@ -150,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     if (grp != 0) return;
 
     if (it.slot < 0) {
-        char* orow = (char*)a.out + it.row * rowbytes;
+        char* orow = (char*)a.out + row * rowbytes;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             if (!act[c]) continue;
@@ -158,7 +179,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
             float o[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * inv;
-            st16(orow + (c * G + gl) * 16, VT::pack(o));
+            st16_nt(orow + (c * G + gl) * 16, VT::pack(o));
         }
     } else {
         const int64_t HD = (int64_t)a.H * a.D;
@@ -190,9 +211,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
     const int h = blockIdx.y;
     Item it;
     if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
-    it.row = uniform64(it.row);
-    it.e0 = uniform64(it.e0);
-    it.e1 = uniform64(it.e1);
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
 
     const int G = a.G, D = a.D;
     const int epw = kWave / G;
@@ -200,6 +219,10 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
     const int gl = lane & (G - 1);
     const int64_t HD = (int64_t)a.H * D;
     const int64_t hoff = (int64_t)h * D;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
 
     float q[KD];
     bool act[KD];
@@ -207,20 +230,19 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
     for (int k = 0; k < KD; ++k) {
         const int d = gl + k * G;
         act[k] = d < D;
-        q[k] = act[k] ? VT::scalar(a.Q, it.row * HD + hoff + d) * a.qscale : 0.0f;
+        q[k] = act[k] ? VT::scalar(a.Q, row * HD + hoff + d) : 0.0f;
     }
     float m = -INFINITY, l = 0.0f, acc[KD];
 #pragma unroll
     for (int k = 0; k < KD; ++k) acc[k] = 0.0f;
 
-    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
         int32_t u[U];
         bool ok[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int64_t ee = e + (int64_t)j * epw;
-            ok[j] = ee < it.e1;
-            u[j] = ok[j] ? a.indices[ee] : 0;
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
         float kv[U][KD], vv[U][KD];
 #pragma unroll
@@ -233,13 +255,15 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
 #pragma unroll
             for (int k = 0; k < KD; ++k)
                 vv[j][k] = (ok[j] && act[k]) ? VT::scalar(a.V, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
         float s[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             float d = 0.0f;
 #pragma unroll
             for (int k = 0; k < KD; ++k) d = __builtin_fmaf(q[k], kv[j][k], d);
-            d = seg_sum(d, G);
+            d = seg_sum(d, G) * a.qscale;
             s[j] = ok[j] ? d : -INFINITY;
         }
         float mb = s[0];
@@ -252,7 +276,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
         for (int k = 0; k < KD; ++k) acc[k] *= sc;
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const float p = exp2_(s[j] - mn);
+            const float p = ok[j] ? exp2_(s[j] - mn) : 0.0f;
             l += p;
 #pragma unroll
             for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(p, vv[j][k], acc[k]);
@@ -277,7 +301,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
         const float inv = l > 0.0f ? 1.0f / l : 0.0f;
 #pragma unroll
         for (int k = 0; k < KD; ++k)
-            if (act[k]) VT::store_scalar(a.out, it.row * HD + hoff + gl + k * G, acc[k] * inv);
+            if (act[k]) VT::store_scalar(a.out, row * HD + hoff + gl + k * G, acc[k] * inv);
     } else {
         if (gl == 0) {
             a.plan.pm[it.slot * a.H + h] = m;
@@ -291,28 +315,70 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
 
 // ------------------------------------------------------------ merge of split rows
 //
-// One wave per heavy row: for each element (h, d) combine the row's chunks
-// in chunk order: M = max m_i, L = sum l_i 2^(m_i - M), A = sum acc_i 2^(m_i - M),
-// out = A / L.  The same associative form of the softmax the running-max loop uses.
-template <int DT>
+// One wave per heavy row; for each head the row's chunks are combined as
+// M = max m_i, L = sum l_i 2^(m_i - M), A = sum acc_i 2^(m_i - M), out = A / L:
+// the associative form of the softmax that the running-max loop also uses.
+// Lanes run over chunks for (M, L) and over the head's D elements for A,
+// which is summed in chunk order.
+__device__ __forceinline__ float wave_max(float x) {
+    for (int off = 1; off < kWave; off <<= 1) x = fmaxf(x, __shfl_xor(x, off, kWave));
+    return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+    for (int off = 1; off < kWave; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// One wave per (heavy row, head h = blockIdx.y).  The chunk loop is unrolled
+// so that eight partial rows are in flight per lane.
+template <int DT, int T>
 __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
     using VT = Vec<DT>;
+    constexpr int UN = 8;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y;
     if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
     const HeavyRow hr = a.plan.heavy[hs];
-    const int64_t HD = (int64_t)a.H * a.D;
-    for (int64_t j = lane; j < HD; j += kWave) {
-        const int h = (int)(j / a.D);
-        float M = -INFINITY;
-        for (int i = 0; i < hr.nch; ++i) M = fmaxf(M, a.plan.pm[(hr.base + i) * a.H + h]);
-        float L = 0.0f, A = 0.0f;
-        for (int i = 0; i < hr.nch; ++i) {
-            const float w = exp2_(a.plan.pm[(hr.base + i) * a.H + h] - M);
-            L = __builtin_fmaf(a.plan.pl[(hr.base + i) * a.H + h], w, L);
-            A = __builtin_fmaf(a.plan.pacc[(hr.base + i) * HD + j], w, A);
+    const int H = a.H, D = a.D, nch = hr.nch;
+    const int64_t HD = (int64_t)H * D;
+    const float* pm = a.plan.pm + hr.base * H + h;
+    const float* pl = a.plan.pl + hr.base * H + h;
+    const float* pa = a.plan.pacc + hr.base * HD + (int64_t)h * D;
+    float M = -INFINITY;
+    for (int i = lane; i < nch; i += kWave) M = fmaxf(M, pm[(int64_t)i * H]);
+    M = wave_max(M);
+    float L = 0.0f;
+    for (int i = lane; i < nch; i += kWave) L += pl[(int64_t)i * H] * exp2_(pm[(int64_t)i * H] - M);
+    L = wave_sum(L);
+    float A[T];  // D <= 64 * T elements, lane holds d = lane + 64 t
+#pragma unroll
+    for (int t = 0; t < T; ++t) A[t] = 0.0f;
+    for (int ib = 0; ib < nch; ib += kWave) {
+        const int i = ib + lane;
+        const float wl = i < nch ? exp2_(pm[(int64_t)i * H] - M) : 0.0f;
+        const int nb = nch - ib < kWave ? nch - ib : kWave;
+        for (int k0 = 0; k0 < nb; k0 += UN) {
+            float v[UN][T];
+#pragma unroll
+            for (int k = 0; k < UN; ++k)
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int d = lane + t * kWave;
+                    v[k][t] = (k0 + k < nb && d < D) ? pa[(int64_t)(ib + k0 + k) * HD + d] : 0.0f;
+                }
+#pragma unroll
+            for (int k = 0; k < UN; ++k) {
+                const float w = __shfl(wl, (k0 + k) & (kWave - 1), kWave);
+#pragma unroll
+                for (int t = 0; t < T; ++t) A[t] = __builtin_fmaf(v[k][t], w, A[t]);
+            }
         }
-        VT::store_scalar(a.out, (int64_t)hr.row * HD + j, A / L);
+    }
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+        const int d = lane + t * kWave;
+        if (d < D) VT::store_scalar(a.out, (int64_t)hr.row * HD + (int64_t)h * D + d, A[t] / L);
     }
 }
 
@@ -324,18 +390,19 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     if (a0.vec) {
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
-            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16)
-                fused_vec_kernel<DT, 2, 4, 64, 16><<<grid, block, 0, s>>>(a);
-            else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4)
-                fused_vec_kernel<DT, 1, 8, 32, 4><<<grid, block, 0, s>>>(a);
+            const bool full = a.R == a.NC * a.G;
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
+                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, true><<<grid, block, 0, s>>>(a);
+            else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
+                fused_vec_kernel<DT, 1, GT_BF16_D32_U, 32, 4, true, false><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
-                fused_vec_kernel<DT, 1, 8, 0, 0><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 1, 8, 0, 0, false, false><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
-                fused_vec_kernel<DT, 2, 4, 0, 0><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, 4, 0, 0, false, false><<<grid, block, 0, s>>>(a);
             else if (a.NC == 3)
-                fused_vec_kernel<DT, 3, 2, 0, 0><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 3, 2, 0, 0, false, false><<<grid, block, 0, s>>>(a);
             else
-                fused_vec_kernel<DT, 4, 2, 0, 0><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 4, 2, 0, 0, false, false><<<grid, block, 0, s>>>(a);
         });
     }
     return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
@@ -359,10 +426,15 @@ hipError_t launch_fused(const Args& a, hipStream_t s, hipEvent_t ev0, hipEvent_t
 hipError_t launch_fused_merge(const Args& a, hipStream_t s) {
     const dim3 block(kBlock);
     return for_slices(a, a.plan.max_heavy, [&](const Args& as, unsigned gx) {
-        if (a.dtype == kF32)
-            fused_merge_kernel<kF32><<<gx, block, 0, s>>>(as);
-        else
-            fused_merge_kernel<kBF16><<<gx, block, 0, s>>>(as);
+        const dim3 grid(gx, a.H);
+        const int T = (a.D + kWave - 1) / kWave;
+        if (a.dtype == kF32) {
+            if (T == 1) fused_merge_kernel<kF32, 1><<<grid, block, 0, s>>>(as);
+            else fused_merge_kernel<kF32, 4><<<grid, block, 0, s>>>(as);
+        } else {
+            if (T == 1) fused_merge_kernel<kBF16, 1><<<grid, block, 0, s>>>(as);
+            else fused_merge_kernel<kBF16, 4><<<grid, block, 0, s>>>(as);
+        }
     });
 }
 

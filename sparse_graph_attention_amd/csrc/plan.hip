@@ -16,14 +16,34 @@ __global__ void reset_kernel(PlanCounters* c) {
 // table maps each id back to (row, chunk index, heavy slot).  Slot order
 // depends on scheduling, but each chunk's result does not, and the merges
 // read a row's chunks in chunk order, so outputs are deterministic.
+// The wave adds up its heavy rows and chunks with a prefix scan and takes
+// its ranges with one atomic per counter (64x fewer atomics on two hot words).
 __global__ __launch_bounds__(256) void plan_kernel(const int64_t* __restrict__ indptr, int64_t N, Plan p) {
     const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (v >= N) return;
-    const int64_t deg = indptr[v + 1] - indptr[v];
-    if (deg <= p.chunk) return;
-    const int64_t nch = (deg + p.chunk - 1) / p.chunk;
-    const uint32_t hs = atomicAdd(&p.counters->nheavy, 1u);
-    const uint32_t base = atomicAdd(&p.counters->nchunks, (uint32_t)nch);
+    const int lane = threadIdx.x & 63;
+    const int64_t deg = v < N ? indptr[v + 1] - indptr[v] : 0;
+    const bool heavy = deg > p.chunk;
+    const int64_t nch = heavy ? (deg + p.chunk - 1) / p.chunk : 0;
+    uint32_t hin = heavy ? 1u : 0u, cin = (uint32_t)nch;  // inclusive prefix sums over the wave
+    for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t h = __shfl_up(hin, off, 64), c = __shfl_up(cin, off, 64);
+        if (lane >= off) {
+            hin += h;
+            cin += c;
+        }
+    }
+    const uint32_t htot = __shfl(hin, 63, 64), ctot = __shfl(cin, 63, 64);
+    if (htot == 0) return;
+    uint32_t hb = 0, cb = 0;
+    if (lane == 0) {
+        hb = atomicAdd(&p.counters->nheavy, htot);
+        cb = atomicAdd(&p.counters->nchunks, ctot);
+    }
+    hb = __shfl(hb, 0, 64);
+    cb = __shfl(cb, 0, 64);
+    if (!heavy) return;
+    const uint32_t hs = hb + hin - 1;
+    const uint32_t base = cb + cin - (uint32_t)nch;
     // a valid CSR never trips these (the host sizes both tables for it); a
     // malformed one must not write past them
     if ((int64_t)hs >= p.max_heavy || (int64_t)base + nch > p.max_chunks) return;
@@ -32,6 +52,7 @@ __global__ __launch_bounds__(256) void plan_kernel(const int64_t* __restrict__ i
 }
 
 hipError_t launch_plan(const Args& a, hipStream_t s) {
+    if (a.plan.max_heavy == 0) return hipSuccess;  // no row can be split: nothing to list
     reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -83,7 +83,7 @@ def test_unfused_reject():
 
 def test_config():
     old = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
-    assert old == 1024
+    assert old == 512
     try:
         gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 7)
         assert gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES) == 7
