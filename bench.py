@@ -13,7 +13,7 @@ matches the current kernel source), and the CPU oracle timed on a bounded
 sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--calib-copy]
+                  [--no-cpu-baseline] [--no-stages] [--calib-copy]
 """
 import argparse
 import hashlib
@@ -79,6 +79,52 @@ def algorithmic_bytes(w):
     return nnz * HD * b + 2 * w["E"] * HD * b + w["N"] * HD * b + 4 * w["E"] + 8 * (w["N"] + 1)
 
 
+def stage_bytes(w):
+    """Algorithmic bytes of the unfused stages (scores and weights are fp32 [E][H])."""
+    import numpy as np
+
+    b = 4 if w["dtype"] == 0 else 2
+    N, E, H, HD = w["N"], w["E"], w["H"], w["H"] * w["D"]
+    nnz = int((np.diff(w["indptr"]) > 0).sum())
+    csr = 4 * E + 8 * (N + 1)
+    return {
+        "sddmm": nnz * HD * b + E * HD * b + E * H * 4 + csr,
+        "edge_softmax": 2 * E * H * 4 + 8 * (N + 1),
+        "spmm": E * H * 4 + E * HD * b + N * HD * b + csr,
+    }
+
+
+def time_stages(gt, t, w, steps, warmup):
+    """Event-timed unfused stages on the same inputs: ms per call and algorithmic GB/s."""
+    import torch
+
+    scores = torch.empty((w["E"], w["H"]), dtype=torch.float32, device=t["Q"].device)
+    alpha = torch.empty_like(scores)
+    out = torch.empty_like(t["Q"])
+    calls = {
+        "sddmm": lambda: gt.gt_sddmm(t["indptr"], t["indices"], t["Q"], t["K"], scores=scores),
+        "edge_softmax": lambda: gt.gt_edge_softmax(t["indptr"], scores, alpha=alpha),
+        "spmm": lambda: gt.gt_spmm(t["indptr"], t["indices"], alpha, t["V"], out=out),
+    }
+    nbytes = stage_bytes(w)
+    res = {}
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = {"ms": ms, "algorithmic_bytes": nbytes[name], "GBps": nbytes[name] / (ms * 1e-3) / 1e9}
+        log("stage %s: %.3f ms, %.0f GB/s algorithmic" % (name, ms, res[name]["GBps"]))
+    del scores, alpha, out
+    return res
+
+
 def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     """The oracle as it stands on a fixed random sample of destination rows."""
     import numpy as np
@@ -128,6 +174,7 @@ def main():
     ap.add_argument("--workload", default="powerlaw", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--no-stages", action="store_true", help="skip timing the unfused stages")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -209,10 +256,13 @@ def main():
             "algorithmic_bytes": alg,
         },
         "cpu_baseline": None,
+        "stages": None,
     }
+    out_host = out.float().cpu().numpy() if out.dtype == torch.bfloat16 else out.cpu().numpy()
+    if not args.no_stages:
+        line["stages"] = time_stages(gt, t, w, max(3, args.steps // 2), 2)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, out.float().cpu().numpy() if out.dtype == torch.bfloat16
-                                            else out.cpu().numpy())
+        line["cpu_baseline"] = cpu_baseline(w, out_host)
     print(json.dumps(line), flush=True)
 
 

@@ -107,6 +107,20 @@ __device__ __forceinline__ bool resolve_item(const Plan& p, const int64_t* __res
     return true;
 }
 
+// Source ids of the U edges a group takes from the batch starting at eb:
+// edges eb + grp + j*epw, clamped into the item so that every load is valid
+// (the caller masks the clamped ones).  Unconditional loads issue back to
+// back; with one group per wave they are scalar loads.
+template <int U>
+__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int64_t eb, int grp, int epw, int64_t e1,
+                                         int32_t (&u)[U]) {
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int64_t ee = eb + grp + (int64_t)j * epw;
+        u[j] = idx[ee < e1 ? ee : e1 - 1];
+    }
+}
+
 // ---------------------------------------------------------------- numerics
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }

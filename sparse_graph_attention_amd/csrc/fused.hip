@@ -24,23 +24,12 @@
 // right behind them (unconditional, clamped loads; scalar loads when one
 // group spans the wave), so no gather waits on an index load.  Output rows
 // are written with the non-temporal hint (never re-read); the fp32 8x64
-// instance also gathers K/V that way (measured faster there, slower for the
-// 512-byte bf16 rows).
+// instance also gathers K/V that way when K+V exceed 1 GB (measured faster
+// there; slower when K/V partly fit the Infinity Cache, and for the 512-byte
+// bf16 rows).
 #include "kernels.hpp"
 
 namespace gt {
-
-// Source ids of the U edges a group takes from the batch starting at eb:
-// edges eb + grp + j*epw, clamped into the item so that every load is valid.
-template <int U>
-__device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int64_t eb, int grp, int epw, int64_t e1,
-                                         int32_t (&u)[U]) {
-#pragma unroll
-    for (int j = 0; j < U; ++j) {
-        const int64_t ee = eb + grp + (int64_t)j * epw;
-        u[j] = idx[ee < e1 ? ee : e1 - 1];
-    }
-}
 
 // ------------------------------------------------------------ vector layout
 //
@@ -391,8 +380,13 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
-            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
+            // Streaming K/V gathers pay off only when K and V are far larger than
+            // the 256 MB Infinity Cache; smaller ones are partly served from it.
+            const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv)
                 fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, true><<<grid, block, 0, s>>>(a);
+            else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
+                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, false><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 fused_vec_kernel<DT, 1, GT_BF16_D32_U, 32, 4, true, false><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)

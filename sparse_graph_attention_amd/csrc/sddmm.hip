@@ -45,14 +45,16 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
         }
     }
     const char* Kb = (const char*)a.K;
-    for (int64_t e = it.e0 + grp; e < it.e1; e += (int64_t)epw * U) {
+    const int64_t e0 = it.e0, e1 = it.e1;
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(a.indices, e0, grp, epw, e1, un);
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
         int32_t u[U];
         bool ok[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const int64_t ee = e + (int64_t)j * epw;
-            ok[j] = ee < it.e1;
-            u[j] = ok[j] ? a.indices[ee] : 0;
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+            u[j] = un[j];
         }
         U4 kr[U][NC];
 #pragma unroll
@@ -60,6 +62,9 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
 #pragma unroll
             for (int c = 0; c < NC; ++c)
                 kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+        // the next batch's source ids load behind this batch's gathers
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(a.indices, nb, grp, epw, e1, un);
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
 #pragma unroll
                 for (int k = 0; k < VN; ++k) d = __builtin_fmaf(q[c][k], kf[k], d);
                 d = seg_sum(d, lph);
-                if (ok[j] && writer[c]) a.scores_out[(e + (int64_t)j * epw) * a.H + head[c]] = d * a.qscale;
+                if (ok[j] && writer[c]) a.scores_out[(eb + grp + (int64_t)j * epw) * a.H + head[c]] = d * a.qscale;
             }
     }
 }
