@@ -27,49 +27,169 @@ __device__ __forceinline__ float wave_sum_stride(float x, int hstride) {
     return x;
 }
 
-// Per-(item) statistics and, for whole rows, the weights.
-__global__ __launch_bounds__(kBlock) void softmax_kernel(const Args a) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    Item it;
-    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
-    it.e0 = uniform64(it.e0);
-    it.e1 = uniform64(it.e1);
-    if (it.e1 == it.e0) return;
+// Elements per lane kept in registers when a whole item fits: 64 x 64 scores
+// (a 512-edge chunk of 8 heads) for chunks, 64 x 32 for rows (fewer registers,
+// more waves: row blocks are latency-bound).
+constexpr int kChunkCache = 64;
+constexpr int kRowCache = 32;
+// Loads in flight per lane in the streaming loops.
+constexpr int kBatch = 8;
+
+// One wave over edges [e0, e1) of one destination: the statistics of a chunk
+// (slot >= 0), or the weights of a whole row (slot < 0).
+template <int kCache>
+__device__ __forceinline__ void softmax_wave(const Args& a, int64_t e0, int64_t e1, int64_t slot, int lane) {
     const int H = a.H;
     const float* s = a.scores_in;  // may alias alpha_out (in place)
     float* alpha = a.alpha_out;
-
     if ((kWave % H) == 0) {
         // lane j covers flat elements e0*H + j + 64t; its head is j mod H
-        const int64_t i0 = it.e0 * H, i1 = it.e1 * H;
+        const int64_t i0 = e0 * H, i1 = e1 * H;
+        if (i1 - i0 <= (int64_t)kWave * kCache) {
+            // the whole item fits in registers: one read, all loads in flight at once
+            float v[kCache];
+#pragma unroll
+            for (int t = 0; t < kCache; ++t) {
+                const int64_t i = i0 + lane + (int64_t)t * kWave;
+                v[t] = i < i1 ? s[i] : -INFINITY;
+            }
+            float m = -INFINITY;
+#pragma unroll
+            for (int t = 0; t < kCache; ++t) m = fmaxf(m, v[t]);
+            m = wave_max_stride(m, H);
+            float l = 0.0f;
+#pragma unroll
+            for (int t = 0; t < kCache; ++t) {
+                v[t] = v[t] == -INFINITY ? 0.0f : expd(v[t], m);
+                l += v[t];
+            }
+            l = wave_sum_stride(l, H);
+            if (slot < 0) {
+#pragma unroll
+                for (int t = 0; t < kCache; ++t) {
+                    const int64_t i = i0 + lane + (int64_t)t * kWave;
+                    if (i < i1) alpha[i] = v[t] / l;
+                }
+            } else if (lane < H) {
+                a.plan.pm[slot * H + lane] = m;
+                a.plan.pl[slot * H + lane] = l;
+            }
+            return;
+        }
+        // larger items: three streaming passes, kBatch loads in flight per lane
         float m = -INFINITY;
-        for (int64_t i = i0 + lane; i < i1; i += kWave) m = fmaxf(m, s[i]);
+        for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : -INFINITY;
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) m = fmaxf(m, v[t]);
+        }
         m = wave_max_stride(m, H);
         float l = 0.0f;
-        for (int64_t i = i0 + lane; i < i1; i += kWave) l += expd(s[i], m);
+        for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : -INFINITY;
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) l += v[t] == -INFINITY ? 0.0f : expd(v[t], m);
+        }
         l = wave_sum_stride(l, H);
-        if (it.slot < 0) {
-            for (int64_t i = i0 + lane; i < i1; i += kWave) alpha[i] = expd(s[i], m) / l;
+        if (slot < 0) {
+            for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
+                float v[kBatch];
+#pragma unroll
+                for (int t = 0; t < kBatch; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : 0.0f;
+#pragma unroll
+                for (int t = 0; t < kBatch; ++t)
+                    if (ib + t * kWave < i1) alpha[ib + t * kWave] = expd(v[t], m) / l;
+            }
         } else if (lane < H) {
-            a.plan.pm[it.slot * H + lane] = m;
-            a.plan.pl[it.slot * H + lane] = l;
+            a.plan.pm[slot * H + lane] = m;
+            a.plan.pl[slot * H + lane] = l;
         }
     } else {
         for (int h = 0; h < H; ++h) {
             float m = -INFINITY;
-            for (int64_t e = it.e0 + lane; e < it.e1; e += kWave) m = fmaxf(m, s[e * H + h]);
+            for (int64_t e = e0 + lane; e < e1; e += kWave) m = fmaxf(m, s[e * H + h]);
             m = wave_max_stride(m, 1);
             float l = 0.0f;
-            for (int64_t e = it.e0 + lane; e < it.e1; e += kWave) l += expd(s[e * H + h], m);
+            for (int64_t e = e0 + lane; e < e1; e += kWave) l += expd(s[e * H + h], m);
             l = wave_sum_stride(l, 1);
-            if (it.slot < 0) {
-                for (int64_t e = it.e0 + lane; e < it.e1; e += kWave) alpha[e * H + h] = expd(s[e * H + h], m) / l;
+            if (slot < 0) {
+                for (int64_t e = e0 + lane; e < e1; e += kWave) alpha[e * H + h] = expd(s[e * H + h], m) / l;
             } else if (lane == 0) {
-                a.plan.pm[it.slot * H + h] = m;
-                a.plan.pl[it.slot * H + h] = l;
+                a.plan.pm[slot * H + h] = m;
+                a.plan.pl[slot * H + h] = l;
             }
         }
+    }
+}
+
+// Rows of at most this many in-edges are done by one lane per (row, head).
+constexpr int kSmallDeg = 32;
+
+// Chunks of heavy rows: their statistics only (one wave per chunk item).
+__global__ __launch_bounds__(kBlock) void softmax_chunk_kernel(const Args a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (item >= a.plan.max_chunks) return;
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    softmax_wave<kChunkCache>(a, uniform64(it.e0), uniform64(it.e1), it.slot, lane);
+}
+
+// Rows that are not split.  When H divides 64 an item is a block of 64/H
+// consecutive rows with lane j on (row j/H, head j%H): rows of degree <=
+// kSmallDeg are done by their own lanes, larger ones by the whole wave, one
+// by one.  Otherwise an item is one row.
+__global__ __launch_bounds__(kBlock) void softmax_kernel(const Args a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = a.H;
+    if ((kWave % H) != 0) {
+        Item it;
+        if (!resolve_item(a.plan, a.indptr, a.N, item + a.plan.max_chunks, it)) return;
+        const int64_t e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+        if (e1 > e0) softmax_wave<kRowCache>(a, e0, e1, -1, lane);
+        return;
+    }
+    const int rpw = kWave / H;
+    const int64_t r0 = item * rpw;
+    if (r0 >= a.N) return;
+    const int64_t r = r0 + lane / H;
+    const int h = lane % H;
+    int64_t b = 0, e = 0;
+    if (r < a.N) {
+        b = a.indptr[r];
+        e = a.indptr[r + 1];
+    }
+    const int64_t deg = e - b;
+    if (deg > 0 && deg <= kSmallDeg) {
+        // the lane's (row, head) scores in registers: one read with all loads in flight
+        const float* s = a.scores_in;  // may alias alpha_out (in place)
+        float v[kSmallDeg];
+#pragma unroll
+        for (int t = 0; t < kSmallDeg; ++t) v[t] = t < deg ? s[(b + t) * H + h] : -INFINITY;
+        float m = -INFINITY;
+#pragma unroll
+        for (int t = 0; t < kSmallDeg; ++t) m = fmaxf(m, v[t]);
+        float l = 0.0f;
+#pragma unroll
+        for (int t = 0; t < kSmallDeg; ++t) {
+            v[t] = t < deg ? expd(v[t], m) : 0.0f;
+            l += v[t];
+        }
+#pragma unroll
+        for (int t = 0; t < kSmallDeg; ++t)
+            if (t < deg) a.alpha_out[(b + t) * H + h] = v[t] / l;
+    }
+    uint64_t big = __ballot(h == 0 && deg > kSmallDeg && deg <= a.plan.chunk);
+    while (big) {
+        const int j = __builtin_ctzll(big);
+        big &= big - 1;
+        const int64_t row = r0 + j / H;
+        softmax_wave<kRowCache>(a, a.indptr[row], a.indptr[row + 1], -1, lane);
     }
 }
 
@@ -99,18 +219,38 @@ __global__ __launch_bounds__(kBlock) void softmax_chunk_norm_kernel(const Args a
     const int H = a.H;
     const float* s = a.scores_in;  // may alias alpha_out (in place)
     const float* st = a.plan.hstat + (int64_t)it.hslot * H * 2;
-    for (int64_t i = it.e0 * H + lane; i < it.e1 * H; i += kWave) {
-        const int h = (int)(i % H);
-        a.alpha_out[i] = expd(s[i], st[2 * h]) / st[2 * h + 1];
+    const int64_t i0 = it.e0 * H, i1 = it.e1 * H;
+    if ((kWave % H) == 0) {
+        // the lane's head is fixed (i0 and the stride are multiples of H)
+        const int h = lane % H;
+        const float M = st[2 * h], L = st[2 * h + 1];
+        for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
+            float v[kBatch];
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : 0.0f;
+#pragma unroll
+            for (int t = 0; t < kBatch; ++t)
+                if (ib + t * kWave < i1) a.alpha_out[ib + t * kWave] = expd(v[t], M) / L;
+        }
+    } else {
+        for (int64_t i = i0 + lane; i < i1; i += kWave) {
+            const int h = (int)(i % H);
+            a.alpha_out[i] = expd(s[i], st[2 * h]) / st[2 * h + 1];
+        }
     }
 }
 
 hipError_t launch_softmax(const Args& a, hipStream_t s) {
     const dim3 block(kBlock);
-    hipError_t err = for_slices(a, a.items, [&](const Args& as, unsigned gx) {
+    const int64_t rows = (kWave % a.H) == 0 ? (a.N + kWave / a.H - 1) / (kWave / a.H) : a.N;
+    hipError_t err = for_slices(a, rows, [&](const Args& as, unsigned gx) {
         softmax_kernel<<<gx, block, 0, s>>>(as);
     });
     if (err != hipSuccess || a.plan.max_heavy == 0) return err;
+    err = for_slices(a, a.plan.max_chunks, [&](const Args& as, unsigned gx) {
+        softmax_chunk_kernel<<<gx, block, 0, s>>>(as);
+    });
+    if (err != hipSuccess) return err;
     err = for_slices(a, a.plan.max_heavy, [&](const Args& as, unsigned gx) {
         softmax_merge_kernel<<<gx, block, 0, s>>>(as);
     });
