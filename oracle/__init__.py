@@ -179,3 +179,106 @@ def edge_softmax(*a, **k):
 
 def spmm(*a, **k):
     return default().spmm(*a, **k)
+
+
+# ---------------------------------------------------------------- backward
+
+def _bind_bwd(L):
+    if getattr(L, "_bwd_bound", False):
+        return L
+    L.oracle_row_stats.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _p, _p, _p, _int]
+    L.oracle_dq_rows.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _int]
+    L.oracle_dkv_sources.argtypes = [_i64, _i64, _int, _int, _int, _p, _p, _p, _p, _p, _p, _p, _p, _p, _i64, _p, _p,
+                                     _int]
+    L._bwd_bound = True
+    return L
+
+
+def transpose_csr(indptr, indices):
+    """Source-sorted view of a destination-sorted CSR: for source u, the destinations
+    of its out-edges in edge order (a stable sort of the edges by source)."""
+    indptr, indices = _csr(indptr, indices)
+    N = len(indptr) - 1
+    dst = np.repeat(np.arange(N, dtype=np.int32), np.diff(indptr))
+    order = np.argsort(indices, kind="stable")
+    t_indptr = np.zeros(N + 1, dtype=np.int64)
+    np.cumsum(np.bincount(indices, minlength=N), out=t_indptr[1:])
+    return t_indptr, np.ascontiguousarray(dst[order], dtype=np.int32)
+
+
+class _Bwd:
+    def row_stats(self, indptr, indices, Q, K, V, dO, nthreads=0):
+        """(lse, delta), each [N][H]: log-sum-exp of the scores and sum alpha (dO . v)."""
+        L = _bind_bwd(self.L)
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        lse = np.empty((N, H))
+        delta = np.empty((N, H))
+        rc = L.oracle_row_stats(N, len(indices), H, D, _dtype_of(Q), _p_(indptr), _p_(indices), _p_(Q), _p_(K),
+                                _p_(V), _p_(dO), _p_(lse), _p_(delta), nthreads)
+        if rc:
+            raise ValueError("oracle_row_stats rejected its arguments")
+        return lse, delta
+
+    def dq_rows(self, indptr, indices, Q, K, V, dO, lse, delta, rows, nthreads=0):
+        L = _bind_bwd(self.L)
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        lse = np.ascontiguousarray(lse, dtype=np.float64)
+        delta = np.ascontiguousarray(delta, dtype=np.float64)
+        dq = np.empty((len(rows), H, D))
+        rc = L.oracle_dq_rows(N, len(indices), H, D, _dtype_of(Q), _p_(indptr), _p_(indices), _p_(Q), _p_(K),
+                              _p_(V), _p_(dO), _p_(lse), _p_(delta), _p_(rows), len(rows), _p_(dq), nthreads)
+        if rc:
+            raise ValueError("oracle_dq_rows rejected its arguments")
+        return dq
+
+    def dkv_sources(self, t_indptr, t_indices, Q, K, V, dO, lse, delta, srcs, nthreads=0):
+        L = _bind_bwd(self.L)
+        t_indptr, t_indices = _csr(t_indptr, t_indices)
+        N, H, D = _shape(Q)
+        srcs = np.ascontiguousarray(srcs, dtype=np.int64)
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        lse = np.ascontiguousarray(lse, dtype=np.float64)
+        delta = np.ascontiguousarray(delta, dtype=np.float64)
+        dk = np.empty((len(srcs), H, D))
+        dv = np.empty((len(srcs), H, D))
+        rc = L.oracle_dkv_sources(N, len(t_indices), H, D, _dtype_of(Q), _p_(t_indptr), _p_(t_indices), _p_(Q),
+                                  _p_(K), _p_(V), _p_(dO), _p_(lse), _p_(delta), _p_(srcs), len(srcs), _p_(dk),
+                                  _p_(dv), nthreads)
+        if rc:
+            raise ValueError("oracle_dkv_sources rejected its arguments")
+        return dk, dv
+
+    def bwd(self, indptr, indices, Q, K, V, dO, nthreads=0):
+        """Whole backward: (dQ, dK, dV, lse, delta), all fp64."""
+        N = len(indptr) - 1
+        lse, delta = self.row_stats(indptr, indices, Q, K, V, dO, nthreads)
+        allv = np.arange(N, dtype=np.int64)
+        dq = self.dq_rows(indptr, indices, Q, K, V, dO, lse, delta, allv, nthreads)
+        t_indptr, t_indices = transpose_csr(indptr, indices)
+        dk, dv = self.dkv_sources(t_indptr, t_indices, Q, K, V, dO, lse, delta, allv, nthreads)
+        return dq, dk, dv, lse, delta
+
+
+for _name in ("row_stats", "dq_rows", "dkv_sources", "bwd"):
+    setattr(Oracle, _name, getattr(_Bwd, _name))
+
+
+def bwd(*a, **k):
+    return default().bwd(*a, **k)
+
+
+def row_stats(*a, **k):
+    return default().row_stats(*a, **k)
+
+
+def dq_rows(*a, **k):
+    return default().dq_rows(*a, **k)
+
+
+def dkv_sources(*a, **k):
+    return default().dkv_sources(*a, **k)

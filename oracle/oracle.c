@@ -224,3 +224,132 @@ int oracle_fwd(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* ind
     free(rows);
     return rc;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Backward of the forward above, for a loss L with dL/dout = dO.           */
+/*                                                                          */
+/* With s_e = q_v.k_u / sqrt(D), alpha_e = exp(s_e - lse_v) and              */
+/* lse_v = log sum_e exp(s_e) over the in-edges of v (per head), the chain   */
+/* rule through out_v = sum_e alpha_e v_u and the softmax gives:             */
+/*   dV_u    = sum over out-edges e = (u->v) of alpha_e dO_v                 */
+/*   da_e    = dO_v . v_u                                                    */
+/*   delta_v = sum over in-edges e of v of alpha_e da_e  (= dO_v . out_v)    */
+/*   ds_e    = alpha_e (da_e - delta_v)                                      */
+/*   dQ_v    = sum over in-edges of ds_e k_u / sqrt(D)                       */
+/*   dK_u    = sum over out-edges of ds_e q_v / sqrt(D)                      */
+/* (the softmax Jacobian is diag(alpha) - alpha alpha^T).  Every stored edge */
+/* is its own term.  Rows without in-edges have lse = -inf and contribute    */
+/* nothing.                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Per destination row and head: lse (natural log) and delta = sum alpha da.
+ * lse = -inf and delta = 0 for rows without in-edges.  lse and delta are [N][H].
+ */
+int oracle_row_stats(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                     const void* Q, const void* K, const void* V, const void* dO, double* lse, double* delta,
+                     int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || bad_dtype(dtype)) return 1;
+    int64_t maxdeg = 0;
+    for (int64_t v = 0; v < N; ++v)
+        if (indptr[v + 1] - indptr[v] > maxdeg) maxdeg = indptr[v + 1] - indptr[v];
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(maxdeg > 0 ? maxdeg : 1));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t v = 0; v < N; ++v) {
+            int64_t b = indptr[v], deg = indptr[v + 1] - b;
+            for (int h = 0; h < H; ++h) {
+                double m = -INFINITY, z = 0.0, dl = 0.0;
+                for (int64_t i = 0; i < deg; ++i) {
+                    s[i] = edge_score(Q, K, dtype, H, D, v, indices[b + i], h);
+                    if (s[i] > m) m = s[i];
+                }
+                for (int64_t i = 0; i < deg; ++i) z += exp(s[i] - m);
+                double l = deg > 0 ? m + log(z) : -INFINITY;
+                int64_t go = (v * H + h) * (int64_t)D;
+                for (int64_t i = 0; i < deg; ++i) {
+                    double a = exp(s[i] - l);
+                    int64_t vo = ((int64_t)indices[b + i] * H + h) * (int64_t)D;
+                    double da = 0.0;
+                    for (int d = 0; d < D; ++d) da += elem(dO, dtype, go + d) * elem(V, dtype, vo + d);
+                    dl += a * da;
+                }
+                lse[v * H + h] = l;
+                delta[v * H + h] = dl;
+            }
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/* dQ for the listed destination rows: out is [nrows][H][D]. */
+int oracle_dq_rows(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                   const void* Q, const void* K, const void* V, const void* dO, const double* lse,
+                   const double* delta, const int64_t* rows, int64_t nrows, double* dq, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || nrows < 0 || bad_dtype(dtype)) return 1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return 1;
+    const double rs = 1.0 / sqrt((double)D);
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t v = rows[r];
+        for (int h = 0; h < H; ++h) {
+            double* o = dq + (r * H + h) * (int64_t)D;
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            int64_t go = (v * H + h) * (int64_t)D;
+            for (int64_t e = indptr[v]; e < indptr[v + 1]; ++e) {
+                int64_t u = indices[e];
+                int64_t uo = (u * H + h) * (int64_t)D; /* row u of K and of V */
+                double a = exp(edge_score(Q, K, dtype, H, D, v, u, h) - lse[v * H + h]);
+                double da = 0.0;
+                for (int d = 0; d < D; ++d) da += elem(dO, dtype, go + d) * elem(V, dtype, uo + d);
+                double ds = a * (da - delta[v * H + h]);
+                for (int d = 0; d < D; ++d) o[d] += ds * elem(K, dtype, uo + d) * rs;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * dK and dV for the listed source nodes, using the transposed graph: for
+ * source u, t_indices[t_indptr[u] .. t_indptr[u+1]) are the destinations of
+ * its out-edges.  dk and dv are [nsrc][H][D].
+ */
+int oracle_dkv_sources(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* t_indptr,
+                       const int32_t* t_indices, const void* Q, const void* K, const void* V, const void* dO,
+                       const double* lse, const double* delta, const int64_t* srcs, int64_t nsrc, double* dk,
+                       double* dv, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || nsrc < 0 || bad_dtype(dtype)) return 1;
+    for (int64_t r = 0; r < nsrc; ++r)
+        if (srcs[r] < 0 || srcs[r] >= N) return 1;
+    const double rs = 1.0 / sqrt((double)D);
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nsrc; ++r) {
+        int64_t u = srcs[r];
+        for (int h = 0; h < H; ++h) {
+            double* ok = dk + (r * H + h) * (int64_t)D;
+            double* ov = dv + (r * H + h) * (int64_t)D;
+            for (int d = 0; d < D; ++d) ok[d] = ov[d] = 0.0;
+            int64_t uo = (u * H + h) * (int64_t)D;
+            for (int64_t j = t_indptr[u]; j < t_indptr[u + 1]; ++j) {
+                int64_t v = t_indices[j];
+                int64_t vo = (v * H + h) * (int64_t)D;
+                double a = exp(edge_score(Q, K, dtype, H, D, v, u, h) - lse[v * H + h]);
+                double da = 0.0;
+                for (int d = 0; d < D; ++d) da += elem(dO, dtype, vo + d) * elem(V, dtype, uo + d);
+                double ds = a * (da - delta[v * H + h]);
+                for (int d = 0; d < D; ++d) {
+                    ov[d] += a * elem(dO, dtype, vo + d);
+                    ok[d] += ds * elem(Q, dtype, vo + d) * rs;
+                }
+            }
+        }
+    }
+    return 0;
+}
