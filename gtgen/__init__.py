@@ -34,7 +34,7 @@ from . import _build
 _LIB = None
 
 # counter streams
-S_GRAPH, S_Q, S_K, S_V, S_PERM, S_DEG, S_SRC = 0, 1, 2, 3, 4, 5, 6
+S_GRAPH, S_Q, S_K, S_V, S_PERM, S_DEG, S_SRC, S_DOUT = 0, 1, 2, 3, 4, 5, 6, 7
 
 F32, BF16 = 0, 1
 
@@ -188,6 +188,20 @@ def make_features(N, H, D, dtype, seed=0, scale=1.0):
     """Q, K, V as [N][H][D] arrays: float32, or uint16 bf16 bits when dtype == BF16."""
     gen = normal_f32 if dtype == F32 else normal_bf16
     return tuple(gen(seed, s, (N, H, D), scale) for s in (S_Q, S_K, S_V))
+
+
+def make_grad(N, H, D, dtype, seed=0, scale=1.0):
+    """An upstream gradient dL/dout [N][H][D], drawn like the features (own stream)."""
+    gen = normal_f32 if dtype == F32 else normal_bf16
+    return gen(seed, S_DOUT, (N, H, D), scale)
+
+
+def source_sorted(indptr, indices):
+    """The same edges grouped by source: (t_indptr, t_indices) with t_indices holding
+    each out-edge's destination, out-edges of a source in destination-CSR order."""
+    N = len(indptr) - 1
+    dst = np.repeat(np.arange(N, dtype=np.int32), np.diff(indptr))
+    return coo_to_csr(N, dst, np.ascontiguousarray(indices, dtype=np.int32))
 
 
 def make_workload(name, seed=0, with_features=True):

@@ -93,6 +93,44 @@ int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void*
                       void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
 
 /*
+ * Fused forward that also saves, for the backward, the natural-log
+ * log-sum-exp of every destination's scores:
+ *     lse[v][h] = log sum over in-edges of exp(s)    (float32 [N][H]),
+ * -inf for a destination without in-edges.  out is as gt_sparse_mha_fwd's,
+ * bit for bit.  GT_EINVAL also for a NULL lse with N > 0.
+ */
+int gt_sparse_mha_fwd_lse(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
+                          void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                          hipStream_t stream);
+
+/*
+ * Backward of the fused forward: the gradients that loss.backward() takes
+ * through bsddmm, softmax and bspmm in the training loop of "Graph
+ * Transformer in a Nutshell" (section "Training").  With alpha recomputed as
+ * exp(s - lse) and dout = dL/dout, per edge e = (u -> v) and head h:
+ *     delta[v] = <dout[v], out[v]>,  ds_e = alpha_e (<dout[v], V[u]> - delta[v])
+ *     dQ[v] = sum over in-edges of ds_e K[u] / sqrt(D)
+ *     dK[u] = sum over out-edges of ds_e Q[v] / sqrt(D)
+ *     dV[u] = sum over out-edges of alpha_e dout[v]
+ * (the chain rule through the row softmax, whose Jacobian is
+ * diag(alpha) - alpha alpha^T).
+ * Inputs: the destination-sorted CSR (indptr, indices) of the forward and the
+ * same graph sorted by source, t_indptr int64[N+1] / t_indices int32[E]
+ * holding the DESTINATION of each out-edge (the transpose; duplicated edges
+ * appear as often as in the forward); Q, K, V, out and lse as the forward
+ * took and left them; dout [N][H][D].  Outputs dQ, dK, dV [N][H][D], every
+ * element written (zeros for nodes without in- or out-edges).  All feature
+ * arrays share dtype; accumulation is fp32.  The transpose is trusted like
+ * the CSR: that it matches (indptr, indices) is not checked.  No atomics:
+ * results are deterministic.  Scratch: the per-stream buffer also holds an
+ * fp32 [N][H] delta.  Errors as for gt_sparse_mha_fwd.
+ */
+int gt_sparse_mha_bwd(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr, const int32_t* t_indices,
+                      const void* Q, const void* K, const void* V, const void* out, const void* dout, const float* lse,
+                      void* dQ, void* dK, void* dV, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                      hipStream_t stream);
+
+/*
  * SDDMM stage: scores[e][h] = <Q[v,h,:], K[u_e,h,:]> / sqrt(D) for every edge
  * e = (u_e -> v).  The DGL gist's u_dot_v (source key with destination query)
  * followed by its division by sqrt(d_qkv); the tutorial's bsddmm.

@@ -9,6 +9,10 @@ The functions have the names of the C entry points declared in
 ``include/gtattn.h`` and follow their contracts:
 
 * ``gt_sparse_mha_fwd(indptr, indices, Q, K, V, out=None)`` -- fused forward;
+* ``gt_sparse_mha_fwd_lse(indptr, indices, Q, K, V, out=None, lse=None)`` --
+  fused forward that also returns the per-destination log-sum-exp [N][H];
+* ``gt_sparse_mha_bwd(indptr, indices, t_indptr, t_indices, Q, K, V, out, dout,
+  lse)`` -- (dQ, dK, dV) given the source-sorted transpose of the graph;
 * ``gt_sddmm(indptr, indices, Q, K, scores=None)`` -- scores [E][H] (fp32);
 * ``gt_edge_softmax(indptr, scores, alpha=None)`` -- alpha [E][H] (fp32);
 * ``gt_spmm(indptr, indices, alpha, V, out=None)`` -- out [N][H][D];
@@ -31,6 +35,8 @@ GT_CFG_CHUNK_EDGES = 0
 
 EXPORTS = (
     "gt_sparse_mha_fwd",
+    "gt_sparse_mha_fwd_lse",
+    "gt_sparse_mha_bwd",
     "gt_sddmm",
     "gt_edge_softmax",
     "gt_spmm",
@@ -64,6 +70,8 @@ def lib():
             _build.build()
         L = ctypes.CDLL(_build.LIB)
         L.gt_sparse_mha_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
+        L.gt_sparse_mha_fwd_lse.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
+        L.gt_sparse_mha_bwd.argtypes = [_p] * 13 + [_i64, _i64, _i32, _i32, _i32, _p]
         L.gt_sddmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_edge_softmax.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.gt_spmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
@@ -78,7 +86,7 @@ def lib():
         L.gt_profile_begin.argtypes = [_i32]
         L.gt_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(_i64)]
-        for name in ("gt_sparse_mha_fwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
+        for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
                      "gt_config_set", "gt_profile_begin", "gt_profile_end"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -137,6 +145,56 @@ def gt_sparse_mha_fwd(indptr, indices, Q, K, V, out=None, stream=None):
     _check(lib().gt_sparse_mha_fwd(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), N, E, H, D,
                                    _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd")
     return out
+
+
+def _qkv(indptr, indices, Q, K, V):
+    N, E = _csr(indptr, indices)
+    if Q.dim() != 3 or Q.shape[0] != N or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must all be [N][H][D] with N = len(indptr) - 1")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    return N, E, Q.shape[1], Q.shape[2]
+
+
+def _like(t, Q, name):
+    if t is None:
+        return torch.empty_like(Q)
+    if t.shape != Q.shape or t.dtype != Q.dtype:
+        raise ValueError("%s must match Q in shape and dtype" % name)
+    return t
+
+
+def gt_sparse_mha_fwd_lse(indptr, indices, Q, K, V, out=None, lse=None, stream=None):
+    """(out, lse): the fused forward and the log-sum-exp [N][H] (float32) the backward takes."""
+    N, E, H, D = _qkv(indptr, indices, Q, K, V)
+    out = _like(out, Q, "out")
+    if lse is None:
+        lse = torch.empty((N, H), dtype=torch.float32, device=Q.device)
+    elif lse.shape != (N, H) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [N][H]")
+    _need_gpu(indptr, indices, Q, K, V, out, lse)
+    _check(lib().gt_sparse_mha_fwd_lse(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse),
+                                       N, E, H, D, _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd_lse")
+    return out, lse
+
+
+def gt_sparse_mha_bwd(indptr, indices, t_indptr, t_indices, Q, K, V, out, dout, lse, dQ=None, dK=None, dV=None,
+                      stream=None):
+    """(dQ, dK, dV).  (t_indptr, t_indices) is the graph sorted by source, indices holding destinations."""
+    N, E, H, D = _qkv(indptr, indices, Q, K, V)
+    tN, tE = _csr(t_indptr, t_indices)
+    if (tN, tE) != (N, E):
+        raise ValueError("the transposed graph must have the same N and E")
+    for t, name in ((out, "out"), (dout, "dout")):
+        _like(t, Q, name)
+    if lse.shape != (N, H) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [N][H]")
+    dQ, dK, dV = _like(dQ, Q, "dQ"), _like(dK, Q, "dK"), _like(dV, Q, "dV")
+    _need_gpu(indptr, indices, t_indptr, t_indices, Q, K, V, out, dout, lse, dQ, dK, dV)
+    _check(lib().gt_sparse_mha_bwd(_ptr(indptr), _ptr(indices), _ptr(t_indptr), _ptr(t_indices), _ptr(Q), _ptr(K),
+                                   _ptr(V), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dQ), _ptr(dK), _ptr(dV), N, E, H,
+                                   D, _dtype_code(Q), _stream(stream)), "gt_sparse_mha_bwd")
+    return dQ, dK, dV
 
 
 def gt_sddmm(indptr, indices, Q, K, scores=None, stream=None):

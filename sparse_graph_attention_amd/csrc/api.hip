@@ -75,38 +75,49 @@ int get_scratch(hipStream_t stream, size_t bytes, void** out) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Sizes the plan for (N, E) and carves it out of the stream's scratch.
-int make_plan(const int64_t* indptr, int64_t N, int64_t E, int H, int D, hipStream_t stream, Args& a) {
+// Sizes a plan for a graph of N rows and E edges whose chunk partials are
+// `accw` floats wide; returns its scratch bytes (0 when no row can be split,
+// except for the counters).
+size_t plan_bytes(int64_t N, int64_t E, int H, int64_t accw, Plan& p) {
     const int64_t C = g_chunk.load();
-    Plan& p = a.plan;
     p.chunk = C;
     p.max_heavy = std::min<int64_t>(N, E / (C + 1));
     p.max_chunks = p.max_heavy ? E / C + p.max_heavy : 0;
+    return align256(sizeof(PlanCounters)) + align256(sizeof(HeavyRow) * p.max_heavy) +
+           align256(sizeof(ChunkRef) * p.max_chunks) + 2 * align256(sizeof(float) * p.max_chunks * H) +
+           align256(sizeof(float) * p.max_chunks * accw) + align256(sizeof(float) * p.max_heavy * H * 2);
+}
+
+// Points the plan's arrays into scratch at b (laid out as plan_bytes counts them).
+char* carve_plan(char* b, int H, int64_t accw, Plan& p) {
+    p.counters = (PlanCounters*)b;               b += align256(sizeof(PlanCounters));
+    p.heavy = (HeavyRow*)b;                      b += align256(sizeof(HeavyRow) * p.max_heavy);
+    p.chunks = (ChunkRef*)b;                     b += align256(sizeof(ChunkRef) * p.max_chunks);
+    p.pm = (float*)b;                            b += align256(sizeof(float) * p.max_chunks * H);
+    p.pl = (float*)b;                            b += align256(sizeof(float) * p.max_chunks * H);
+    p.pacc = (float*)b;                          b += align256(sizeof(float) * p.max_chunks * accw);
+    p.hstat = (float*)b;                         b += align256(sizeof(float) * p.max_heavy * H * 2);
+    return b;
+}
+
+int check_plan(const Plan& p) {
     if (p.max_chunks >= ((int64_t)1 << 31))
         return fail(GT_EUNSUPPORTED, "too many chunks (%lld); raise GT_CFG_CHUNK_EDGES", (long long)p.max_chunks);
-    a.items = p.max_chunks + N;
-    // with max_heavy == 0 only the (unused) counters are carved out and no
-    // plan kernel runs: every row is a single item
-    const size_t HD = (size_t)H * D;
-    size_t off = 0;
-    const size_t o_cnt = off;   off += align256(sizeof(PlanCounters));
-    const size_t o_heavy = off; off += align256(sizeof(HeavyRow) * p.max_heavy);
-    const size_t o_chunk = off; off += align256(sizeof(ChunkRef) * p.max_chunks);
-    const size_t o_pm = off;    off += align256(sizeof(float) * p.max_chunks * H);
-    const size_t o_pl = off;    off += align256(sizeof(float) * p.max_chunks * H);
-    const size_t o_pacc = off;  off += align256(sizeof(float) * p.max_chunks * HD);
-    const size_t o_hst = off;   off += align256(sizeof(float) * p.max_heavy * H * 2);
-    void* base = nullptr;
-    int rc = get_scratch(stream, off, &base);
+    return GT_OK;
+}
+
+// Sizes the plan for (N, E), carves it out of the stream's scratch and lists
+// the split rows on the device.
+int make_plan(const int64_t* indptr, int64_t N, int64_t E, int H, int D, hipStream_t stream, Args& a) {
+    (void)indptr;
+    const size_t bytes = plan_bytes(N, E, H, (int64_t)H * D, a.plan);
+    int rc = check_plan(a.plan);
     if (rc) return rc;
-    char* b = (char*)base;
-    p.counters = (PlanCounters*)(b + o_cnt);
-    p.heavy = (HeavyRow*)(b + o_heavy);
-    p.chunks = (ChunkRef*)(b + o_chunk);
-    p.pm = (float*)(b + o_pm);
-    p.pl = (float*)(b + o_pl);
-    p.pacc = (float*)(b + o_pacc);
-    p.hstat = (float*)(b + o_hst);
+    a.items = a.plan.max_chunks + N;
+    void* base = nullptr;
+    rc = get_scratch(stream, bytes, &base);
+    if (rc) return rc;
+    carve_plan((char*)base, H, (int64_t)H * D, a.plan);
     hipError_t e = launch_plan(a, stream);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
     return GT_OK;
@@ -242,8 +253,12 @@ int gt_profile_end(double* kernel_ms, double* call_ms, int64_t* calls) {
     return GT_OK;
 }
 
-int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
-                      void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V, void* out,
+              float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
     int rc = check_common(N, E, H, D, dtype);
     if (rc) return rc;
     if (N == 0) return GT_OK;
@@ -256,6 +271,7 @@ int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void*
     a.K = K;
     a.V = V;
     a.out = out;
+    a.lse_out = lse;
     a.N = N;
     a.E = E;
     a.H = H;
@@ -276,6 +292,84 @@ int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void*
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
     if (ev) (void)hipEventRecord(ev[3], stream);
+    return GT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
+                      void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
+    return fused_fwd(indptr, indices, Q, K, V, out, nullptr, N, E, H, D, dtype, stream);
+}
+
+int gt_sparse_mha_fwd_lse(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
+                          void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                          hipStream_t stream) {
+    if (N > 0 && !lse) return fail(GT_EINVAL, "NULL lse with N > 0");
+    return fused_fwd(indptr, indices, Q, K, V, out, lse, N, E, H, D, dtype, stream);
+}
+
+int gt_sparse_mha_bwd(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr, const int32_t* t_indices,
+                      const void* Q, const void* K, const void* V, const void* out, const void* dout, const float* lse,
+                      void* dQ, void* dK, void* dV, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                      hipStream_t stream) {
+    int rc = check_common(N, E, H, D, dtype);
+    if (rc) return rc;
+    if (N == 0) return GT_OK;
+    if (!indptr || !t_indptr || !Q || !K || !V || !out || !dout || !lse || !dQ || !dK || !dV)
+        return fail(GT_EINVAL, "NULL array with N > 0");
+    if (E > 0 && (!indices || !t_indices)) return fail(GT_EINVAL, "NULL indices with E > 0");
+    Args a{};
+    a.indices = indices;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = out;
+    a.dO = dout;
+    a.lse_in = lse;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.N = N;
+    a.E = E;
+    a.H = H;
+    a.D = D;
+    a.dtype = dtype;
+    a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)D));
+    a.kscale = (float)(1.0 / std::sqrt((double)D));
+    choose_layout(a, {Q, K, V, out, dout, dQ, dK, dV});
+    const int64_t HD = (int64_t)H * D;
+
+    // scratch: plan over destinations (dQ partials HD wide), plan over sources
+    // (dK and dV partials, 2 HD wide), and delta [N][H]
+    Args at = a;
+    const size_t b1 = plan_bytes(N, E, H, HD, a.plan);
+    const size_t b2 = plan_bytes(N, E, H, 2 * HD, at.plan);
+    rc = check_plan(a.plan);
+    if (!rc) rc = check_plan(at.plan);
+    if (rc) return rc;
+    void* base = nullptr;
+    rc = get_scratch(stream, b1 + b2 + align256(sizeof(float) * (size_t)N * H), &base);
+    if (rc) return rc;
+    char* p = carve_plan((char*)base, H, HD, a.plan);
+    p = carve_plan(p, H, 2 * HD, at.plan);
+    a.delta = at.delta = (float*)p;
+
+    a.indptr = indptr;
+    a.indices = indices;
+    a.items = a.plan.max_chunks + N;
+    at.indptr = t_indptr;
+    at.indices = t_indices;
+    at.items = at.plan.max_chunks + N;
+    hipError_t e = launch_plan(a, stream);
+    if (e == hipSuccess) e = launch_plan(at, stream);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    e = launch_bwd_dq(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
+    e = launch_bwd_dkv(at, stream);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
     return GT_OK;
 }
 

@@ -1,0 +1,564 @@
+// bwd.hip -- backward of the fused sparse multi-head attention on gfx950.
+//
+// With s_e = <q_v, k_u>/sqrt(D), alpha_e = exp(s_e - lse_v) (lse saved by the
+// forward) and out_v = sum_e alpha_e v_u, the chain rule through the softmax
+// (Jacobian diag(alpha) - alpha alpha^T) gives, per head:
+//   da_e    = dO_v . v_u
+//   delta_v = sum over in-edges of alpha_e da_e = dO_v . out_v
+//   ds_e    = alpha_e (da_e - delta_v)
+//   dQ_v    = sum over in-edges of v of ds_e k_u / sqrt(D)
+//   dK_u    = sum over out-edges of u of ds_e q_v / sqrt(D)
+//   dV_u    = sum over out-edges of u of alpha_e dO_v
+// The training loop that the "Graph Transformer in a Nutshell" tutorial runs
+// (loss.backward() through bsddmm, softmax and bspmm) needs exactly these.
+//
+// Two passes, each with the forward's lane layouts and work items, and no
+// float atomics (results are deterministic):
+//  1. destination-sorted graph, one wave per row or chunk: gathers k_u and v_u
+//     per in-edge, recomputes alpha from lse, accumulates dQ; writes delta.
+//  2. source-sorted graph (the caller's transposed CSR), one wave per source
+//     or chunk: gathers q_v and dO_v per out-edge, recomputes alpha and ds
+//     from lse_v and delta_v, accumulates dK and dV.
+// Chunks of split rows leave partial sums that a merge adds in chunk order.
+#include "kernels.hpp"
+
+namespace gt {
+
+// ------------------------------------------------------------ dQ, vector layout
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL>
+__global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+
+    const int G = G_ ? G_ : a.G;
+    const int lph = LPH_ ? LPH_ : a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+    const int64_t HD = (int64_t)a.H * a.D;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+
+    // row data: q, dO, and per head delta = dO . out and lse (log2 units)
+    float q[NC][VN], g[NC][VN], dl[NC], ls[NC];
+    bool act[NC];
+    const char* qrow = (const char*)a.Q + row * rowbytes;
+    const char* grow = (const char*)a.dO + row * rowbytes;
+    const char* orow = (const char*)a.O + row * rowbytes;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int vi = c * G + gl;
+        act[c] = FULL || vi < a.R;
+        const U4 zero{0, 0, 0, 0};
+        VT::unpack(act[c] ? ld16(qrow + vi * 16) : zero, q[c]);
+        VT::unpack(act[c] ? ld16(grow + vi * 16) : zero, g[c]);
+        float o[VN];
+        VT::unpack(act[c] ? ld16(orow + vi * 16) : zero, o);
+        float d = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VN; ++k) d = __builtin_fmaf(g[c][k], o[k], d);
+        dl[c] = LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph);
+        ls[c] = act[c] ? a.lse_in[row * a.H + vi / lph] * kLog2e : 0.0f;
+    }
+    float acc[NC][VN];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) acc[c][k] = 0.0f;
+
+    const char* Kb = (const char*)a.K;
+    const char* Vb = (const char*)a.V;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        U4 kr[U][NC], vr[U][NC];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float kf[VN], vf[VN];
+                VT::unpack(kr[j][c], kf);
+                VT::unpack(vr[j][c], vf);
+                float sd = 0.0f, dd = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VN; ++k) {
+                    sd = __builtin_fmaf(q[c][k], kf[k], sd);
+                    dd = __builtin_fmaf(g[c][k], vf[k], dd);
+                }
+                sd = (LPH_ ? seg_sum_c<LPH_>(sd) : seg_sum(sd, lph)) * a.qscale;
+                dd = LPH_ ? seg_sum_c<LPH_>(dd) : seg_sum(dd, lph);
+                const float p = ok[j] ? exp2_(sd - ls[c]) : 0.0f;
+                const float ds = p * (dd - dl[c]);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(ds, kf[k], acc[c][k]);
+            }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int k = 0; k < VN; ++k) acc[c][k] += __shfl_xor(acc[c][k], off, kWave);
+    if (grp != 0) return;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (!act[c]) continue;
+        const int vi = c * G + gl;
+        if ((vi & (lph - 1)) == 0) a.delta[row * a.H + vi / lph] = dl[c];
+        if (it.slot < 0) {
+            float o[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * a.kscale;
+            st16((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(o));
+        } else {
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)vi * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
+        }
+    }
+}
+
+// ------------------------------------------------------------ dK, dV, vector layout
+// a.indptr / a.indices are the source-sorted graph: item rows are sources u,
+// "edges" are their out-edges with the destination v in a.indices.
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL>
+__global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t src = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+
+    const int G = G_ ? G_ : a.G;
+    const int lph = LPH_ ? LPH_ : a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+    const int64_t HD = (int64_t)a.H * a.D;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+
+    float kk[NC][VN], vv[NC][VN];
+    bool act[NC];
+    int head[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int vi = c * G + gl;
+        act[c] = FULL || vi < a.R;
+        head[c] = act[c] ? vi / lph : 0;
+        const U4 zero{0, 0, 0, 0};
+        VT::unpack(act[c] ? ld16((const char*)a.K + src * rowbytes + vi * 16) : zero, kk[c]);
+        VT::unpack(act[c] ? ld16((const char*)a.V + src * rowbytes + vi * 16) : zero, vv[c]);
+    }
+    float dk[NC][VN], dv[NC][VN];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) dk[c][k] = dv[c][k] = 0.0f;
+
+    const char* Qb = (const char*)a.Q;
+    const char* Gb = (const char*)a.dO;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        U4 qr[U][NC], gr[U][NC];
+        float ls[U][NC], dl[U][NC];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const bool go = ok[j] && act[c];
+                qr[j][c] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                gr[j][c] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                ls[j][c] = go ? a.lse_in[(int64_t)u[j] * a.H + head[c]] : 0.0f;
+                dl[j][c] = go ? a.delta[(int64_t)u[j] * a.H + head[c]] : 0.0f;
+            }
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float qf[VN], gf[VN];
+                VT::unpack(qr[j][c], qf);
+                VT::unpack(gr[j][c], gf);
+                float sd = 0.0f, dd = 0.0f;
+#pragma unroll
+                for (int k = 0; k < VN; ++k) {
+                    sd = __builtin_fmaf(qf[k], kk[c][k], sd);
+                    dd = __builtin_fmaf(gf[k], vv[c][k], dd);
+                }
+                sd = (LPH_ ? seg_sum_c<LPH_>(sd) : seg_sum(sd, lph)) * a.qscale;
+                dd = LPH_ ? seg_sum_c<LPH_>(dd) : seg_sum(dd, lph);
+                const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
+                const float ds = p * (dd - dl[j][c]);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) {
+                    dv[c][k] = __builtin_fmaf(p, gf[k], dv[c][k]);
+                    dk[c][k] = __builtin_fmaf(ds, qf[k], dk[c][k]);
+                }
+            }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int k = 0; k < VN; ++k) {
+                dk[c][k] += __shfl_xor(dk[c][k], off, kWave);
+                dv[c][k] += __shfl_xor(dv[c][k], off, kWave);
+            }
+    if (grp != 0) return;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        if (!act[c]) continue;
+        const int vi = c * G + gl;
+        if (it.slot < 0) {
+            float o[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) o[k] = dk[c][k] * a.kscale;
+            st16((char*)a.dK + src * rowbytes + vi * 16, VT::pack(o));
+            st16((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
+        } else {
+            float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)vi * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) {
+                st16(pa + k, Vec<kF32>::pack(&dk[c][k]));
+                st16(pa + HD + k, Vec<kF32>::pack(&dv[c][k]));
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ scalar layout
+// One wave per (item, head h = blockIdx.y); groups of G = pow2ceil(D) lanes,
+// lane j holding elements j + k*G, k < KD.
+template <int DT, int KD, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y;
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+    const int G = a.G, D = a.D;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t HD = (int64_t)a.H * D;
+    const int64_t hoff = (int64_t)h * D;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    float q[KD], g[KD];
+    bool act[KD];
+    float d = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        const int dd = gl + k * G;
+        act[k] = dd < D;
+        q[k] = act[k] ? VT::scalar(a.Q, row * HD + hoff + dd) : 0.0f;
+        g[k] = act[k] ? VT::scalar(a.dO, row * HD + hoff + dd) : 0.0f;
+        d = __builtin_fmaf(g[k], act[k] ? VT::scalar(a.O, row * HD + hoff + dd) : 0.0f, d);
+    }
+    const float dl = seg_sum(d, G);
+    const float ls = a.lse_in[row * a.H + h] * kLog2e;
+    float acc[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) acc[k] = 0.0f;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        float kv[U][KD], vv[U][KD];
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                const bool go = ok[j] && act[k];
+                kv[j][k] = go ? VT::scalar(a.K, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+                vv[j][k] = go ? VT::scalar(a.V, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+            }
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float sd = 0.0f, dd = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                sd = __builtin_fmaf(q[k], kv[j][k], sd);
+                dd = __builtin_fmaf(g[k], vv[j][k], dd);
+            }
+            sd = seg_sum(sd, G) * a.qscale;
+            dd = seg_sum(dd, G);
+            const float p = ok[j] ? exp2_(sd - ls) : 0.0f;
+            const float ds = p * (dd - dl);
+#pragma unroll
+            for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(ds, kv[j][k], acc[k]);
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < KD; ++k) acc[k] += __shfl_xor(acc[k], off, kWave);
+    if (grp != 0) return;
+    if (gl == 0) a.delta[row * a.H + h] = dl;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        if (!act[k]) continue;
+        if (it.slot < 0)
+            VT::store_scalar(a.dQ, row * HD + hoff + gl + k * G, acc[k] * a.kscale);
+        else
+            a.plan.pacc[it.slot * HD + hoff + gl + k * G] = acc[k];
+    }
+}
+
+template <int DT, int KD, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = blockIdx.y;
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t src = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+    const int G = a.G, D = a.D;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int64_t HD = (int64_t)a.H * D;
+    const int64_t hoff = (int64_t)h * D;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    float kk[KD], vv[KD], dk[KD], dv[KD];
+    bool act[KD];
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        const int dd = gl + k * G;
+        act[k] = dd < D;
+        kk[k] = act[k] ? VT::scalar(a.K, src * HD + hoff + dd) : 0.0f;
+        vv[k] = act[k] ? VT::scalar(a.V, src * HD + hoff + dd) : 0.0f;
+        dk[k] = dv[k] = 0.0f;
+    }
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        float qv[U][KD], gv[U][KD], ls[U], dl[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                const bool go = ok[j] && act[k];
+                qv[j][k] = go ? VT::scalar(a.Q, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+                gv[j][k] = go ? VT::scalar(a.dO, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
+            }
+            ls[j] = ok[j] ? a.lse_in[(int64_t)u[j] * a.H + h] : 0.0f;
+            dl[j] = ok[j] ? a.delta[(int64_t)u[j] * a.H + h] : 0.0f;
+        }
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float sd = 0.0f, dd = 0.0f;
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                sd = __builtin_fmaf(qv[j][k], kk[k], sd);
+                dd = __builtin_fmaf(gv[j][k], vv[k], dd);
+            }
+            sd = seg_sum(sd, G) * a.qscale;
+            dd = seg_sum(dd, G);
+            const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
+            const float ds = p * (dd - dl[j]);
+#pragma unroll
+            for (int k = 0; k < KD; ++k) {
+                dv[k] = __builtin_fmaf(p, gv[j][k], dv[k]);
+                dk[k] = __builtin_fmaf(ds, qv[j][k], dk[k]);
+            }
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < KD; ++k) {
+            dk[k] += __shfl_xor(dk[k], off, kWave);
+            dv[k] += __shfl_xor(dv[k], off, kWave);
+        }
+    if (grp != 0) return;
+#pragma unroll
+    for (int k = 0; k < KD; ++k) {
+        if (!act[k]) continue;
+        const int64_t o = hoff + gl + k * G;
+        if (it.slot < 0) {
+            VT::store_scalar(a.dK, src * HD + o, dk[k] * a.kscale);
+            VT::store_scalar(a.dV, src * HD + o, dv[k]);
+        } else {
+            a.plan.pacc[it.slot * 2 * HD + o] = dk[k];
+            a.plan.pacc[it.slot * 2 * HD + HD + o] = dv[k];
+        }
+    }
+}
+
+// ------------------------------------------------------------ merges of split rows
+// One wave per (heavy row, region): the row's chunk partials [chunk][width] are
+// added in chunk order; region r of HD elements goes to dst[r] scaled by scale[r].
+template <int DT>
+__global__ __launch_bounds__(kBlock) void bwd_sum_merge_kernel(const Args a, int regions, void* dst0, float scale0,
+                                                               void* dst1, float scale1) {
+    using VT = Vec<DT>;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = blockIdx.y;
+    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
+    const HeavyRow hr = a.plan.heavy[hs];
+    const int64_t HD = (int64_t)a.H * a.D;
+    const int64_t width = HD * regions;
+    void* dst = r == 0 ? dst0 : dst1;
+    const float scale = r == 0 ? scale0 : scale1;
+    const float* pa = a.plan.pacc + hr.base * width + (int64_t)r * HD;
+    for (int64_t j0 = 0; j0 < HD; j0 += kWave * 4) {
+        float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i = 0; i < hr.nch; ++i)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int64_t j = j0 + lane + t * kWave;
+                if (j < HD) A[t] += pa[(int64_t)i * width + j];
+            }
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int64_t j = j0 + lane + t * kWave;
+            if (j < HD) VT::store_scalar(dst, (int64_t)hr.row * HD + j, A[t] * scale);
+        }
+    }
+}
+
+// ------------------------------------------------------------ launchers
+
+template <int DT>
+static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
+    const dim3 block(kBlock);
+    hipError_t err;
+    if (a0.vec) {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx);
+            const bool full = a.R == a.NC * a.G;
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
+                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true><<<grid, block, 0, s>>>(a);
+            else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
+                bwd_dq_vec_kernel<DT, 1, 8, 32, 4, true><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 1)
+                bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 2)
+                bwd_dq_vec_kernel<DT, 2, 4, 0, 0, false><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 3)
+                bwd_dq_vec_kernel<DT, 3, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+            else
+                bwd_dq_vec_kernel<DT, 4, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+        });
+    } else {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx, a.H);
+            switch (a.KD) {
+                case 1: bwd_dq_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
+                case 2: bwd_dq_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
+                case 3: bwd_dq_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
+                default: bwd_dq_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+            }
+        });
+    }
+    if (err != hipSuccess || a0.plan.max_heavy == 0) return err;
+    return for_slices(a0, a0.plan.max_heavy, [&](const Args& a, unsigned gx) {
+        bwd_sum_merge_kernel<DT><<<dim3(gx, 1), block, 0, s>>>(a, 1, a.dQ, a.kscale, nullptr, 0.0f);
+    });
+}
+
+template <int DT>
+static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
+    const dim3 block(kBlock);
+    hipError_t err;
+    if (a0.vec) {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx);
+            const bool full = a.R == a.NC * a.G;
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
+                bwd_dkv_vec_kernel<DT, 2, 4, 64, 16, true><<<grid, block, 0, s>>>(a);
+            else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
+                bwd_dkv_vec_kernel<DT, 1, 8, 32, 4, true><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 1)
+                bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 2)
+                bwd_dkv_vec_kernel<DT, 2, 4, 0, 0, false><<<grid, block, 0, s>>>(a);
+            else if (a.NC == 3)
+                bwd_dkv_vec_kernel<DT, 3, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+            else
+                bwd_dkv_vec_kernel<DT, 4, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+        });
+    } else {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            const dim3 grid(gx, a.H);
+            switch (a.KD) {
+                case 1: bwd_dkv_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
+                case 2: bwd_dkv_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
+                case 3: bwd_dkv_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
+                default: bwd_dkv_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+            }
+        });
+    }
+    if (err != hipSuccess || a0.plan.max_heavy == 0) return err;
+    return for_slices(a0, a0.plan.max_heavy, [&](const Args& a, unsigned gx) {
+        bwd_sum_merge_kernel<DT><<<dim3(gx, 2), block, 0, s>>>(a, 2, a.dK, a.kscale, a.dV, 1.0f);
+    });
+}
+
+hipError_t launch_bwd_dq(const Args& a, hipStream_t s) {
+    return a.dtype == kF32 ? launch_dq_dt<kF32>(a, s) : launch_dq_dt<kBF16>(a, s);
+}
+
+hipError_t launch_bwd_dkv(const Args& a, hipStream_t s) {
+    return a.dtype == kF32 ? launch_dkv_dt<kF32>(a, s) : launch_dkv_dt<kBF16>(a, s);
+}
+
+}  // namespace gt

@@ -125,6 +125,13 @@ __device__ __forceinline__ void load_ids(const int32_t* __restrict__ idx, int64_
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Natural log-sum-exp of a row's scores from the running state of the
+// log2-domain softmax: max m (log2 units) and sum l of 2^(s - m).
+__device__ __forceinline__ float lse_of(float m, float l) { return l > 0.0f ? (m + log2f(l)) * kLn2 : -INFINITY; }
+
 // exp2(a - b) with exp2(-inf - x) = 0 also when b is -inf
 __device__ __forceinline__ float rescale(float a, float b) { return a == -INFINITY ? 0.0f : exp2_(a - b); }
 

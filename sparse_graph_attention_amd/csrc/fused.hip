@@ -169,6 +169,8 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * inv;
             st16_nt(orow + (c * G + gl) * 16, VT::pack(o));
+            const int vi = c * G + gl;
+            if (a.lse_out && (vi & (lph - 1)) == 0) a.lse_out[row * a.H + vi / lph] = lse_of(m[c], l[c]);
         }
     } else {
         const int64_t HD = (int64_t)a.H * a.D;
@@ -291,6 +293,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
 #pragma unroll
         for (int k = 0; k < KD; ++k)
             if (act[k]) VT::store_scalar(a.out, row * HD + hoff + gl + k * G, acc[k] * inv);
+        if (a.lse_out && gl == 0) a.lse_out[row * a.H + h] = lse_of(m, l);
     } else {
         if (gl == 0) {
             a.plan.pm[it.slot * a.H + h] = m;
@@ -340,6 +343,7 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
     float L = 0.0f;
     for (int i = lane; i < nch; i += kWave) L += pl[(int64_t)i * H] * exp2_(pm[(int64_t)i * H] - M);
     L = wave_sum(L);
+    if (a.lse_out && lane == 0) a.lse_out[(int64_t)hr.row * H + h] = lse_of(M, L);
     float A[T];  // D <= 64 * T elements, lane holds d = lane + 64 t
 #pragma unroll
     for (int t = 0; t < T; ++t) A[t] = 0.0f;

@@ -22,7 +22,17 @@ struct Args {
     float* alpha_out;
     int64_t N, E;
     int H, D, dtype;
-    float qscale;  // fused: log2(e)/sqrt(D); SDDMM: 1/sqrt(D)
+    float qscale;  // fused and backward: log2(e)/sqrt(D); SDDMM: 1/sqrt(D)
+    float kscale;  // backward: 1/sqrt(D)
+    // training: the forward's log-sum-exp and the backward's inputs/outputs
+    float* lse_out;      // [N][H], natural log; written by the forward when non-null
+    const float* lse_in; // [N][H]
+    const void* O;       // the forward's output
+    const void* dO;      // gradient of the loss with respect to the output
+    float* delta;        // [N][H] scratch: sum over in-edges of alpha (dO . v) = dO . O
+    void* dQ;
+    void* dK;
+    void* dV;
     Plan plan;
     // lane layout (chosen on the host)
     int vec;       // 1: 16-byte vector layout, 0: scalar layout
@@ -61,6 +71,10 @@ hipError_t launch_fused_merge(const Args& a, hipStream_t s);
 hipError_t launch_sddmm(const Args& a, hipStream_t s);
 hipError_t launch_softmax(const Args& a, hipStream_t s);
 hipError_t launch_spmm(const Args& a, hipStream_t s);
+// Backward: dQ (and delta) over the destination-sorted graph, then dK and dV
+// over the source-sorted one (a.indptr/a.indices/a.plan describe that graph).
+hipError_t launch_bwd_dq(const Args& a, hipStream_t s);
+hipError_t launch_bwd_dkv(const Args& a, hipStream_t s);
 // CSR check: writes error flags into *flags (device memory, cleared first).
 hipError_t launch_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, uint32_t* flags,
                            hipStream_t s);

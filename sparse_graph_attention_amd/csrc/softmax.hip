@@ -13,8 +13,6 @@
 
 namespace gt {
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 __device__ __forceinline__ float expd(float s, float m) { return exp2_((s - m) * kLog2e); }
 
 // Max and sum over the lanes that share a head (lanes congruent mod `hstride`).

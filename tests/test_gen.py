@@ -85,3 +85,23 @@ def test_lognormal_shape():
     assert deg.sum() == 60_000_000
     assert 2_000 < deg.max() < 10_000
     assert 0.001 < (deg == 0).mean() < 0.02
+
+
+def test_source_sorted_is_the_transpose():
+    indptr, indices = gtgen.make_graph("tiny_random")
+    N = len(indptr) - 1
+    tip, tix = gtgen.source_sorted(indptr, indices)
+    assert tip[0] == 0 and tip[-1] == len(indices)
+    fwd = sorted((int(u), v) for v in range(N) for u in indices[indptr[v]:indptr[v + 1]])
+    back = sorted((u, int(v)) for u in range(N) for v in tix[tip[u]:tip[u + 1]])
+    assert fwd == back
+    # out-edges of a source keep destination-CSR order (stable)
+    for u in range(N):
+        assert np.all(np.diff(tix[tip[u]:tip[u + 1]]) >= 0)
+
+
+def test_grad_stream_differs_from_features():
+    Q, K, V = gtgen.make_features(10, 2, 4, gtgen.F32, seed=3)
+    g = gtgen.make_grad(10, 2, 4, gtgen.F32, seed=3)
+    assert g.shape == Q.shape and not np.array_equal(g, Q) and not np.array_equal(g, V)
+    assert np.array_equal(g, gtgen.make_grad(10, 2, 4, gtgen.F32, seed=3))
