@@ -13,7 +13,10 @@ matches the current kernel source), and the CPU oracle timed on a bounded
 sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--no-stages] [--calib-copy]
+                  [--no-cpu-baseline] [--no-stages] [--no-backward] [--calib-copy]
+
+Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM)
+and the backward (gt_sparse_mha_bwd), each event-timed on the same inputs.
 """
 import argparse
 import hashlib
@@ -125,6 +128,60 @@ def time_stages(gt, t, w, steps, warmup):
     return res
 
 
+def backward_bytes(w):
+    """Algorithmic bytes of gt_sparse_mha_bwd: the destination pass gathers K and V
+    per edge and reads Q, dO, out, lse of each row with in-edges, writing dQ (all
+    rows) and delta; the source pass gathers Q, dO, lse and delta per edge and
+    reads K, V of each source with out-edges, writing dK and dV; both CSRs once."""
+    import numpy as np
+
+    b = 4 if w["dtype"] == 0 else 2
+    N, E, H, HD = w["N"], w["E"], w["H"], w["H"] * w["D"]
+    nnz = int((np.diff(w["indptr"]) > 0).sum())
+    nsrc = int((np.bincount(w["indices"], minlength=N) > 0).sum())
+    csr = 4 * E + 8 * (N + 1)
+    dq = E * 2 * HD * b + nnz * (3 * HD * b + 8 * H) + N * HD * b + csr
+    dkv = E * (2 * HD * b + 8 * H) + nsrc * 2 * HD * b + N * 2 * HD * b + csr
+    return dq + dkv
+
+
+def time_backward(gt, t, w, steps, warmup):
+    """Event-timed gt_sparse_mha_bwd (after a gt_sparse_mha_fwd_lse) on the same inputs."""
+    import numpy as np
+    import torch
+
+    import gtgen
+
+    dev = t["Q"].device
+    tip, tix = gtgen.source_sorted(w["indptr"], w["indices"])
+    tip, tix = torch.from_numpy(tip).to(dev), torch.from_numpy(tix).to(dev)
+    g = gtgen.make_grad(w["N"], w["H"], w["D"], w["dtype"], seed=11)
+    dO = (torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16) if g.dtype == np.uint16
+          else torch.from_numpy(g).to(dev))
+    out, lse = gt.gt_sparse_mha_fwd_lse(t["indptr"], t["indices"], t["Q"], t["K"], t["V"])
+    grads = [torch.empty_like(t["Q"]) for _ in range(3)]
+
+    def call():
+        gt.gt_sparse_mha_bwd(t["indptr"], t["indices"], tip, tix, t["Q"], t["K"], t["V"], out, dO, lse, *grads)
+
+    for _ in range(warmup):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    nbytes = backward_bytes(w)
+    res = {"ms": ms, "edge_heads_per_s": w["E"] * w["H"] / (ms * 1e-3), "algorithmic_bytes": nbytes,
+           "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    log("backward: %.3f ms, %.0f GB/s algorithmic (%.0f%% of HBM peak)" % (ms, res["GBps"], 100 * res["frac"]))
+    del grads, out, lse, dO, tip, tix
+    return res
+
+
 def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     """The oracle as it stands on a fixed random sample of destination rows."""
     import numpy as np
@@ -175,6 +232,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip timing the unfused stages")
+    ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -257,10 +315,13 @@ def main():
         },
         "cpu_baseline": None,
         "stages": None,
+        "backward": None,
     }
     out_host = out.float().cpu().numpy() if out.dtype == torch.bfloat16 else out.cpu().numpy()
     if not args.no_stages:
         line["stages"] = time_stages(gt, t, w, max(3, args.steps // 2), 2)
+    if not args.no_backward:
+        line["backward"] = time_backward(gt, t, w, max(3, args.steps // 2), 2)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, out_host)
     print(json.dumps(line), flush=True)
