@@ -239,7 +239,8 @@ class _Bwd:
     def dkv_sources(self, t_indptr, t_indices, Q, K, V, dO, lse, delta, srcs, nthreads=0):
         L = _bind_bwd(self.L)
         t_indptr, t_indices = _csr(t_indptr, t_indices)
-        N, H, D = _shape(Q)
+        _, H, D = _shape(Q)
+        N = len(t_indptr) - 1  # source nodes (rows of K, V, dK, dV)
         srcs = np.ascontiguousarray(srcs, dtype=np.int64)
         Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
         lse = np.ascontiguousarray(lse, dtype=np.float64)
@@ -264,12 +265,53 @@ class _Bwd:
         return dq, dk, dv, lse, delta
 
 
+class _Graph:
+    def coo_to_csr(self, n_dst, src, dst, n_src=None):
+        """(indptr int64[n_dst+1], indices int32[E], perm int64[E]): stable grouping by destination."""
+        L = self.L
+        if not getattr(L, "_graph_bound", False):
+            L.oracle_coo_to_csr.argtypes = [_i64, _i64, _i64, _p, _p, _p, _p, _p]
+            L._graph_bound = True
+        src = np.ascontiguousarray(src, dtype=np.int32)
+        dst = np.ascontiguousarray(dst, dtype=np.int32)
+        if src.shape != dst.shape:
+            raise ValueError("src and dst differ in length")
+        n_src = n_dst if n_src is None else n_src
+        E = len(src)
+        indptr = np.empty(n_dst + 1, dtype=np.int64)
+        indices = np.empty(E, dtype=np.int32)
+        perm = np.empty(E, dtype=np.int64)
+        rc = L.oracle_coo_to_csr(n_dst, n_src, E, _p_(src), _p_(dst), _p_(indptr), _p_(indices), _p_(perm))
+        if rc:
+            raise ValueError("oracle_coo_to_csr rejected its arguments")
+        return indptr, indices, perm
+
+    def source_sorted(self, indptr, indices, n_src=None):
+        """The CSR's edges grouped by source (destinations listed in CSR order)."""
+        indptr, indices = _csr(indptr, indices)
+        n_dst = len(indptr) - 1
+        n_src = n_dst if n_src is None else n_src
+        dst = np.repeat(np.arange(n_dst, dtype=np.int32), np.diff(indptr))
+        t_indptr, t_indices, _ = self.coo_to_csr(n_src, dst, indices, n_src=n_dst)
+        return t_indptr, t_indices
+
+
 for _name in ("row_stats", "dq_rows", "dkv_sources", "bwd"):
     setattr(Oracle, _name, getattr(_Bwd, _name))
+for _name in ("coo_to_csr", "source_sorted"):
+    setattr(Oracle, _name, getattr(_Graph, _name))
 
 
 def bwd(*a, **k):
     return default().bwd(*a, **k)
+
+
+def coo_to_csr(*a, **k):
+    return default().coo_to_csr(*a, **k)
+
+
+def source_sorted(*a, **k):
+    return default().source_sorted(*a, **k)
 
 
 def row_stats(*a, **k):

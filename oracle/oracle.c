@@ -353,3 +353,39 @@ int oracle_dkv_sources(int64_t N, int64_t E, int H, int D, int dtype, const int6
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Graph construction.  "Graph Transformer in a Nutshell", section "Graph   */
+/* Transformer Model": GTModel.forward stacks the (src, dst) pairs of       */
+/* g.edges() into one sparse adjacency matrix and hands it to every layer. */
+/* The attention consumes it grouped by destination (the CSR above); the    */
+/* backward also grouped by source (the transpose).                         */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * COO -> destination-sorted CSR by a counting sort: count the in-degrees,
+ * take their running sum as indptr, then walk the edges in COO order and put
+ * each one at the next free slot of its destination's row.  Row v thus lists
+ * the sources of v's in-edges in COO order; perm[p] (if non-NULL) is the COO
+ * id of the edge at CSR position p.  src in [0, n_src), dst in [0, n_dst);
+ * indptr has n_dst + 1 entries.  Returns 1 for an id out of range.
+ */
+int oracle_coo_to_csr(int64_t n_dst, int64_t n_src, int64_t E, const int32_t* src, const int32_t* dst,
+                      int64_t* indptr, int32_t* indices, int64_t* perm) {
+    if (n_dst < 0 || n_src < 0 || E < 0) return 1;
+    for (int64_t e = 0; e < E; ++e)
+        if (src[e] < 0 || src[e] >= n_src || dst[e] < 0 || dst[e] >= n_dst) return 1;
+    for (int64_t v = 0; v <= n_dst; ++v) indptr[v] = 0;
+    for (int64_t e = 0; e < E; ++e) indptr[dst[e] + 1] += 1;
+    for (int64_t v = 0; v < n_dst; ++v) indptr[v + 1] += indptr[v];
+    int64_t* next = (int64_t*)malloc(sizeof(int64_t) * (size_t)(n_dst > 0 ? n_dst : 1));
+    if (!next) return 2;
+    for (int64_t v = 0; v < n_dst; ++v) next[v] = indptr[v];
+    for (int64_t e = 0; e < E; ++e) {
+        int64_t p = next[dst[e]]++;
+        indices[p] = src[e];
+        if (perm) perm[p] = e;
+    }
+    free(next);
+    return 0;
+}
