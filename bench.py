@@ -13,10 +13,12 @@ matches the current kernel source), and the CPU oracle timed on a bounded
 sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--no-stages] [--no-backward] [--calib-copy]
+                  [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan]
+                  [--calib-copy]
 
-Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM)
-and the backward (gt_sparse_mha_bwd), each event-timed on the same inputs.
+Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM),
+the backward (gt_sparse_mha_bwd), and graph construction (COO to CSR, a plan
+with its transpose, the forward on a plan), each event-timed on the same inputs.
 """
 import argparse
 import hashlib
@@ -182,6 +184,52 @@ def time_backward(gt, t, w, steps, warmup):
     return res
 
 
+def time_plan(gt, t, w, steps):
+    """Graph construction from shuffled COO arrays (gt_coo_to_csr; gt_plan_create_coo with the
+    transpose) and the forward on a plan, event-timed on the current stream."""
+    import numpy as np
+    import torch
+
+    import gtgen
+
+    dev = t["Q"].device
+    N = w["N"]
+    dst = np.repeat(np.arange(N, dtype=np.int32), np.diff(w["indptr"]))
+    order = gtgen.permutation(7, len(dst))
+    src_t = torch.from_numpy(np.ascontiguousarray(w["indices"][order])).to(dev)
+    dst_t = torch.from_numpy(np.ascontiguousarray(dst[order])).to(dev)
+    del dst, order
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        total = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            r = fn()
+            e1.record()
+            torch.cuda.synchronize()
+            total += e0.elapsed_time(e1)
+            if isinstance(r, gt.GtPlan):
+                r.destroy()
+        return total / reps
+
+    res = {"coo_to_csr_ms": timed(lambda: gt.gt_coo_to_csr(src_t, dst_t, N), steps),
+           "plan_create_coo_ms": timed(lambda: gt.gt_plan_create_coo(src_t, dst_t, N, transpose=True), steps)}
+    plan = gt.gt_plan_create_coo(src_t, dst_t, N, transpose=True)
+    out = torch.empty_like(t["Q"])
+    res["fwd_plan_ms"] = timed(lambda: gt.gt_sparse_mha_fwd_plan(plan, t["Q"], t["K"], t["V"], out=out), steps)
+    res["fwd_ms"] = timed(lambda: gt.gt_sparse_mha_fwd(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], out=out),
+                          steps)
+    plan.destroy()
+    res["edges_per_s_coo_to_csr"] = w["E"] / (res["coo_to_csr_ms"] * 1e-3)
+    log("plan: COO->CSR %.3f ms, plan with transpose %.3f ms; forward on a plan %.3f ms vs %.3f ms"
+        % (res["coo_to_csr_ms"], res["plan_create_coo_ms"], res["fwd_plan_ms"], res["fwd_ms"]))
+    del src_t, dst_t, out
+    return res
+
+
 def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     """The oracle as it stands on a fixed random sample of destination rows."""
     import numpy as np
@@ -233,6 +281,7 @@ def main():
     ap.add_argument("--calib-copy", action="store_true")
     ap.add_argument("--no-stages", action="store_true", help="skip timing the unfused stages")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
+    ap.add_argument("--no-plan", action="store_true", help="skip timing graph construction and plans")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -316,12 +365,15 @@ def main():
         "cpu_baseline": None,
         "stages": None,
         "backward": None,
+        "plan": None,
     }
     out_host = out.float().cpu().numpy() if out.dtype == torch.bfloat16 else out.cpu().numpy()
     if not args.no_stages:
         line["stages"] = time_stages(gt, t, w, max(3, args.steps // 2), 2)
     if not args.no_backward:
         line["backward"] = time_backward(gt, t, w, max(3, args.steps // 2), 2)
+    if not args.no_plan:
+        line["plan"] = time_plan(gt, t, w, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, out_host)
     print(json.dumps(line), flush=True)

@@ -107,6 +107,14 @@ def random_coo(seed, N, E, stream=S_GRAPH):
     return src, dst
 
 
+def permutation(seed, n, stream=S_PERM):
+    """A seeded uniform random permutation of range(n) (Fisher-Yates), int64."""
+    out = np.empty(n, dtype=np.int64)
+    if n:
+        lib().gtgen_permutation(seed, stream, n, _ptr(out))
+    return out
+
+
 def coo_to_csr(N, src, dst, return_perm=False):
     """Stable counting sort by destination -> (indptr int64[N+1], indices int32[E])."""
     src = np.ascontiguousarray(src, dtype=np.int32)

@@ -162,6 +162,75 @@ int gt_spmm(const int64_t* indptr, const int32_t* indices, const float* alpha, c
  */
 int gt_validate_csr(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, hipStream_t stream);
 
+/*
+ * Graph construction on the device.  "Graph Transformer in a Nutshell",
+ * section "Graph Transformer Model": GTModel.forward stacks the (src, dst)
+ * pairs of g.edges() into one sparse adjacency matrix and hands it to every
+ * layer.  These calls build that structure once, on the GPU, in the forms the
+ * attention needs; results are unique (stable grouping) and deterministic.
+ *
+ * gt_coo_to_csr: COO edge arrays src, dst (int32[E], edge i = src[i] ->
+ * dst[i]) to the destination-sorted CSR: indptr int64[n_dst + 1], indices
+ * int32[E] (sources), each row's edges in COO order; perm (nullable) int32[E]
+ * gets the COO id of the edge at each CSR position.  Ids must lie in
+ * [0, n_src) and [0, n_dst); ids outside give an unspecified (but in-bounds)
+ * result, which gt_validate_csr detects.  GT_EUNSUPPORTED for E >= 2^31.
+ * Uses the per-stream scratch; asynchronous.
+ */
+int gt_coo_to_csr(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t n_src, int64_t E, int64_t* indptr,
+                  int32_t* indices, int32_t* perm, hipStream_t stream);
+
+/*
+ * A plan: a graph prepared once and reused by every layer and step.  It owns
+ * device copies of the destination-sorted CSR (n_dst rows whose in-edges come
+ * from n_src source nodes), with GT_PLAN_TRANSPOSE also the source-sorted
+ * graph that the backward needs (t_indptr int64[n_src + 1], t_indices
+ * int32[E] holding destinations, each source's out-edges in CSR order), and
+ * the list of rows split into chunks (at the split threshold current when
+ * the plan is built).  n_src != n_dst describes a shard of destination rows
+ * whose sources index a larger K/V: Q, out, lse, dout, dQ have n_dst rows;
+ * K, V, dK, dV have n_src rows.
+ *
+ * gt_plan_create copies a caller CSR; gt_plan_create_coo builds it from COO
+ * arrays as gt_coo_to_csr does.  Both allocate the plan's device memory with
+ * hipMalloc (so they are not for graph capture), enqueue the construction on
+ * `stream` and return without waiting: the plan is ready for work on
+ * `stream`, and for other streams once they are ordered after it.  The
+ * library keeps no caller pointer.  gt_plan_destroy waits for the device to
+ * finish queued work, then frees the plan.  gt_plan_info returns the plan's
+ * sizes and device arrays (owned by the plan; t_* are NULL without
+ * GT_PLAN_TRANSPOSE); any output pointer may be NULL.  gt_plan_copy_graph
+ * copies the plan's graph into caller device arrays of those sizes (any may
+ * be NULL; asking for t_* of a plan without a transpose is GT_EINVAL),
+ * enqueued on `stream`.
+ * Errors: GT_EINVAL for negative sizes, node counts >= 2^31, NULL arrays or
+ * unknown flags; GT_EUNSUPPORTED for E >= 2^31 or too many chunks; GT_ENOMEM.
+ */
+typedef struct gt_plan_s* gt_plan;
+typedef enum { GT_PLAN_TRANSPOSE = 1 } gt_plan_flags;
+int gt_plan_create(const int64_t* indptr, const int32_t* indices, int64_t n_dst, int64_t n_src, int64_t E,
+                   int32_t flags, hipStream_t stream, gt_plan* plan);
+int gt_plan_create_coo(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t n_src, int64_t E,
+                       int32_t flags, hipStream_t stream, gt_plan* plan);
+int gt_plan_destroy(gt_plan plan);
+int gt_plan_info(gt_plan plan, int64_t* n_dst, int64_t* n_src, int64_t* E, const int64_t** indptr,
+                 const int32_t** indices, const int64_t** t_indptr, const int32_t** t_indices);
+int gt_plan_copy_graph(gt_plan plan, int64_t* indptr, int32_t* indices, int64_t* t_indptr, int32_t* t_indices,
+                       hipStream_t stream);
+
+/*
+ * gt_sparse_mha_fwd_lse / gt_sparse_mha_bwd on a plan: the same kernels and
+ * results (bit for bit, for the same graph and split threshold), without
+ * rebuilding the split-row list each call.  lse may be NULL in the forward.
+ * The backward needs a plan built with GT_PLAN_TRANSPOSE (GT_EINVAL
+ * otherwise).  The plan must belong to the current device.
+ */
+int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, void* out, float* lse,
+                           int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
+int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, const void* out,
+                           const void* dout, const float* lse, void* dQ, void* dK, void* dV, int32_t H, int32_t D,
+                           int32_t dtype, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* gt_status_string(int status);
 

@@ -16,7 +16,12 @@ The functions have the names of the C entry points declared in
 * ``gt_sddmm(indptr, indices, Q, K, scores=None)`` -- scores [E][H] (fp32);
 * ``gt_edge_softmax(indptr, scores, alpha=None)`` -- alpha [E][H] (fp32);
 * ``gt_spmm(indptr, indices, alpha, V, out=None)`` -- out [N][H][D];
-* ``gt_validate_csr(indptr, indices, N)`` -- device-side CSR check.
+* ``gt_validate_csr(indptr, indices, N)`` -- device-side CSR check;
+* ``gt_coo_to_csr(src, dst, n_dst)`` -- (indptr, indices[, perm]) built on the GPU;
+* ``gt_plan_create(indptr, indices)`` / ``gt_plan_create_coo(src, dst, n_dst)``
+  -- a reusable graph plan (``GtPlan``), ``gt_plan_destroy``, ``gt_plan_info``,
+  ``gt_plan_copy_graph``;
+* ``gt_sparse_mha_fwd_plan(plan, Q, K, V)`` / ``gt_sparse_mha_bwd_plan(plan, ...)``.
 
 Graphs are destination-sorted CSR: ``indptr`` int64 [N+1], ``indices`` int32
 [E] holding the source of each in-edge.  Features are [N][H][D] tensors of
@@ -32,6 +37,7 @@ from . import _build
 GT_F32, GT_BF16 = 0, 1
 GT_OK, GT_EINVAL, GT_EUNSUPPORTED, GT_ENOMEM, GT_EHIP = 0, 1, 2, 3, 4
 GT_CFG_CHUNK_EDGES = 0
+GT_PLAN_TRANSPOSE = 1
 
 EXPORTS = (
     "gt_sparse_mha_fwd",
@@ -41,6 +47,14 @@ EXPORTS = (
     "gt_edge_softmax",
     "gt_spmm",
     "gt_validate_csr",
+    "gt_coo_to_csr",
+    "gt_plan_create",
+    "gt_plan_create_coo",
+    "gt_plan_destroy",
+    "gt_plan_info",
+    "gt_plan_copy_graph",
+    "gt_sparse_mha_fwd_plan",
+    "gt_sparse_mha_bwd_plan",
     "gt_status_string",
     "gt_last_error",
     "gt_config_set",
@@ -76,6 +90,14 @@ def lib():
         L.gt_edge_softmax.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.gt_spmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_validate_csr.argtypes = [_p, _p, _i64, _i64, _p]
+        L.gt_coo_to_csr.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
+        L.gt_plan_create.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _p, ctypes.POINTER(_p)]
+        L.gt_plan_create_coo.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _p, ctypes.POINTER(_p)]
+        L.gt_plan_destroy.argtypes = [_p]
+        L.gt_plan_info.argtypes = [_p] + [ctypes.POINTER(_i64)] * 3 + [ctypes.POINTER(_p)] * 4
+        L.gt_plan_copy_graph.argtypes = [_p] * 6
+        L.gt_sparse_mha_fwd_plan.argtypes = [_p] * 6 + [_i32, _i32, _i32, _p]
+        L.gt_sparse_mha_bwd_plan.argtypes = [_p] * 10 + [_i32, _i32, _i32, _p]
         L.gt_status_string.restype = ctypes.c_char_p
         L.gt_status_string.argtypes = [ctypes.c_int]
         L.gt_last_error.restype = ctypes.c_char_p
@@ -86,6 +108,9 @@ def lib():
         L.gt_profile_begin.argtypes = [_i32]
         L.gt_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(_i64)]
+        for name in ("gt_coo_to_csr", "gt_plan_create", "gt_plan_create_coo", "gt_plan_destroy", "gt_plan_info",
+                     "gt_plan_copy_graph", "gt_sparse_mha_fwd_plan", "gt_sparse_mha_bwd_plan"):
+            getattr(L, name).restype = ctypes.c_int
         for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
                      "gt_config_set", "gt_profile_begin", "gt_profile_end"):
             getattr(L, name).restype = ctypes.c_int
@@ -256,6 +281,130 @@ def gt_validate_csr(indptr, indices, N=None, stream=None):
         return False
     _check(rc, "gt_validate_csr")
     return True
+
+
+def _coo(src, dst):
+    if src.dtype != torch.int32 or dst.dtype != torch.int32 or src.shape != dst.shape or src.dim() != 1:
+        raise TypeError("src and dst must be int32 vectors of one length")
+    return src.numel()
+
+
+def gt_coo_to_csr(src, dst, n_dst, n_src=None, want_perm=False, stream=None):
+    """(indptr int64[n_dst+1], indices int32[E][, perm int32[E]]), grouped by destination on the GPU."""
+    E = _coo(src, dst)
+    n_src = n_dst if n_src is None else n_src
+    indptr = torch.empty(n_dst + 1, dtype=torch.int64, device=src.device)
+    indices = torch.empty(E, dtype=torch.int32, device=src.device)
+    perm = torch.empty(E, dtype=torch.int32, device=src.device) if want_perm else None
+    _need_gpu(src, dst, indptr, indices, perm)
+    _check(lib().gt_coo_to_csr(_ptr(src), _ptr(dst), n_dst, n_src, E, _ptr(indptr), _ptr(indices), _ptr(perm),
+                               _stream(stream)), "gt_coo_to_csr")
+    return (indptr, indices, perm) if want_perm else (indptr, indices)
+
+
+class GtPlan:
+    """Owner of a gt_plan handle; destroy() (or garbage collection) frees it."""
+
+    def __init__(self, handle):
+        self.handle = handle
+
+    def destroy(self):
+        if self.handle:
+            lib().gt_plan_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.destroy()
+        except Exception:
+            pass
+
+
+def gt_plan_create(indptr, indices, n_src=None, transpose=True, stream=None):
+    n_dst, E = _csr(indptr, indices)
+    n_src = n_dst if n_src is None else n_src
+    _need_gpu(indptr, indices)
+    h = _p()
+    _check(lib().gt_plan_create(_ptr(indptr), _ptr(indices), n_dst, n_src, E,
+                                GT_PLAN_TRANSPOSE if transpose else 0, _stream(stream), ctypes.byref(h)),
+           "gt_plan_create")
+    return GtPlan(h.value)
+
+
+def gt_plan_create_coo(src, dst, n_dst, n_src=None, transpose=True, stream=None):
+    E = _coo(src, dst)
+    n_src = n_dst if n_src is None else n_src
+    _need_gpu(src, dst)
+    h = _p()
+    _check(lib().gt_plan_create_coo(_ptr(src), _ptr(dst), n_dst, n_src, E, GT_PLAN_TRANSPOSE if transpose else 0,
+                                    _stream(stream), ctypes.byref(h)), "gt_plan_create_coo")
+    return GtPlan(h.value)
+
+
+def gt_plan_destroy(plan):
+    plan.destroy()
+
+
+def gt_plan_info(plan):
+    """dict(n_dst, n_src, E, transpose): the plan's sizes."""
+    n = [_i64() for _ in range(3)]
+    tptr = _p()
+    _check(lib().gt_plan_info(plan.handle, *[ctypes.byref(x) for x in n], None, None, ctypes.byref(tptr), None),
+           "gt_plan_info")
+    return dict(n_dst=n[0].value, n_src=n[1].value, E=n[2].value, transpose=bool(tptr.value))
+
+
+def gt_plan_copy_graph(plan, device=None, stream=None):
+    """The plan's (indptr, indices, t_indptr, t_indices) as new device tensors (t_* None without a transpose)."""
+    info = gt_plan_info(plan)
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    ip = torch.empty(info["n_dst"] + 1, dtype=torch.int64, device=device)
+    ix = torch.empty(info["E"], dtype=torch.int32, device=device)
+    tip = torch.empty(info["n_src"] + 1, dtype=torch.int64, device=device) if info["transpose"] else None
+    tix = torch.empty(info["E"], dtype=torch.int32, device=device) if info["transpose"] else None
+    _check(lib().gt_plan_copy_graph(plan.handle, _ptr(ip), _ptr(ix) if info["E"] else None, _ptr(tip),
+                                    _ptr(tix) if (tix is not None and info["E"]) else None, _stream(stream)),
+           "gt_plan_copy_graph")
+    return ip, ix, tip, tix
+
+
+def gt_sparse_mha_fwd_plan(plan, Q, K, V, out=None, lse=None, want_lse=False, stream=None):
+    """out (and lse when want_lse or lse is given) for the plan's graph; Q/out have n_dst rows, K/V n_src."""
+    info = gt_plan_info(plan)
+    if Q.dim() != 3 or Q.shape[0] != info["n_dst"] or K.shape != V.shape or K.shape[0] != info["n_src"] or \
+            K.shape[1:] != Q.shape[1:]:
+        raise ValueError("Q must be [n_dst][H][D], K and V [n_src][H][D]")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    H, D = Q.shape[1], Q.shape[2]
+    out = _like(out, Q, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((info["n_dst"], H), dtype=torch.float32, device=Q.device)
+    if lse is not None and (lse.shape != (info["n_dst"], H) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [n_dst][H]")
+    _need_gpu(Q, K, V, out, lse)
+    _check(lib().gt_sparse_mha_fwd_plan(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), H, D,
+                                        _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd_plan")
+    return (out, lse) if lse is not None else out
+
+
+def gt_sparse_mha_bwd_plan(plan, Q, K, V, out, dout, lse, dQ=None, dK=None, dV=None, stream=None):
+    """(dQ, dK, dV) for the plan's graph (built with a transpose)."""
+    info = gt_plan_info(plan)
+    if Q.dim() != 3 or Q.shape[0] != info["n_dst"] or K.shape != V.shape or K.shape[0] != info["n_src"] or \
+            K.shape[1:] != Q.shape[1:]:
+        raise ValueError("Q must be [n_dst][H][D], K and V [n_src][H][D]")
+    H, D = Q.shape[1], Q.shape[2]
+    for t, name in ((out, "out"), (dout, "dout")):
+        _like(t, Q, name)
+    if lse.shape != (info["n_dst"], H) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [n_dst][H]")
+    dQ, dK, dV = _like(dQ, Q, "dQ"), _like(dK, K, "dK"), _like(dV, K, "dV")
+    _need_gpu(Q, K, V, out, dout, lse, dQ, dK, dV)
+    _check(lib().gt_sparse_mha_bwd_plan(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), _ptr(lse),
+                                        _ptr(dQ), _ptr(dK), _ptr(dV), H, D, _dtype_code(Q), _stream(stream)),
+           "gt_sparse_mha_bwd_plan")
+    return dQ, dK, dV
 
 
 def gt_config_set(key, value):

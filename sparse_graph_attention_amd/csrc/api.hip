@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <map>
+#include <new>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -75,24 +76,36 @@ int get_scratch(hipStream_t stream, size_t bytes, void** out) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Sizes a plan for a graph of N rows and E edges whose chunk partials are
-// `accw` floats wide; returns its scratch bytes (0 when no row can be split,
-// except for the counters).
-size_t plan_bytes(int64_t N, int64_t E, int H, int64_t accw, Plan& p) {
+// A plan has tables (counters, heavy rows, chunk list: built once per graph)
+// and partials (per-chunk results, sized by the features: per call).
+// Sizes the tables for a graph of N rows and E edges at the current split
+// threshold.
+void size_plan(int64_t N, int64_t E, Plan& p) {
     const int64_t C = g_chunk.load();
     p.chunk = C;
     p.max_heavy = std::min<int64_t>(N, E / (C + 1));
     p.max_chunks = p.max_heavy ? E / C + p.max_heavy : 0;
-    return align256(sizeof(PlanCounters)) + align256(sizeof(HeavyRow) * p.max_heavy) +
-           align256(sizeof(ChunkRef) * p.max_chunks) + 2 * align256(sizeof(float) * p.max_chunks * H) +
-           align256(sizeof(float) * p.max_chunks * accw) + align256(sizeof(float) * p.max_heavy * H * 2);
 }
 
-// Points the plan's arrays into scratch at b (laid out as plan_bytes counts them).
-char* carve_plan(char* b, int H, int64_t accw, Plan& p) {
+size_t table_bytes(const Plan& p) {
+    return align256(sizeof(PlanCounters)) + align256(sizeof(HeavyRow) * p.max_heavy) +
+           align256(sizeof(ChunkRef) * p.max_chunks);
+}
+
+// Partials of chunks `accw` floats wide.
+size_t partial_bytes(const Plan& p, int H, int64_t accw) {
+    return 2 * align256(sizeof(float) * p.max_chunks * H) + align256(sizeof(float) * p.max_chunks * accw) +
+           align256(sizeof(float) * p.max_heavy * H * 2);
+}
+
+char* carve_tables(char* b, Plan& p) {
     p.counters = (PlanCounters*)b;               b += align256(sizeof(PlanCounters));
     p.heavy = (HeavyRow*)b;                      b += align256(sizeof(HeavyRow) * p.max_heavy);
     p.chunks = (ChunkRef*)b;                     b += align256(sizeof(ChunkRef) * p.max_chunks);
+    return b;
+}
+
+char* carve_partials(char* b, int H, int64_t accw, Plan& p) {
     p.pm = (float*)b;                            b += align256(sizeof(float) * p.max_chunks * H);
     p.pl = (float*)b;                            b += align256(sizeof(float) * p.max_chunks * H);
     p.pacc = (float*)b;                          b += align256(sizeof(float) * p.max_chunks * accw);
@@ -106,18 +119,19 @@ int check_plan(const Plan& p) {
     return GT_OK;
 }
 
-// Sizes the plan for (N, E), carves it out of the stream's scratch and lists
-// the split rows on the device.
+// Sizes the plan for (N, E), carves tables and partials out of the stream's
+// scratch and lists the split rows on the device.
 int make_plan(const int64_t* indptr, int64_t N, int64_t E, int H, int D, hipStream_t stream, Args& a) {
     (void)indptr;
-    const size_t bytes = plan_bytes(N, E, H, (int64_t)H * D, a.plan);
+    size_plan(N, E, a.plan);
     int rc = check_plan(a.plan);
     if (rc) return rc;
+    const int64_t accw = (int64_t)H * D;
     a.items = a.plan.max_chunks + N;
     void* base = nullptr;
-    rc = get_scratch(stream, bytes, &base);
+    rc = get_scratch(stream, table_bytes(a.plan) + partial_bytes(a.plan, H, accw), &base);
     if (rc) return rc;
-    carve_plan((char*)base, H, (int64_t)H * D, a.plan);
+    carve_partials(carve_tables((char*)base, a.plan), H, accw, a.plan);
     hipError_t e = launch_plan(a, stream);
     if (e != hipSuccess) return hip_fail(e, "plan launch");
     return GT_OK;
@@ -257,6 +271,41 @@ int gt_profile_end(double* kernel_ms, double* call_ms, int64_t* calls) {
 
 namespace {
 
+// The fused forward on a's CSR (a.N rows), features and layout.  Without
+// `tables` the plan is built in the stream's scratch; with them (a prebuilt
+// plan of this graph) only the chunk partials come from scratch.
+int run_fwd(Args& a, const Plan* tables, hipStream_t stream) {
+    hipEvent_t* ev = nullptr;
+    if (g_prof.on && g_prof.used < g_prof.capacity) ev = &g_prof.ev[(size_t)(g_prof.used++) * 4];
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    int rc;
+    if (tables) {
+        const int64_t accw = (int64_t)a.H * a.D;
+        a.plan = *tables;
+        void* base = nullptr;
+        rc = get_scratch(stream, partial_bytes(a.plan, a.H, accw), &base);
+        if (rc) return rc;
+        carve_partials((char*)base, a.H, accw, a.plan);
+        a.items = a.plan.max_chunks + a.N;
+    } else {
+        rc = make_plan(a.indptr, a.N, a.E, a.H, a.D, stream, a);
+        if (rc) return rc;
+    }
+    hipError_t e = launch_fused(a, stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
+    if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+    if (a.plan.max_heavy) {
+        e = launch_fused_merge(a, stream);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    }
+    if (ev) (void)hipEventRecord(ev[3], stream);
+    return GT_OK;
+}
+
+void set_scales(Args& a) {
+    a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)a.D));
+    a.kscale = (float)(1.0 / std::sqrt((double)a.D));
+}
+
 int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V, void* out,
               float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
     int rc = check_common(N, E, H, D, dtype);
@@ -277,22 +326,86 @@ int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, cons
     a.H = H;
     a.D = D;
     a.dtype = dtype;
-    a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)D));
+    set_scales(a);
     choose_layout(a, {Q, K, V, out});
+    return run_fwd(a, nullptr, stream);
+}
 
-    hipEvent_t* ev = nullptr;
-    if (g_prof.on && g_prof.used < g_prof.capacity) ev = &g_prof.ev[(size_t)(g_prof.used++) * 4];
-    if (ev) (void)hipEventRecord(ev[0], stream);
-    rc = make_plan(indptr, N, E, H, D, stream, a);
-    if (rc) return rc;
-    hipError_t e = launch_fused(a, stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
-    if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
-    if (a.plan.max_heavy) {
-        e = launch_fused_merge(a, stream);
-        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+// The backward: a over the destination-sorted graph (a.N destinations), at
+// over the source-sorted one (at.N sources).  Without tables both plans are
+// built in scratch; with them only partials and delta come from scratch.
+int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStream_t stream) {
+    const int64_t HD = (int64_t)a.H * a.D;
+    size_t bytes = align256(sizeof(float) * (size_t)a.N * a.H);  // delta
+    if (tables) {
+        a.plan = *tables;
+        at.plan = *t_tables;
+    } else {
+        size_plan(a.N, a.E, a.plan);
+        size_plan(at.N, at.E, at.plan);
+        int rc = check_plan(a.plan);
+        if (!rc) rc = check_plan(at.plan);
+        if (rc) return rc;
+        bytes += table_bytes(a.plan) + table_bytes(at.plan);
     }
-    if (ev) (void)hipEventRecord(ev[3], stream);
+    bytes += partial_bytes(a.plan, a.H, HD) + partial_bytes(at.plan, a.H, 2 * HD);
+    void* base = nullptr;
+    int rc = get_scratch(stream, bytes, &base);
+    if (rc) return rc;
+    char* p = (char*)base;
+    a.delta = at.delta = (float*)p;
+    p += align256(sizeof(float) * (size_t)a.N * a.H);
+    if (!tables) {
+        p = carve_tables(p, a.plan);
+        p = carve_tables(p, at.plan);
+    }
+    p = carve_partials(p, a.H, HD, a.plan);
+    carve_partials(p, a.H, 2 * HD, at.plan);
+    a.items = a.plan.max_chunks + a.N;
+    at.items = at.plan.max_chunks + at.N;
+    hipError_t e = hipSuccess;
+    if (!tables) {
+        e = launch_plan(a, stream);
+        if (e == hipSuccess) e = launch_plan(at, stream);
+        if (e != hipSuccess) return hip_fail(e, "plan launch");
+    }
+    e = launch_bwd_dq(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
+    e = launch_bwd_dkv(at, stream);
+    if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
     return GT_OK;
+}
+
+// Arguments of the backward over (destination CSR, source CSR) with n_dst
+// destinations (rows of Q, out, dout, lse, dQ) and n_src sources (rows of K,
+// V, dK, dV).
+void bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
+              const int32_t* t_indices, const void* Q, const void* K, const void* V, const void* out, const void* dout,
+              const float* lse, void* dQ, void* dK, void* dV, int64_t n_dst, int64_t n_src, int64_t E, int32_t H,
+              int32_t D, int32_t dtype) {
+    a = Args{};
+    a.indptr = indptr;
+    a.indices = indices;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.O = out;
+    a.dO = dout;
+    a.lse_in = lse;
+    a.dQ = dQ;
+    a.dK = dK;
+    a.dV = dV;
+    a.N = n_dst;
+    a.E = E;
+    a.H = H;
+    a.D = D;
+    a.dtype = dtype;
+    set_scales(a);
+    choose_layout(a, {Q, K, V, out, dout, dQ, dK, dV});
+    at = a;
+    at.indptr = t_indptr;
+    at.indices = t_indices;
+    at.N = n_src;
 }
 
 }  // namespace
@@ -321,56 +434,9 @@ int gt_sparse_mha_bwd(const int64_t* indptr, const int32_t* indices, const int64
     if (!indptr || !t_indptr || !Q || !K || !V || !out || !dout || !lse || !dQ || !dK || !dV)
         return fail(GT_EINVAL, "NULL array with N > 0");
     if (E > 0 && (!indices || !t_indices)) return fail(GT_EINVAL, "NULL indices with E > 0");
-    Args a{};
-    a.indices = indices;
-    a.Q = Q;
-    a.K = K;
-    a.V = V;
-    a.O = out;
-    a.dO = dout;
-    a.lse_in = lse;
-    a.dQ = dQ;
-    a.dK = dK;
-    a.dV = dV;
-    a.N = N;
-    a.E = E;
-    a.H = H;
-    a.D = D;
-    a.dtype = dtype;
-    a.qscale = (float)(1.4426950408889634074 / std::sqrt((double)D));
-    a.kscale = (float)(1.0 / std::sqrt((double)D));
-    choose_layout(a, {Q, K, V, out, dout, dQ, dK, dV});
-    const int64_t HD = (int64_t)H * D;
-
-    // scratch: plan over destinations (dQ partials HD wide), plan over sources
-    // (dK and dV partials, 2 HD wide), and delta [N][H]
-    Args at = a;
-    const size_t b1 = plan_bytes(N, E, H, HD, a.plan);
-    const size_t b2 = plan_bytes(N, E, H, 2 * HD, at.plan);
-    rc = check_plan(a.plan);
-    if (!rc) rc = check_plan(at.plan);
-    if (rc) return rc;
-    void* base = nullptr;
-    rc = get_scratch(stream, b1 + b2 + align256(sizeof(float) * (size_t)N * H), &base);
-    if (rc) return rc;
-    char* p = carve_plan((char*)base, H, HD, a.plan);
-    p = carve_plan(p, H, 2 * HD, at.plan);
-    a.delta = at.delta = (float*)p;
-
-    a.indptr = indptr;
-    a.indices = indices;
-    a.items = a.plan.max_chunks + N;
-    at.indptr = t_indptr;
-    at.indices = t_indices;
-    at.items = at.plan.max_chunks + N;
-    hipError_t e = launch_plan(a, stream);
-    if (e == hipSuccess) e = launch_plan(at, stream);
-    if (e != hipSuccess) return hip_fail(e, "plan launch");
-    e = launch_bwd_dq(a, stream);
-    if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
-    e = launch_bwd_dkv(at, stream);
-    if (e != hipSuccess) return hip_fail(e, "dK/dV kernel launch");
-    return GT_OK;
+    Args a, at;
+    bwd_args(a, at, indptr, indices, t_indptr, t_indices, Q, K, V, out, dout, lse, dQ, dK, dV, N, N, E, H, D, dtype);
+    return run_bwd(a, at, nullptr, nullptr, stream);
 }
 
 int gt_sddmm(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, float* scores, int64_t N,
@@ -442,6 +508,291 @@ int gt_spmm(const int64_t* indptr, const int32_t* indices, const float* alpha, c
     if (rc) return rc;
     hipError_t e = launch_spmm(a, stream);
     return e == hipSuccess ? GT_OK : hip_fail(e, "spmm launch");
+}
+
+// ------------------------------------------------------------------ graph plans
+
+}  // extern "C"
+
+struct gt_plan_s {
+    int device = 0;
+    int64_t n_dst = 0, n_src = 0, E = 0;
+    int flags = 0;
+    void* mem = nullptr;
+    int64_t* indptr = nullptr;
+    int32_t* indices = nullptr;
+    int64_t* t_indptr = nullptr;
+    int32_t* t_indices = nullptr;
+    Plan tables{};    // split rows of the destination-sorted graph
+    Plan t_tables{};  // split rows of the source-sorted graph
+};
+
+namespace {
+
+int check_graph(int64_t n_dst, int64_t n_src, int64_t E) {
+    if (n_dst < 0 || n_src < 0 || E < 0) return fail(GT_EINVAL, "node and edge counts must be >= 0");
+    if (n_dst >= ((int64_t)1 << 31) || n_src >= ((int64_t)1 << 31)) return fail(GT_EINVAL, "node counts must be < 2^31");
+    if (E >= ((int64_t)1 << 31)) return fail(GT_EUNSUPPORTED, "graph construction needs E < 2^31 (E = %lld)", (long long)E);
+    return GT_OK;
+}
+
+// Groups E items by key (keys < nrows), stably: offsets[nrows + 1] from the
+// sorted keys, and out[j] = vals_src[position of the j-th item]; the sorted
+// positions go to perm when it is non-null.  `scratch` holds
+// sort_scratch_bytes(E).
+hipError_t group_by_key(const uint32_t* keys, const uint32_t* vals_src, int64_t E, int64_t nrows, int64_t* offsets,
+                        uint32_t* out, uint32_t* perm, void* scratch, hipStream_t s) {
+    const uint32_t *ks = nullptr, *vs = nullptr;
+    hipError_t e = radix_sort_pairs(keys, nullptr, E, key_bits_for(nrows), scratch, perm, s, &ks, &vs);
+    if (e == hipSuccess) e = launch_lower_bounds(ks, E, nrows, offsets, s);
+    if (e == hipSuccess) e = launch_gather_u32(vals_src, vs, out, E, s);
+    return e;
+}
+
+// Source-sorted copy of a destination-sorted graph in the plan.
+int build_transpose(gt_plan_s* P, hipStream_t stream) {
+    void* base = nullptr;
+    const size_t rows_bytes = align256(sizeof(uint32_t) * (size_t)P->E);
+    int rc = get_scratch(stream, rows_bytes + sort_scratch_bytes(P->E), &base);
+    if (rc) return rc;
+    uint32_t* rows = (uint32_t*)base;
+    hipError_t e = launch_row_of_position(P->indptr, P->n_dst, P->E, rows, stream);
+    if (e == hipSuccess)
+        e = group_by_key((const uint32_t*)P->indices, rows, P->E, P->n_src, P->t_indptr, (uint32_t*)P->t_indices,
+                         nullptr, (char*)base + rows_bytes, stream);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "transpose launch");
+}
+
+// Allocates a plan for (n_dst, n_src, E): CSR, transpose (with
+// GT_PLAN_TRANSPOSE) and the split-row tables, in one device allocation.
+int alloc_plan(int64_t n_dst, int64_t n_src, int64_t E, int32_t flags, gt_plan_s** out) {
+    if (flags & ~GT_PLAN_TRANSPOSE) return fail(GT_EINVAL, "unknown plan flags 0x%x", flags);
+    auto* P = new (std::nothrow) gt_plan_s;
+    if (!P) return fail(GT_ENOMEM, "host allocation of a plan failed");
+    P->n_dst = n_dst;
+    P->n_src = n_src;
+    P->E = E;
+    P->flags = flags;
+    const bool tr = flags & GT_PLAN_TRANSPOSE;
+    size_plan(n_dst, E, P->tables);
+    size_plan(tr ? n_src : 0, tr ? E : 0, P->t_tables);
+    int rc = check_plan(P->tables);
+    if (!rc) rc = check_plan(P->t_tables);
+    hipError_t e = hipSuccess;
+    if (!rc) e = hipGetDevice(&P->device);
+    if (!rc && e != hipSuccess) rc = hip_fail(e, "hipGetDevice");
+    const size_t bytes = align256(sizeof(int64_t) * (size_t)(n_dst + 1)) + align256(sizeof(int32_t) * (size_t)E) +
+                         (tr ? align256(sizeof(int64_t) * (size_t)(n_src + 1)) + align256(sizeof(int32_t) * (size_t)E)
+                             : 0) +
+                         table_bytes(P->tables) + table_bytes(P->t_tables);
+    if (!rc) {
+        e = hipMalloc(&P->mem, bytes);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            P->mem = nullptr;
+            rc = fail(GT_ENOMEM, "hipMalloc of %zu plan bytes failed: %s", bytes, hipGetErrorString(e));
+        }
+    }
+    if (rc) {
+        delete P;
+        return rc;
+    }
+    char* b = (char*)P->mem;
+    P->indptr = (int64_t*)b;      b += align256(sizeof(int64_t) * (size_t)(n_dst + 1));
+    P->indices = (int32_t*)b;     b += align256(sizeof(int32_t) * (size_t)E);
+    if (tr) {
+        P->t_indptr = (int64_t*)b;   b += align256(sizeof(int64_t) * (size_t)(n_src + 1));
+        P->t_indices = (int32_t*)b;  b += align256(sizeof(int32_t) * (size_t)E);
+    }
+    b = carve_tables(b, P->tables);
+    carve_tables(b, P->t_tables);
+    *out = P;
+    return GT_OK;
+}
+
+// With the plan's CSR in place: the transpose if asked for, then the tables.
+int finish_plan(gt_plan_s* P, hipStream_t stream) {
+    int rc = GT_OK;
+    if (P->flags & GT_PLAN_TRANSPOSE) rc = build_transpose(P, stream);
+    if (rc) return rc;
+    Args a{};
+    a.indptr = P->indptr;
+    a.N = P->n_dst;
+    a.plan = P->tables;
+    hipError_t e = launch_plan(a, stream);
+    if (e == hipSuccess && (P->flags & GT_PLAN_TRANSPOSE)) {
+        a.indptr = P->t_indptr;
+        a.N = P->n_src;
+        a.plan = P->t_tables;
+        e = launch_plan(a, stream);
+    }
+    return e == hipSuccess ? GT_OK : hip_fail(e, "plan launch");
+}
+
+void free_plan(gt_plan_s* P) {
+    if (!P) return;
+    if (P->mem) {
+        (void)hipDeviceSynchronize();  // no queued kernel may still read it
+        (void)hipFree(P->mem);
+    }
+    delete P;
+}
+
+int check_plan_use(const gt_plan_s* P) {
+    if (!P) return fail(GT_EINVAL, "NULL plan");
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev != P->device) return fail(GT_EINVAL, "plan was built on device %d, current device is %d", P->device, dev);
+    return GT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gt_coo_to_csr(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t n_src, int64_t E, int64_t* indptr,
+                  int32_t* indices, int32_t* perm, hipStream_t stream) {
+    int rc = check_graph(n_dst, n_src, E);
+    if (rc) return rc;
+    if (!indptr) return fail(GT_EINVAL, "NULL indptr");
+    if (E > 0 && (!src || !dst || !indices)) return fail(GT_EINVAL, "NULL COO or indices array with E > 0");
+    void* base = nullptr;
+    rc = get_scratch(stream, sort_scratch_bytes(E), &base);
+    if (rc) return rc;
+    hipError_t e = group_by_key((const uint32_t*)dst, (const uint32_t*)src, E, n_dst, indptr, (uint32_t*)indices,
+                                (uint32_t*)perm, base, stream);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "COO to CSR launch");
+}
+
+int gt_plan_create(const int64_t* indptr, const int32_t* indices, int64_t n_dst, int64_t n_src, int64_t E,
+                   int32_t flags, hipStream_t stream, gt_plan* plan) {
+    if (!plan) return fail(GT_EINVAL, "NULL plan pointer");
+    *plan = nullptr;
+    int rc = check_graph(n_dst, n_src, E);
+    if (rc) return rc;
+    if (!indptr) return fail(GT_EINVAL, "NULL indptr");
+    if (E > 0 && !indices) return fail(GT_EINVAL, "NULL indices with E > 0");
+    gt_plan_s* P = nullptr;
+    rc = alloc_plan(n_dst, n_src, E, flags, &P);
+    if (rc) return rc;
+    hipError_t e = hipMemcpyAsync(P->indptr, indptr, sizeof(int64_t) * (size_t)(n_dst + 1), hipMemcpyDeviceToDevice,
+                                  stream);
+    if (e == hipSuccess && E > 0)
+        e = hipMemcpyAsync(P->indices, indices, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToDevice, stream);
+    rc = e == hipSuccess ? finish_plan(P, stream) : hip_fail(e, "CSR copy");
+    if (rc) {
+        free_plan(P);
+        return rc;
+    }
+    *plan = P;
+    return GT_OK;
+}
+
+int gt_plan_create_coo(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t n_src, int64_t E,
+                       int32_t flags, hipStream_t stream, gt_plan* plan) {
+    if (!plan) return fail(GT_EINVAL, "NULL plan pointer");
+    *plan = nullptr;
+    int rc = check_graph(n_dst, n_src, E);
+    if (rc) return rc;
+    if (E > 0 && (!src || !dst)) return fail(GT_EINVAL, "NULL COO array with E > 0");
+    gt_plan_s* P = nullptr;
+    rc = alloc_plan(n_dst, n_src, E, flags, &P);
+    if (rc) return rc;
+    void* base = nullptr;
+    rc = get_scratch(stream, sort_scratch_bytes(E), &base);
+    if (!rc) {
+        hipError_t e = group_by_key((const uint32_t*)dst, (const uint32_t*)src, E, n_dst, P->indptr,
+                                    (uint32_t*)P->indices, nullptr, base, stream);
+        rc = e == hipSuccess ? finish_plan(P, stream) : hip_fail(e, "COO to CSR launch");
+    }
+    if (rc) {
+        free_plan(P);
+        return rc;
+    }
+    *plan = P;
+    return GT_OK;
+}
+
+int gt_plan_destroy(gt_plan plan) {
+    free_plan(plan);
+    return GT_OK;
+}
+
+int gt_plan_info(gt_plan plan, int64_t* n_dst, int64_t* n_src, int64_t* E, const int64_t** indptr,
+                 const int32_t** indices, const int64_t** t_indptr, const int32_t** t_indices) {
+    if (!plan) return fail(GT_EINVAL, "NULL plan");
+    if (n_dst) *n_dst = plan->n_dst;
+    if (n_src) *n_src = plan->n_src;
+    if (E) *E = plan->E;
+    if (indptr) *indptr = plan->indptr;
+    if (indices) *indices = plan->indices;
+    if (t_indptr) *t_indptr = plan->t_indptr;
+    if (t_indices) *t_indices = plan->t_indices;
+    return GT_OK;
+}
+
+int gt_plan_copy_graph(gt_plan plan, int64_t* indptr, int32_t* indices, int64_t* t_indptr, int32_t* t_indices,
+                       hipStream_t stream) {
+    int rc = check_plan_use(plan);
+    if (rc) return rc;
+    if ((t_indptr || t_indices) && !(plan->flags & GT_PLAN_TRANSPOSE))
+        return fail(GT_EINVAL, "the plan was built without GT_PLAN_TRANSPOSE");
+    struct Item {
+        void* dst;
+        const void* src;
+        size_t bytes;
+    } items[4] = {{indptr, plan->indptr, sizeof(int64_t) * (size_t)(plan->n_dst + 1)},
+                  {indices, plan->indices, sizeof(int32_t) * (size_t)plan->E},
+                  {t_indptr, plan->t_indptr, sizeof(int64_t) * (size_t)(plan->n_src + 1)},
+                  {t_indices, plan->t_indices, sizeof(int32_t) * (size_t)plan->E}};
+    for (const Item& it : items) {
+        if (!it.dst || it.bytes == 0) continue;
+        hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, stream);
+        if (e != hipSuccess) return hip_fail(e, "plan graph copy");
+    }
+    return GT_OK;
+}
+
+int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, void* out, float* lse,
+                           int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
+    int rc = check_plan_use(plan);
+    if (!rc) rc = check_common(plan->n_dst, plan->E, H, D, dtype);
+    if (rc) return rc;
+    if (plan->n_dst == 0) return GT_OK;
+    if (!Q || !out || (plan->E > 0 && (!K || !V))) return fail(GT_EINVAL, "NULL feature array");
+    Args a{};
+    a.indptr = plan->indptr;
+    a.indices = plan->indices;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.out = out;
+    a.lse_out = lse;
+    a.N = plan->n_dst;
+    a.E = plan->E;
+    a.H = H;
+    a.D = D;
+    a.dtype = dtype;
+    set_scales(a);
+    choose_layout(a, {Q, K, V, out});
+    return run_fwd(a, &plan->tables, stream);
+}
+
+int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, const void* out,
+                           const void* dout, const float* lse, void* dQ, void* dK, void* dV, int32_t H, int32_t D,
+                           int32_t dtype, hipStream_t stream) {
+    int rc = check_plan_use(plan);
+    if (!rc) rc = check_common(std::max(plan->n_dst, plan->n_src), plan->E, H, D, dtype);
+    if (rc) return rc;
+    if (!(plan->flags & GT_PLAN_TRANSPOSE)) return fail(GT_EINVAL, "the plan was built without GT_PLAN_TRANSPOSE");
+    if (plan->n_dst == 0 && plan->n_src == 0) return GT_OK;
+    if ((plan->n_dst > 0 && (!Q || !out || !dout || !lse || !dQ)) || (plan->n_src > 0 && (!K || !V || !dK || !dV)))
+        return fail(GT_EINVAL, "NULL array");
+    Args a, at;
+    bwd_args(a, at, plan->indptr, plan->indices, plan->t_indptr, plan->t_indices, Q, K, V, out, dout, lse, dQ, dK, dV,
+             plan->n_dst, plan->n_src, plan->E, H, D, dtype);
+    return run_bwd(a, at, &plan->tables, &plan->t_tables, stream);
 }
 
 int gt_validate_csr(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, hipStream_t stream) {

@@ -1,0 +1,316 @@
+// graph.hip -- graph construction on the device: a stable LSD radix sort of
+// 32-bit keys carrying 32-bit values, an exclusive scan, and the helpers that
+// turn sorted keys into a CSR (row offsets by binary search, row ids of CSR
+// positions, gathers).
+//
+// "Graph Transformer in a Nutshell", section "Graph Transformer Model":
+// GTModel.forward stacks the (src, dst) pairs of g.edges() into one sparse
+// adjacency matrix used by all its layers.  Here that matrix is built once on
+// the device, grouped by destination (the attention's CSR) and by source (the
+// backward's transpose): a stable sort of the edges by destination id (or
+// source id) keeps each row's edges in their input order, so the result is
+// unique and bit-reproducible.
+//
+// Sort pass (8-bit digits, tiles of kSortTile keys per block of 4 waves):
+//  1. radix_count_kernel: per-tile digit histogram -> hist[digit][tile];
+//  2. exclusive scan of hist in that digit-major order -> the first output
+//     slot of each (digit, tile);
+//  3. radix_scatter_kernel: each wave ranks its keys in input order with a
+//     ballot multisplit (lanes with equal digits find each other through one
+//     ballot per key bit; the lowest such lane takes their slots with one LDS
+//     atomic), then adds the counts of earlier waves of its tile.
+// Keys of equal digit keep their input order, so every pass is stable.
+#include "kernels.hpp"
+
+namespace gt {
+
+namespace {
+
+constexpr int kSortWaves = 4;
+constexpr int kSortItems = 8;                               // 64-key chunks per wave
+constexpr int kWaveSpan = kWave * kSortItems;               // keys per wave
+constexpr int64_t kSortTile = (int64_t)kSortWaves * kWaveSpan;  // keys per block
+constexpr int kScanThreads = 256;
+constexpr int kScanItems = 16;
+constexpr int64_t kScanTile = (int64_t)kScanThreads * kScanItems;
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane ? (~0ull >> (64 - lane)) : 0ull; }
+
+// Lanes of the wave whose key has the same digit (and are in range).
+__device__ __forceinline__ uint64_t digit_peers(uint32_t digit, int bits, bool valid) {
+    uint64_t peers = __ballot(valid);
+    for (int b = 0; b < bits; ++b) {
+        const bool bit = (digit >> b) & 1u;
+        const uint64_t ones = __ballot(bit);
+        peers &= bit ? ones : ~ones;
+    }
+    return valid ? peers : 0ull;
+}
+
+__global__ __launch_bounds__(kSortWaves * kWave) void radix_count_kernel(const uint32_t* __restrict__ keys, int64_t n,
+                                                                          int shift, int bits, uint32_t* hist,
+                                                                          int64_t ntiles) {
+    __shared__ uint32_t cnt[256];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
+    cnt[t] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)w * kWaveSpan;
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int i = 0; i < kSortItems; ++i) {
+        const int64_t e = base + (int64_t)i * kWave + lane;
+        const bool valid = e < n;
+        const uint32_t d = valid ? (keys[e] >> shift) & mask : 0u;
+        const uint64_t peers = digit_peers(d, bits, valid);
+        if (valid && (int)__builtin_ctzll(peers) == lane) atomicAdd(&cnt[d], (uint32_t)__builtin_popcountll(peers));
+    }
+    __syncthreads();
+    if (t <= (int)mask) hist[(int64_t)t * ntiles + blockIdx.x] = cnt[t];
+}
+
+template <bool IOTA>
+__global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
+    uint32_t* __restrict__ vals_out, int64_t n, int shift, int bits, const uint32_t* __restrict__ first,
+    int64_t ntiles) {
+    __shared__ uint32_t cnt[kSortWaves][256];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
+    for (int j = 0; j < kSortWaves; ++j) cnt[j][t] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)w * kWaveSpan;
+    const uint32_t mask = (1u << bits) - 1u;
+    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const int64_t e = base + (int64_t)i * kWave + lane;
+        const bool valid = e < n;
+        key[i] = valid ? keys_in[e] : 0u;
+        val[i] = valid ? (IOTA ? (uint32_t)e : vals_in[e]) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const int64_t e = base + (int64_t)i * kWave + lane;
+        const bool valid = e < n;
+        const uint32_t d = (key[i] >> shift) & mask;
+        const uint64_t peers = digit_peers(d, bits, valid);
+        const int leader = valid ? (int)__builtin_ctzll(peers) : lane;
+        uint32_t old = 0;
+        if (valid && leader == lane) old = atomicAdd(&cnt[w][d], (uint32_t)__builtin_popcountll(peers));
+        old = __shfl(old, leader, kWave);
+        rank[i] = old + (uint32_t)__builtin_popcountll(peers & lanes_below(lane));
+    }
+    __syncthreads();
+    if (t <= (int)mask) {  // counts of earlier waves of the tile, per digit
+        uint32_t run = 0;
+        for (int j = 0; j < kSortWaves; ++j) {
+            const uint32_t c = cnt[j][t];
+            cnt[j][t] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const int64_t e = base + (int64_t)i * kWave + lane;
+        if (e >= n) continue;
+        const uint32_t d = (key[i] >> shift) & mask;
+        const int64_t pos = (int64_t)first[(int64_t)d * ntiles + blockIdx.x] + cnt[w][d] + rank[i];
+        keys_out[pos] = key[i];
+        vals_out[pos] = val[i];
+    }
+}
+
+// ---------------------------------------------------------------- exclusive scan (uint32)
+
+// Sum of each kScanTile-element tile.
+__global__ __launch_bounds__(kScanThreads) void scan_sums_kernel(const uint32_t* __restrict__ in, int64_t n,
+                                                                  uint32_t* __restrict__ sums) {
+    __shared__ uint32_t part[kScanThreads / kWave];
+    const int t = threadIdx.x;
+    const int64_t b = (int64_t)blockIdx.x * kScanTile;
+    uint32_t s = 0;
+    for (int i = 0; i < kScanItems; ++i) {
+        const int64_t e = b + (int64_t)i * kScanThreads + t;
+        if (e < n) s += in[e];
+    }
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, kWave);
+    if ((t & (kWave - 1)) == 0) part[t >> 6] = s;
+    __syncthreads();
+    if (t == 0) {
+        uint32_t tot = 0;
+        for (int j = 0; j < kScanThreads / kWave; ++j) tot += part[j];
+        sums[blockIdx.x] = tot;
+    }
+}
+
+// out = exclusive scan of in (tile by tile), plus offsets[tile] when given.
+// Thread t owns kScanItems consecutive elements; in and out may alias.
+__global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(const uint32_t* in, uint32_t* out, int64_t n,
+                                                                   const uint32_t* __restrict__ offsets) {
+    __shared__ uint32_t wsum[kScanThreads / kWave];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
+    const int64_t b = (int64_t)blockIdx.x * kScanTile + (int64_t)t * kScanItems;
+    uint32_t x[kScanItems];
+    uint32_t s = 0;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        x[i] = b + i < n ? in[b + i] : 0u;
+        s += x[i];
+    }
+    uint32_t inc = s;  // inclusive scan of thread sums within the wave
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    uint32_t run = offsets ? offsets[blockIdx.x] : 0u;
+    for (int j = 0; j < w; ++j) run += wsum[j];
+    run += inc - s;
+#pragma unroll
+    for (int i = 0; i < kScanItems; ++i) {
+        if (b + i < n) out[b + i] = run;
+        run += x[i];
+    }
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Scratch (in uint32 words) that scan_exclusive needs for n elements.
+int64_t scan_words(int64_t n) {
+    int64_t w = 0;
+    for (int64_t m = cdiv(n, kScanTile); m > 1; m = cdiv(m, kScanTile)) w += m + 64;
+    return w + 64;
+}
+
+// In-place exclusive scan of a[0..n) with tmp of scan_words(n) words.
+hipError_t scan_exclusive(uint32_t* a, int64_t n, uint32_t* tmp, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t tiles = cdiv(n, kScanTile);
+    if (tiles == 1) {
+        scan_apply_kernel<<<1, kScanThreads, 0, s>>>(a, a, n, nullptr);
+        return hipGetLastError();
+    }
+    uint32_t* sums = tmp;
+    scan_sums_kernel<<<(unsigned)tiles, kScanThreads, 0, s>>>(a, n, sums);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    err = scan_exclusive(sums, tiles, tmp + tiles + 64, s);
+    if (err != hipSuccess) return err;
+    scan_apply_kernel<<<(unsigned)tiles, kScanThreads, 0, s>>>(a, a, n, sums);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- CSR helpers
+
+// offsets[v] = number of sorted keys below v, for v in [0, nrows]: the row
+// offsets of the rows the keys name.  One binary search per row.
+__global__ __launch_bounds__(256) void lower_bounds_kernel(const uint32_t* __restrict__ keys, int64_t n, int64_t nrows,
+                                                            int64_t* __restrict__ offsets) {
+    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (v > nrows) return;
+    int64_t lo = 0, hi = n;
+    while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo) >> 1);
+        if ((int64_t)keys[mid] < v)
+            lo = mid + 1;
+        else
+            hi = mid;
+    }
+    offsets[v] = lo;
+}
+
+// rows[p] = the row holding CSR position p (binary search in indptr).
+__global__ __launch_bounds__(256) void row_of_position_kernel(const int64_t* __restrict__ indptr, int64_t nrows,
+                                                               int64_t n, uint32_t* __restrict__ rows) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p >= n) return;
+    int64_t lo = 0, hi = nrows;  // last row r with indptr[r] <= p
+    while (hi - lo > 1) {
+        const int64_t mid = lo + ((hi - lo) >> 1);
+        if (indptr[mid] <= p)
+            lo = mid;
+        else
+            hi = mid;
+    }
+    rows[p] = (uint32_t)lo;
+}
+
+// out[p] = src[idx[p]].
+__global__ __launch_bounds__(256) void gather_kernel(const uint32_t* __restrict__ src, const uint32_t* __restrict__ idx,
+                                                      uint32_t* __restrict__ out, int64_t n) {
+    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (p < n) out[p] = src[idx[p]];
+}
+
+unsigned grid256(int64_t n) { return (unsigned)cdiv(n, 256); }
+
+}  // namespace
+
+int key_bits_for(int64_t nkeys) {
+    int b = 0;
+    while (b < 32 && ((int64_t)1 << b) < nkeys) ++b;
+    return b;
+}
+
+size_t sort_scratch_bytes(int64_t n) {
+    const int64_t tiles = cdiv(n > 0 ? n : 1, kSortTile);
+    return sizeof(uint32_t) * (size_t)(4 * n + 256 * tiles + scan_words(256 * tiles) + 1024);
+}
+
+hipError_t radix_sort_pairs(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int key_bits, void* scratch,
+                            uint32_t* vals_final, hipStream_t s, const uint32_t** keys_sorted,
+                            const uint32_t** vals_sorted) {
+    const int64_t tiles = cdiv(n > 0 ? n : 1, kSortTile);
+    uint32_t* kb[2] = {(uint32_t*)scratch, (uint32_t*)scratch + n};
+    uint32_t* vb[2] = {(uint32_t*)scratch + 2 * n, (uint32_t*)scratch + 3 * n};
+    uint32_t* hist = (uint32_t*)scratch + 4 * n;
+    uint32_t* tmp = hist + 256 * tiles;
+    const int passes = key_bits > 0 ? (key_bits + 7) / 8 : 1;
+    const uint32_t* kin = keys_in;
+    const uint32_t* vin = vals_in;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        const int bits = key_bits - shift < 8 ? (key_bits - shift > 0 ? key_bits - shift : 1) : 8;
+        uint32_t* kout = kb[p & 1];
+        uint32_t* vout = (p == passes - 1 && vals_final) ? vals_final : vb[p & 1];
+        if (n > 0) {
+            radix_count_kernel<<<(unsigned)tiles, kSortWaves * kWave, 0, s>>>(kin, n, shift, bits, hist, tiles);
+            hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+            err = scan_exclusive(hist, ((int64_t)1 << bits) * tiles, tmp, s);
+            if (err != hipSuccess) return err;
+            if (vin)
+                radix_scatter_kernel<false><<<(unsigned)tiles, kSortWaves * kWave, 0, s>>>(kin, vin, kout, vout, n,
+                                                                                        shift, bits, hist, tiles);
+            else
+                radix_scatter_kernel<true><<<(unsigned)tiles, kSortWaves * kWave, 0, s>>>(kin, nullptr, kout, vout, n,
+                                                                                       shift, bits, hist, tiles);
+            err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        }
+        kin = kout;
+        vin = vout;
+    }
+    *keys_sorted = kin;
+    *vals_sorted = vin;
+    return hipSuccess;
+}
+
+hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, int64_t* offsets, hipStream_t s) {
+    lower_bounds_kernel<<<grid256(nrows + 1), 256, 0, s>>>(keys, n, nrows, offsets);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_of_position(const int64_t* indptr, int64_t nrows, int64_t n, uint32_t* rows, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    row_of_position_kernel<<<grid256(n), 256, 0, s>>>(indptr, nrows, n, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_u32(const uint32_t* src, const uint32_t* idx, uint32_t* out, int64_t n, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    gather_kernel<<<grid256(n), 256, 0, s>>>(src, idx, out, n);
+    return hipGetLastError();
+}
+
+}  // namespace gt

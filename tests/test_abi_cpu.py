@@ -104,3 +104,25 @@ def test_binding_refuses_cpu_tensors():
     Q = torch.zeros(1, 8, 64)
     with pytest.raises(ValueError):
         gt.gt_sparse_mha_fwd(indptr, indices, Q, Q, Q)
+
+
+def test_graph_and_plan_reject():
+    L = gt.lib()
+    p = ctypes.c_void_p(1)
+    h = ctypes.c_void_p()
+    assert L.gt_coo_to_csr(p, p, -1, 4, 4, p, p, None, S) == gt.GT_EINVAL
+    assert L.gt_coo_to_csr(p, p, 4, 4, 1 << 31, p, p, None, S) == gt.GT_EUNSUPPORTED
+    assert L.gt_coo_to_csr(p, p, 4, 1 << 31, 4, p, p, None, S) == gt.GT_EINVAL
+    assert L.gt_coo_to_csr(None, p, 4, 4, 4, p, p, None, S) == gt.GT_EINVAL
+    assert L.gt_coo_to_csr(p, p, 4, 4, 4, None, p, None, S) == gt.GT_EINVAL
+    assert L.gt_plan_create(p, p, 4, 4, 4, 0, S, None) == gt.GT_EINVAL
+    assert L.gt_plan_create(p, p, -4, 4, 4, 0, S, ctypes.byref(h)) == gt.GT_EINVAL
+    assert h.value is None
+    assert L.gt_plan_create(p, p, 4, 4, 4, 4, S, ctypes.byref(h)) == gt.GT_EINVAL  # unknown flag
+    assert L.gt_plan_create(None, p, 4, 4, 4, 0, S, ctypes.byref(h)) == gt.GT_EINVAL
+    assert L.gt_plan_create_coo(None, p, 4, 4, 4, 1, S, ctypes.byref(h)) == gt.GT_EINVAL
+    assert L.gt_plan_info(None, None, None, None, None, None, None, None) == gt.GT_EINVAL
+    assert L.gt_plan_destroy(None) == gt.GT_OK
+    assert L.gt_plan_copy_graph(None, p, p, None, None, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_fwd_plan(None, p, p, p, p, None, 8, 64, 0, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_bwd_plan(None, p, p, p, p, p, p, p, p, p, 8, 64, 0, S) == gt.GT_EINVAL
