@@ -286,20 +286,168 @@ class _Graph:
             raise ValueError("oracle_coo_to_csr rejected its arguments")
         return indptr, indices, perm
 
-    def source_sorted(self, indptr, indices, n_src=None):
-        """The CSR's edges grouped by source (destinations listed in CSR order)."""
+    def source_sorted(self, indptr, indices, n_src=None, want_perm=False):
+        """The CSR's edges grouped by source (destinations listed in CSR order);
+        with want_perm also t_perm, the CSR position of each out-edge."""
         indptr, indices = _csr(indptr, indices)
         n_dst = len(indptr) - 1
         n_src = n_dst if n_src is None else n_src
         dst = np.repeat(np.arange(n_dst, dtype=np.int32), np.diff(indptr))
-        t_indptr, t_indices, _ = self.coo_to_csr(n_src, dst, indices, n_src=n_dst)
-        return t_indptr, t_indices
+        t_indptr, t_indices, perm = self.coo_to_csr(n_src, dst, indices, n_src=n_dst)
+        return (t_indptr, t_indices, perm.astype(np.int32)) if want_perm else (t_indptr, t_indices)
 
 
 for _name in ("row_stats", "dq_rows", "dkv_sources", "bwd"):
     setattr(Oracle, _name, getattr(_Bwd, _name))
 for _name in ("coo_to_csr", "source_sorted"):
     setattr(Oracle, _name, getattr(_Graph, _name))
+
+
+_dbl = ctypes.c_double
+_u64 = ctypes.c_uint64
+
+
+def _bind_ex(L):
+    if not getattr(L, "_ex_bound", False):
+        L.oracle_philox_word.restype = _u64
+        L.oracle_philox_word.argtypes = [_u64, _u64]
+        L.oracle_fwd_rows_ex.argtypes = [_i64, _i64, _int, _int, _int] + [_p] * 7 + [_dbl, _u64, _p, _i64, _p, _p, _int]
+        L.oracle_row_stats_ex.argtypes = [_i64, _i64, _int, _int, _int] + [_p] * 8 + [_dbl, _u64, _p, _p, _int]
+        L.oracle_dq_rows_ex.argtypes = ([_i64, _i64, _int, _int, _int] + [_p] * 8 + [_dbl, _u64, _p, _p, _p, _i64]
+                                        + [_p] * 3 + [_int])
+        L.oracle_dkv_sources_ex.argtypes = ([_i64, _i64, _int, _int, _int] + [_p] * 9 + [_dbl, _u64, _p, _p, _p, _i64]
+                                            + [_p] * 2 + [_int])
+        L._ex_bound = True
+    return L
+
+
+def _f32_or_none(x):
+    return None if x is None else np.ascontiguousarray(x, dtype=np.float32)
+
+
+class _Ex:
+    """The logit variants (additive bias [E][H], edge weights [E]) and attention
+    dropout (probability p, generator seed), as defined in oracle.c."""
+
+    def philox_word(self, seed, i):
+        return int(_bind_ex(self.L).oracle_philox_word(seed, i))
+
+    def fwd_ex(self, indptr, indices, Q, K, V, bias=None, ew=None, drop_p=0.0, seed=0, rows=None, want_lse=False,
+               nthreads=0):
+        L = _bind_ex(self.L)
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        rows = np.arange(N, dtype=np.int64) if rows is None else np.ascontiguousarray(rows, dtype=np.int64)
+        Q, K, V = (np.ascontiguousarray(x) for x in (Q, K, V))
+        bias, ew = _f32_or_none(bias), _f32_or_none(ew)
+        out = np.empty((len(rows), H, D))
+        lse = np.empty((len(rows), H)) if want_lse else None
+        rc = L.oracle_fwd_rows_ex(N, len(indices), H, D, _dtype_of(Q), _p_(indptr), _p_(indices), _p_(Q), _p_(K),
+                                  _p_(V), _p_(bias), _p_(ew), float(drop_p), seed, _p_(rows), len(rows), _p_(out),
+                                  _p_(lse), nthreads)
+        if rc:
+            raise ValueError("oracle_fwd_rows_ex rejected its arguments")
+        return (out, lse) if want_lse else out
+
+    def row_stats_ex(self, indptr, indices, Q, K, V, dO, bias=None, ew=None, drop_p=0.0, seed=0, nthreads=0):
+        L = _bind_ex(self.L)
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        bias, ew = _f32_or_none(bias), _f32_or_none(ew)
+        lse = np.empty((N, H))
+        delta = np.empty((N, H))
+        rc = L.oracle_row_stats_ex(N, len(indices), H, D, _dtype_of(Q), _p_(indptr), _p_(indices), _p_(Q), _p_(K),
+                                   _p_(V), _p_(dO), _p_(bias), _p_(ew), float(drop_p), seed, _p_(lse), _p_(delta),
+                                   nthreads)
+        if rc:
+            raise ValueError("oracle_row_stats_ex rejected its arguments")
+        return lse, delta
+
+    def dq_rows_ex(self, indptr, indices, Q, K, V, dO, lse, delta, rows, bias=None, ew=None, drop_p=0.0, seed=0,
+                   dbias=None, dw=None, nthreads=0):
+        """dQ of the rows; fills dbias [E][H] / dw [E] (if given) at the rows' edges."""
+        L = _bind_ex(self.L)
+        indptr, indices = _csr(indptr, indices)
+        N, H, D = _shape(Q)
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        bias, ew = _f32_or_none(bias), _f32_or_none(ew)
+        lse = np.ascontiguousarray(lse, dtype=np.float64)
+        delta = np.ascontiguousarray(delta, dtype=np.float64)
+        for a in (dbias, dw):
+            assert a is None or (a.dtype == np.float64 and a.flags.c_contiguous)
+        dq = np.empty((len(rows), H, D))
+        rc = L.oracle_dq_rows_ex(N, len(indices), H, D, _dtype_of(Q), _p_(indptr), _p_(indices), _p_(Q), _p_(K),
+                                 _p_(V), _p_(dO), _p_(bias), _p_(ew), float(drop_p), seed, _p_(lse), _p_(delta),
+                                 _p_(rows), len(rows), _p_(dq), _p_(dbias), _p_(dw), nthreads)
+        if rc:
+            raise ValueError("oracle_dq_rows_ex rejected its arguments")
+        return dq
+
+    def dkv_sources_ex(self, t_indptr, t_indices, t_perm, Q, K, V, dO, lse, delta, srcs, bias=None, ew=None,
+                       drop_p=0.0, seed=0, nthreads=0):
+        L = _bind_ex(self.L)
+        t_indptr, t_indices = _csr(t_indptr, t_indices)
+        t_perm = np.ascontiguousarray(t_perm, dtype=np.int32)
+        _, H, D = _shape(Q)
+        N = len(t_indptr) - 1
+        srcs = np.ascontiguousarray(srcs, dtype=np.int64)
+        Q, K, V, dO = (np.ascontiguousarray(x) for x in (Q, K, V, dO))
+        bias, ew = _f32_or_none(bias), _f32_or_none(ew)
+        lse = np.ascontiguousarray(lse, dtype=np.float64)
+        delta = np.ascontiguousarray(delta, dtype=np.float64)
+        dk = np.empty((len(srcs), H, D))
+        dv = np.empty((len(srcs), H, D))
+        rc = L.oracle_dkv_sources_ex(N, len(t_indices), H, D, _dtype_of(Q), _p_(t_indptr), _p_(t_indices),
+                                     _p_(t_perm), _p_(Q), _p_(K), _p_(V), _p_(dO), _p_(bias), _p_(ew), float(drop_p),
+                                     seed, _p_(lse), _p_(delta), _p_(srcs), len(srcs), _p_(dk), _p_(dv), nthreads)
+        if rc:
+            raise ValueError("oracle_dkv_sources_ex rejected its arguments")
+        return dk, dv
+
+    def bwd_ex(self, indptr, indices, Q, K, V, dO, bias=None, ew=None, drop_p=0.0, seed=0, nthreads=0):
+        """Whole backward with the variants: dict(dq, dk, dv, dbias, dw, lse, delta), fp64."""
+        N = len(indptr) - 1
+        E = len(indices)
+        H = Q.shape[1]
+        kw = dict(bias=bias, ew=ew, drop_p=drop_p, seed=seed, nthreads=nthreads)
+        lse, delta = self.row_stats_ex(indptr, indices, Q, K, V, dO, **kw)
+        allv = np.arange(N, dtype=np.int64)
+        dbias = np.zeros((E, H))
+        dw = np.zeros(E)
+        dq = self.dq_rows_ex(indptr, indices, Q, K, V, dO, lse, delta, allv, dbias=dbias, dw=dw, **kw)
+        t_indptr, t_indices, t_perm = self.source_sorted(indptr, indices, want_perm=True)
+        dk, dv = self.dkv_sources_ex(t_indptr, t_indices, t_perm, Q, K, V, dO, lse, delta, allv, **kw)
+        return dict(dq=dq, dk=dk, dv=dv, dbias=dbias, dw=dw, lse=lse, delta=delta)
+
+
+for _name in ("philox_word", "fwd_ex", "row_stats_ex", "dq_rows_ex", "dkv_sources_ex", "bwd_ex"):
+    setattr(Oracle, _name, getattr(_Ex, _name))
+
+
+def fwd_ex(*a, **k):
+    return default().fwd_ex(*a, **k)
+
+
+def bwd_ex(*a, **k):
+    return default().bwd_ex(*a, **k)
+
+
+def row_stats_ex(*a, **k):
+    return default().row_stats_ex(*a, **k)
+
+
+def dq_rows_ex(*a, **k):
+    return default().dq_rows_ex(*a, **k)
+
+
+def dkv_sources_ex(*a, **k):
+    return default().dkv_sources_ex(*a, **k)
+
+
+def philox_word(*a, **k):
+    return default().philox_word(*a, **k)
 
 
 def bwd(*a, **k):

@@ -389,3 +389,247 @@ int oracle_coo_to_csr(int64_t n_dst, int64_t n_src, int64_t E, const int32_t* sr
     free(next);
     return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Logit variants and attention dropout.                                    */
+/*  - additive bias: "Graph Transformer theory, derivation and              */
+/*    implementation", section on the shortest-path bias and degree         */
+/*    encoding (Graphormer type), spatial encoding: a learnable scalar is   */
+/*    added to each logit, e_ij = q_i.k_j / sqrt(d_k) + b.  Here any bias   */
+/*    per (edge, head), bias[e*H + h].                                      */
+/*  - edge weights: "Graph Transformer in a Nutshell", section "Sparse      */
+/*    Multi-head Attention": A takes values in [0, 1] and the scaled logit  */
+/*    is the Hadamard product (QK^T) o A / sqrt(d), so a weighted edge      */
+/*    multiplies its scaled dot product: s_e = w_e <q_v, k_u> / sqrt(D)      */
+/*    (+ bias).  The softmax still runs over the stored edges only.         */
+/*  - dropout: the gist's TransLayer.forward applies drop_att to the edge  */
+/*    softmax's output.  In training an attention weight is dropped with    */
+/*    probability p and the kept ones are divided by 1 - p; the softmax's   */
+/*    normaliser is unchanged.  The keep decision for (edge e, head h) uses */
+/*    word i = e*H + h of the counter-based generator Philox4x64-10         */
+/*    (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as easy as  */
+/*    1, 2, 3", SC 2011): block i/4 + 1 under key (seed, 0), word i mod 4;  */
+/*    the weight is kept iff the word's upper 32 bits are >= floor(p 2^32). */
+/* ------------------------------------------------------------------------ */
+
+static uint64_t philox_word(uint64_t seed, uint64_t i) {
+    const uint64_t M0 = 0xD2E7470EE14C6C93ull, M1 = 0xCA5A826395121157ull;
+    const uint64_t W0 = 0x9E3779B97F4A7C15ull, W1 = 0xBB67AE8584CAA73Bull;
+    uint64_t c0 = i / 4 + 1, c1 = 0, c2 = 0, c3 = 0, k0 = seed, k1 = 0;
+    for (int r = 0; r < 10; ++r) {
+        unsigned __int128 p0 = (unsigned __int128)M0 * c0, p1 = (unsigned __int128)M1 * c2;
+        uint64_t hi0 = (uint64_t)(p0 >> 64), lo0 = (uint64_t)p0;
+        uint64_t hi1 = (uint64_t)(p1 >> 64), lo1 = (uint64_t)p1;
+        uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+        c0 = n0;
+        c1 = lo1;
+        c2 = n2;
+        c3 = lo0;
+        k0 += W0;
+        k1 += W1;
+    }
+    switch (i % 4) {
+        case 0: return c0;
+        case 1: return c1;
+        case 2: return c2;
+        default: return c3;
+    }
+}
+
+uint64_t oracle_philox_word(uint64_t seed, uint64_t i) { return philox_word(seed, i); }
+
+/* dropout multiplier of (edge e, head h): 0 or 1 / (1 - p); 1 when p == 0 */
+static double drop_scale(double p, uint64_t seed, int64_t e, int H, int h) {
+    if (p <= 0.0) return 1.0;
+    uint32_t thresh = (uint32_t)floor(p * 4294967296.0);
+    uint32_t hi = (uint32_t)(philox_word(seed, (uint64_t)e * (uint64_t)H + (uint64_t)h) >> 32);
+    return hi >= thresh ? 1.0 / (1.0 - p) : 0.0;
+}
+
+/* logit of edge e (source u) for destination v, head h, with the variants */
+static double edge_logit(const void* Q, const void* K, int dtype, int H, int D, int64_t v, int64_t u, int h,
+                         int64_t e, const float* bias, const float* ew) {
+    double s = edge_score(Q, K, dtype, H, D, v, u, h);
+    if (ew) s *= (double)ew[e];
+    if (bias) s += (double)bias[e * H + h];
+    return s;
+}
+
+static int bad_p(double p) { return !(p >= 0.0 && p < 1.0); }
+
+/*
+ * Forward with the variants for the listed destination rows: out
+ * [nrows][H][D] and (if non-NULL) lse [nrows][H] of the logits.
+ */
+int oracle_fwd_rows_ex(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                       const void* Q, const void* K, const void* V, const float* bias, const float* ew, double drop_p,
+                       uint64_t seed, const int64_t* rows, int64_t nrows, double* out, double* lse, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || nrows < 0 || bad_dtype(dtype) || bad_p(drop_p)) return 1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return 1;
+    int64_t maxdeg = 0;
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t deg = indptr[rows[r] + 1] - indptr[rows[r]];
+        if (deg > maxdeg) maxdeg = deg;
+    }
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(maxdeg > 0 ? maxdeg : 1));
+#pragma omp for schedule(dynamic, 16)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t v = rows[r], b = indptr[v], deg = indptr[v + 1] - b;
+            for (int h = 0; h < H; ++h) {
+                double* o = out + (r * H + h) * (int64_t)D;
+                for (int d = 0; d < D; ++d) o[d] = 0.0;
+                double m = -INFINITY, z = 0.0;
+                for (int64_t i = 0; i < deg; ++i) {
+                    s[i] = edge_logit(Q, K, dtype, H, D, v, indices[b + i], h, b + i, bias, ew);
+                    if (s[i] > m) m = s[i];
+                }
+                for (int64_t i = 0; i < deg; ++i) z += exp(s[i] - m);
+                for (int64_t i = 0; i < deg; ++i) {
+                    double a = exp(s[i] - m) / z * drop_scale(drop_p, seed, b + i, H, h);
+                    int64_t uo = ((int64_t)indices[b + i] * H + h) * (int64_t)D;
+                    for (int d = 0; d < D; ++d) o[d] += a * elem(V, dtype, uo + d);
+                }
+                if (lse) lse[r * H + h] = deg > 0 ? m + log(z) : -INFINITY;
+            }
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * Backward with the variants.  With alpha_e = exp(s_e - lse_v), the dropout
+ * multiplier c_e and da_e = dO_v . v_u:
+ *   delta_v = sum alpha_e c_e da_e (= dO_v . out_v)
+ *   ds_e    = alpha_e (c_e da_e - delta_v)         (= dL/dbias_e)
+ *   dQ_v    = sum over in-edges  ds_e w_e k_u / sqrt(D)
+ *   dK_u    = sum over out-edges ds_e w_e q_v / sqrt(D)
+ *   dV_u    = sum over out-edges alpha_e c_e dO_v
+ *   dw_e    = sum over heads ds_e <q_v, k_u> / sqrt(D)
+ * row_stats_ex: lse and delta [N][H] of every row.
+ */
+int oracle_row_stats_ex(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                        const void* Q, const void* K, const void* V, const void* dO, const float* bias, const float* ew,
+                        double drop_p, uint64_t seed, double* lse, double* delta, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || bad_dtype(dtype) || bad_p(drop_p)) return 1;
+    int64_t maxdeg = 0;
+    for (int64_t v = 0; v < N; ++v)
+        if (indptr[v + 1] - indptr[v] > maxdeg) maxdeg = indptr[v + 1] - indptr[v];
+    set_threads(nthreads);
+#pragma omp parallel
+    {
+        double* s = (double*)malloc(sizeof(double) * (size_t)(maxdeg > 0 ? maxdeg : 1));
+#pragma omp for schedule(dynamic, 64)
+        for (int64_t v = 0; v < N; ++v) {
+            int64_t b = indptr[v], deg = indptr[v + 1] - b;
+            for (int h = 0; h < H; ++h) {
+                double m = -INFINITY, z = 0.0, dl = 0.0;
+                for (int64_t i = 0; i < deg; ++i) {
+                    s[i] = edge_logit(Q, K, dtype, H, D, v, indices[b + i], h, b + i, bias, ew);
+                    if (s[i] > m) m = s[i];
+                }
+                for (int64_t i = 0; i < deg; ++i) z += exp(s[i] - m);
+                double l = deg > 0 ? m + log(z) : -INFINITY;
+                int64_t go = (v * H + h) * (int64_t)D;
+                for (int64_t i = 0; i < deg; ++i) {
+                    double a = exp(s[i] - l) * drop_scale(drop_p, seed, b + i, H, h);
+                    int64_t uo = ((int64_t)indices[b + i] * H + h) * (int64_t)D;
+                    double da = 0.0;
+                    for (int d = 0; d < D; ++d) da += elem(dO, dtype, go + d) * elem(V, dtype, uo + d);
+                    dl += a * da;
+                }
+                lse[v * H + h] = l;
+                delta[v * H + h] = dl;
+            }
+        }
+        free(s);
+    }
+    return 0;
+}
+
+/*
+ * dQ [nrows][H][D] of the listed destination rows; for their edges also
+ * dbias[e*H + h] and dw[e] when those are non-NULL (full-size arrays; other
+ * entries are left as they are).
+ */
+int oracle_dq_rows_ex(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* indptr, const int32_t* indices,
+                      const void* Q, const void* K, const void* V, const void* dO, const float* bias, const float* ew,
+                      double drop_p, uint64_t seed, const double* lse, const double* delta, const int64_t* rows,
+                      int64_t nrows, double* dq, double* dbias, double* dw, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || nrows < 0 || bad_dtype(dtype) || bad_p(drop_p)) return 1;
+    for (int64_t r = 0; r < nrows; ++r)
+        if (rows[r] < 0 || rows[r] >= N) return 1;
+    const double rs = 1.0 / sqrt((double)D);
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t v = rows[r];
+        for (int64_t e = indptr[v]; e < indptr[v + 1]; ++e)
+            if (dw) dw[e] = 0.0;
+        for (int h = 0; h < H; ++h) {
+            double* o = dq + (r * H + h) * (int64_t)D;
+            for (int d = 0; d < D; ++d) o[d] = 0.0;
+            int64_t go = (v * H + h) * (int64_t)D;
+            for (int64_t e = indptr[v]; e < indptr[v + 1]; ++e) {
+                int64_t u = indices[e];
+                int64_t uo = (u * H + h) * (int64_t)D;
+                double dot = edge_score(Q, K, dtype, H, D, v, u, h);
+                double w = ew ? (double)ew[e] : 1.0;
+                double a = exp(edge_logit(Q, K, dtype, H, D, v, u, h, e, bias, ew) - lse[v * H + h]);
+                double da = 0.0;
+                for (int d = 0; d < D; ++d) da += elem(dO, dtype, go + d) * elem(V, dtype, uo + d);
+                double ds = a * (drop_scale(drop_p, seed, e, H, h) * da - delta[v * H + h]);
+                for (int d = 0; d < D; ++d) o[d] += ds * w * elem(K, dtype, uo + d) * rs;
+                if (dbias) dbias[e * H + h] = ds;
+                if (dw) dw[e] += ds * dot;
+            }
+        }
+    }
+    return 0;
+}
+
+/*
+ * dK, dV [nsrc][H][D] of the listed sources over the source-sorted graph;
+ * t_perm[j] is the destination-CSR position of out-edge j (the edge id that
+ * bias, weights and the dropout words are indexed by).
+ */
+int oracle_dkv_sources_ex(int64_t N, int64_t E, int H, int D, int dtype, const int64_t* t_indptr,
+                          const int32_t* t_indices, const int32_t* t_perm, const void* Q, const void* K,
+                          const void* V, const void* dO, const float* bias, const float* ew, double drop_p,
+                          uint64_t seed, const double* lse, const double* delta, const int64_t* srcs, int64_t nsrc,
+                          double* dk, double* dv, int nthreads) {
+    if (N < 0 || E < 0 || H < 1 || D < 1 || nsrc < 0 || bad_dtype(dtype) || bad_p(drop_p)) return 1;
+    for (int64_t r = 0; r < nsrc; ++r)
+        if (srcs[r] < 0 || srcs[r] >= N) return 1;
+    const double rs = 1.0 / sqrt((double)D);
+    set_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 16)
+    for (int64_t r = 0; r < nsrc; ++r) {
+        int64_t u = srcs[r];
+        for (int h = 0; h < H; ++h) {
+            double* ok = dk + (r * H + h) * (int64_t)D;
+            double* ov = dv + (r * H + h) * (int64_t)D;
+            for (int d = 0; d < D; ++d) ok[d] = ov[d] = 0.0;
+            int64_t uo = (u * H + h) * (int64_t)D;
+            for (int64_t j = t_indptr[u]; j < t_indptr[u + 1]; ++j) {
+                int64_t v = t_indices[j], e = t_perm[j];
+                int64_t vo = (v * H + h) * (int64_t)D;
+                double w = ew ? (double)ew[e] : 1.0;
+                double c = drop_scale(drop_p, seed, e, H, h);
+                double a = exp(edge_logit(Q, K, dtype, H, D, v, u, h, e, bias, ew) - lse[v * H + h]);
+                double da = 0.0;
+                for (int d = 0; d < D; ++d) da += elem(dO, dtype, vo + d) * elem(V, dtype, uo + d);
+                double ds = a * (c * da - delta[v * H + h]);
+                for (int d = 0; d < D; ++d) {
+                    ov[d] += a * c * elem(dO, dtype, vo + d);
+                    ok[d] += ds * w * elem(Q, dtype, vo + d) * rs;
+                }
+            }
+        }
+    }
+    return 0;
+}
