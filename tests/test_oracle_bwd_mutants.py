@@ -36,10 +36,12 @@ def workdir():
 def test_bwd_mutant_is_caught(name, workdir):
     old, new = MUTANTS[name]
     src = open(_build.SRC).read()
-    assert src.count(old) == 1, "mutation target must occur once: %r" % old
+    # the plain backward precedes the variants' copy of some of its lines: the
+    # first occurrence is the one in the plain backward
+    assert src.count(old) >= 1, "mutation target not found: %r" % old
     path_c = os.path.join(workdir, "oracle_%s.c" % name)
     path_so = os.path.join(workdir, "liboracle_%s.so" % name)
-    open(path_c, "w").write(src.replace(old, new))
+    open(path_c, "w").write(src.replace(old, new, 1))
     _build.build(src=path_c, out=path_so, extra_flags=("-w",))
     orc = Oracle(path_so)
     failed = []
