@@ -204,12 +204,16 @@ def make_grad(N, H, D, dtype, seed=0, scale=1.0):
     return gen(seed, S_DOUT, (N, H, D), scale)
 
 
-def source_sorted(indptr, indices):
+def source_sorted(indptr, indices, want_perm=False):
     """The same edges grouped by source: (t_indptr, t_indices) with t_indices holding
-    each out-edge's destination, out-edges of a source in destination-CSR order."""
+    each out-edge's destination, out-edges of a source in destination-CSR order;
+    with want_perm also t_perm (int32), each out-edge's destination-CSR position."""
     N = len(indptr) - 1
     dst = np.repeat(np.arange(N, dtype=np.int32), np.diff(indptr))
-    return coo_to_csr(N, dst, np.ascontiguousarray(indices, dtype=np.int32))
+    if not want_perm:
+        return coo_to_csr(N, dst, np.ascontiguousarray(indices, dtype=np.int32))
+    t_indptr, t_indices, perm = coo_to_csr(N, dst, np.ascontiguousarray(indices, dtype=np.int32), return_perm=True)
+    return t_indptr, t_indices, perm.astype(np.int32)
 
 
 def make_workload(name, seed=0, with_features=True):

@@ -163,6 +163,56 @@ int gt_spmm(const int64_t* indptr, const int32_t* indices, const float* alpha, c
 int gt_validate_csr(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, hipStream_t stream);
 
 /*
+ * Logit variants and attention dropout.
+ *  - bias (float32 [E][H], CSR edge order, or NULL) is added to each logit:
+ *    the shortest-path bias of "Graph Transformer theory, derivation and
+ *    implementation" (section on the Graphormer-type shortest-path bias and
+ *    degree encoding: a learnable scalar added to e_ij), or any other
+ *    relative encoding given per edge and head;
+ *  - edge_weight (float32 [E], or NULL) multiplies the scaled dot product:
+ *    A's values in the Hadamard product (QK^T) o A / sqrt(d) of "Graph
+ *    Transformer in a Nutshell" (section "Sparse Multi-head Attention").
+ *    The softmax still runs over the stored edges only;
+ *  - dropout_p in [0, 1): the drop_att of the gist's TransLayer.forward in
+ *    training.  Each weight alpha[e][h] is zeroed with probability p and the
+ *    kept ones are divided by 1 - p; the normaliser is the full softmax's.
+ *    Keep decisions come from the counter-based generator Philox4x64-10
+ *    (Salmon et al., SC 2011) under key (dropout_seed, 0): word i = e*H + h
+ *    is word i mod 4 of counter block (i/4 + 1, 0, 0, 0) (the stream of
+ *    numpy.random.Philox(key=(seed, 0))), and the weight is kept iff the
+ *    word's upper 32 bits are >= floor(p * 2^32) (so p < 2^-32 drops
+ *    nothing and no 1/(1 - p) is applied).  The same seed gives the same
+ *    mask in the forward and the backward.
+ * So s[e][h] = edge_weight[e] * <Q[v,h,:], K[u,h,:]> / sqrt(D) + bias[e][h].
+ */
+typedef struct {
+    const float* bias;
+    const float* edge_weight;
+    double dropout_p;
+    uint64_t dropout_seed;
+} gt_logit_opts;
+
+/* gt_sparse_mha_fwd_lse with options (opts NULL: none; lse may be NULL). */
+int gt_sparse_mha_fwd_ex(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
+                         void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                         const gt_logit_opts* opts, hipStream_t stream);
+
+/*
+ * gt_sparse_mha_bwd with options.  With c_e the dropout multiplier (0 or
+ * 1/(1 - p)) and w_e the edge weight: ds_e = alpha_e (c_e <dout[v], V[u]> -
+ * delta[v]); dQ and dK sums carry w_e; dV[u] sums alpha_e c_e dout[v].
+ * Optional outputs: dbias (float32 [E][H], = ds) and dweight (float32 [E],
+ * = sum over heads of ds <Q[v], K[u]> / sqrt(D)).  t_perm (int32[E]) gives,
+ * for each entry of the transpose, its position in the CSR; it is required
+ * (GT_EINVAL) when bias, edge weights or dropout are on.
+ */
+int gt_sparse_mha_bwd_ex(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
+                         const int32_t* t_indices, const int32_t* t_perm, const void* Q, const void* K, const void* V,
+                         const void* out, const void* dout, const float* lse, void* dQ, void* dK, void* dV,
+                         float* dbias, float* dweight, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                         const gt_logit_opts* opts, hipStream_t stream);
+
+/*
  * Graph construction on the device.  "Graph Transformer in a Nutshell",
  * section "Graph Transformer Model": GTModel.forward stacks the (src, dst)
  * pairs of g.edges() into one sparse adjacency matrix and hands it to every
@@ -185,7 +235,8 @@ int gt_coo_to_csr(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t
  * device copies of the destination-sorted CSR (n_dst rows whose in-edges come
  * from n_src source nodes), with GT_PLAN_TRANSPOSE also the source-sorted
  * graph that the backward needs (t_indptr int64[n_src + 1], t_indices
- * int32[E] holding destinations, each source's out-edges in CSR order), and
+ * int32[E] holding destinations, each source's out-edges in CSR order, and
+ * t_perm int32[E], the CSR position of each of those out-edges), and
  * the list of rows split into chunks (at the split threshold current when
  * the plan is built).  n_src != n_dst describes a shard of destination rows
  * whose sources index a larger K/V: Q, out, lse, dout, dQ have n_dst rows;
@@ -214,22 +265,25 @@ int gt_plan_create_coo(const int32_t* src, const int32_t* dst, int64_t n_dst, in
                        int32_t flags, hipStream_t stream, gt_plan* plan);
 int gt_plan_destroy(gt_plan plan);
 int gt_plan_info(gt_plan plan, int64_t* n_dst, int64_t* n_src, int64_t* E, const int64_t** indptr,
-                 const int32_t** indices, const int64_t** t_indptr, const int32_t** t_indices);
+                 const int32_t** indices, const int64_t** t_indptr, const int32_t** t_indices,
+                 const int32_t** t_perm);
 int gt_plan_copy_graph(gt_plan plan, int64_t* indptr, int32_t* indices, int64_t* t_indptr, int32_t* t_indices,
-                       hipStream_t stream);
+                       int32_t* t_perm, hipStream_t stream);
 
 /*
- * gt_sparse_mha_fwd_lse / gt_sparse_mha_bwd on a plan: the same kernels and
- * results (bit for bit, for the same graph and split threshold), without
- * rebuilding the split-row list each call.  lse may be NULL in the forward.
+ * gt_sparse_mha_fwd_ex / gt_sparse_mha_bwd_ex on a plan: the same kernels
+ * and results (bit for bit, for the same graph and split threshold), without
+ * rebuilding the split-row list each call.  lse, opts, dbias and dweight may
+ * be NULL.
  * The backward needs a plan built with GT_PLAN_TRANSPOSE (GT_EINVAL
  * otherwise).  The plan must belong to the current device.
  */
 int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, void* out, float* lse,
-                           int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
+                           int32_t H, int32_t D, int32_t dtype, const gt_logit_opts* opts, hipStream_t stream);
 int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, const void* out,
-                           const void* dout, const float* lse, void* dQ, void* dK, void* dV, int32_t H, int32_t D,
-                           int32_t dtype, hipStream_t stream);
+                           const void* dout, const float* lse, void* dQ, void* dK, void* dV, float* dbias,
+                           float* dweight, int32_t H, int32_t D, int32_t dtype, const gt_logit_opts* opts,
+                           hipStream_t stream);
 
 /* Static text for a status code. */
 const char* gt_status_string(int status);

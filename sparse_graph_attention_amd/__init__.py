@@ -17,6 +17,9 @@ The functions have the names of the C entry points declared in
 * ``gt_edge_softmax(indptr, scores, alpha=None)`` -- alpha [E][H] (fp32);
 * ``gt_spmm(indptr, indices, alpha, V, out=None)`` -- out [N][H][D];
 * ``gt_validate_csr(indptr, indices, N)`` -- device-side CSR check;
+* ``gt_sparse_mha_fwd_ex`` / ``gt_sparse_mha_bwd_ex`` -- with an additive
+  logit bias [E][H], edge weights [E] and attention dropout (keyword
+  arguments ``bias``, ``edge_weight``, ``dropout_p``, ``dropout_seed``);
 * ``gt_coo_to_csr(src, dst, n_dst)`` -- (indptr, indices[, perm]) built on the GPU;
 * ``gt_plan_create(indptr, indices)`` / ``gt_plan_create_coo(src, dst, n_dst)``
   -- a reusable graph plan (``GtPlan``), ``gt_plan_destroy``, ``gt_plan_info``,
@@ -43,6 +46,8 @@ EXPORTS = (
     "gt_sparse_mha_fwd",
     "gt_sparse_mha_fwd_lse",
     "gt_sparse_mha_bwd",
+    "gt_sparse_mha_fwd_ex",
+    "gt_sparse_mha_bwd_ex",
     "gt_sddmm",
     "gt_edge_softmax",
     "gt_spmm",
@@ -69,6 +74,12 @@ _i64 = ctypes.c_int64
 _i32 = ctypes.c_int32
 
 
+class LogitOpts(ctypes.Structure):
+    """gt_logit_opts."""
+    _fields_ = [("bias", ctypes.c_void_p), ("edge_weight", ctypes.c_void_p), ("dropout_p", ctypes.c_double),
+                ("dropout_seed", ctypes.c_uint64)]
+
+
 class GtError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
@@ -86,6 +97,9 @@ def lib():
         L.gt_sparse_mha_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_sparse_mha_fwd_lse.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_sparse_mha_bwd.argtypes = [_p] * 13 + [_i64, _i64, _i32, _i32, _i32, _p]
+        _o = ctypes.POINTER(LogitOpts)
+        L.gt_sparse_mha_fwd_ex.argtypes = [_p] * 7 + [_i64, _i64, _i32, _i32, _i32, _o, _p]
+        L.gt_sparse_mha_bwd_ex.argtypes = [_p] * 16 + [_i64, _i64, _i32, _i32, _i32, _o, _p]
         L.gt_sddmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_edge_softmax.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.gt_spmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
@@ -94,10 +108,10 @@ def lib():
         L.gt_plan_create.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _p, ctypes.POINTER(_p)]
         L.gt_plan_create_coo.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _p, ctypes.POINTER(_p)]
         L.gt_plan_destroy.argtypes = [_p]
-        L.gt_plan_info.argtypes = [_p] + [ctypes.POINTER(_i64)] * 3 + [ctypes.POINTER(_p)] * 4
-        L.gt_plan_copy_graph.argtypes = [_p] * 6
-        L.gt_sparse_mha_fwd_plan.argtypes = [_p] * 6 + [_i32, _i32, _i32, _p]
-        L.gt_sparse_mha_bwd_plan.argtypes = [_p] * 10 + [_i32, _i32, _i32, _p]
+        L.gt_plan_info.argtypes = [_p] + [ctypes.POINTER(_i64)] * 3 + [ctypes.POINTER(_p)] * 5
+        L.gt_plan_copy_graph.argtypes = [_p] * 7
+        L.gt_sparse_mha_fwd_plan.argtypes = [_p] * 6 + [_i32, _i32, _i32, ctypes.POINTER(LogitOpts), _p]
+        L.gt_sparse_mha_bwd_plan.argtypes = [_p] * 12 + [_i32, _i32, _i32, ctypes.POINTER(LogitOpts), _p]
         L.gt_status_string.restype = ctypes.c_char_p
         L.gt_status_string.argtypes = [ctypes.c_int]
         L.gt_last_error.restype = ctypes.c_char_p
@@ -110,6 +124,8 @@ def lib():
                                      ctypes.POINTER(_i64)]
         for name in ("gt_coo_to_csr", "gt_plan_create", "gt_plan_create_coo", "gt_plan_destroy", "gt_plan_info",
                      "gt_plan_copy_graph", "gt_sparse_mha_fwd_plan", "gt_sparse_mha_bwd_plan"):
+            getattr(L, name).restype = ctypes.c_int
+        for name in ("gt_sparse_mha_fwd_ex", "gt_sparse_mha_bwd_ex"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
                      "gt_config_set", "gt_profile_begin", "gt_profile_end"):
@@ -220,6 +236,67 @@ def gt_sparse_mha_bwd(indptr, indices, t_indptr, t_indices, Q, K, V, out, dout, 
                                    _ptr(V), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dQ), _ptr(dK), _ptr(dV), N, E, H,
                                    D, _dtype_code(Q), _stream(stream)), "gt_sparse_mha_bwd")
     return dQ, dK, dV
+
+
+def _opts(E, H, device, bias, edge_weight, dropout_p, dropout_seed):
+    """(LogitOpts or None, tensors to keep alive)."""
+    if bias is None and edge_weight is None and not dropout_p:
+        return None, ()
+    if bias is not None and (bias.shape != (E, H) or bias.dtype != torch.float32):
+        raise ValueError("bias must be float32 [E][H]")
+    if edge_weight is not None and (edge_weight.shape != (E,) or edge_weight.dtype != torch.float32):
+        raise ValueError("edge_weight must be float32 [E]")
+    _need_gpu(bias, edge_weight)
+    o = LogitOpts(None if bias is None else bias.data_ptr(), None if edge_weight is None else edge_weight.data_ptr(),
+                  float(dropout_p), int(dropout_seed))
+    return o, (bias, edge_weight)
+
+
+def _optref(o):
+    return None if o is None else ctypes.byref(o)
+
+
+def gt_sparse_mha_fwd_ex(indptr, indices, Q, K, V, out=None, lse=None, want_lse=False, bias=None, edge_weight=None,
+                         dropout_p=0.0, dropout_seed=0, stream=None):
+    """out (and lse when want_lse or lse is given) with the logit variants and dropout."""
+    N, E, H, D = _qkv(indptr, indices, Q, K, V)
+    out = _like(out, Q, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((N, H), dtype=torch.float32, device=Q.device)
+    if lse is not None and (lse.shape != (N, H) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [N][H]")
+    o, _keep = _opts(E, H, Q.device, bias, edge_weight, dropout_p, dropout_seed)
+    _need_gpu(indptr, indices, Q, K, V, out, lse)
+    _check(lib().gt_sparse_mha_fwd_ex(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse),
+                                      N, E, H, D, _dtype_code(Q), _optref(o), _stream(stream)),
+           "gt_sparse_mha_fwd_ex")
+    return (out, lse) if lse is not None else out
+
+
+def gt_sparse_mha_bwd_ex(indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, bias=None,
+                         edge_weight=None, dropout_p=0.0, dropout_seed=0, want_dbias=False, want_dweight=False,
+                         stream=None):
+    """(dQ, dK, dV, dbias or None, dweight or None)."""
+    N, E, H, D = _qkv(indptr, indices, Q, K, V)
+    tN, tE = _csr(t_indptr, t_indices)
+    if (tN, tE) != (N, E):
+        raise ValueError("the transposed graph must have the same N and E")
+    if t_perm is not None and (t_perm.shape != (E,) or t_perm.dtype != torch.int32):
+        raise ValueError("t_perm must be int32 [E]")
+    for t, name in ((out, "out"), (dout, "dout")):
+        _like(t, Q, name)
+    if lse.shape != (N, H) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [N][H]")
+    dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
+    dbias = torch.empty((E, H), dtype=torch.float32, device=Q.device) if want_dbias else None
+    dweight = torch.empty(E, dtype=torch.float32, device=Q.device) if want_dweight else None
+    o, _keep = _opts(E, H, Q.device, bias, edge_weight, dropout_p, dropout_seed)
+    _need_gpu(indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse)
+    _check(lib().gt_sparse_mha_bwd_ex(_ptr(indptr), _ptr(indices), _ptr(t_indptr), _ptr(t_indices), _ptr(t_perm),
+                                      _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dQ), _ptr(dK),
+                                      _ptr(dV), _ptr(dbias), _ptr(dweight), N, E, H, D, _dtype_code(Q), _optref(o),
+                                      _stream(stream)), "gt_sparse_mha_bwd_ex")
+    return dQ, dK, dV, dbias, dweight
 
 
 def gt_sddmm(indptr, indices, Q, K, scores=None, stream=None):
@@ -349,26 +426,31 @@ def gt_plan_info(plan):
     """dict(n_dst, n_src, E, transpose): the plan's sizes."""
     n = [_i64() for _ in range(3)]
     tptr = _p()
-    _check(lib().gt_plan_info(plan.handle, *[ctypes.byref(x) for x in n], None, None, ctypes.byref(tptr), None),
+    _check(lib().gt_plan_info(plan.handle, *[ctypes.byref(x) for x in n], None, None, ctypes.byref(tptr), None, None),
            "gt_plan_info")
     return dict(n_dst=n[0].value, n_src=n[1].value, E=n[2].value, transpose=bool(tptr.value))
 
 
 def gt_plan_copy_graph(plan, device=None, stream=None):
-    """The plan's (indptr, indices, t_indptr, t_indices) as new device tensors (t_* None without a transpose)."""
+    """The plan's (indptr, indices, t_indptr, t_indices, t_perm) as new device tensors
+    (t_* None without a transpose)."""
     info = gt_plan_info(plan)
     device = device or torch.device("cuda", torch.cuda.current_device())
     ip = torch.empty(info["n_dst"] + 1, dtype=torch.int64, device=device)
     ix = torch.empty(info["E"], dtype=torch.int32, device=device)
     tip = torch.empty(info["n_src"] + 1, dtype=torch.int64, device=device) if info["transpose"] else None
     tix = torch.empty(info["E"], dtype=torch.int32, device=device) if info["transpose"] else None
-    _check(lib().gt_plan_copy_graph(plan.handle, _ptr(ip), _ptr(ix) if info["E"] else None, _ptr(tip),
-                                    _ptr(tix) if (tix is not None and info["E"]) else None, _stream(stream)),
+    tpm = torch.empty(info["E"], dtype=torch.int32, device=device) if info["transpose"] else None
+    some = info["E"] > 0
+    _check(lib().gt_plan_copy_graph(plan.handle, _ptr(ip), _ptr(ix) if some else None, _ptr(tip),
+                                    _ptr(tix) if (tix is not None and some) else None,
+                                    _ptr(tpm) if (tpm is not None and some) else None, _stream(stream)),
            "gt_plan_copy_graph")
-    return ip, ix, tip, tix
+    return ip, ix, tip, tix, tpm
 
 
-def gt_sparse_mha_fwd_plan(plan, Q, K, V, out=None, lse=None, want_lse=False, stream=None):
+def gt_sparse_mha_fwd_plan(plan, Q, K, V, out=None, lse=None, want_lse=False, bias=None, edge_weight=None,
+                           dropout_p=0.0, dropout_seed=0, stream=None):
     """out (and lse when want_lse or lse is given) for the plan's graph; Q/out have n_dst rows, K/V n_src."""
     info = gt_plan_info(plan)
     if Q.dim() != 3 or Q.shape[0] != info["n_dst"] or K.shape != V.shape or K.shape[0] != info["n_src"] or \
@@ -382,14 +464,17 @@ def gt_sparse_mha_fwd_plan(plan, Q, K, V, out=None, lse=None, want_lse=False, st
         lse = torch.empty((info["n_dst"], H), dtype=torch.float32, device=Q.device)
     if lse is not None and (lse.shape != (info["n_dst"], H) or lse.dtype != torch.float32):
         raise ValueError("lse must be float32 [n_dst][H]")
+    o, _keep = _opts(info["E"], H, Q.device, bias, edge_weight, dropout_p, dropout_seed)
     _need_gpu(Q, K, V, out, lse)
     _check(lib().gt_sparse_mha_fwd_plan(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(lse), H, D,
-                                        _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd_plan")
+                                        _dtype_code(Q), _optref(o), _stream(stream)), "gt_sparse_mha_fwd_plan")
     return (out, lse) if lse is not None else out
 
 
-def gt_sparse_mha_bwd_plan(plan, Q, K, V, out, dout, lse, dQ=None, dK=None, dV=None, stream=None):
-    """(dQ, dK, dV) for the plan's graph (built with a transpose)."""
+def gt_sparse_mha_bwd_plan(plan, Q, K, V, out, dout, lse, dQ=None, dK=None, dV=None, bias=None, edge_weight=None,
+                           dropout_p=0.0, dropout_seed=0, want_dbias=False, want_dweight=False, stream=None):
+    """(dQ, dK, dV) for the plan's graph (built with a transpose); with want_dbias or
+    want_dweight also (dbias or None, dweight or None)."""
     info = gt_plan_info(plan)
     if Q.dim() != 3 or Q.shape[0] != info["n_dst"] or K.shape != V.shape or K.shape[0] != info["n_src"] or \
             K.shape[1:] != Q.shape[1:]:
@@ -400,10 +485,16 @@ def gt_sparse_mha_bwd_plan(plan, Q, K, V, out, dout, lse, dQ=None, dK=None, dV=N
     if lse.shape != (info["n_dst"], H) or lse.dtype != torch.float32:
         raise ValueError("lse must be float32 [n_dst][H]")
     dQ, dK, dV = _like(dQ, Q, "dQ"), _like(dK, K, "dK"), _like(dV, K, "dV")
+    E = info["E"]
+    dbias = torch.empty((E, H), dtype=torch.float32, device=Q.device) if want_dbias else None
+    dweight = torch.empty(E, dtype=torch.float32, device=Q.device) if want_dweight else None
+    o, _keep = _opts(E, H, Q.device, bias, edge_weight, dropout_p, dropout_seed)
     _need_gpu(Q, K, V, out, dout, lse, dQ, dK, dV)
     _check(lib().gt_sparse_mha_bwd_plan(plan.handle, _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), _ptr(lse),
-                                        _ptr(dQ), _ptr(dK), _ptr(dV), H, D, _dtype_code(Q), _stream(stream)),
-           "gt_sparse_mha_bwd_plan")
+                                        _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dbias), _ptr(dweight), H, D,
+                                        _dtype_code(Q), _optref(o), _stream(stream)), "gt_sparse_mha_bwd_plan")
+    if want_dbias or want_dweight:
+        return dQ, dK, dV, dbias, dweight
     return dQ, dK, dV
 
 

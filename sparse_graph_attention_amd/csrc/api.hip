@@ -306,8 +306,22 @@ void set_scales(Args& a) {
     a.kscale = (float)(1.0 / std::sqrt((double)a.D));
 }
 
+// Logit variants and dropout from the caller's options (nullptr: none).
+int set_options(Args& a, const gt_logit_opts* o) {
+    if (!o) return GT_OK;
+    const double p = o->dropout_p;
+    if (!(p >= 0.0 && p < 1.0)) return fail(GT_EINVAL, "dropout_p = %g is outside [0, 1)", p);
+    a.bias = o->bias;
+    a.ew = o->edge_weight;
+    a.drop_seed = o->dropout_seed;
+    a.drop_thresh = (uint32_t)std::floor(p * 4294967296.0);
+    a.drop_scale = (float)(1.0 / (1.0 - p));
+    return GT_OK;
+}
+
 int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V, void* out,
-              float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
+              float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, const gt_logit_opts* opts,
+              hipStream_t stream) {
     int rc = check_common(N, E, H, D, dtype);
     if (rc) return rc;
     if (N == 0) return GT_OK;
@@ -327,6 +341,8 @@ int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, cons
     a.D = D;
     a.dtype = dtype;
     set_scales(a);
+    rc = set_options(a, opts);
+    if (rc) return rc;
     choose_layout(a, {Q, K, V, out});
     return run_fwd(a, nullptr, stream);
 }
@@ -349,12 +365,19 @@ int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStre
         bytes += table_bytes(a.plan) + table_bytes(at.plan);
     }
     bytes += partial_bytes(a.plan, a.H, HD) + partial_bytes(at.plan, a.H, 2 * HD);
+    const bool dew_part = a.dew && !a.vec;  // one-head waves: dw's per-head terms go through scratch
+    const size_t part_bytes = dew_part ? align256(sizeof(float) * (size_t)a.E * a.H) : 0;
+    bytes += part_bytes;
     void* base = nullptr;
     int rc = get_scratch(stream, bytes, &base);
     if (rc) return rc;
     char* p = (char*)base;
     a.delta = at.delta = (float*)p;
     p += align256(sizeof(float) * (size_t)a.N * a.H);
+    if (dew_part) {
+        a.dew_part = (float*)p;
+        p += part_bytes;
+    }
     if (!tables) {
         p = carve_tables(p, a.plan);
         p = carve_tables(p, at.plan);
@@ -379,10 +402,11 @@ int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStre
 // Arguments of the backward over (destination CSR, source CSR) with n_dst
 // destinations (rows of Q, out, dout, lse, dQ) and n_src sources (rows of K,
 // V, dK, dV).
-void bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
-              const int32_t* t_indices, const void* Q, const void* K, const void* V, const void* out, const void* dout,
-              const float* lse, void* dQ, void* dK, void* dV, int64_t n_dst, int64_t n_src, int64_t E, int32_t H,
-              int32_t D, int32_t dtype) {
+int bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
+             const int32_t* t_indices, const int32_t* t_perm, const void* Q, const void* K, const void* V,
+             const void* out, const void* dout, const float* lse, void* dQ, void* dK, void* dV, float* dbias,
+             float* dew, int64_t n_dst, int64_t n_src, int64_t E, int32_t H, int32_t D, int32_t dtype,
+             const gt_logit_opts* opts) {
     a = Args{};
     a.indptr = indptr;
     a.indices = indices;
@@ -401,11 +425,21 @@ void bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, 
     a.D = D;
     a.dtype = dtype;
     set_scales(a);
+    int rc = set_options(a, opts);
+    if (rc) return rc;
     choose_layout(a, {Q, K, V, out, dout, dQ, dK, dV});
     at = a;
     at.indptr = t_indptr;
     at.indices = t_indices;
+    at.t_perm = t_perm;
     at.N = n_src;
+    // the destination pass writes the per-edge gradients; the source pass
+    // needs the CSR positions of its out-edges only for per-edge inputs
+    a.dbias = dbias;
+    a.dew = dew;
+    if (extended(at) && E > 0 && !t_perm)
+        return fail(GT_EINVAL, "bias, edge weights or dropout need the transpose's CSR positions (t_perm)");
+    return GT_OK;
 }
 
 }  // namespace
@@ -414,14 +448,20 @@ extern "C" {
 
 int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
                       void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
-    return fused_fwd(indptr, indices, Q, K, V, out, nullptr, N, E, H, D, dtype, stream);
+    return fused_fwd(indptr, indices, Q, K, V, out, nullptr, N, E, H, D, dtype, nullptr, stream);
 }
 
 int gt_sparse_mha_fwd_lse(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
                           void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
                           hipStream_t stream) {
     if (N > 0 && !lse) return fail(GT_EINVAL, "NULL lse with N > 0");
-    return fused_fwd(indptr, indices, Q, K, V, out, lse, N, E, H, D, dtype, stream);
+    return fused_fwd(indptr, indices, Q, K, V, out, lse, N, E, H, D, dtype, nullptr, stream);
+}
+
+int gt_sparse_mha_fwd_ex(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K, const void* V,
+                         void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                         const gt_logit_opts* opts, hipStream_t stream) {
+    return fused_fwd(indptr, indices, Q, K, V, out, lse, N, E, H, D, dtype, opts, stream);
 }
 
 int gt_sparse_mha_bwd(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr, const int32_t* t_indices,
@@ -435,7 +475,27 @@ int gt_sparse_mha_bwd(const int64_t* indptr, const int32_t* indices, const int64
         return fail(GT_EINVAL, "NULL array with N > 0");
     if (E > 0 && (!indices || !t_indices)) return fail(GT_EINVAL, "NULL indices with E > 0");
     Args a, at;
-    bwd_args(a, at, indptr, indices, t_indptr, t_indices, Q, K, V, out, dout, lse, dQ, dK, dV, N, N, E, H, D, dtype);
+    rc = bwd_args(a, at, indptr, indices, t_indptr, t_indices, nullptr, Q, K, V, out, dout, lse, dQ, dK, dV, nullptr,
+                  nullptr, N, N, E, H, D, dtype, nullptr);
+    if (rc) return rc;
+    return run_bwd(a, at, nullptr, nullptr, stream);
+}
+
+int gt_sparse_mha_bwd_ex(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
+                         const int32_t* t_indices, const int32_t* t_perm, const void* Q, const void* K, const void* V,
+                         const void* out, const void* dout, const float* lse, void* dQ, void* dK, void* dV,
+                         float* dbias, float* dweight, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                         const gt_logit_opts* opts, hipStream_t stream) {
+    int rc = check_common(N, E, H, D, dtype);
+    if (rc) return rc;
+    if (N == 0) return GT_OK;
+    if (!indptr || !t_indptr || !Q || !K || !V || !out || !dout || !lse || !dQ || !dK || !dV)
+        return fail(GT_EINVAL, "NULL array with N > 0");
+    if (E > 0 && (!indices || !t_indices)) return fail(GT_EINVAL, "NULL indices with E > 0");
+    Args a, at;
+    rc = bwd_args(a, at, indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, dQ, dK, dV, dbias,
+                  dweight, N, N, E, H, D, dtype, opts);
+    if (rc) return rc;
     return run_bwd(a, at, nullptr, nullptr, stream);
 }
 
@@ -523,6 +583,7 @@ struct gt_plan_s {
     int32_t* indices = nullptr;
     int64_t* t_indptr = nullptr;
     int32_t* t_indices = nullptr;
+    int32_t* t_perm = nullptr;  // CSR position of each out-edge of the transpose
     Plan tables{};    // split rows of the destination-sorted graph
     Plan t_tables{};  // split rows of the source-sorted graph
 };
@@ -559,7 +620,7 @@ int build_transpose(gt_plan_s* P, hipStream_t stream) {
     hipError_t e = launch_row_of_position(P->indptr, P->n_dst, P->E, rows, stream);
     if (e == hipSuccess)
         e = group_by_key((const uint32_t*)P->indices, rows, P->E, P->n_src, P->t_indptr, (uint32_t*)P->t_indices,
-                         nullptr, (char*)base + rows_bytes, stream);
+                         (uint32_t*)P->t_perm, (char*)base + rows_bytes, stream);
     return e == hipSuccess ? GT_OK : hip_fail(e, "transpose launch");
 }
 
@@ -582,7 +643,7 @@ int alloc_plan(int64_t n_dst, int64_t n_src, int64_t E, int32_t flags, gt_plan_s
     if (!rc) e = hipGetDevice(&P->device);
     if (!rc && e != hipSuccess) rc = hip_fail(e, "hipGetDevice");
     const size_t bytes = align256(sizeof(int64_t) * (size_t)(n_dst + 1)) + align256(sizeof(int32_t) * (size_t)E) +
-                         (tr ? align256(sizeof(int64_t) * (size_t)(n_src + 1)) + align256(sizeof(int32_t) * (size_t)E)
+                         (tr ? align256(sizeof(int64_t) * (size_t)(n_src + 1)) + 2 * align256(sizeof(int32_t) * (size_t)E)
                              : 0) +
                          table_bytes(P->tables) + table_bytes(P->t_tables);
     if (!rc) {
@@ -603,6 +664,7 @@ int alloc_plan(int64_t n_dst, int64_t n_src, int64_t E, int32_t flags, gt_plan_s
     if (tr) {
         P->t_indptr = (int64_t*)b;   b += align256(sizeof(int64_t) * (size_t)(n_src + 1));
         P->t_indices = (int32_t*)b;  b += align256(sizeof(int32_t) * (size_t)E);
+        P->t_perm = (int32_t*)b;     b += align256(sizeof(int32_t) * (size_t)E);
     }
     b = carve_tables(b, P->tables);
     carve_tables(b, P->t_tables);
@@ -720,7 +782,8 @@ int gt_plan_destroy(gt_plan plan) {
 }
 
 int gt_plan_info(gt_plan plan, int64_t* n_dst, int64_t* n_src, int64_t* E, const int64_t** indptr,
-                 const int32_t** indices, const int64_t** t_indptr, const int32_t** t_indices) {
+                 const int32_t** indices, const int64_t** t_indptr, const int32_t** t_indices,
+                 const int32_t** t_perm) {
     if (!plan) return fail(GT_EINVAL, "NULL plan");
     if (n_dst) *n_dst = plan->n_dst;
     if (n_src) *n_src = plan->n_src;
@@ -729,23 +792,25 @@ int gt_plan_info(gt_plan plan, int64_t* n_dst, int64_t* n_src, int64_t* E, const
     if (indices) *indices = plan->indices;
     if (t_indptr) *t_indptr = plan->t_indptr;
     if (t_indices) *t_indices = plan->t_indices;
+    if (t_perm) *t_perm = plan->t_perm;
     return GT_OK;
 }
 
 int gt_plan_copy_graph(gt_plan plan, int64_t* indptr, int32_t* indices, int64_t* t_indptr, int32_t* t_indices,
-                       hipStream_t stream) {
+                       int32_t* t_perm, hipStream_t stream) {
     int rc = check_plan_use(plan);
     if (rc) return rc;
-    if ((t_indptr || t_indices) && !(plan->flags & GT_PLAN_TRANSPOSE))
+    if ((t_indptr || t_indices || t_perm) && !(plan->flags & GT_PLAN_TRANSPOSE))
         return fail(GT_EINVAL, "the plan was built without GT_PLAN_TRANSPOSE");
     struct Item {
         void* dst;
         const void* src;
         size_t bytes;
-    } items[4] = {{indptr, plan->indptr, sizeof(int64_t) * (size_t)(plan->n_dst + 1)},
+    } items[5] = {{indptr, plan->indptr, sizeof(int64_t) * (size_t)(plan->n_dst + 1)},
                   {indices, plan->indices, sizeof(int32_t) * (size_t)plan->E},
                   {t_indptr, plan->t_indptr, sizeof(int64_t) * (size_t)(plan->n_src + 1)},
-                  {t_indices, plan->t_indices, sizeof(int32_t) * (size_t)plan->E}};
+                  {t_indices, plan->t_indices, sizeof(int32_t) * (size_t)plan->E},
+                  {t_perm, plan->t_perm, sizeof(int32_t) * (size_t)plan->E}};
     for (const Item& it : items) {
         if (!it.dst || it.bytes == 0) continue;
         hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, stream);
@@ -755,7 +820,7 @@ int gt_plan_copy_graph(gt_plan plan, int64_t* indptr, int32_t* indices, int64_t*
 }
 
 int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, void* out, float* lse,
-                           int32_t H, int32_t D, int32_t dtype, hipStream_t stream) {
+                           int32_t H, int32_t D, int32_t dtype, const gt_logit_opts* opts, hipStream_t stream) {
     int rc = check_plan_use(plan);
     if (!rc) rc = check_common(plan->n_dst, plan->E, H, D, dtype);
     if (rc) return rc;
@@ -775,13 +840,16 @@ int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     a.D = D;
     a.dtype = dtype;
     set_scales(a);
+    rc = set_options(a, opts);
+    if (rc) return rc;
     choose_layout(a, {Q, K, V, out});
     return run_fwd(a, &plan->tables, stream);
 }
 
 int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, const void* out,
-                           const void* dout, const float* lse, void* dQ, void* dK, void* dV, int32_t H, int32_t D,
-                           int32_t dtype, hipStream_t stream) {
+                           const void* dout, const float* lse, void* dQ, void* dK, void* dV, float* dbias,
+                           float* dweight, int32_t H, int32_t D, int32_t dtype, const gt_logit_opts* opts,
+                           hipStream_t stream) {
     int rc = check_plan_use(plan);
     if (!rc) rc = check_common(std::max(plan->n_dst, plan->n_src), plan->E, H, D, dtype);
     if (rc) return rc;
@@ -790,8 +858,9 @@ int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     if ((plan->n_dst > 0 && (!Q || !out || !dout || !lse || !dQ)) || (plan->n_src > 0 && (!K || !V || !dK || !dV)))
         return fail(GT_EINVAL, "NULL array");
     Args a, at;
-    bwd_args(a, at, plan->indptr, plan->indices, plan->t_indptr, plan->t_indices, Q, K, V, out, dout, lse, dQ, dK, dV,
-             plan->n_dst, plan->n_src, plan->E, H, D, dtype);
+    rc = bwd_args(a, at, plan->indptr, plan->indices, plan->t_indptr, plan->t_indices, plan->t_perm, Q, K, V, out,
+                  dout, lse, dQ, dK, dV, dbias, dweight, plan->n_dst, plan->n_src, plan->E, H, D, dtype, opts);
+    if (rc) return rc;
     return run_bwd(a, at, &plan->tables, &plan->t_tables, stream);
 }
 

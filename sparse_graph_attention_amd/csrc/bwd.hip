@@ -25,7 +25,7 @@
 namespace gt {
 
 // ------------------------------------------------------------ dQ, vector layout
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool XL>
 __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     // row data: q, dO, and per head delta = dO . out and lse (log2 units)
     float q[NC][VN], g[NC][VN], dl[NC], ls[NC];
     bool act[NC];
+    int head[NC];
     const char* qrow = (const char*)a.Q + row * rowbytes;
     const char* grow = (const char*)a.dO + row * rowbytes;
     const char* orow = (const char*)a.O + row * rowbytes;
@@ -57,6 +58,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
         act[c] = FULL || vi < a.R;
+        head[c] = act[c] ? vi / lph : 0;
         const U4 zero{0, 0, 0, 0};
         VT::unpack(act[c] ? ld16(qrow + vi * 16) : zero, q[c]);
         VT::unpack(act[c] ? ld16(grow + vi * 16) : zero, g[c]);
@@ -97,8 +99,20 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
                 vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        int64_t ej[U];
+        float xw[U], xb[U][NC];
+        if constexpr (XL) {
 #pragma unroll
-        for (int j = 0; j < U; ++j)
+            for (int j = 0; j < U; ++j) {
+                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
+                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej[j] * a.H + head[c]] * kLog2e : 0.0f;
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float tw = 0.0f;  // extended: sum over this lane's heads of ds * <q, k> / sqrt(D)
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 float kf[VN], vf[VN];
@@ -112,11 +126,34 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
                 }
                 sd = (LPH_ ? seg_sum_c<LPH_>(sd) : seg_sum(sd, lph)) * a.qscale;
                 dd = LPH_ ? seg_sum_c<LPH_>(dd) : seg_sum(dd, lph);
-                const float p = ok[j] ? exp2_(sd - ls[c]) : 0.0f;
-                const float ds = p * (dd - dl[c]);
+                if constexpr (XL) {
+                    const float raw = sd;
+                    sd = __builtin_fmaf(sd, xw[j], xb[j][c]);
+                    const float p = ok[j] ? exp2_(sd - ls[c]) : 0.0f;
+                    float keep = 1.0f;
+                    if (a.drop_thresh)
+                        keep = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + head[c]) >= a.drop_thresh
+                                   ? a.drop_scale : 0.0f;
+                    const float ds = p * (keep * dd - dl[c]);
+                    const bool lead = ok[j] && act[c] && (gl & (lph - 1)) == 0;
+                    if (a.dbias && lead) a.dbias[ej[j] * a.H + head[c]] = ds;
+                    if (lead) tw = __builtin_fmaf(ds, raw * kLn2, tw);
+                    const float dsw = ds * xw[j];
 #pragma unroll
-                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(ds, kf[k], acc[c][k]);
+                    for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(dsw, kf[k], acc[c][k]);
+                } else {
+                    const float p = ok[j] ? exp2_(sd - ls[c]) : 0.0f;
+                    const float ds = p * (dd - dl[c]);
+#pragma unroll
+                    for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(ds, kf[k], acc[c][k]);
+                }
             }
+            if constexpr (XL)
+                if (a.dew) {
+                    tw = seg_sum(tw, G);  // over the group's heads
+                    if (ok[j] && gl == 0) a.dew[ej[j]] = tw;
+                }
+        }
     }
     for (int off = G; off < kWave; off <<= 1)
 #pragma unroll
@@ -145,7 +182,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
 // ------------------------------------------------------------ dK, dV, vector layout
 // a.indptr / a.indices are the source-sorted graph: item rows are sources u,
 // "edges" are their out-edges with the destination v in a.indices.
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool XL>
 __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -164,8 +201,11 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     const int64_t HD = (int64_t)a.H * a.D;
     const int32_t* __restrict__ idx = a.indices;
 
-    int32_t un[U];
-    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    int32_t un[U], pn[U];  // destinations and (extended) their CSR positions
+    if (e1 > e0) {
+        load_ids<U>(idx, e0, grp, epw, e1, un);
+        if constexpr (XL) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
+    }
 
     float kk[NC][VN], vv[NC][VN];
     bool act[NC];
@@ -188,15 +228,25 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     const char* Qb = (const char*)a.Q;
     const char* Gb = (const char*)a.dO;
     for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
-        int32_t u[U];
+        int32_t u[U], ep[U];
         bool ok[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             u[j] = un[j];
+            if constexpr (XL) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
         U4 qr[U][NC], gr[U][NC];
         float ls[U][NC], dl[U][NC];
+        float xw[U], xb[U][NC];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                xw[j] = a.ew ? a.ew[ep[j]] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[(int64_t)ep[j] * a.H + head[c]] * kLog2e : 0.0f;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -208,7 +258,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
                 dl[j][c] = go ? a.delta[(int64_t)u[j] * a.H + head[c]] : 0.0f;
             }
         const int64_t nb = eb + (int64_t)epw * U;
-        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        if (nb < e1) {
+            load_ids<U>(idx, nb, grp, epw, e1, un);
+            if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -224,12 +277,28 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
                 }
                 sd = (LPH_ ? seg_sum_c<LPH_>(sd) : seg_sum(sd, lph)) * a.qscale;
                 dd = LPH_ ? seg_sum_c<LPH_>(dd) : seg_sum(dd, lph);
-                const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
-                const float ds = p * (dd - dl[j][c]);
+                if constexpr (XL) {
+                    sd = __builtin_fmaf(sd, xw[j], xb[j][c]);
+                    const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
+                    float keep = 1.0f;
+                    if (a.drop_thresh)
+                        keep = philox_hi32(a.drop_seed, (uint64_t)ep[j] * a.H + head[c]) >= a.drop_thresh
+                                   ? a.drop_scale : 0.0f;
+                    const float pk = p * keep;
+                    const float dsw = p * (keep * dd - dl[j][c]) * xw[j];
 #pragma unroll
-                for (int k = 0; k < VN; ++k) {
-                    dv[c][k] = __builtin_fmaf(p, gf[k], dv[c][k]);
-                    dk[c][k] = __builtin_fmaf(ds, qf[k], dk[c][k]);
+                    for (int k = 0; k < VN; ++k) {
+                        dv[c][k] = __builtin_fmaf(pk, gf[k], dv[c][k]);
+                        dk[c][k] = __builtin_fmaf(dsw, qf[k], dk[c][k]);
+                    }
+                } else {
+                    const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
+                    const float ds = p * (dd - dl[j][c]);
+#pragma unroll
+                    for (int k = 0; k < VN; ++k) {
+                        dv[c][k] = __builtin_fmaf(p, gf[k], dv[c][k]);
+                        dk[c][k] = __builtin_fmaf(ds, qf[k], dk[c][k]);
+                    }
                 }
             }
     }
@@ -266,7 +335,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 // ------------------------------------------------------------ scalar layout
 // One wave per (item, head h = blockIdx.y); groups of G = pow2ceil(D) lanes,
 // lane j holding elements j + k*G, k < KD.
-template <int DT, int KD, int U>
+template <int DT, int KD, int U, bool XL>
 __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
     using VT = Vec<DT>;
     const int lane = threadIdx.x & (kWave - 1);
@@ -320,6 +389,16 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
             }
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        int64_t ej[U];
+        float xw[U], xb[U];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
+                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
+                xb[j] = a.bias ? a.bias[ej[j] * a.H + h] * kLog2e : 0.0f;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             float sd = 0.0f, dd = 0.0f;
@@ -330,10 +409,29 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
             }
             sd = seg_sum(sd, G) * a.qscale;
             dd = seg_sum(dd, G);
-            const float p = ok[j] ? exp2_(sd - ls) : 0.0f;
-            const float ds = p * (dd - dl);
+            if constexpr (XL) {
+                const float raw = sd;
+                sd = __builtin_fmaf(sd, xw[j], xb[j]);
+                const float p = ok[j] ? exp2_(sd - ls) : 0.0f;
+                float keep = 1.0f;
+                if (a.drop_thresh)
+                    keep = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
+                const float ds = p * (keep * dd - dl);
+                // one wave per head: the per-head terms of dw go to scratch and
+                // sum_heads_kernel adds them up in head order
+                if (ok[j] && gl == 0) {
+                    if (a.dbias) a.dbias[ej[j] * a.H + h] = ds;
+                    if (a.dew) a.dew_part[ej[j] * a.H + h] = ds * raw * kLn2;
+                }
+                const float dsw = ds * xw[j];
 #pragma unroll
-            for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(ds, kv[j][k], acc[k]);
+                for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(dsw, kv[j][k], acc[k]);
+            } else {
+                const float p = ok[j] ? exp2_(sd - ls) : 0.0f;
+                const float ds = p * (dd - dl);
+#pragma unroll
+                for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(ds, kv[j][k], acc[k]);
+            }
         }
     }
     for (int off = G; off < kWave; off <<= 1)
@@ -351,7 +449,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
     }
 }
 
-template <int DT, int KD, int U>
+template <int DT, int KD, int U, bool XL>
 __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
     using VT = Vec<DT>;
     const int lane = threadIdx.x & (kWave - 1);
@@ -368,8 +466,11 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
     const int64_t hoff = (int64_t)h * D;
     const int32_t* __restrict__ idx = a.indices;
 
-    int32_t un[U];
-    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    int32_t un[U], pn[U];
+    if (e1 > e0) {
+        load_ids<U>(idx, e0, grp, epw, e1, un);
+        if constexpr (XL) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
+    }
     float kk[KD], vv[KD], dk[KD], dv[KD];
     bool act[KD];
 #pragma unroll
@@ -381,14 +482,23 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
         dk[k] = dv[k] = 0.0f;
     }
     for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
-        int32_t u[U];
+        int32_t u[U], ep[U];
         bool ok[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             u[j] = un[j];
+            if constexpr (XL) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
         float qv[U][KD], gv[U][KD], ls[U], dl[U];
+        float xw[U], xb[U];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                xw[j] = a.ew ? a.ew[ep[j]] : 1.0f;
+                xb[j] = a.bias ? a.bias[(int64_t)ep[j] * a.H + h] * kLog2e : 0.0f;
+            }
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
 #pragma unroll
@@ -401,7 +511,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
             dl[j] = ok[j] ? a.delta[(int64_t)u[j] * a.H + h] : 0.0f;
         }
         const int64_t nb = eb + (int64_t)epw * U;
-        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        if (nb < e1) {
+            load_ids<U>(idx, nb, grp, epw, e1, un);
+            if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             float sd = 0.0f, dd = 0.0f;
@@ -412,12 +525,27 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
             }
             sd = seg_sum(sd, G) * a.qscale;
             dd = seg_sum(dd, G);
-            const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
-            const float ds = p * (dd - dl[j]);
+            if constexpr (XL) {
+                sd = __builtin_fmaf(sd, xw[j], xb[j]);
+                const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
+                float keep = 1.0f;
+                if (a.drop_thresh)
+                    keep = philox_hi32(a.drop_seed, (uint64_t)ep[j] * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
+                const float pk = p * keep;
+                const float dsw = p * (keep * dd - dl[j]) * xw[j];
 #pragma unroll
-            for (int k = 0; k < KD; ++k) {
-                dv[k] = __builtin_fmaf(p, gv[j][k], dv[k]);
-                dk[k] = __builtin_fmaf(ds, qv[j][k], dk[k]);
+                for (int k = 0; k < KD; ++k) {
+                    dv[k] = __builtin_fmaf(pk, gv[j][k], dv[k]);
+                    dk[k] = __builtin_fmaf(dsw, qv[j][k], dk[k]);
+                }
+            } else {
+                const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
+                const float ds = p * (dd - dl[j]);
+#pragma unroll
+                for (int k = 0; k < KD; ++k) {
+                    dv[k] = __builtin_fmaf(p, gv[j][k], dv[k]);
+                    dk[k] = __builtin_fmaf(ds, qv[j][k], dk[k]);
+                }
             }
         }
     }
@@ -491,9 +619,20 @@ __global__ __launch_bounds__(kBlock) void bwd_sum_merge_kernel(const Args a, int
     }
 }
 
+// dw[e] = sum over heads, in head order, of the per-head terms the scalar
+// layout's one-head waves left in part[e][h].
+__global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict__ part, int64_t E, int H,
+                                                        float* __restrict__ dw) {
+    const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= E) return;
+    float t = 0.0f;
+    for (int h = 0; h < H; ++h) t += part[e * H + h];
+    dw[e] = t;
+}
+
 // ------------------------------------------------------------ launchers
 
-template <int DT>
+template <int DT, bool XL>
 static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
@@ -502,28 +641,32 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dq_vec_kernel<DT, 1, 8, 32, 4, true><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 1, 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
-                bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
-                bwd_dq_vec_kernel<DT, 2, 4, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 2, 4, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 3)
-                bwd_dq_vec_kernel<DT, 3, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 3, 2, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else
-                bwd_dq_vec_kernel<DT, 4, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 4, 2, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
         });
     } else {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx, a.H);
             switch (a.KD) {
-                case 1: bwd_dq_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
-                case 2: bwd_dq_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
-                case 3: bwd_dq_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
-                default: bwd_dq_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+                case 1: bwd_dq_scalar_kernel<DT, 1, 8, XL><<<grid, block, 0, s>>>(a); break;
+                case 2: bwd_dq_scalar_kernel<DT, 2, 8, XL><<<grid, block, 0, s>>>(a); break;
+                case 3: bwd_dq_scalar_kernel<DT, 3, 4, XL><<<grid, block, 0, s>>>(a); break;
+                default: bwd_dq_scalar_kernel<DT, 4, 4, XL><<<grid, block, 0, s>>>(a); break;
             }
         });
+        if (err == hipSuccess && XL && a0.dew && a0.E > 0) {
+            sum_heads_kernel<<<(unsigned)((a0.E + 255) / 256), 256, 0, s>>>(a0.dew_part, a0.E, a0.H, a0.dew);
+            err = hipGetLastError();
+        }
     }
     if (err != hipSuccess || a0.plan.max_heavy == 0) return err;
     return for_slices(a0, a0.plan.max_heavy, [&](const Args& a, unsigned gx) {
@@ -532,7 +675,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     });
 }
 
-template <int DT>
+template <int DT, bool XL>
 static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
@@ -541,26 +684,26 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                bwd_dkv_vec_kernel<DT, 2, 4, 64, 16, true><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dkv_vec_kernel<DT, 1, 8, 32, 4, true><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 1, 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
-                bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
-                bwd_dkv_vec_kernel<DT, 2, 4, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 2, 4, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 3)
-                bwd_dkv_vec_kernel<DT, 3, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 3, 2, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else
-                bwd_dkv_vec_kernel<DT, 4, 2, 0, 0, false><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 4, 2, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
         });
     } else {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx, a.H);
             switch (a.KD) {
-                case 1: bwd_dkv_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
-                case 2: bwd_dkv_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
-                case 3: bwd_dkv_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
-                default: bwd_dkv_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+                case 1: bwd_dkv_scalar_kernel<DT, 1, 8, XL><<<grid, block, 0, s>>>(a); break;
+                case 2: bwd_dkv_scalar_kernel<DT, 2, 8, XL><<<grid, block, 0, s>>>(a); break;
+                case 3: bwd_dkv_scalar_kernel<DT, 3, 4, XL><<<grid, block, 0, s>>>(a); break;
+                default: bwd_dkv_scalar_kernel<DT, 4, 4, XL><<<grid, block, 0, s>>>(a); break;
             }
         });
     }
@@ -572,11 +715,15 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
 }
 
 hipError_t launch_bwd_dq(const Args& a, hipStream_t s) {
-    return a.dtype == kF32 ? launch_dq_dt<kF32>(a, s) : launch_dq_dt<kBF16>(a, s);
+    const bool xl = extended(a);
+    return a.dtype == kF32 ? (xl ? launch_dq_dt<kF32, true>(a, s) : launch_dq_dt<kF32, false>(a, s))
+                           : (xl ? launch_dq_dt<kBF16, true>(a, s) : launch_dq_dt<kBF16, false>(a, s));
 }
 
 hipError_t launch_bwd_dkv(const Args& a, hipStream_t s) {
-    return a.dtype == kF32 ? launch_dkv_dt<kF32>(a, s) : launch_dkv_dt<kBF16>(a, s);
+    const bool xl = extended(a);
+    return a.dtype == kF32 ? (xl ? launch_dkv_dt<kF32, true>(a, s) : launch_dkv_dt<kF32, false>(a, s))
+                           : (xl ? launch_dkv_dt<kBF16, true>(a, s) : launch_dkv_dt<kBF16, false>(a, s));
 }
 
 }  // namespace gt

@@ -180,6 +180,34 @@ __device__ __forceinline__ float seg_sum_c(float x) {
     return x;
 }
 
+// ---------------------------------------------------------------- dropout words
+//
+// Attention dropout ("Efficient Sparse Transformer implementation with DGL's
+// builtin operators", TransLayer.forward: drop_att on the edge softmax) draws
+// its keep decisions from the counter-based generator Philox4x64-10 (Salmon,
+// Moraes, Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3",
+// SC 2011): word i of the stream under key (seed, 0) is word i mod 4 of the
+// block whose counter is (i / 4 + 1, 0, 0, 0).  Ten rounds of two 64x64->128
+// bit products; the key is bumped by the two Weyl constants after each round.
+// Returns the word's upper 32 bits.
+__device__ __forceinline__ uint32_t philox_hi32(uint64_t seed, uint64_t i) {
+    uint64_t c0 = i / 4 + 1, c1 = 0, c2 = 0, c3 = 0, k0 = seed, k1 = 0;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t a0 = 0xD2E7470EE14C6C93ull * c0, h0 = __umul64hi(0xD2E7470EE14C6C93ull, c0);
+        const uint64_t a2 = 0xCA5A826395121157ull * c2, h2 = __umul64hi(0xCA5A826395121157ull, c2);
+        c0 = h2 ^ c1 ^ k0;
+        c1 = a2;
+        c2 = h0 ^ c3 ^ k1;
+        c3 = a0;
+        k0 += 0x9E3779B97F4A7C15ull;
+        k1 += 0xBB67AE8584CAA73Bull;
+    }
+    const uint32_t w = (uint32_t)(i & 3);
+    const uint64_t x = w == 0 ? c0 : w == 1 ? c1 : w == 2 ? c2 : c3;
+    return (uint32_t)(x >> 32);
+}
+
 // ---------------------------------------------------------------- 16-byte vectors
 
 struct alignas(16) U4 {

@@ -36,7 +36,7 @@ namespace gt {
 // G_ and LPH_ are compile-time lane-group and lanes-per-head sizes when
 // nonzero, else read from the arguments.  FULL: the row is exactly NC*G
 // vectors (no idle lanes).  U edges per group are in flight.
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool NTL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool NTL, bool XL>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -59,11 +59,13 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 
     float q[NC][VN];
     bool act[NC];
+    int head[NC];
     const char* qrow = (const char*)a.Q + row * rowbytes;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
         act[c] = FULL || vi < a.R;
+        head[c] = act[c] ? vi / lph : 0;
         // unscaled: the scale goes on the reduced score, so nothing waits for Q
         // before the first gathers are issued
         const U4 r = act[c] ? ld16(qrow + vi * 16) : U4{0, 0, 0, 0};
@@ -102,6 +104,19 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        // extended logits: s = w_e * s + bias[e][h] (log2 units); edge ids
+        // clamped into the item like the source ids
+        int64_t ej[U];
+        float xw[U], xb[U][NC];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
+                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej[j] * a.H + head[c]] * kLog2e : 0.0f;
+            }
+        }
 
         float s[U][NC];
 #pragma unroll
@@ -114,6 +129,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 #pragma unroll
                 for (int k = 0; k < VN; ++k) d = __builtin_fmaf(q[c][k], kf[k], d);
                 d = (LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph)) * a.qscale;
+                if constexpr (XL) d = __builtin_fmaf(d, xw[j], xb[j][c]);
                 s[j][c] = ok[j] ? d : -INFINITY;
             }
 #pragma unroll
@@ -131,10 +147,15 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 // a group with no edge left in this batch has mn = -inf: keep p at 0
                 const float p = ok[j] ? exp2_(s[j][c] - mn) : 0.0f;
                 l[c] += p;
+                float pv = p;  // dropout zeroes the weight, not its share of the normaliser
+                if constexpr (XL)
+                    if (a.drop_thresh)
+                        pv = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + head[c]) >= a.drop_thresh
+                                 ? p * a.drop_scale : 0.0f;
                 float vf[VN];
                 VT::unpack(vr[j][c], vf);
 #pragma unroll
-                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(p, vf[k], acc[c][k]);
+                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(pv, vf[k], acc[c][k]);
             }
             m[c] = mn;
         }
@@ -194,7 +215,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 //
 // One wave per (item, head); a group of G = pow2ceil(D) lanes (<= 64) covers
 // one edge's head, lane j holding elements j + k*G, k < KD.
-template <int DT, int KD, int U>
+template <int DT, int KD, int U, bool XL>
 __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
     using VT = Vec<DT>;
     const int lane = threadIdx.x & (kWave - 1);
@@ -248,6 +269,16 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
                 vv[j][k] = (ok[j] && act[k]) ? VT::scalar(a.V, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        int64_t ej[U];
+        float xw[U], xb[U];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
+                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
+                xb[j] = a.bias ? a.bias[ej[j] * a.H + h] * kLog2e : 0.0f;
+            }
+        }
         float s[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
@@ -255,6 +286,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
 #pragma unroll
             for (int k = 0; k < KD; ++k) d = __builtin_fmaf(q[k], kv[j][k], d);
             d = seg_sum(d, G) * a.qscale;
+            if constexpr (XL) d = __builtin_fmaf(d, xw[j], xb[j]);
             s[j] = ok[j] ? d : -INFINITY;
         }
         float mb = s[0];
@@ -269,8 +301,13 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
         for (int j = 0; j < U; ++j) {
             const float p = ok[j] ? exp2_(s[j] - mn) : 0.0f;
             l += p;
+            float pv = p;
+            if constexpr (XL)
+                if (a.drop_thresh)
+                    pv = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + h) >= a.drop_thresh ? p * a.drop_scale
+                                                                                            : 0.0f;
 #pragma unroll
-            for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(p, vv[j][k], acc[k]);
+            for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(pv, vv[j][k], acc[k]);
         }
         m = mn;
     }
@@ -377,7 +414,7 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 
 // ------------------------------------------------------------ launchers
 
-template <int DT>
+template <int DT, bool XL>
 static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     if (a0.vec) {
@@ -388,35 +425,37 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
             // the 256 MB Infinity Cache; smaller ones are partly served from it.
             const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv)
-                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, true><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, false><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                fused_vec_kernel<DT, 1, GT_BF16_D32_U, 32, 4, true, false><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 1, GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
-                fused_vec_kernel<DT, 1, 8, 0, 0, false, false><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 1, 8, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
-                fused_vec_kernel<DT, 2, 4, 0, 0, false, false><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, 4, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 3)
-                fused_vec_kernel<DT, 3, 2, 0, 0, false, false><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 3, 2, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
             else
-                fused_vec_kernel<DT, 4, 2, 0, 0, false, false><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 4, 2, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
         });
     }
     return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
         const dim3 grid(gx, a.H);
         switch (a.KD) {
-            case 1: fused_scalar_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
-            case 2: fused_scalar_kernel<DT, 2, 8><<<grid, block, 0, s>>>(a); break;
-            case 3: fused_scalar_kernel<DT, 3, 4><<<grid, block, 0, s>>>(a); break;
-            default: fused_scalar_kernel<DT, 4, 4><<<grid, block, 0, s>>>(a); break;
+            case 1: fused_scalar_kernel<DT, 1, 8, XL><<<grid, block, 0, s>>>(a); break;
+            case 2: fused_scalar_kernel<DT, 2, 8, XL><<<grid, block, 0, s>>>(a); break;
+            case 3: fused_scalar_kernel<DT, 3, 4, XL><<<grid, block, 0, s>>>(a); break;
+            default: fused_scalar_kernel<DT, 4, 4, XL><<<grid, block, 0, s>>>(a); break;
         }
     });
 }
 
 hipError_t launch_fused(const Args& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
-    const hipError_t err = a.dtype == kF32 ? launch_fused_dt<kF32>(a, s) : launch_fused_dt<kBF16>(a, s);
+    const bool xl = extended(a);
+    const hipError_t err = a.dtype == kF32 ? (xl ? launch_fused_dt<kF32, true>(a, s) : launch_fused_dt<kF32, false>(a, s))
+                                           : (xl ? launch_fused_dt<kBF16, true>(a, s) : launch_fused_dt<kBF16, false>(a, s));
     if (ev1) (void)hipEventRecord(ev1, s);
     return err;
 }

@@ -33,6 +33,17 @@ struct Args {
     void* dQ;
     void* dK;
     void* dV;
+    // logit variants and attention dropout (the "extended logit" kernels; all
+    // off when bias == ew == nullptr, drop_thresh == 0 and no dbias/dew)
+    const float* bias;      // [E][H] added to the natural-log logit, CSR edge order
+    const float* ew;        // [E] multiplies the scaled dot product
+    uint64_t drop_seed;     // Philox4x64-10 key
+    uint32_t drop_thresh;   // keep iff the word's upper 32 bits >= this; 0: no dropout
+    float drop_scale;       // 1 / (1 - p)
+    const int32_t* t_perm;  // source pass: CSR position of each out-edge
+    float* dbias;           // backward output [E][H] or nullptr
+    float* dew;             // backward output [E] or nullptr
+    float* dew_part;        // scratch [E][H]: per-head terms of dew (scalar layout)
     Plan plan;
     // lane layout (chosen on the host)
     int vec;       // 1: 16-byte vector layout, 0: scalar layout
@@ -45,6 +56,9 @@ struct Args {
     int64_t items;      // max_chunks + N
     int64_t item_base;  // first item of the current launch slice
 };
+
+// Whether a launch needs the extended-logit kernels.
+inline bool extended(const Args& a) { return a.bias || a.ew || a.drop_thresh || a.dbias || a.dew; }
 
 // Items per launch slice: keeps gridDim.x * blockDim.x below 2^32.
 constexpr int64_t kSliceItems = (int64_t)1 << 24;

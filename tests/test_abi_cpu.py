@@ -121,8 +121,21 @@ def test_graph_and_plan_reject():
     assert L.gt_plan_create(p, p, 4, 4, 4, 4, S, ctypes.byref(h)) == gt.GT_EINVAL  # unknown flag
     assert L.gt_plan_create(None, p, 4, 4, 4, 0, S, ctypes.byref(h)) == gt.GT_EINVAL
     assert L.gt_plan_create_coo(None, p, 4, 4, 4, 1, S, ctypes.byref(h)) == gt.GT_EINVAL
-    assert L.gt_plan_info(None, None, None, None, None, None, None, None) == gt.GT_EINVAL
+    assert L.gt_plan_info(None, None, None, None, None, None, None, None, None) == gt.GT_EINVAL
     assert L.gt_plan_destroy(None) == gt.GT_OK
-    assert L.gt_plan_copy_graph(None, p, p, None, None, S) == gt.GT_EINVAL
-    assert L.gt_sparse_mha_fwd_plan(None, p, p, p, p, None, 8, 64, 0, S) == gt.GT_EINVAL
-    assert L.gt_sparse_mha_bwd_plan(None, p, p, p, p, p, p, p, p, p, 8, 64, 0, S) == gt.GT_EINVAL
+    assert L.gt_plan_copy_graph(None, p, p, None, None, None, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_fwd_plan(None, p, p, p, p, None, 8, 64, 0, None, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_bwd_plan(None, p, p, p, p, p, p, p, p, p, None, None, 8, 64, 0, None, S) == gt.GT_EINVAL
+
+
+def test_logit_options_reject():
+    L = gt.lib()
+    p = ctypes.c_void_p(1)
+    for bad in (-0.1, 1.0, 2.0, float("nan")):
+        o = gt.LogitOpts(None, None, bad, 0)
+        assert L.gt_sparse_mha_fwd_ex(p, p, p, p, p, p, None, 4, 4, 8, 64, 0, ctypes.byref(o), S) == gt.GT_EINVAL
+    # a bias needs the transpose's CSR positions in the backward
+    o = gt.LogitOpts(1, None, 0.0, 0)
+    assert L.gt_sparse_mha_bwd_ex(p, p, p, p, None, p, p, p, p, p, p, p, p, p, None, None, 4, 4, 8, 64, 0,
+                                  ctypes.byref(o), S) == gt.GT_EINVAL
+    assert "t_perm" in gt.gt_last_error()

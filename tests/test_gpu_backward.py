@@ -4,10 +4,10 @@ the C ABI) with the fp64 oracle, on the GPU.
 The backward consumes the GPU forward's own out and lse, as a training step
 does.  Tolerances are relative to the magnitude sums of each gradient, which
 bound both the gradient and the rounding errors of its terms (ds_e =
-alpha_e (da_e - delta_v) never exceeds alpha_e (|da_e| + |dO_v|.|out_v|)):
+alpha_e (da_e - delta_v) never exceeds alpha_e (|dO_v|.|v_u| + |dO_v|.|out_v|)):
 
-    B_dQ[v] = sum over in-edges  alpha_e (|da_e| + |dO_v|.|out_v|) |k_u| / sqrt(D)
-    B_dK[u] = sum over out-edges alpha_e (|da_e| + |dO_v|.|out_v|) |q_v| / sqrt(D)
+    B_dQ[v] = sum over in-edges  alpha_e (|dO_v|.|v_u| + |dO_v|.|out_v|) |k_u| / sqrt(D)
+    B_dK[u] = sum over out-edges alpha_e (|dO_v|.|v_u| + |dO_v|.|out_v|) |q_v| / sqrt(D)
     B_dV[u] = sum over out-edges alpha_e |dO_v|
 
 elementwise |gpu - oracle| <= rtol * B + atol, with (rtol, atol) = (1e-5,
@@ -78,9 +78,9 @@ def edge_terms(w, lse, out_e, e_dst, e_src):
     Q, K, V, G = (widen(w[k][idx]) for k, idx in (("Q", e_dst), ("K", e_src), ("V", e_src), ("dO", e_dst)))
     s = np.einsum("ehd,ehd->eh", Q, K) / math.sqrt(w["D"])
     alpha = np.exp(s - lse[e_dst])
-    da = np.einsum("ehd,ehd->eh", G, V)
+    da = np.einsum("ehd,ehd->eh", np.abs(G), np.abs(V))  # bounds |dO.v| and its rounding
     dabs = np.einsum("ehd,ehd->eh", np.abs(G), np.abs(out_e))
-    return alpha, alpha * (np.abs(da) + dabs)
+    return alpha, alpha * (da + dabs)
 
 
 def bound_dq(w, lse, out_of, rows):

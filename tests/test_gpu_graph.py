@@ -93,7 +93,7 @@ def plan_arrays(plan):
     info = gt.gt_plan_info(plan)
     arrays = gt.gt_plan_copy_graph(plan)
     torch.cuda.synchronize()
-    for k, v in zip(("indptr", "indices", "t_indptr", "t_indices"), arrays):
+    for k, v in zip(("indptr", "indices", "t_indptr", "t_indices", "t_perm"), arrays):
         info[k] = None if v is None else v.cpu().numpy()
     return info
 
@@ -108,8 +108,9 @@ def test_plan_graph_matches_oracle(name):
     p = plan_arrays(plan)
     rip, rix, _ = oracle.coo_to_csr(w["N"], src, dst)
     assert np.array_equal(p["indptr"], rip) and np.array_equal(p["indices"], rix)
-    tip, tix = oracle.source_sorted(rip, rix)
+    tip, tix, tpm = oracle.source_sorted(rip, rix, want_perm=True)
     assert np.array_equal(p["t_indptr"], tip) and np.array_equal(p["t_indices"], tix)
+    assert np.array_equal(p["t_perm"], tpm)
     plan.destroy()
     say("plan from CSR %s" % name)
     t = to_dev(w)
@@ -228,7 +229,7 @@ def test_coo_plan_bf16_is_bitwise_the_plain_call_on_its_graph():
     src, dst = shuffled_coo(w["indptr"], w["indices"], 4)
     d = dev()
     plan = gt.gt_plan_create_coo(torch.from_numpy(src).to(d), torch.from_numpy(dst).to(d), w["N"])
-    ip, ix, tip, tix = gt.gt_plan_copy_graph(plan)
+    ip, ix, tip, tix, _ = gt.gt_plan_copy_graph(plan)
     say("bf16 plan vs plain on the plan's graph")
     out, lse = gt.gt_sparse_mha_fwd_lse(ip, ix, t["Q"], t["K"], t["V"])
     dq, dk, dv = gt.gt_sparse_mha_bwd(ip, ix, tip, tix, t["Q"], t["K"], t["V"], out, dO, lse)

@@ -1,0 +1,292 @@
+"""Parity of the logit variants (additive bias [E][H], edge weights [E]) and
+attention dropout with the fp64 oracle, on the GPU, through the C ABI.
+
+Forward: out with the forward tolerances (fp32 rtol 1e-5, atol 1e-6; bf16
+rtol 2e-2, atol 1e-5) and lse to 1e-5 (1 + |lse|).  Backward: as in
+test_gpu_backward, relative to the magnitude sums of each gradient, which
+with dropout multipliers c_e (0 or 1/(1-p)) and weights w_e read
+
+    B_dQ[v]  = sum over in-edges  alpha_e (c_e |dO_v|.|v_u| + |dO_v|.|out_v|) w_e |k_u| / sqrt(D)
+    B_dK[u]  = sum over out-edges alpha_e (c_e |dO_v|.|v_u| + |dO_v|.|out_v|) w_e |q_v| / sqrt(D)
+    B_dV[u]  = sum over out-edges alpha_e c_e |dO_v|
+    B_db[e]  = alpha_e (c_e |dO_v|.|v_u| + |dO_v|.|out_v|)
+    B_dw[e]  = sum over heads B_db[e] |q_v|.|k_u| / sqrt(D)
+
+(rtol 1e-5 for fp32, 2e-2 for bf16).  The dropout mask the bound uses comes
+from numpy's Philox4x64-10 generator, independently of both sides.  Neutral
+options (zero bias, unit weights, p = 0) must reproduce the plain kernels to
+rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import gtgen
+import oracle
+import sparse_graph_attention_amd as gt
+from tests.test_gpu_backward import check_bound, check_lse, to_torch, widen, with_grad
+from tests.test_gpu_parity import (BF16_TOL, F32_TOL, assert_close, chunk_edges, dev, host, oracle_inputs,
+                                   random_graph, sample_rows, say, to_dev, workload)
+
+pytestmark = pytest.mark.gpu
+
+F32_BTOL = (1e-5, 1e-7)
+BF16_BTOL = (2e-2, 1e-5)
+
+
+def tols(w):
+    return (F32_TOL, F32_BTOL) if w["dtype"] == gtgen.F32 else (BF16_TOL, BF16_BTOL)
+
+
+def keep_mask(seed, E, H, p):
+    """c[e, h] for all edges: 0 or 1/(1-p), from numpy's Philox4x64-10 stream
+    (word e*H + h, kept iff its upper 32 bits >= floor(p 2^32)); float32."""
+    bg = np.random.Philox(key=np.array([seed, 0], dtype=np.uint64))
+    thresh = np.uint64(math.floor(p * 2.0 ** 32))
+    out = np.empty(E * H, dtype=np.float32)
+    step = 1 << 24
+    for i in range(0, E * H, step):
+        n = min(step, E * H - i)
+        words = bg.random_raw(n).astype(np.uint64)
+        out[i:i + n] = np.where((words >> np.uint64(32)) >= thresh, np.float32(1.0 / (1.0 - p)), np.float32(0.0))
+    return out.reshape(E, H)
+
+
+def make_opts(w, seed, bias=True, weights=True, p=0.0):
+    rng = np.random.default_rng(seed)
+    E, H = w["E"], w["H"]
+    o = dict(bias=rng.normal(0, 1.0, (E, H)).astype(np.float32) if bias else None,
+             ew=rng.uniform(0.2, 1.0, E).astype(np.float32) if weights else None,
+             drop_p=p, seed=seed * 7919 + 3)
+    return o
+
+
+def gpu_opts(o):
+    d = dev()
+    return dict(bias=None if o["bias"] is None else torch.from_numpy(o["bias"]).to(d),
+                edge_weight=None if o["ew"] is None else torch.from_numpy(o["ew"]).to(d),
+                dropout_p=o["drop_p"], dropout_seed=o["seed"])
+
+
+def oracle_opts(o):
+    return dict(bias=o["bias"], ew=o["ew"], drop_p=o["drop_p"], seed=o["seed"])
+
+
+def run_ex(w, o, t=None):
+    t = t or to_dev(w)
+    d = dev()
+    t["dO"] = to_torch(w["dO"])
+    tip, tix, tpm = gtgen.source_sorted(w["indptr"], w["indices"], want_perm=True)
+    g = gpu_opts(o)
+    out, lse = gt.gt_sparse_mha_fwd_ex(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], want_lse=True, **g)
+    res = gt.gt_sparse_mha_bwd_ex(t["indptr"], t["indices"], torch.from_numpy(tip).to(d),
+                                  torch.from_numpy(tix).to(d), torch.from_numpy(tpm).to(d), t["Q"], t["K"], t["V"],
+                                  out, t["dO"], lse, want_dbias=True, want_dweight=True, **g)
+    torch.cuda.synchronize()
+    return (out, lse) + tuple(res)
+
+
+def edge_bounds(w, o, lse, out_of, e_dst, e_src, e_ids):
+    """alpha*c [n][H] and the weight alpha (c |da| + |dO_v|.|out_v|) [n][H] of the listed edges."""
+    Q, K, V, G = (widen(w[k][idx]) for k, idx in (("Q", e_dst), ("K", e_src), ("V", e_src), ("dO", e_dst)))
+    dot = np.einsum("ehd,ehd->eh", Q, K) / math.sqrt(w["D"])
+    s = dot * (o["ew"][e_ids][:, None] if o["ew"] is not None else 1.0)
+    if o["bias"] is not None:
+        s = s + o["bias"][e_ids]
+    alpha = np.exp(s - lse[e_dst])
+    if o["drop_p"]:
+        if "c_all" not in o:
+            o["c_all"] = keep_mask(o["seed"], w["E"], w["H"], o["drop_p"])
+        c = o["c_all"][e_ids].astype(np.float64)
+    else:
+        c = np.ones_like(alpha)
+    da = np.einsum("ehd,ehd->eh", np.abs(G), np.abs(V))  # bounds |dO.v| and its rounding
+    outs = np.stack([out_of(v) for v in e_dst]) if len(e_dst) else np.zeros((0, w["H"], w["D"]))
+    dabs = np.einsum("ehd,ehd->eh", np.abs(G), np.abs(outs))
+    wt = alpha * (c * da + dabs)
+    absdot = np.einsum("ehd,ehd->eh", np.abs(Q), np.abs(K)) / math.sqrt(w["D"])
+    return alpha * c, wt, absdot
+
+
+def check_full(w, o):
+    say("ex %s N=%d E=%d H=%d D=%d dtype=%d bias=%s ew=%s p=%g chunk=%d" % (
+        w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"], o["bias"] is not None, o["ew"] is not None,
+        o["drop_p"], gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+    out, lse, dq, dk, dv, dbias, dw = run_ex(w, o)
+    ftol, btol = tols(w)
+    kw = oracle_opts(o)
+    rout, rlse = oracle.fwd_ex(*oracle_inputs(w), want_lse=True, **kw)
+    assert_close(host(out), rout, ftol, "out " + w["name"])
+    check_lse(host(lse), rlse, "lse " + w["name"])
+    g = oracle.bwd_ex(*oracle_inputs(w), w["dO"], **kw)
+    N, H, D = w["N"], w["H"], w["D"]
+    e_dst = np.repeat(np.arange(N), np.diff(w["indptr"]))
+    e_src = w["indices"].astype(np.int64)
+    e_ids = np.arange(w["E"])
+    ac, wt, absdot = edge_bounds(w, o, g["lse"], lambda v: rout[v], e_dst, e_src, e_ids)
+    ww = (o["ew"][:, None, None] if o["ew"] is not None else 1.0)
+    Qa, Ka, Ga = (np.abs(widen(w[k])) for k in ("Q", "K", "dO"))
+    BQ = np.zeros((N, H, D))
+    BK = np.zeros((N, H, D))
+    BV = np.zeros((N, H, D))
+    np.add.at(BQ, e_dst, wt[:, :, None] * ww * Ka[e_src] / math.sqrt(D))
+    np.add.at(BK, e_src, wt[:, :, None] * ww * Qa[e_dst] / math.sqrt(D))
+    np.add.at(BV, e_src, ac[:, :, None] * Ga[e_dst])
+    check_bound(host(dq), g["dq"], BQ, btol, "dQ " + w["name"])
+    check_bound(host(dk), g["dk"], BK, btol, "dK " + w["name"])
+    check_bound(host(dv), g["dv"], BV, btol, "dV " + w["name"])
+    check_bound(host(dbias), g["dbias"], wt, btol, "dbias " + w["name"])
+    check_bound(host(dw), g["dw"], (wt * absdot).sum(1), btol, "dweight " + w["name"])
+
+
+VARIANTS = {
+    "bias": dict(bias=True, weights=False, p=0.0),
+    "weights": dict(bias=False, weights=True, p=0.0),
+    "dropout": dict(bias=False, weights=False, p=0.25),
+    "all": dict(bias=True, weights=True, p=0.4),
+}
+
+
+@pytest.mark.parametrize("variant", sorted(VARIANTS))
+@pytest.mark.parametrize("name,chunk", [("tiny_random", 1024), ("tiny_random", 2), ("molecules", 1024),
+                                        ("molecules", 3)])
+def test_variants_small(variant, name, chunk):
+    w = with_grad(workload(name))
+    with chunk_edges(chunk):
+        check_full(w, make_opts(w, 5, **VARIANTS[variant]))
+
+
+@pytest.mark.parametrize("H,D", [(8, 64), (3, 5), (4, 33), (2, 256), (16, 64), (8, 32), (64, 4)])
+@pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
+def test_variants_shapes(H, D, dtype):
+    w = with_grad(random_graph(H * 100 + D, 60, 800, H, D, dtype))
+    with chunk_edges(40):
+        check_full(w, make_opts(w, H + D, bias=True, weights=True, p=0.3))
+
+
+def test_one_hub_row_and_source():
+    from tests.test_gpu_parity import custom
+    N, E = 40, 2500
+    other = gtgen.random_coo(3, N, E)[0]
+    with chunk_edges(100):
+        for src, dst in ((other, np.full(E, 9)), (np.full(E, 9), other)):
+            w = with_grad(custom(N, src, dst, 8, 64, seed=7))
+            check_full(w, make_opts(w, 8, bias=True, weights=True, p=0.2))
+
+
+@pytest.mark.parametrize("name", ["regular16", "molecules"])
+def test_neutral_options_match_the_plain_kernels(name):
+    w = with_grad(workload(name))
+    t = to_dev(w)
+    d = dev()
+    say("neutral options %s" % name)
+    E, H = w["E"], w["H"]
+    zeros = torch.zeros((E, H), dtype=torch.float32, device=d)
+    ones = torch.ones(E, dtype=torch.float32, device=d)
+    tip, tix, tpm = (torch.from_numpy(x).to(d) for x in gtgen.source_sorted(w["indptr"], w["indices"],
+                                                                            want_perm=True))
+    dO = to_torch(w["dO"])
+    with chunk_edges(7):
+        out, lse = gt.gt_sparse_mha_fwd_lse(t["indptr"], t["indices"], t["Q"], t["K"], t["V"])
+        xout, xlse = gt.gt_sparse_mha_fwd_ex(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], want_lse=True,
+                                             bias=zeros, edge_weight=ones)
+        dq, dk, dv = gt.gt_sparse_mha_bwd(t["indptr"], t["indices"], tip, tix, t["Q"], t["K"], t["V"], out, dO, lse)
+        xq, xk, xv, _, _ = gt.gt_sparse_mha_bwd_ex(t["indptr"], t["indices"], tip, tix, tpm, t["Q"], t["K"],
+                                                   t["V"], out, dO, lse, bias=zeros, edge_weight=ones,
+                                                   want_dbias=True)
+        torch.cuda.synchronize()
+    # same arithmetic; the two kernel variants differ only in how the compiler
+    # contracts multiply-adds around the logit, so agreement is to rounding
+    for x, y in ((xout, out), (xlse, lse), (xq, dq), (xk, dk), (xv, dv)):
+        assert torch.allclose(x, y, rtol=1e-5, atol=1e-6 * float(y.abs().max()))
+
+
+def test_plan_with_options_is_bitwise_the_plain_call():
+    w = with_grad(workload("regular16"))
+    t = to_dev(w)
+    o = make_opts(w, 12, bias=True, weights=True, p=0.3)
+    g = gpu_opts(o)
+    say("plan with options")
+    with chunk_edges(5):
+        out, lse, dq, dk, dv, db, dw = run_ex(w, o, t)
+        plan = gt.gt_plan_create(t["indptr"], t["indices"], transpose=True)
+        pout, plse = gt.gt_sparse_mha_fwd_plan(plan, t["Q"], t["K"], t["V"], want_lse=True, **g)
+        pq, pk, pv, pb, pw = gt.gt_sparse_mha_bwd_plan(plan, t["Q"], t["K"], t["V"], out, t["dO"], lse,
+                                                       want_dbias=True, want_dweight=True, **g)
+        torch.cuda.synchronize()
+    for x, y in ((pout, out), (plse, lse), (pq, dq), (pk, dk), (pv, dv), (pb, db), (pw, dw)):
+        assert torch.equal(x, y)
+    plan.destroy()
+
+
+def test_dropout_is_deterministic_and_seeded():
+    w = with_grad(workload("tiny_random"))
+    t = to_dev(w)
+    o = make_opts(w, 3, bias=False, weights=False, p=0.5)
+    a = run_ex(w, o, dict(t))
+    b = run_ex(w, o, dict(t))
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+    c = run_ex(w, dict(o, seed=o["seed"] + 1), dict(t))
+    assert not torch.equal(a[0], c[0])
+
+
+@pytest.mark.parametrize("name,p", [("powerlaw", 0.2), ("lognormal", 0.0)])
+def test_variants_large_sampled(name, p):
+    w = with_grad(workload(name))
+    o = make_opts(w, 21, bias=True, weights=True, p=p)
+    say("ex %s sampled N=%d E=%d" % (name, w["N"], w["E"]))
+    out, lse, dq, dk, dv, dbias, dw = (host(x) for x in run_ex(w, o))
+    ftol, btol = tols(w)
+    kw = oracle_opts(o)
+    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    rows = sample_rows(w["indptr"], chunk, n_random=600)
+    rlse, rdelta = oracle.row_stats_ex(*oracle_inputs(w), w["dO"], **kw)
+    check_lse(lse, rlse, "lse " + name)
+    tip, tix, tpm = gtgen.source_sorted(w["indptr"], w["indices"], want_perm=True)
+    srcs = sample_rows(tip, chunk, n_random=600, seed=1)
+    need = np.unique(np.concatenate([rows] + [tix[tip[u]:tip[u + 1]] for u in srcs]).astype(np.int64))
+    rout = oracle.fwd_ex(*oracle_inputs(w), rows=need, **kw)
+    pos = {int(v): i for i, v in enumerate(need)}
+    out_of = lambda v: rout[pos[int(v)]]  # noqa: E731
+    assert_close(out[rows], np.stack([out_of(v) for v in rows]), ftol, "out %s" % name)
+    H, D, ip = w["H"], w["D"], w["indptr"]
+    rdb = np.zeros((w["E"], H))
+    rdw = np.zeros(w["E"])
+    rq = oracle.dq_rows_ex(*oracle_inputs(w), w["dO"], rlse, rdelta, rows, dbias=rdb, dw=rdw, **kw)
+    Ka, Qa, Ga = (np.abs(widen(w[k])) for k in ("K", "Q", "dO"))
+    BQ = np.zeros((len(rows), H, D))
+    eds = []
+    Bdb = []
+    Bdw = []
+    for i, v in enumerate(rows):
+        e_ids = np.arange(ip[v], ip[v + 1])
+        if not len(e_ids):
+            continue
+        src = w["indices"][e_ids].astype(np.int64)
+        dst = np.full(len(e_ids), v)
+        ac, wt, absdot = edge_bounds(w, o, rlse, out_of, dst, src, e_ids)
+        BQ[i] = (wt[:, :, None] * o["ew"][e_ids][:, None, None] * Ka[src]).sum(0) / math.sqrt(D)
+        eds.append(e_ids)
+        Bdb.append(wt)
+        Bdw.append((wt * absdot).sum(1))
+    check_bound(dq[rows], rq, BQ, btol, "dQ %s (%d rows)" % (name, len(rows)))
+    eds = np.concatenate(eds)
+    check_bound(dbias[eds], rdb[eds], np.concatenate(Bdb), btol, "dbias %s" % name)
+    check_bound(dw[eds], rdw[eds], np.concatenate(Bdw), btol, "dweight %s" % name)
+    rk, rv = oracle.dkv_sources_ex(tip, tix, tpm, w["Q"], w["K"], w["V"], w["dO"], rlse, rdelta, srcs, **kw)
+    BK = np.zeros((len(srcs), H, D))
+    BV = np.zeros((len(srcs), H, D))
+    for i, u in enumerate(srcs):
+        js = np.arange(tip[u], tip[u + 1])
+        if not len(js):
+            continue
+        dst = tix[js].astype(np.int64)
+        e_ids = tpm[js].astype(np.int64)
+        ac, wt, _ = edge_bounds(w, o, rlse, out_of, dst, np.full(len(js), u), e_ids)
+        BK[i] = (wt[:, :, None] * o["ew"][e_ids][:, None, None] * Qa[dst]).sum(0) / math.sqrt(D)
+        BV[i] = (ac[:, :, None] * Ga[dst]).sum(0)
+    check_bound(dk[srcs], rk, BK, btol, "dK %s (%d sources)" % (name, len(srcs)))
+    check_bound(dv[srcs], rv, BV, btol, "dV %s (%d sources)" % (name, len(srcs)))
