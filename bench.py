@@ -13,12 +13,14 @@ matches the current kernel source), and the CPU oracle timed on a bounded
 sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan]
+                  [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan] [--no-variants]
                   [--calib-copy]
 
 Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM),
-the backward (gt_sparse_mha_bwd), and graph construction (COO to CSR, a plan
-with its transpose, the forward on a plan), each event-timed on the same inputs.
+the backward (gt_sparse_mha_bwd), graph construction (COO to CSR, a plan with
+its transpose, the forward on a plan), and the forward and backward with an
+additive bias, edge weights and attention dropout, each event-timed on the
+same inputs.
 """
 import argparse
 import hashlib
@@ -230,6 +232,57 @@ def time_plan(gt, t, w, steps):
     return res
 
 
+def time_variants(gt, t, w, steps, warmup=2):
+    """Forward and backward with an additive bias [E][H], edge weights [E] and
+    attention dropout (p = 0.1), event-timed; algorithmic bytes add the bias
+    and weights (and, in the backward, the transpose's CSR positions)."""
+    import numpy as np
+    import torch
+
+    import gtgen
+
+    dev = t["Q"].device
+    E, H = w["E"], w["H"]
+    bias = (torch.from_numpy(gtgen.normal_f32(3, 11, (E, H))) * 0.5).to(dev)
+    ew = torch.from_numpy(gtgen.uniform_f64(3, 12, E, 0.2, 1.0).astype(np.float32)).to(dev)
+    opts = dict(bias=bias, edge_weight=ew, dropout_p=0.1, dropout_seed=1234)
+    tip, tix, tpm = (torch.from_numpy(x).to(dev) for x in gtgen.source_sorted(w["indptr"], w["indices"],
+                                                                              want_perm=True))
+    g = gtgen.make_grad(w["N"], H, w["D"], w["dtype"], seed=11)
+    dO = (torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16) if g.dtype == np.uint16
+          else torch.from_numpy(g).to(dev))
+    out = torch.empty_like(t["Q"])
+    lse = torch.empty((w["N"], H), dtype=torch.float32, device=dev)
+
+    def fwd():
+        gt.gt_sparse_mha_fwd_ex(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], out=out, lse=lse, **opts)
+
+    def bwd():
+        gt.gt_sparse_mha_bwd_ex(t["indptr"], t["indices"], tip, tix, tpm, t["Q"], t["K"], t["V"], out, dO, lse,
+                                **opts)
+
+    res = {}
+    extra = E * H * 4 + E * 4
+    for name, fn, nbytes in (("fwd_ms", fwd, algorithmic_bytes(w) + extra),
+                             ("bwd_ms", bwd, backward_bytes(w) + 2 * extra + 4 * E)):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name] = ms
+        res[name.replace("_ms", "_GBps")] = nbytes / (ms * 1e-3) / 1e9
+    log("variants (bias, weights, dropout 0.1): forward %.3f ms (%.0f GB/s), backward %.3f ms (%.0f GB/s)"
+        % (res["fwd_ms"], res["fwd_GBps"], res["bwd_ms"], res["bwd_GBps"]))
+    del bias, ew, tip, tix, tpm, dO, out, lse
+    return res
+
+
 def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     """The oracle as it stands on a fixed random sample of destination rows."""
     import numpy as np
@@ -282,6 +335,7 @@ def main():
     ap.add_argument("--no-stages", action="store_true", help="skip timing the unfused stages")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     ap.add_argument("--no-plan", action="store_true", help="skip timing graph construction and plans")
+    ap.add_argument("--no-variants", action="store_true", help="skip timing the logit variants and dropout")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -366,6 +420,7 @@ def main():
         "stages": None,
         "backward": None,
         "plan": None,
+        "variants": None,
     }
     out_host = out.float().cpu().numpy() if out.dtype == torch.bfloat16 else out.cpu().numpy()
     if not args.no_stages:
@@ -374,6 +429,8 @@ def main():
         line["backward"] = time_backward(gt, t, w, max(3, args.steps // 2), 2)
     if not args.no_plan:
         line["plan"] = time_plan(gt, t, w, max(3, args.steps // 4))
+    if not args.no_variants:
+        line["variants"] = time_variants(gt, t, w, max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, out_host)
     print(json.dumps(line), flush=True)

@@ -86,6 +86,16 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
+        auto ej = [&](int j) -> int64_t { return ok[j] ? eb + grp + (int64_t)j * epw : e0; };
+        float xw[U], xb[U][NC];
+        if constexpr (XL) {  // ahead of the gathers: waiting for them never waits for a gather
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej(j) * a.H + head[c]] * kLog2e : 0.0f;
+            }
+        }
         U4 kr[U][NC], vr[U][NC];
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -99,16 +109,13 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
                 vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
-        int64_t ej[U];
-        float xw[U], xb[U][NC];
+        DropBatch db;
+        bool bdrop = false;
         if constexpr (XL) {
-#pragma unroll
-            for (int j = 0; j < U; ++j) {
-                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
-                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
-#pragma unroll
-                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej[j] * a.H + head[c]] * kLog2e : 0.0f;
-            }
+            bdrop = a.drop_thresh && drop_batched(a.H, -1, epw * U);
+            if (bdrop)
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane,
+                                [&](int k) { return eb + k; });
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
@@ -131,12 +138,14 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
                     sd = __builtin_fmaf(sd, xw[j], xb[j][c]);
                     const float p = ok[j] ? exp2_(sd - ls[c]) : 0.0f;
                     float keep = 1.0f;
-                    if (a.drop_thresh)
-                        keep = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + head[c]) >= a.drop_thresh
+                    if (bdrop)
+                        keep = drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ej(j), head[c]);
+                    else if (a.drop_thresh)
+                        keep = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + head[c]) >= a.drop_thresh
                                    ? a.drop_scale : 0.0f;
                     const float ds = p * (keep * dd - dl[c]);
                     const bool lead = ok[j] && act[c] && (gl & (lph - 1)) == 0;
-                    if (a.dbias && lead) a.dbias[ej[j] * a.H + head[c]] = ds;
+                    if (a.dbias && lead) a.dbias[ej(j) * a.H + head[c]] = ds;
                     if (lead) tw = __builtin_fmaf(ds, raw * kLn2, tw);
                     const float dsw = ds * xw[j];
 #pragma unroll
@@ -151,7 +160,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
             if constexpr (XL)
                 if (a.dew) {
                     tw = seg_sum(tw, G);  // over the group's heads
-                    if (ok[j] && gl == 0) a.dew[ej[j]] = tw;
+                    if (ok[j] && gl == 0) a.dew[ej(j)] = tw;
                 }
         }
     }
@@ -236,8 +245,6 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
             if constexpr (XL) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
-        U4 qr[U][NC], gr[U][NC];
-        float ls[U][NC], dl[U][NC];
         float xw[U], xb[U][NC];
         if constexpr (XL) {
 #pragma unroll
@@ -247,6 +254,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
                 for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[(int64_t)ep[j] * a.H + head[c]] * kLog2e : 0.0f;
             }
         }
+        U4 qr[U][NC], gr[U][NC];
+        float ls[U][NC], dl[U][NC];
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
@@ -261,6 +270,21 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
         if (nb < e1) {
             load_ids<U>(idx, nb, grp, epw, e1, un);
             if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+        }
+        DropBatch db;
+        bool bdrop = false;
+        if constexpr (XL) {
+            bdrop = a.drop_thresh && drop_batched(a.H, -1, epw * U);
+            if (bdrop)  // slot k's CSR position sits in ep[k / epw] of group k % epw
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane, [&](int k) {
+                    int64_t r = 0;
+#pragma unroll
+                    for (int jj = 0; jj < U; ++jj) {
+                        const int v = __shfl(ep[jj], (k % epw) * G, kWave);
+                        if (jj == k / epw) r = v;
+                    }
+                    return r;
+                });
         }
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -281,7 +305,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
                     sd = __builtin_fmaf(sd, xw[j], xb[j][c]);
                     const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
                     float keep = 1.0f;
-                    if (a.drop_thresh)
+                    if (bdrop)
+                        keep = drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ep[j], head[c]);
+                    else if (a.drop_thresh)
                         keep = philox_hi32(a.drop_seed, (uint64_t)ep[j] * a.H + head[c]) >= a.drop_thresh
                                    ? a.drop_scale : 0.0f;
                     const float pk = p * keep;
@@ -378,6 +404,15 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
+        auto ej = [&](int j) -> int64_t { return ok[j] ? eb + grp + (int64_t)j * epw : e0; };
+        float xw[U], xb[U];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
+                xb[j] = a.bias ? a.bias[ej(j) * a.H + h] * kLog2e : 0.0f;
+            }
+        }
         float kv[U][KD], vv[U][KD];
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -389,15 +424,12 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
             }
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
-        int64_t ej[U];
-        float xw[U], xb[U];
+        DropBatch db;
+        bool bdrop = false;
         if constexpr (XL) {
-#pragma unroll
-            for (int j = 0; j < U; ++j) {
-                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
-                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
-                xb[j] = a.bias ? a.bias[ej[j] * a.H + h] * kLog2e : 0.0f;
-            }
+            bdrop = a.drop_thresh && drop_batched(a.H, h, epw * U);
+            if (bdrop)
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, h, epw * U, lane, [&](int k) { return eb + k; });
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
@@ -414,14 +446,16 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
                 sd = __builtin_fmaf(sd, xw[j], xb[j]);
                 const float p = ok[j] ? exp2_(sd - ls) : 0.0f;
                 float keep = 1.0f;
-                if (a.drop_thresh)
-                    keep = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
+                if (bdrop)
+                    keep = drop_mult(db, a.drop_scale, a.H, h, grp + j * epw, ej(j), h);
+                else if (a.drop_thresh)
+                    keep = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
                 const float ds = p * (keep * dd - dl);
                 // one wave per head: the per-head terms of dw go to scratch and
                 // sum_heads_kernel adds them up in head order
                 if (ok[j] && gl == 0) {
-                    if (a.dbias) a.dbias[ej[j] * a.H + h] = ds;
-                    if (a.dew) a.dew_part[ej[j] * a.H + h] = ds * raw * kLn2;
+                    if (a.dbias) a.dbias[ej(j) * a.H + h] = ds;
+                    if (a.dew) a.dew_part[ej(j) * a.H + h] = ds * raw * kLn2;
                 }
                 const float dsw = ds * xw[j];
 #pragma unroll
@@ -490,7 +524,6 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
             if constexpr (XL) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
-        float qv[U][KD], gv[U][KD], ls[U], dl[U];
         float xw[U], xb[U];
         if constexpr (XL) {
 #pragma unroll
@@ -499,6 +532,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
                 xb[j] = a.bias ? a.bias[(int64_t)ep[j] * a.H + h] * kLog2e : 0.0f;
             }
         }
+        float qv[U][KD], gv[U][KD], ls[U], dl[U];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
 #pragma unroll
@@ -515,6 +549,21 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
             load_ids<U>(idx, nb, grp, epw, e1, un);
             if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
         }
+        DropBatch db;
+        bool bdrop = false;
+        if constexpr (XL) {
+            bdrop = a.drop_thresh && drop_batched(a.H, h, epw * U);
+            if (bdrop)
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, h, epw * U, lane, [&](int k) {
+                    int64_t r = 0;
+#pragma unroll
+                    for (int jj = 0; jj < U; ++jj) {
+                        const int v = __shfl(ep[jj], (k % epw) * G, kWave);
+                        if (jj == k / epw) r = v;
+                    }
+                    return r;
+                });
+        }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             float sd = 0.0f, dd = 0.0f;
@@ -529,7 +578,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
                 sd = __builtin_fmaf(sd, xw[j], xb[j]);
                 const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
                 float keep = 1.0f;
-                if (a.drop_thresh)
+                if (bdrop)
+                    keep = drop_mult(db, a.drop_scale, a.H, h, grp + j * epw, ep[j], h);
+                else if (a.drop_thresh)
                     keep = philox_hi32(a.drop_seed, (uint64_t)ep[j] * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
                 const float pk = p * keep;
                 const float dsw = p * (keep * dd - dl[j]) * xw[j];
@@ -641,9 +692,9 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 2, XL ? 2 : 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dq_vec_kernel<DT, 1, 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 1, XL ? 2 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
@@ -684,9 +735,9 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                bwd_dkv_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 2, XL ? 2 : 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dkv_vec_kernel<DT, 1, 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 1, XL ? 2 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)

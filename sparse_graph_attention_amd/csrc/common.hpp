@@ -189,9 +189,9 @@ __device__ __forceinline__ float seg_sum_c(float x) {
 // SC 2011): word i of the stream under key (seed, 0) is word i mod 4 of the
 // block whose counter is (i / 4 + 1, 0, 0, 0).  Ten rounds of two 64x64->128
 // bit products; the key is bumped by the two Weyl constants after each round.
-// Returns the word's upper 32 bits.
-__device__ __forceinline__ uint32_t philox_hi32(uint64_t seed, uint64_t i) {
-    uint64_t c0 = i / 4 + 1, c1 = 0, c2 = 0, c3 = 0, k0 = seed, k1 = 0;
+// philox_block_hi gives the upper 32 bits of the four words of one block.
+__device__ __forceinline__ void philox_block_hi(uint64_t seed, uint64_t ctr, uint32_t out[4]) {
+    uint64_t c0 = ctr, c1 = 0, c2 = 0, c3 = 0, k0 = seed, k1 = 0;
 #pragma unroll
     for (int r = 0; r < 10; ++r) {
         const uint64_t a0 = 0xD2E7470EE14C6C93ull * c0, h0 = __umul64hi(0xD2E7470EE14C6C93ull, c0);
@@ -203,9 +203,85 @@ __device__ __forceinline__ uint32_t philox_hi32(uint64_t seed, uint64_t i) {
         k0 += 0x9E3779B97F4A7C15ull;
         k1 += 0xBB67AE8584CAA73Bull;
     }
-    const uint32_t w = (uint32_t)(i & 3);
-    const uint64_t x = w == 0 ? c0 : w == 1 ? c1 : w == 2 ? c2 : c3;
-    return (uint32_t)(x >> 32);
+    out[0] = (uint32_t)(c0 >> 32);
+    out[1] = (uint32_t)(c1 >> 32);
+    out[2] = (uint32_t)(c2 >> 32);
+    out[3] = (uint32_t)(c3 >> 32);
+}
+
+// Upper 32 bits of word i of the stream.
+__device__ __forceinline__ uint32_t philox_hi32(uint64_t seed, uint64_t i) {
+    uint32_t w[4];
+    philox_block_hi(seed, i / 4 + 1, w);
+    const uint32_t k = (uint32_t)(i & 3);
+    return k == 0 ? w[0] : k == 1 ? w[1] : k == 2 ? w[2] : w[3];
+}
+
+// Keep decisions of a batch of edges, computed once per wave: a batch has
+// nslots edge slots (slot k = group + j * edges-per-wave), and slot k's edge
+// needs the words of indices pos(k) * H + h.  The blocks involved are spread
+// over the lanes, bpe blocks per slot (lane L -> slot L / bpe, block L % bpe,
+// in rounds of 64 lanes); each lane keeps its block's four keep bits.  One
+// Philox evaluation per round replaces one per (edge, vector) per lane.
+constexpr int kDropRounds = 2;
+
+struct DropBatch {
+    uint32_t kb[kDropRounds];
+    int rounds;
+};
+
+// Blocks per slot: all heads of an edge (hsel < 0), or one head.
+__device__ __forceinline__ int drop_bpe(int H, int hsel) {
+    return hsel >= 0 ? 1 : (H % 4 == 0 ? H / 4 : (H + 3) / 4 + 1);
+}
+
+__device__ __forceinline__ int64_t drop_first_block(int64_t pos, int H, int hsel) {
+    return hsel >= 0 ? (pos * H + hsel) / 4 : (pos * H) / 4;
+}
+
+// Whether a batch fits the rounds (else each lane draws its own words).
+__device__ __forceinline__ bool drop_batched(int H, int hsel, int nslots) {
+    return nslots * drop_bpe(H, hsel) <= 64 * kDropRounds;
+}
+
+// pos_of(k) must be called by every lane (it may use cross-lane shuffles).
+template <typename PosOf>
+__device__ __forceinline__ void drop_batch_init(DropBatch& d, uint64_t seed, uint32_t thresh, int H, int hsel,
+                                                int nslots, int lane, PosOf pos_of) {
+    const int bpe = drop_bpe(H, hsel);
+    d.rounds = (nslots * bpe + 63) >> 6;
+#pragma unroll
+    for (int r = 0; r < kDropRounds; ++r) {
+        d.kb[r] = 0;
+        if (r < d.rounds) {
+            const int L = r * 64 + lane;
+            const int k = L / bpe, m = L - k * bpe;
+            const int64_t pos = pos_of(k < nslots ? k : 0);
+            if (k < nslots) {
+                uint32_t w[4];
+                philox_block_hi(seed, (uint64_t)(drop_first_block(pos, H, hsel) + m) + 1, w);
+                d.kb[r] = (uint32_t)(w[0] >= thresh) | (uint32_t)(w[1] >= thresh) << 1 |
+                          (uint32_t)(w[2] >= thresh) << 2 | (uint32_t)(w[3] >= thresh) << 3;
+            }
+        }
+    }
+}
+
+// The dropout multiplier (0 or scale) of slot k (edge at CSR position pos),
+// head h.  Every lane must call it (cross-lane shuffles).
+__device__ __forceinline__ float drop_mult(const DropBatch& d, float scale, int H, int hsel, int k, int64_t pos,
+                                           int h) {
+    const int bpe = drop_bpe(H, hsel);
+    const int64_t i = pos * H + h;
+    const int L = k * bpe + (int)(i / 4 - drop_first_block(pos, H, hsel));
+    uint32_t bits = 0;
+#pragma unroll
+    for (int r = 0; r < kDropRounds; ++r)
+        if (r < d.rounds) {
+            const uint32_t t = (uint32_t)__shfl((int)d.kb[r], L & 63, 64);
+            if ((L >> 6) == r) bits = t;
+        }
+    return (bits >> (i & 3)) & 1u ? scale : 0.0f;
 }
 
 // ---------------------------------------------------------------- 16-byte vectors

@@ -91,6 +91,19 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
+        // extended logits: s = w_e * s + bias[e][h] (log2 units); edge ids
+        // clamped into the item like the source ids; loaded ahead of the gathers
+        // so that waiting for them never waits for a gather
+        auto ej = [&](int j) -> int64_t { return ok[j] ? eb + grp + (int64_t)j * epw : e0; };
+        float xw[U], xb[U][NC];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej(j) * a.H + head[c]] * kLog2e : 0.0f;
+            }
+        }
         U4 kr[U][NC], vr[U][NC];
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -104,18 +117,13 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
-        // extended logits: s = w_e * s + bias[e][h] (log2 units); edge ids
-        // clamped into the item like the source ids
-        int64_t ej[U];
-        float xw[U], xb[U][NC];
+        DropBatch db;
+        bool bdrop = false;
         if constexpr (XL) {
-#pragma unroll
-            for (int j = 0; j < U; ++j) {
-                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
-                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
-#pragma unroll
-                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej[j] * a.H + head[c]] * kLog2e : 0.0f;
-            }
+            bdrop = a.drop_thresh && drop_batched(a.H, -1, epw * U);
+            if (bdrop)
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane,
+                                [&](int k) { return eb + k; });
         }
 
         float s[U][NC];
@@ -148,10 +156,13 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 const float p = ok[j] ? exp2_(s[j][c] - mn) : 0.0f;
                 l[c] += p;
                 float pv = p;  // dropout zeroes the weight, not its share of the normaliser
-                if constexpr (XL)
-                    if (a.drop_thresh)
-                        pv = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + head[c]) >= a.drop_thresh
+                if constexpr (XL) {
+                    if (bdrop)
+                        pv = p * drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ej(j), head[c]);
+                    else if (a.drop_thresh)
+                        pv = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + head[c]) >= a.drop_thresh
                                  ? p * a.drop_scale : 0.0f;
+                }
                 float vf[VN];
                 VT::unpack(vr[j][c], vf);
 #pragma unroll
@@ -256,6 +267,15 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
+        auto ej = [&](int j) -> int64_t { return ok[j] ? eb + grp + (int64_t)j * epw : e0; };
+        float xw[U], xb[U];
+        if constexpr (XL) {
+#pragma unroll
+            for (int j = 0; j < U; ++j) {
+                xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
+                xb[j] = a.bias ? a.bias[ej(j) * a.H + h] * kLog2e : 0.0f;
+            }
+        }
         float kv[U][KD], vv[U][KD];
 #pragma unroll
         for (int j = 0; j < U; ++j)
@@ -269,15 +289,12 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
                 vv[j][k] = (ok[j] && act[k]) ? VT::scalar(a.V, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
-        int64_t ej[U];
-        float xw[U], xb[U];
+        DropBatch db;
+        bool bdrop = false;
         if constexpr (XL) {
-#pragma unroll
-            for (int j = 0; j < U; ++j) {
-                ej[j] = ok[j] ? eb + grp + (int64_t)j * epw : e0;
-                xw[j] = a.ew ? a.ew[ej[j]] : 1.0f;
-                xb[j] = a.bias ? a.bias[ej[j] * a.H + h] * kLog2e : 0.0f;
-            }
+            bdrop = a.drop_thresh && drop_batched(a.H, h, epw * U);
+            if (bdrop)
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, h, epw * U, lane, [&](int k) { return eb + k; });
         }
         float s[U];
 #pragma unroll
@@ -302,10 +319,13 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
             const float p = ok[j] ? exp2_(s[j] - mn) : 0.0f;
             l += p;
             float pv = p;
-            if constexpr (XL)
-                if (a.drop_thresh)
-                    pv = philox_hi32(a.drop_seed, (uint64_t)ej[j] * a.H + h) >= a.drop_thresh ? p * a.drop_scale
+            if constexpr (XL) {
+                if (bdrop)
+                    pv = p * drop_mult(db, a.drop_scale, a.H, h, grp + j * epw, ej(j), h);
+                else if (a.drop_thresh)
+                    pv = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + h) >= a.drop_thresh ? p * a.drop_scale
                                                                                             : 0.0f;
+            }
 #pragma unroll
             for (int k = 0; k < KD; ++k) acc[k] = __builtin_fmaf(pv, vv[j][k], acc[k]);
         }
@@ -425,11 +445,12 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
             // the 256 MB Infinity Cache; smaller ones are partly served from it.
             const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv)
-                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, XL ? 2 : GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                fused_vec_kernel<DT, 2, GT_F32_D64_U, 64, 16, true, false, XL><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, XL ? 2 : GT_F32_D64_U, 64, 16, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                fused_vec_kernel<DT, 1, GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
+                // the extended kernel keeps per-edge inputs live: fewer edges in flight
+                fused_vec_kernel<DT, 1, XL ? 4 : GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 fused_vec_kernel<DT, 1, 8, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
