@@ -14,13 +14,14 @@ sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan] [--no-variants]
+                  [--no-layout]
                   [--calib-copy]
 
 Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM),
 the backward (gt_sparse_mha_bwd), graph construction (COO to CSR, a plan with
 its transpose, the forward on a plan), and the forward and backward with an
 additive bias, edge weights and attention dropout, each event-timed on the
-same inputs.
+same inputs, and the forward with head-innermost [N][D][H] features.
 """
 import argparse
 import hashlib
@@ -44,6 +45,7 @@ DESCRIPTIONS = {
     "lognormal": "log-normal graph: N=2,400,000, E=60,000,000, in-degree log-normal (mean 25, sigma 1.2), "
                  "uniform sources, H=8, D=32, bf16 in/out, fp32 accumulation",
     "regular16": "in-degree-16 graph: N=100,000, E=1,600,000, uniform sources, H=8, D=64, fp32",
+    "molecules": "128 molecule-like graphs batched (N ~ 4,000, E ~ 8,500, symmetric), H=8, D=10, fp32",
 }
 
 
@@ -283,6 +285,42 @@ def time_variants(gt, t, w, steps, warmup=2):
     return res
 
 
+def time_layout(gt, t, w, steps, warmup=3):
+    """The forward with features [N][H][D] (gt_sparse_mha_fwd) and [N][D][H]
+    (gt_sparse_mha_fwd_layout: its own kernel where the shape allows, else
+    transposed copies), event-timed; algorithmic bytes as for the step."""
+    import torch
+
+    def ndh(x):
+        return x.transpose(1, 2).contiguous()
+
+    Qn, Kn, Vn = ndh(t["Q"]), ndh(t["K"]), ndh(t["V"])
+    out = torch.empty_like(t["Q"])
+    outn = torch.empty_like(Qn)
+    calls = {
+        "nhd": lambda: gt.gt_sparse_mha_fwd(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], out=out),
+        "ndh": lambda: gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], Qn, Kn, Vn, layout="ndh", out=outn),
+    }
+    res = {}
+    nbytes = algorithmic_bytes(w)
+    for name, fn in calls.items():
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        res[name + "_ms"] = ms
+        res[name + "_GBps"] = nbytes / (ms * 1e-3) / 1e9
+    log("layout: [N][H][D] %.4f ms, [N][D][H] %.4f ms" % (res["nhd_ms"], res["ndh_ms"]))
+    del Qn, Kn, Vn, out, outn
+    return res
+
+
 def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     """The oracle as it stands on a fixed random sample of destination rows."""
     import numpy as np
@@ -336,6 +374,7 @@ def main():
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     ap.add_argument("--no-plan", action="store_true", help="skip timing graph construction and plans")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the logit variants and dropout")
+    ap.add_argument("--no-layout", action="store_true", help="skip timing the head-innermost layout")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -421,6 +460,7 @@ def main():
         "backward": None,
         "plan": None,
         "variants": None,
+        "layout": None,
     }
     out_host = out.float().cpu().numpy() if out.dtype == torch.bfloat16 else out.cpu().numpy()
     if not args.no_stages:
@@ -431,6 +471,8 @@ def main():
         line["plan"] = time_plan(gt, t, w, max(3, args.steps // 4))
     if not args.no_variants:
         line["variants"] = time_variants(gt, t, w, max(3, args.steps // 4))
+    if not args.no_layout:
+        line["layout"] = time_layout(gt, t, w, 200 if w["E"] < 10 ** 6 else max(3, args.steps // 4))
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, out_host)
     print(json.dumps(line), flush=True)

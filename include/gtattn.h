@@ -213,6 +213,34 @@ int gt_sparse_mha_bwd_ex(const int64_t* indptr, const int32_t* indices, const in
                          const gt_logit_opts* opts, hipStream_t stream);
 
 /*
+ * Feature layouts.  GT_LAYOUT_NHD: [N][H][D], D contiguous (the gist's
+ * (N, h, d) view; every other entry point).  GT_LAYOUT_NDH: [N][D][H], head
+ * innermost, as "Graph Transformer in a Nutshell" reshapes q, k, v to
+ * [N, dh, nh] in SparseMHA.forward.  The layout applies to Q, K, V, out,
+ * dout, dQ, dK and dV; lse, bias and the other arrays are unchanged.
+ * gt_sparse_mha_fwd_layout / gt_sparse_mha_bwd_layout are gt_sparse_mha_fwd_ex
+ * / gt_sparse_mha_bwd_ex with a layout argument (GT_EINVAL for an unknown
+ * one).  For GT_LAYOUT_NDH the forward without logit options runs a kernel of
+ * its own when H is a multiple of the 16-byte vector (4 fp32 or 8 bf16
+ * elements) with a power-of-two quotient and D * H fits 64 vectors (1 KB);
+ * other shapes, the options and the backward go through [N][H][D] copies in
+ * the per-stream scratch (transposed on the device).
+ *
+ * (The tutorial also normalises along A[src, dst]'s rows, i.e. over each
+ * source's out-edges with the source's query: that is these calls on the
+ * transposed graph, e.g. a plan built from (dst, src) pairs.)
+ */
+typedef enum { GT_LAYOUT_NHD = 0, GT_LAYOUT_NDH = 1 } gt_layout;
+int gt_sparse_mha_fwd_layout(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K,
+                             const void* V, void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D,
+                             int32_t dtype, int32_t layout, const gt_logit_opts* opts, hipStream_t stream);
+int gt_sparse_mha_bwd_layout(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
+                             const int32_t* t_indices, const int32_t* t_perm, const void* Q, const void* K,
+                             const void* V, const void* out, const void* dout, const float* lse, void* dQ, void* dK,
+                             void* dV, float* dbias, float* dweight, int64_t N, int64_t E, int32_t H, int32_t D,
+                             int32_t dtype, int32_t layout, const gt_logit_opts* opts, hipStream_t stream);
+
+/*
  * Graph construction on the device.  "Graph Transformer in a Nutshell",
  * section "Graph Transformer Model": GTModel.forward stacks the (src, dst)
  * pairs of g.edges() into one sparse adjacency matrix and hands it to every

@@ -20,6 +20,8 @@ The functions have the names of the C entry points declared in
 * ``gt_sparse_mha_fwd_ex`` / ``gt_sparse_mha_bwd_ex`` -- with an additive
   logit bias [E][H], edge weights [E] and attention dropout (keyword
   arguments ``bias``, ``edge_weight``, ``dropout_p``, ``dropout_seed``);
+* ``gt_sparse_mha_fwd_layout`` / ``gt_sparse_mha_bwd_layout`` -- the same with
+  features in the head-innermost layout [N][D][H] (``layout="ndh"``);
 * ``gt_coo_to_csr(src, dst, n_dst)`` -- (indptr, indices[, perm]) built on the GPU;
 * ``gt_plan_create(indptr, indices)`` / ``gt_plan_create_coo(src, dst, n_dst)``
   -- a reusable graph plan (``GtPlan``), ``gt_plan_destroy``, ``gt_plan_info``,
@@ -41,6 +43,7 @@ GT_F32, GT_BF16 = 0, 1
 GT_OK, GT_EINVAL, GT_EUNSUPPORTED, GT_ENOMEM, GT_EHIP = 0, 1, 2, 3, 4
 GT_CFG_CHUNK_EDGES = 0
 GT_PLAN_TRANSPOSE = 1
+GT_LAYOUT_NHD, GT_LAYOUT_NDH = 0, 1
 
 EXPORTS = (
     "gt_sparse_mha_fwd",
@@ -48,6 +51,8 @@ EXPORTS = (
     "gt_sparse_mha_bwd",
     "gt_sparse_mha_fwd_ex",
     "gt_sparse_mha_bwd_ex",
+    "gt_sparse_mha_fwd_layout",
+    "gt_sparse_mha_bwd_layout",
     "gt_sddmm",
     "gt_edge_softmax",
     "gt_spmm",
@@ -100,6 +105,8 @@ def lib():
         _o = ctypes.POINTER(LogitOpts)
         L.gt_sparse_mha_fwd_ex.argtypes = [_p] * 7 + [_i64, _i64, _i32, _i32, _i32, _o, _p]
         L.gt_sparse_mha_bwd_ex.argtypes = [_p] * 16 + [_i64, _i64, _i32, _i32, _i32, _o, _p]
+        L.gt_sparse_mha_fwd_layout.argtypes = [_p] * 7 + [_i64, _i64, _i32, _i32, _i32, _i32, _o, _p]
+        L.gt_sparse_mha_bwd_layout.argtypes = [_p] * 16 + [_i64, _i64, _i32, _i32, _i32, _i32, _o, _p]
         L.gt_sddmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_edge_softmax.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.gt_spmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
@@ -125,7 +132,8 @@ def lib():
         for name in ("gt_coo_to_csr", "gt_plan_create", "gt_plan_create_coo", "gt_plan_destroy", "gt_plan_info",
                      "gt_plan_copy_graph", "gt_sparse_mha_fwd_plan", "gt_sparse_mha_bwd_plan"):
             getattr(L, name).restype = ctypes.c_int
-        for name in ("gt_sparse_mha_fwd_ex", "gt_sparse_mha_bwd_ex"):
+        for name in ("gt_sparse_mha_fwd_ex", "gt_sparse_mha_bwd_ex", "gt_sparse_mha_fwd_layout",
+                     "gt_sparse_mha_bwd_layout"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
                      "gt_config_set", "gt_profile_begin", "gt_profile_end"):
@@ -296,6 +304,66 @@ def gt_sparse_mha_bwd_ex(indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, 
                                       _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), _ptr(lse), _ptr(dQ), _ptr(dK),
                                       _ptr(dV), _ptr(dbias), _ptr(dweight), N, E, H, D, _dtype_code(Q), _optref(o),
                                       _stream(stream)), "gt_sparse_mha_bwd_ex")
+    return dQ, dK, dV, dbias, dweight
+
+
+def _layout_code(layout):
+    codes = {"nhd": GT_LAYOUT_NHD, "ndh": GT_LAYOUT_NDH}
+    if layout not in codes:
+        raise ValueError("layout must be 'nhd' ([N][H][D]) or 'ndh' ([N][D][H])")
+    return codes[layout]
+
+
+def _heads_dims(Q, layout):
+    return (Q.shape[1], Q.shape[2]) if layout == "nhd" else (Q.shape[2], Q.shape[1])
+
+
+def gt_sparse_mha_fwd_layout(indptr, indices, Q, K, V, layout="ndh", out=None, lse=None, want_lse=False, bias=None,
+                             edge_weight=None, dropout_p=0.0, dropout_seed=0, stream=None):
+    """gt_sparse_mha_fwd_ex with features [N][D][H] (layout 'ndh') or [N][H][D] ('nhd')."""
+    code = _layout_code(layout)
+    N, E = _csr(indptr, indices)
+    if Q.dim() != 3 or Q.shape[0] != N or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must all be [N][.][.] with N = len(indptr) - 1")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    H, D = _heads_dims(Q, layout)
+    out = _like(out, Q, "out")
+    if lse is None and want_lse:
+        lse = torch.empty((N, H), dtype=torch.float32, device=Q.device)
+    if lse is not None and (lse.shape != (N, H) or lse.dtype != torch.float32):
+        raise ValueError("lse must be float32 [N][H]")
+    o, _keep = _opts(E, H, Q.device, bias, edge_weight, dropout_p, dropout_seed)
+    _need_gpu(indptr, indices, Q, K, V, out, lse)
+    _check(lib().gt_sparse_mha_fwd_layout(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out),
+                                          _ptr(lse), N, E, H, D, _dtype_code(Q), code, _optref(o), _stream(stream)),
+           "gt_sparse_mha_fwd_layout")
+    return (out, lse) if lse is not None else out
+
+
+def gt_sparse_mha_bwd_layout(indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, layout="ndh",
+                             bias=None, edge_weight=None, dropout_p=0.0, dropout_seed=0, want_dbias=False,
+                             want_dweight=False, stream=None):
+    """gt_sparse_mha_bwd_ex with features in the given layout: (dQ, dK, dV, dbias or None, dweight or None)."""
+    code = _layout_code(layout)
+    N, E = _csr(indptr, indices)
+    if Q.dim() != 3 or Q.shape[0] != N or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must all be [N][.][.] with N = len(indptr) - 1")
+    H, D = _heads_dims(Q, layout)
+    for t, name in ((out, "out"), (dout, "dout")):
+        _like(t, Q, name)
+    if lse.shape != (N, H) or lse.dtype != torch.float32:
+        raise ValueError("lse must be float32 [N][H]")
+    dQ, dK, dV = (torch.empty_like(Q) for _ in range(3))
+    dbias = torch.empty((E, H), dtype=torch.float32, device=Q.device) if want_dbias else None
+    dweight = torch.empty(E, dtype=torch.float32, device=Q.device) if want_dweight else None
+    o, _keep = _opts(E, H, Q.device, bias, edge_weight, dropout_p, dropout_seed)
+    _need_gpu(indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse)
+    _check(lib().gt_sparse_mha_bwd_layout(_ptr(indptr), _ptr(indices), _ptr(t_indptr), _ptr(t_indices),
+                                          _ptr(t_perm), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), _ptr(dout), _ptr(lse),
+                                          _ptr(dQ), _ptr(dK), _ptr(dV), _ptr(dbias), _ptr(dweight), N, E, H, D,
+                                          _dtype_code(Q), code, _optref(o), _stream(stream)),
+           "gt_sparse_mha_bwd_layout")
     return dQ, dK, dV, dbias, dweight
 
 

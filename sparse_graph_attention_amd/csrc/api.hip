@@ -173,6 +173,24 @@ void choose_layout(Args& a, std::initializer_list<const void*> feats) {
     }
 }
 
+// The head-innermost kernel: a 16-byte vector holds VN heads of one d, the
+// vectors of a d are a power of two, and a row is at most 64 vectors.
+bool choose_layout_ndh(Args& a, std::initializer_list<const void*> feats) {
+    const int vn = a.dtype == GT_F32 ? 4 : 8;
+    if (a.H % vn != 0 || !pow2(a.H / vn)) return false;
+    const int64_t R = (int64_t)a.D * (a.H / vn);
+    if (R > kWave) return false;
+    for (const void* p : feats)
+        if (!aligned16(p)) return false;
+    a.vec = 2;
+    a.ndh = 1;
+    a.lph = a.H / vn;
+    a.R = (int)R;
+    a.G = pow2ceil(R);
+    a.NC = 1;
+    return true;
+}
+
 int check_common(int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype) {
     if (N < 0 || E < 0) return fail(GT_EINVAL, "N (%lld) and E (%lld) must be >= 0", (long long)N, (long long)E);
     if (N >= ((int64_t)1 << 31)) return fail(GT_EINVAL, "N (%lld) must be < 2^31", (long long)N);
@@ -350,7 +368,8 @@ int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, cons
 // The backward: a over the destination-sorted graph (a.N destinations), at
 // over the source-sorted one (at.N sources).  Without tables both plans are
 // built in scratch; with them only partials and delta come from scratch.
-int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStream_t stream) {
+// Scratch bytes of run_bwd (sizes the plans when no tables are given).
+int bwd_scratch_bytes(Args& a, Args& at, const Plan* tables, const Plan* t_tables, size_t* out) {
     const int64_t HD = (int64_t)a.H * a.D;
     size_t bytes = align256(sizeof(float) * (size_t)a.N * a.H);  // delta
     if (tables) {
@@ -365,9 +384,28 @@ int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStre
         bytes += table_bytes(a.plan) + table_bytes(at.plan);
     }
     bytes += partial_bytes(a.plan, a.H, HD) + partial_bytes(at.plan, a.H, 2 * HD);
+    if (a.dew && !a.vec) bytes += align256(sizeof(float) * (size_t)a.E * a.H);
+    *out = bytes;
+    return GT_OK;
+}
+
+// Scratch bytes of run_fwd without tables.
+int fwd_scratch_bytes(int64_t N, int64_t E, int H, int D, size_t* out) {
+    Plan p{};
+    size_plan(N, E, p);
+    int rc = check_plan(p);
+    if (rc) return rc;
+    *out = table_bytes(p) + partial_bytes(p, H, (int64_t)H * D);
+    return GT_OK;
+}
+
+int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStream_t stream) {
+    const int64_t HD = (int64_t)a.H * a.D;
+    size_t bytes = 0;
+    int brc = bwd_scratch_bytes(a, at, tables, t_tables, &bytes);
+    if (brc) return brc;
     const bool dew_part = a.dew && !a.vec;  // one-head waves: dw's per-head terms go through scratch
     const size_t part_bytes = dew_part ? align256(sizeof(float) * (size_t)a.E * a.H) : 0;
-    bytes += part_bytes;
     void* base = nullptr;
     int rc = get_scratch(stream, bytes, &base);
     if (rc) return rc;
@@ -568,6 +606,107 @@ int gt_spmm(const int64_t* indptr, const int32_t* indices, const float* alpha, c
     if (rc) return rc;
     hipError_t e = launch_spmm(a, stream);
     return e == hipSuccess ? GT_OK : hip_fail(e, "spmm launch");
+}
+
+int gt_sparse_mha_fwd_layout(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K,
+                             const void* V, void* out, float* lse, int64_t N, int64_t E, int32_t H, int32_t D,
+                             int32_t dtype, int32_t layout, const gt_logit_opts* opts, hipStream_t stream) {
+    if (layout == GT_LAYOUT_NHD) return fused_fwd(indptr, indices, Q, K, V, out, lse, N, E, H, D, dtype, opts, stream);
+    if (layout != GT_LAYOUT_NDH) return fail(GT_EINVAL, "unknown layout %d", layout);
+    int rc = check_common(N, E, H, D, dtype);
+    if (rc) return rc;
+    if (N == 0) return GT_OK;
+    if (!indptr || !Q || !K || !V || !out) return fail(GT_EINVAL, "NULL array with N > 0");
+    if (E > 0 && !indices) return fail(GT_EINVAL, "NULL indices with E > 0");
+    Args a{};
+    a.indptr = indptr;
+    a.indices = indices;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.out = out;
+    a.lse_out = lse;
+    a.N = N;
+    a.E = E;
+    a.H = H;
+    a.D = D;
+    a.dtype = dtype;
+    set_scales(a);
+    rc = set_options(a, opts);
+    if (rc) return rc;
+    if (!extended(a) && choose_layout_ndh(a, {Q, K, V, out})) return run_fwd(a, nullptr, stream);
+    // other shapes and the logit options: through [N][H][D] copies in scratch,
+    // after the plan's part of it
+    size_t pb = 0;
+    rc = fwd_scratch_bytes(N, E, H, D, &pb);
+    if (rc) return rc;
+    const size_t fb = align256((size_t)N * H * D * (dtype == GT_F32 ? 4 : 2));
+    void* base = nullptr;
+    rc = get_scratch(stream, align256(pb) + 4 * fb, &base);
+    if (rc) return rc;
+    char* t = (char*)base + align256(pb);
+    void *Qt = t, *Kt = t + fb, *Vt = t + 2 * fb, *Ot = t + 3 * fb;
+    hipError_t e = launch_transpose_rows(Q, Qt, N, D, H, dtype, stream);
+    if (e == hipSuccess) e = launch_transpose_rows(K, Kt, N, D, H, dtype, stream);
+    if (e == hipSuccess) e = launch_transpose_rows(V, Vt, N, D, H, dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "layout transpose");
+    a.Q = Qt;
+    a.K = Kt;
+    a.V = Vt;
+    a.out = Ot;
+    choose_layout(a, {Qt, Kt, Vt, Ot});
+    rc = run_fwd(a, nullptr, stream);
+    if (rc) return rc;
+    e = launch_transpose_rows(Ot, out, N, H, D, dtype, stream);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "layout transpose");
+}
+
+int gt_sparse_mha_bwd_layout(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr,
+                             const int32_t* t_indices, const int32_t* t_perm, const void* Q, const void* K,
+                             const void* V, const void* out, const void* dout, const float* lse, void* dQ, void* dK,
+                             void* dV, float* dbias, float* dweight, int64_t N, int64_t E, int32_t H, int32_t D,
+                             int32_t dtype, int32_t layout, const gt_logit_opts* opts, hipStream_t stream) {
+    if (layout == GT_LAYOUT_NHD)
+        return gt_sparse_mha_bwd_ex(indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, dQ, dK, dV,
+                                    dbias, dweight, N, E, H, D, dtype, opts, stream);
+    if (layout != GT_LAYOUT_NDH) return fail(GT_EINVAL, "unknown layout %d", layout);
+    int rc = check_common(N, E, H, D, dtype);
+    if (rc) return rc;
+    if (N == 0) return GT_OK;
+    if (!indptr || !t_indptr || !Q || !K || !V || !out || !dout || !lse || !dQ || !dK || !dV)
+        return fail(GT_EINVAL, "NULL array with N > 0");
+    if (E > 0 && (!indices || !t_indices)) return fail(GT_EINVAL, "NULL indices with E > 0");
+    // through [N][H][D] copies: five inputs and three gradients after the
+    // backward's own part of the scratch
+    const size_t fb = align256((size_t)N * H * D * (dtype == GT_F32 ? 4 : 2));
+    const void* src[5] = {Q, K, V, out, dout};
+    void* cp[8];
+    Args a, at;
+    // sized with placeholder (aligned) feature pointers: only the sizes matter here
+    rc = bwd_args(a, at, indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, dQ, dK, dV, dbias,
+                  dweight, N, N, E, H, D, dtype, opts);
+    if (rc) return rc;
+    a.vec = at.vec = 1;  // the copies are aligned; only the dew scratch depends on it, sized below for both cases
+    size_t bb = 0;
+    rc = bwd_scratch_bytes(a, at, nullptr, nullptr, &bb);
+    if (rc) return rc;
+    if (dweight) bb += align256(sizeof(float) * (size_t)E * H);
+    void* base = nullptr;
+    rc = get_scratch(stream, align256(bb) + 8 * fb, &base);
+    if (rc) return rc;
+    char* t = (char*)base + align256(bb);
+    for (int i = 0; i < 8; ++i) cp[i] = t + i * fb;
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 5 && e == hipSuccess; ++i) e = launch_transpose_rows(src[i], cp[i], N, D, H, dtype, stream);
+    if (e != hipSuccess) return hip_fail(e, "layout transpose");
+    rc = bwd_args(a, at, indptr, indices, t_indptr, t_indices, t_perm, cp[0], cp[1], cp[2], cp[3], cp[4], lse, cp[5],
+                  cp[6], cp[7], dbias, dweight, N, N, E, H, D, dtype, opts);
+    if (rc) return rc;
+    rc = run_bwd(a, at, nullptr, nullptr, stream);
+    if (rc) return rc;
+    void* dst[3] = {dQ, dK, dV};
+    for (int i = 0; i < 3 && e == hipSuccess; ++i) e = launch_transpose_rows(cp[5 + i], dst[i], N, H, D, dtype, stream);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "layout transpose");
 }
 
 // ------------------------------------------------------------------ graph plans

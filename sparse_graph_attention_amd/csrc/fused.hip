@@ -27,6 +27,8 @@
 // instance also gathers K/V that way when K+V exceed 1 GB (measured faster
 // there; slower when K/V partly fit the Infinity Cache, and for the 512-byte
 // bf16 rows).
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace gt {
@@ -362,6 +364,163 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
     }
 }
 
+// ------------------------------------------------------------ head-innermost layout
+//
+// Features [N][D][H] ("Graph Transformer in a Nutshell", SparseMHA.forward:
+// q, k, v reshaped to [N, dh, nh]).  A 16-byte vector of a row then holds VN
+// consecutive heads of one d, so a lane group covers all heads of an edge at
+// once: lane gl holds vector gl (d = gl / HV, heads (gl % HV) * VN .. +VN-1,
+// HV = H / VN a power of two, R = D * HV <= 64 vectors, G = pow2ceil(R)).  A
+// head's dot product sums the lane products over the lanes with the same
+// gl % HV (xor offsets HV .. G/2); every lane keeps VN running softmax states,
+// one per head it holds.  For the tutorial's shape (H 8, D 10, fp32) a row is
+// 20 vectors, a group 32 lanes and a wave takes two edges at a time, where the
+// [N][H][D] layout needs one wave per head with 10-element heads.
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+
+    const int G = a.G, HV = a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const bool act = gl < a.R;
+    const int hg = gl & (HV - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    float q[VN];
+    VT::unpack(act ? ld16((const char*)a.Q + row * rowbytes + gl * 16) : U4{0, 0, 0, 0}, q);
+    float m[VN], l[VN], acc[VN];
+#pragma unroll
+    for (int k = 0; k < VN; ++k) {
+        m[k] = -INFINITY;
+        l[k] = 0.0f;
+        acc[k] = 0.0f;
+    }
+    const char* Kb = (const char*)a.K;
+    const char* Vb = (const char*)a.V;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        U4 kr[U], vr[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) kr[j] = (ok[j] && act) ? ld16(Kb + (int64_t)u[j] * rowbytes + gl * 16) : U4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < U; ++j) vr[j] = (ok[j] && act) ? ld16(Vb + (int64_t)u[j] * rowbytes + gl * 16) : U4{0, 0, 0, 0};
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        float s[U][VN];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float kf[VN];
+            VT::unpack(kr[j], kf);
+#pragma unroll
+            for (int k = 0; k < VN; ++k) s[j][k] = q[k] * kf[k];
+            for (int off = HV; off < G; off <<= 1)
+#pragma unroll
+                for (int k = 0; k < VN; ++k) s[j][k] += __shfl_xor(s[j][k], off, kWave);
+#pragma unroll
+            for (int k = 0; k < VN; ++k) s[j][k] = ok[j] ? s[j][k] * a.qscale : -INFINITY;
+        }
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+            float mb = s[0][k];
+#pragma unroll
+            for (int j = 1; j < U; ++j) mb = fmaxf(mb, s[j][k]);
+            const float mn = fmaxf(m[k], mb);
+            const float sc = rescale(m[k], mn);
+            l[k] *= sc;
+            acc[k] *= sc;
+            m[k] = mn;
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float vf[VN];
+            VT::unpack(vr[j], vf);
+#pragma unroll
+            for (int k = 0; k < VN; ++k) {
+                const float p = ok[j] ? exp2_(s[j][k] - m[k]) : 0.0f;
+                l[k] += p;
+                acc[k] = __builtin_fmaf(p, vf[k], acc[k]);
+            }
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+            const float mo = __shfl_xor(m[k], off, kWave);
+            const float lo = __shfl_xor(l[k], off, kWave);
+            const float ao = __shfl_xor(acc[k], off, kWave);
+            const float mn = fmaxf(m[k], mo);
+            const float sa = rescale(m[k], mn), sb = rescale(mo, mn);
+            l[k] = l[k] * sa + lo * sb;
+            acc[k] = acc[k] * sa + ao * sb;
+            m[k] = mn;
+        }
+    }
+    if (grp != 0 || !act) return;
+    const bool first_d = gl < HV;  // the lanes of d = 0 carry each head's (m, l) once
+    if (it.slot < 0) {
+        float o[VN];
+#pragma unroll
+        for (int k = 0; k < VN; ++k) o[k] = l[k] > 0.0f ? acc[k] / l[k] : 0.0f;
+        st16_nt((char*)a.out + row * rowbytes + gl * 16, VT::pack(o));
+        if (a.lse_out && first_d)
+#pragma unroll
+            for (int k = 0; k < VN; ++k) a.lse_out[row * a.H + hg * VN + k] = lse_of(m[k], l[k]);
+    } else {
+        const int64_t HD = (int64_t)a.H * a.D;
+        if (first_d)
+#pragma unroll
+            for (int k = 0; k < VN; ++k) {
+                a.plan.pm[it.slot * a.H + hg * VN + k] = m[k];
+                a.plan.pl[it.slot * a.H + hg * VN + k] = l[k];
+            }
+        float* pa = a.plan.pacc + it.slot * HD + (int64_t)gl * VN;
+#pragma unroll
+        for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[k]));
+    }
+}
+
+// Per node, src [A][B] -> dst [B][A]; grid-stride over the elements, reads
+// coalesced.
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_rows_kernel(const T* __restrict__ src, T* __restrict__ dst, int64_t n,
+                                                              int A, int B) {
+    const int64_t AB = (int64_t)A * B;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t node = i / AB;
+        const int r = (int)(i - node * AB);
+        const int x = r / B, y = r - x * B;
+        dst[node * AB + (int64_t)y * A + x] = src[i];
+    }
+}
+
+hipError_t launch_transpose_rows(const void* src, void* dst, int64_t N, int A, int B, int dtype, hipStream_t s) {
+    const int64_t n = N * A * B;
+    if (n == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, (int64_t)1 << 20);
+    if (dtype == kF32)
+        transpose_rows_kernel<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, n, A, B);
+    else
+        transpose_rows_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, n, A, B);
+    return hipGetLastError();
+}
+
 // ------------------------------------------------------------ merge of split rows
 //
 // One wave per heavy row; for each head the row's chunks are combined as
@@ -393,7 +552,9 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
     const int64_t HD = (int64_t)H * D;
     const float* pm = a.plan.pm + hr.base * H + h;
     const float* pl = a.plan.pl + hr.base * H + h;
-    const float* pa = a.plan.pacc + hr.base * HD + (int64_t)h * D;
+    // element (h, d) of a row: h*D + d, or d*H + h in the head-innermost layout
+    const int64_t hoff = a.ndh ? h : (int64_t)h * D, dstride = a.ndh ? H : 1;
+    const float* pa = a.plan.pacc + hr.base * HD + hoff;
     float M = -INFINITY;
     for (int i = lane; i < nch; i += kWave) M = fmaxf(M, pm[(int64_t)i * H]);
     M = wave_max(M);
@@ -415,7 +576,7 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 #pragma unroll
                 for (int t = 0; t < T; ++t) {
                     const int d = lane + t * kWave;
-                    v[k][t] = (k0 + k < nb && d < D) ? pa[(int64_t)(ib + k0 + k) * HD + d] : 0.0f;
+                    v[k][t] = (k0 + k < nb && d < D) ? pa[(int64_t)(ib + k0 + k) * HD + d * dstride] : 0.0f;
                 }
 #pragma unroll
             for (int k = 0; k < UN; ++k) {
@@ -428,7 +589,7 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const int d = lane + t * kWave;
-        if (d < D) VT::store_scalar(a.out, (int64_t)hr.row * HD + (int64_t)h * D + d, A[t] / L);
+        if (d < D) VT::store_scalar(a.out, (int64_t)hr.row * HD + hoff + d * dstride, A[t] / L);
     }
 }
 
@@ -437,6 +598,11 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 template <int DT, bool XL>
 static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
+    if (a0.vec == 2) {  // head-innermost layout (plain logits only)
+        return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            fused_ndh_kernel<DT, 4><<<dim3(gx), block, 0, s>>>(a);
+        });
+    }
     if (a0.vec) {
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);

@@ -52,10 +52,14 @@ struct Args {
     int R;         // vector layout: 16-byte vectors per node row
     int NC;        // vector layout: vectors per lane
     int KD;        // scalar layout: elements per lane
+    int ndh;       // features are [N][D][H] (head innermost); vec = 2 selects fused_ndh_kernel
     // grid
     int64_t items;      // max_chunks + N
     int64_t item_base;  // first item of the current launch slice
 };
+
+// Per node, src [A][B] -> dst [B][A] (elementwise; bf16 moved as 16-bit words).
+hipError_t launch_transpose_rows(const void* src, void* dst, int64_t N, int A, int B, int dtype, hipStream_t s);
 
 // Whether a launch needs the extended-logit kernels.
 inline bool extended(const Args& a) { return a.bias || a.ew || a.drop_thresh || a.dbias || a.dew; }

@@ -139,3 +139,14 @@ def test_logit_options_reject():
     assert L.gt_sparse_mha_bwd_ex(p, p, p, p, None, p, p, p, p, p, p, p, p, p, None, None, 4, 4, 8, 64, 0,
                                   ctypes.byref(o), S) == gt.GT_EINVAL
     assert "t_perm" in gt.gt_last_error()
+
+
+def test_layout_reject():
+    L = gt.lib()
+    p = ctypes.c_void_p(1)
+    assert L.gt_sparse_mha_fwd_layout(p, p, p, p, p, p, None, 4, 4, 8, 64, 0, 2, None, S) == gt.GT_EINVAL
+    assert "layout" in gt.gt_last_error()
+    assert L.gt_sparse_mha_fwd_layout(p, p, p, p, p, p, None, -1, 4, 8, 64, 0, 1, None, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_bwd_layout(p, p, p, p, None, p, p, p, p, p, p, p, p, p, None, None, 4, 4, 8, 64, 0, 5,
+                                      None, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_fwd_layout(p, p, p, p, p, p, None, 0, 0, 8, 64, 0, 1, None, S) == gt.GT_OK
