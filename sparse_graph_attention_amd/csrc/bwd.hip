@@ -20,14 +20,25 @@
 //     or chunk: gathers q_v and dO_v per out-edge, recomputes alpha and ds
 //     from lse_v and delta_v, accumulates dK and dV.
 // Chunks of split rows leave partial sums that a merge adds in chunk order.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace gt {
 
 // ------------------------------------------------------------ dQ, vector layout
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool XL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, int XL>
 __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     using VT = Vec<DT>;
+    // hot instances: the heads per edge are known, so the batched dropout
+    // words always fit and the per-lane fallback compiles away
+    constexpr int kHc = (G_ && LPH_ && FULL) ? NC * G_ / LPH_ : 0;
+    constexpr bool kBatched =
+        kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * (kHc % 4 == 0 ? kHc / 4 : (kHc + 3) / 4 + 1) <= 64 * kDropRounds;
+    constexpr bool kSlots = kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * kHc <= 64 * kSlotRounds;
+    // rounds of 64 values for a batch's bias and weights (exact for the hot instances)
+    constexpr int kBR = kSlots ? ((kWave / G_) * U * kHc + 63) / 64 : kSlotRounds;
+    constexpr int kWR = kSlots ? ((kWave / G_) * U + 63) / 64 : kSlotRounds;
     constexpr int VN = VT::n;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -88,12 +99,21 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
         }
         auto ej = [&](int j) -> int64_t { return ok[j] ? eb + grp + (int64_t)j * epw : e0; };
         float xw[U], xb[U][NC];
+        SlotBatch<kBR> bb;
+        SlotBatch<kWR> wb;
+        bool sb = false;
         if constexpr (XL) {  // ahead of the gathers: waiting for them never waits for a gather
+            sb = kSlots || slot_batched(epw * U, a.H);
+            if (sb) {
+                if (a.bias) slot_batch_load(bb, a.bias, eb, e1, epw * U, a.H, lane);
+                if (a.ew) slot_batch_load(wb, a.ew, eb, e1, epw * U, 1, lane);
+            } else {
 #pragma unroll
-            for (int j = 0; j < U; ++j) {
-                xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
+                for (int j = 0; j < U; ++j) {
+                    xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej(j) * a.H + head[c]] * kLog2e : 0.0f;
+                    for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej(j) * a.H + head[c]] * kLog2e : 0.0f;
+                }
             }
         }
         U4 kr[U][NC], vr[U][NC];
@@ -112,7 +132,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
         DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
-            bdrop = a.drop_thresh && drop_batched(a.H, -1, epw * U);
+            bdrop = XL == 2 && (kBatched || drop_batched(a.H, -1, epw * U));
             if (bdrop)
                 drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane,
                                 [&](int k) { return eb + k; });
@@ -135,19 +155,22 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
                 dd = LPH_ ? seg_sum_c<LPH_>(dd) : seg_sum(dd, lph);
                 if constexpr (XL) {
                     const float raw = sd;
-                    sd = __builtin_fmaf(sd, xw[j], xb[j][c]);
+                    const int k = grp + j * epw;
+                    const float w = sb ? (a.ew ? slot_batch_get(wb, k) : 1.0f) : xw[j];
+                    const float b = sb ? (a.bias ? slot_batch_get(bb, k * a.H + head[c]) * kLog2e : 0.0f) : xb[j][c];
+                    sd = __builtin_fmaf(sd, w, b);
                     const float p = ok[j] ? exp2_(sd - ls[c]) : 0.0f;
                     float keep = 1.0f;
-                    if (bdrop)
+                    if (XL == 2 && (kBatched || bdrop))
                         keep = drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ej(j), head[c]);
-                    else if (a.drop_thresh)
+                    else if (XL == 2 && !kBatched)
                         keep = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + head[c]) >= a.drop_thresh
                                    ? a.drop_scale : 0.0f;
                     const float ds = p * (keep * dd - dl[c]);
                     const bool lead = ok[j] && act[c] && (gl & (lph - 1)) == 0;
                     if (a.dbias && lead) a.dbias[ej(j) * a.H + head[c]] = ds;
                     if (lead) tw = __builtin_fmaf(ds, raw * kLn2, tw);
-                    const float dsw = ds * xw[j];
+                    const float dsw = ds * w;
 #pragma unroll
                     for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(dsw, kf[k], acc[c][k]);
                 } else {
@@ -174,7 +197,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     for (int c = 0; c < NC; ++c) {
         if (!act[c]) continue;
         const int vi = c * G + gl;
-        if ((vi & (lph - 1)) == 0) a.delta[row * a.H + vi / lph] = dl[c];
+        if ((vi & (lph - 1)) == 0) a.stats[row * a.H + vi / lph] = make_float2(ls[c], dl[c]);
         if (it.slot < 0) {
             float o[VN];
 #pragma unroll
@@ -191,9 +214,18 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
 // ------------------------------------------------------------ dK, dV, vector layout
 // a.indptr / a.indices are the source-sorted graph: item rows are sources u,
 // "edges" are their out-edges with the destination v in a.indices.
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool XL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, int XL>
 __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     using VT = Vec<DT>;
+    // hot instances: the heads per edge are known, so the batched dropout
+    // words always fit and the per-lane fallback compiles away
+    constexpr int kHc = (G_ && LPH_ && FULL) ? NC * G_ / LPH_ : 0;
+    constexpr bool kBatched =
+        kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * (kHc % 4 == 0 ? kHc / 4 : (kHc + 3) / 4 + 1) <= 64 * kDropRounds;
+    constexpr bool kSlots = kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * kHc <= 64 * kSlotRounds;
+    // rounds of 64 values for a batch's bias and weights (exact for the hot instances)
+    constexpr int kBR = kSlots ? ((kWave / G_) * U * kHc + 63) / 64 : kSlotRounds;
+    constexpr int kWR = kSlots ? ((kWave / G_) * U + 63) / 64 : kSlotRounds;
     constexpr int VN = VT::n;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -213,7 +245,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     int32_t un[U], pn[U];  // destinations and (extended) their CSR positions
     if (e1 > e0) {
         load_ids<U>(idx, e0, grp, epw, e1, un);
-        if constexpr (XL) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
+        if constexpr (XL == 2) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
     }
 
     float kk[NC][VN], vv[NC][VN];
@@ -233,6 +265,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     for (int c = 0; c < NC; ++c)
 #pragma unroll
         for (int k = 0; k < VN; ++k) dk[c][k] = dv[c][k] = 0.0f;
+    // per-head values of an edge are loaded by lane h of the group for head h
+    // (H <= G in this layout) and handed to the lanes of head h by a shuffle
+    const int hsrc = gl < a.H ? gl : 0;
+    const int gbase = grp * G;
 
     const char* Qb = (const char*)a.Q;
     const char* Gb = (const char*)a.dO;
@@ -242,39 +278,51 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             u[j] = un[j];
-            if constexpr (XL) ep[j] = pn[j];
+            if constexpr (XL == 2) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
+        // per-edge inputs in out-edge order (copies made for this pass), so a
+        // batch's are contiguous like the destination pass's
         float xw[U], xb[U][NC];
+        SlotBatch<kBR> bb;
+        SlotBatch<kWR> wb;
+        bool sb = false;
         if constexpr (XL) {
+            sb = kSlots || slot_batched(epw * U, a.H);
+            if (sb) {
+                if (a.bias_t) slot_batch_load(bb, a.bias_t, eb, e1, epw * U, a.H, lane);
+                if (a.ew_t) slot_batch_load(wb, a.ew_t, eb, e1, epw * U, 1, lane);
+            } else {
 #pragma unroll
-            for (int j = 0; j < U; ++j) {
-                xw[j] = a.ew ? a.ew[ep[j]] : 1.0f;
+                for (int j = 0; j < U; ++j) {
+                    const int64_t jp = ok[j] ? eb + grp + (int64_t)j * epw : e0;
+                    xw[j] = a.ew_t ? a.ew_t[jp] : 1.0f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[(int64_t)ep[j] * a.H + head[c]] * kLog2e : 0.0f;
+                    for (int c = 0; c < NC; ++c) xb[j][c] = a.bias_t ? a.bias_t[jp * a.H + head[c]] * kLog2e : 0.0f;
+                }
             }
         }
         U4 qr[U][NC], gr[U][NC];
-        float ls[U][NC], dl[U][NC];
+        float2 st[U];  // the destination's (lse, delta) of head hsrc: one 8-byte load per edge
 #pragma unroll
-        for (int j = 0; j < U; ++j)
+        for (int j = 0; j < U; ++j) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const bool go = ok[j] && act[c];
                 qr[j][c] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
                 gr[j][c] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
-                ls[j][c] = go ? a.lse_in[(int64_t)u[j] * a.H + head[c]] : 0.0f;
-                dl[j][c] = go ? a.delta[(int64_t)u[j] * a.H + head[c]] : 0.0f;
             }
+            st[j] = ok[j] ? a.stats[(int64_t)u[j] * a.H + hsrc] : make_float2(0.0f, 0.0f);
+        }
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) {
             load_ids<U>(idx, nb, grp, epw, e1, un);
-            if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+            if constexpr (XL == 2) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
         }
         DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
-            bdrop = a.drop_thresh && drop_batched(a.H, -1, epw * U);
+            bdrop = XL == 2 && (kBatched || drop_batched(a.H, -1, epw * U));
             if (bdrop)  // slot k's CSR position sits in ep[k / epw] of group k % epw
                 drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane, [&](int k) {
                     int64_t r = 0;
@@ -301,25 +349,30 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
                 }
                 sd = (LPH_ ? seg_sum_c<LPH_>(sd) : seg_sum(sd, lph)) * a.qscale;
                 dd = LPH_ ? seg_sum_c<LPH_>(dd) : seg_sum(dd, lph);
+                const float lsj = __shfl(st[j].x, gbase + head[c], kWave);
+                const float dlj = __shfl(st[j].y, gbase + head[c], kWave);
                 if constexpr (XL) {
-                    sd = __builtin_fmaf(sd, xw[j], xb[j][c]);
-                    const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
+                    const int k = grp + j * epw;
+                    const float w = sb ? (a.ew_t ? slot_batch_get(wb, k) : 1.0f) : xw[j];
+                    const float b = sb ? (a.bias_t ? slot_batch_get(bb, k * a.H + head[c]) * kLog2e : 0.0f) : xb[j][c];
+                    sd = __builtin_fmaf(sd, w, b);
+                    const float p = ok[j] ? exp2_(sd - lsj) : 0.0f;
                     float keep = 1.0f;
-                    if (bdrop)
+                    if (XL == 2 && (kBatched || bdrop))
                         keep = drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ep[j], head[c]);
-                    else if (a.drop_thresh)
+                    else if (XL == 2 && !kBatched)
                         keep = philox_hi32(a.drop_seed, (uint64_t)ep[j] * a.H + head[c]) >= a.drop_thresh
                                    ? a.drop_scale : 0.0f;
                     const float pk = p * keep;
-                    const float dsw = p * (keep * dd - dl[j][c]) * xw[j];
+                    const float dsw = p * (keep * dd - dlj) * w;
 #pragma unroll
                     for (int k = 0; k < VN; ++k) {
                         dv[c][k] = __builtin_fmaf(pk, gf[k], dv[c][k]);
                         dk[c][k] = __builtin_fmaf(dsw, qf[k], dk[c][k]);
                     }
                 } else {
-                    const float p = ok[j] ? exp2_(sd - ls[j][c] * kLog2e) : 0.0f;
-                    const float ds = p * (dd - dl[j][c]);
+                    const float p = ok[j] ? exp2_(sd - lsj) : 0.0f;
+                    const float ds = p * (dd - dlj);
 #pragma unroll
                     for (int k = 0; k < VN; ++k) {
                         dv[c][k] = __builtin_fmaf(p, gf[k], dv[c][k]);
@@ -361,9 +414,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 // ------------------------------------------------------------ scalar layout
 // One wave per (item, head h = blockIdx.y); groups of G = pow2ceil(D) lanes,
 // lane j holding elements j + k*G, k < KD.
-template <int DT, int KD, int U, bool XL>
+template <int DT, int KD, int U, int XL>
 __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
     using VT = Vec<DT>;
+    constexpr bool kBatched = false;  // the batch size depends on D and H: checked at run time
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.y;
@@ -427,7 +481,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
         DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
-            bdrop = a.drop_thresh && drop_batched(a.H, h, epw * U);
+            bdrop = XL == 2 && (kBatched || drop_batched(a.H, h, epw * U));
             if (bdrop)
                 drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, h, epw * U, lane, [&](int k) { return eb + k; });
         }
@@ -446,9 +500,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
                 sd = __builtin_fmaf(sd, xw[j], xb[j]);
                 const float p = ok[j] ? exp2_(sd - ls) : 0.0f;
                 float keep = 1.0f;
-                if (bdrop)
+                if (XL == 2 && (kBatched || bdrop))
                     keep = drop_mult(db, a.drop_scale, a.H, h, grp + j * epw, ej(j), h);
-                else if (a.drop_thresh)
+                else if (XL == 2 && !kBatched)
                     keep = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
                 const float ds = p * (keep * dd - dl);
                 // one wave per head: the per-head terms of dw go to scratch and
@@ -472,7 +526,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
 #pragma unroll
         for (int k = 0; k < KD; ++k) acc[k] += __shfl_xor(acc[k], off, kWave);
     if (grp != 0) return;
-    if (gl == 0) a.delta[row * a.H + h] = dl;
+    if (gl == 0) a.stats[row * a.H + h] = make_float2(ls, dl);
 #pragma unroll
     for (int k = 0; k < KD; ++k) {
         if (!act[k]) continue;
@@ -483,9 +537,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_scalar_kernel(const Args a) {
     }
 }
 
-template <int DT, int KD, int U, bool XL>
+template <int DT, int KD, int U, int XL>
 __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
     using VT = Vec<DT>;
+    constexpr bool kBatched = false;  // the batch size depends on D and H: checked at run time
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.y;
@@ -503,7 +558,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
     int32_t un[U], pn[U];
     if (e1 > e0) {
         load_ids<U>(idx, e0, grp, epw, e1, un);
-        if constexpr (XL) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
+        if constexpr (XL == 2) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
     }
     float kk[KD], vv[KD], dk[KD], dv[KD];
     bool act[KD];
@@ -521,15 +576,16 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             u[j] = un[j];
-            if constexpr (XL) ep[j] = pn[j];
+            if constexpr (XL == 2) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
         float xw[U], xb[U];
         if constexpr (XL) {
 #pragma unroll
             for (int j = 0; j < U; ++j) {
-                xw[j] = a.ew ? a.ew[ep[j]] : 1.0f;
-                xb[j] = a.bias ? a.bias[(int64_t)ep[j] * a.H + h] * kLog2e : 0.0f;
+                const int64_t jp = ok[j] ? eb + grp + (int64_t)j * epw : e0;
+                xw[j] = a.ew_t ? a.ew_t[jp] : 1.0f;
+                xb[j] = a.bias_t ? a.bias_t[jp * a.H + h] * kLog2e : 0.0f;
             }
         }
         float qv[U][KD], gv[U][KD], ls[U], dl[U];
@@ -541,18 +597,19 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
                 qv[j][k] = go ? VT::scalar(a.Q, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
                 gv[j][k] = go ? VT::scalar(a.dO, (int64_t)u[j] * HD + hoff + gl + k * G) : 0.0f;
             }
-            ls[j] = ok[j] ? a.lse_in[(int64_t)u[j] * a.H + h] : 0.0f;
-            dl[j] = ok[j] ? a.delta[(int64_t)u[j] * a.H + h] : 0.0f;
+            const float2 t = ok[j] ? a.stats[(int64_t)u[j] * a.H + h] : make_float2(0.0f, 0.0f);
+            ls[j] = t.x;
+            dl[j] = t.y;
         }
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) {
             load_ids<U>(idx, nb, grp, epw, e1, un);
-            if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+            if constexpr (XL == 2) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
         }
         DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
-            bdrop = a.drop_thresh && drop_batched(a.H, h, epw * U);
+            bdrop = XL == 2 && (kBatched || drop_batched(a.H, h, epw * U));
             if (bdrop)
                 drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, h, epw * U, lane, [&](int k) {
                     int64_t r = 0;
@@ -576,11 +633,11 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
             dd = seg_sum(dd, G);
             if constexpr (XL) {
                 sd = __builtin_fmaf(sd, xw[j], xb[j]);
-                const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
+                const float p = ok[j] ? exp2_(sd - ls[j]) : 0.0f;
                 float keep = 1.0f;
-                if (bdrop)
+                if (XL == 2 && (kBatched || bdrop))
                     keep = drop_mult(db, a.drop_scale, a.H, h, grp + j * epw, ep[j], h);
-                else if (a.drop_thresh)
+                else if (XL == 2 && !kBatched)
                     keep = philox_hi32(a.drop_seed, (uint64_t)ep[j] * a.H + h) >= a.drop_thresh ? a.drop_scale : 0.0f;
                 const float pk = p * keep;
                 const float dsw = p * (keep * dd - dl[j]) * xw[j];
@@ -590,7 +647,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
                     dk[k] = __builtin_fmaf(dsw, qv[j][k], dk[k]);
                 }
             } else {
-                const float p = ok[j] ? exp2_(sd - ls[j] * kLog2e) : 0.0f;
+                const float p = ok[j] ? exp2_(sd - ls[j]) : 0.0f;
                 const float ds = p * (dd - dl[j]);
 #pragma unroll
                 for (int k = 0; k < KD; ++k) {
@@ -670,6 +727,22 @@ __global__ __launch_bounds__(kBlock) void bwd_sum_merge_kernel(const Args a, int
     }
 }
 
+// Per-edge inputs in the source pass's order: dst[j][h] = src[perm[j]][h].
+__global__ __launch_bounds__(256) void permute_edges_kernel(const int32_t* __restrict__ perm, int64_t E, int H,
+                                                            const float* __restrict__ src, float* __restrict__ dst) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < E * H; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t j = i / H;
+        dst[i] = src[(int64_t)perm[j] * H + (i - j * H)];
+    }
+}
+
+hipError_t launch_permute_edges(const int32_t* perm, int64_t E, int H, const float* src, float* dst, hipStream_t s) {
+    if (E == 0) return hipSuccess;
+    const unsigned grid = (unsigned)std::min<int64_t>((E * H + 255) / 256, (int64_t)1 << 20);
+    permute_edges_kernel<<<grid, 256, 0, s>>>(perm, E, H, src, dst);
+    return hipGetLastError();
+}
+
 // dw[e] = sum over heads, in head order, of the per-head terms the scalar
 // layout's one-head waves left in part[e][h].
 __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict__ part, int64_t E, int H,
@@ -683,7 +756,7 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
 
 // ------------------------------------------------------------ launchers
 
-template <int DT, bool XL>
+template <int DT, int XL>
 static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
@@ -692,9 +765,9 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                bwd_dq_vec_kernel<DT, 2, XL ? 2 : 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dq_vec_kernel<DT, 1, XL ? 2 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 1, XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
@@ -726,7 +799,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     });
 }
 
-template <int DT, bool XL>
+template <int DT, int XL>
 static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
@@ -737,7 +810,7 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dkv_vec_kernel<DT, 2, XL ? 2 : 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dkv_vec_kernel<DT, 1, XL ? 2 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
@@ -765,16 +838,21 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     });
 }
 
+// 0: plain logits; 1: bias, edge weights, dbias or dweight; 2: with dropout
+static int xl_level(const Args& a) { return extended(a) ? (a.drop_thresh ? 2 : 1) : 0; }
+
 hipError_t launch_bwd_dq(const Args& a, hipStream_t s) {
-    const bool xl = extended(a);
-    return a.dtype == kF32 ? (xl ? launch_dq_dt<kF32, true>(a, s) : launch_dq_dt<kF32, false>(a, s))
-                           : (xl ? launch_dq_dt<kBF16, true>(a, s) : launch_dq_dt<kBF16, false>(a, s));
+    const int xl = xl_level(a);
+    if (a.dtype == kF32)
+        return xl == 0 ? launch_dq_dt<kF32, 0>(a, s) : xl == 1 ? launch_dq_dt<kF32, 1>(a, s) : launch_dq_dt<kF32, 2>(a, s);
+    return xl == 0 ? launch_dq_dt<kBF16, 0>(a, s) : xl == 1 ? launch_dq_dt<kBF16, 1>(a, s) : launch_dq_dt<kBF16, 2>(a, s);
 }
 
 hipError_t launch_bwd_dkv(const Args& a, hipStream_t s) {
-    const bool xl = extended(a);
-    return a.dtype == kF32 ? (xl ? launch_dkv_dt<kF32, true>(a, s) : launch_dkv_dt<kF32, false>(a, s))
-                           : (xl ? launch_dkv_dt<kBF16, true>(a, s) : launch_dkv_dt<kBF16, false>(a, s));
+    const int xl = xl_level(a);
+    if (a.dtype == kF32)
+        return xl == 0 ? launch_dkv_dt<kF32, 0>(a, s) : xl == 1 ? launch_dkv_dt<kF32, 1>(a, s) : launch_dkv_dt<kF32, 2>(a, s);
+    return xl == 0 ? launch_dkv_dt<kBF16, 0>(a, s) : xl == 1 ? launch_dkv_dt<kBF16, 1>(a, s) : launch_dkv_dt<kBF16, 2>(a, s);
 }
 
 }  // namespace gt

@@ -284,6 +284,54 @@ __device__ __forceinline__ float drop_mult(const DropBatch& d, float scale, int 
     return (bits >> (i & 3)) & 1u ? scale : 0.0f;
 }
 
+// ---------------------------------------------------------------- per-edge inputs of a batch
+//
+// A batch's edge slots k = group + j * edges-per-wave are the consecutive
+// edges eb + k of the pass's edge order, so per-edge inputs (bias [E][per],
+// weights [E]) of a batch are one contiguous run: the wave loads it 64 values
+// at a time (one coalesced load per 64 values instead of one per edge and
+// lane vector) and hands each value to the lanes that need it by a shuffle.
+constexpr int kSlotRounds = 4;  // shapes known only at run time
+
+template <int R>
+struct SlotBatch {
+    float v[R];
+    int rounds;
+};
+
+__device__ __forceinline__ bool slot_batched(int nslots, int per) { return nslots * per <= 64 * kSlotRounds; }
+
+// Values src[(eb + k) * per + h] for the batch's nslots slots; those past the
+// item's last edge e1 read as 0.  R bounds the rounds of 64 values.
+template <int R>
+__device__ __forceinline__ void slot_batch_load(SlotBatch<R>& b, const float* __restrict__ src, int64_t eb, int64_t e1,
+                                                int nslots, int per, int lane) {
+    b.rounds = (nslots * per + 63) >> 6;
+    const int64_t lim = (e1 - eb) * per;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        b.v[r] = 0.0f;
+        if (r < b.rounds) {
+            const int i = r * 64 + lane;
+            if (i < lim) b.v[r] = src[eb * per + i];
+        }
+    }
+}
+
+// Value i = k * per + h of the batch; every lane must call it.
+template <int R>
+__device__ __forceinline__ float slot_batch_get(const SlotBatch<R>& b, int i) {
+    if constexpr (R == 1) return __shfl(b.v[0], i & 63, 64);
+    float x = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+        if (r < b.rounds) {
+            const float t = __shfl(b.v[r], i & 63, 64);
+            if ((i >> 6) == r) x = t;
+        }
+    return x;
+}
+
 // ---------------------------------------------------------------- 16-byte vectors
 
 struct alignas(16) U4 {

@@ -38,9 +38,18 @@ namespace gt {
 // G_ and LPH_ are compile-time lane-group and lanes-per-head sizes when
 // nonzero, else read from the arguments.  FULL: the row is exactly NC*G
 // vectors (no idle lanes).  U edges per group are in flight.
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool NTL, bool XL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool NTL, int XL>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     using VT = Vec<DT>;
+    // hot instances: the heads per edge are known, so the batched dropout
+    // words always fit and the per-lane fallback compiles away
+    constexpr int kHc = (G_ && LPH_ && FULL) ? NC * G_ / LPH_ : 0;
+    constexpr bool kBatched =
+        kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * (kHc % 4 == 0 ? kHc / 4 : (kHc + 3) / 4 + 1) <= 64 * kDropRounds;
+    constexpr bool kSlots = kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * kHc <= 64 * kSlotRounds;
+    // rounds of 64 values for a batch's bias and weights (exact for the hot instances)
+    constexpr int kBR = kSlots ? ((kWave / G_) * U * kHc + 63) / 64 : kSlotRounds;
+    constexpr int kWR = kSlots ? ((kWave / G_) * U + 63) / 64 : kSlotRounds;
     constexpr int VN = VT::n;
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -98,12 +107,21 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
         // so that waiting for them never waits for a gather
         auto ej = [&](int j) -> int64_t { return ok[j] ? eb + grp + (int64_t)j * epw : e0; };
         float xw[U], xb[U][NC];
+        SlotBatch<kBR> bb;
+        SlotBatch<kWR> wb;
+        bool sb = false;
         if constexpr (XL) {
+            sb = kSlots || slot_batched(epw * U, a.H);
+            if (sb) {
+                if (a.bias) slot_batch_load(bb, a.bias, eb, e1, epw * U, a.H, lane);
+                if (a.ew) slot_batch_load(wb, a.ew, eb, e1, epw * U, 1, lane);
+            } else {
 #pragma unroll
-            for (int j = 0; j < U; ++j) {
-                xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
+                for (int j = 0; j < U; ++j) {
+                    xw[j] = a.ew ? a.ew[ej(j)] : 1.0f;
 #pragma unroll
-                for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej(j) * a.H + head[c]] * kLog2e : 0.0f;
+                    for (int c = 0; c < NC; ++c) xb[j][c] = a.bias ? a.bias[ej(j) * a.H + head[c]] * kLog2e : 0.0f;
+                }
             }
         }
         U4 kr[U][NC], vr[U][NC];
@@ -122,7 +140,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
         DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
-            bdrop = a.drop_thresh && drop_batched(a.H, -1, epw * U);
+            bdrop = XL == 2 && (kBatched || drop_batched(a.H, -1, epw * U));
             if (bdrop)
                 drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane,
                                 [&](int k) { return eb + k; });
@@ -139,7 +157,12 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 #pragma unroll
                 for (int k = 0; k < VN; ++k) d = __builtin_fmaf(q[c][k], kf[k], d);
                 d = (LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph)) * a.qscale;
-                if constexpr (XL) d = __builtin_fmaf(d, xw[j], xb[j][c]);
+                if constexpr (XL) {
+                    const int k = grp + j * epw;
+                    const float w = sb ? (a.ew ? slot_batch_get(wb, k) : 1.0f) : xw[j];
+                    const float b = sb ? (a.bias ? slot_batch_get(bb, k * a.H + head[c]) * kLog2e : 0.0f) : xb[j][c];
+                    d = __builtin_fmaf(d, w, b);
+                }
                 s[j][c] = ok[j] ? d : -INFINITY;
             }
 #pragma unroll
@@ -159,9 +182,9 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 l[c] += p;
                 float pv = p;  // dropout zeroes the weight, not its share of the normaliser
                 if constexpr (XL) {
-                    if (bdrop)
+                    if (XL == 2 && (kBatched || bdrop))
                         pv = p * drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ej(j), head[c]);
-                    else if (a.drop_thresh)
+                    else if (XL == 2 && !kBatched)
                         pv = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + head[c]) >= a.drop_thresh
                                  ? p * a.drop_scale : 0.0f;
                 }
@@ -228,9 +251,10 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 //
 // One wave per (item, head); a group of G = pow2ceil(D) lanes (<= 64) covers
 // one edge's head, lane j holding elements j + k*G, k < KD.
-template <int DT, int KD, int U, bool XL>
+template <int DT, int KD, int U, int XL>
 __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
     using VT = Vec<DT>;
+    constexpr bool kBatched = false;  // the batch size depends on D and H: checked at run time
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int h = blockIdx.y;
@@ -294,7 +318,7 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
         DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
-            bdrop = a.drop_thresh && drop_batched(a.H, h, epw * U);
+            bdrop = XL == 2 && (kBatched || drop_batched(a.H, h, epw * U));
             if (bdrop)
                 drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, h, epw * U, lane, [&](int k) { return eb + k; });
         }
@@ -322,9 +346,9 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
             l += p;
             float pv = p;
             if constexpr (XL) {
-                if (bdrop)
+                if (XL == 2 && (kBatched || bdrop))
                     pv = p * drop_mult(db, a.drop_scale, a.H, h, grp + j * epw, ej(j), h);
-                else if (a.drop_thresh)
+                else if (XL == 2 && !kBatched)
                     pv = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + h) >= a.drop_thresh ? p * a.drop_scale
                                                                                             : 0.0f;
             }
@@ -595,7 +619,7 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 
 // ------------------------------------------------------------ launchers
 
-template <int DT, bool XL>
+template <int DT, int XL>
 static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     if (a0.vec == 2) {  // head-innermost layout (plain logits only)
@@ -611,12 +635,12 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
             // the 256 MB Infinity Cache; smaller ones are partly served from it.
             const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv)
-                fused_vec_kernel<DT, 2, XL ? 2 : GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, XL == 2 ? 4 : GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                fused_vec_kernel<DT, 2, XL ? 2 : GT_F32_D64_U, 64, 16, true, false, XL><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 2, XL == 2 ? 4 : GT_F32_D64_U, 64, 16, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 // the extended kernel keeps per-edge inputs live: fewer edges in flight
-                fused_vec_kernel<DT, 1, XL ? 4 : GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 1, XL == 2 ? 4 : GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 fused_vec_kernel<DT, 1, 8, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
@@ -640,9 +664,13 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
 
 hipError_t launch_fused(const Args& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (ev0) (void)hipEventRecord(ev0, s);
-    const bool xl = extended(a);
-    const hipError_t err = a.dtype == kF32 ? (xl ? launch_fused_dt<kF32, true>(a, s) : launch_fused_dt<kF32, false>(a, s))
-                                           : (xl ? launch_fused_dt<kBF16, true>(a, s) : launch_fused_dt<kBF16, false>(a, s));
+    // 0: plain logits; 1: bias and edge weights; 2: with dropout
+    const int xl = extended(a) ? (a.drop_thresh ? 2 : 1) : 0;
+    hipError_t err;
+    if (a.dtype == kF32)
+        err = xl == 0 ? launch_fused_dt<kF32, 0>(a, s) : xl == 1 ? launch_fused_dt<kF32, 1>(a, s) : launch_fused_dt<kF32, 2>(a, s);
+    else
+        err = xl == 0 ? launch_fused_dt<kBF16, 0>(a, s) : xl == 1 ? launch_fused_dt<kBF16, 1>(a, s) : launch_fused_dt<kBF16, 2>(a, s);
     if (ev1) (void)hipEventRecord(ev1, s);
     return err;
 }
