@@ -5,7 +5,8 @@ split rows) over the power-law workload: N=1,000,000 nodes, E=16,000,000
 edges, in-degrees Zipf(1.8) clipped at 50,000, uniform sources, H=8 heads of
 D=64, fp32; inputs resident in HBM before timing starts.
 
-Prints one JSON line: edge-heads/s of the whole call, the roofline of the
+Prints one JSON line: edge-heads/s of the whole call (and per-call median and
+minimum event times, back to back and after an L2 / Infinity Cache flush), the roofline of the
 dominant kernel (the fused attention kernel, timed with HIP events on its own
 stream over the timed region) against MI355X's 8 TB/s HBM peak, the HBM
 traffic counted by rocprofv3 (from the committed counter summary, when it
@@ -321,6 +322,35 @@ def time_layout(gt, t, w, steps, warmup=3):
     return res
 
 
+def time_calls(step, reps, flush_gib=1.0):
+    """Per-call event times of step(): back to back, and with a write of a
+    flush_gib GiB buffer between calls (evicting the L2 and the 256 MB
+    Infinity Cache; the write is outside the timed span)."""
+    import statistics
+
+    import torch
+
+    junk = torch.empty(int(flush_gib * (1 << 30)) // 4, dtype=torch.float32, device="cuda")
+    res = {}
+    for name, flush in (("back_to_back", False), ("flushed", True)):
+        times = []
+        for _ in range(reps):
+            if flush:
+                junk.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        res[name] = {"median_ms": statistics.median(times), "min_ms": min(times)}
+    del junk
+    log("per call: back to back median %.3f ms (min %.3f), after a cache flush median %.3f ms (min %.3f)"
+        % (res["back_to_back"]["median_ms"], res["back_to_back"]["min_ms"], res["flushed"]["median_ms"],
+           res["flushed"]["min_ms"]))
+    return res
+
+
 def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     """The oracle as it stands on a fixed random sample of destination rows."""
     import numpy as np
@@ -456,6 +486,7 @@ def main():
             "algorithmic_bytes": alg,
         },
         "cpu_baseline": None,
+        "calls": time_calls(step, max(5, args.steps)),
         "stages": None,
         "backward": None,
         "plan": None,
