@@ -27,7 +27,7 @@
 namespace gt {
 
 // ------------------------------------------------------------ dQ, vector layout
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, int XL>
+template <int DT, int NC, int U, int G_, int LPH_, bool FULL, int XL, bool NTL = false>
 __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     // hot instances: the heads per edge are known, so the batched dropout
@@ -121,12 +121,12 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
         DropBatch db;
@@ -764,7 +764,11 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
-            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
+            // streamed K/V gathers when K and V are far larger than the Infinity Cache
+            const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv && XL == 0)
+                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL, true><<<grid, block, 0, s>>>(a);
+            else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 bwd_dq_vec_kernel<DT, 1, XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
