@@ -287,24 +287,41 @@ def time_variants(gt, t, w, steps, warmup=2):
 
 
 def time_layout(gt, t, w, steps, warmup=3):
-    """The forward with features [N][H][D] (gt_sparse_mha_fwd) and [N][D][H]
-    (gt_sparse_mha_fwd_layout: its own kernel where the shape allows, else
-    transposed copies), event-timed; algorithmic bytes as for the step."""
+    """The forward and the backward with features [N][H][D] (gt_sparse_mha_fwd,
+    gt_sparse_mha_bwd) and [N][D][H] (gt_sparse_mha_fwd_layout,
+    gt_sparse_mha_bwd_layout: their own kernels where the shape allows, else
+    transposed copies), event-timed; algorithmic bytes as for the step and
+    for the backward."""
+    import numpy as np
     import torch
+
+    import gtgen
 
     def ndh(x):
         return x.transpose(1, 2).contiguous()
 
+    dev = t["Q"].device
     Qn, Kn, Vn = ndh(t["Q"]), ndh(t["K"]), ndh(t["V"])
     out = torch.empty_like(t["Q"])
     outn = torch.empty_like(Qn)
+    tip, tix = (torch.from_numpy(x).to(dev) for x in gtgen.source_sorted(w["indptr"], w["indices"]))
+    g = gtgen.make_grad(w["N"], w["H"], w["D"], w["dtype"], seed=11)
+    dO = (torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16) if g.dtype == np.uint16
+          else torch.from_numpy(g).to(dev))
+    dOn = ndh(dO)
+    fo, lse = gt.gt_sparse_mha_fwd_lse(t["indptr"], t["indices"], t["Q"], t["K"], t["V"])
+    fon = ndh(fo)
     calls = {
         "nhd": lambda: gt.gt_sparse_mha_fwd(t["indptr"], t["indices"], t["Q"], t["K"], t["V"], out=out),
         "ndh": lambda: gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], Qn, Kn, Vn, layout="ndh", out=outn),
+        "bwd_nhd": lambda: gt.gt_sparse_mha_bwd(t["indptr"], t["indices"], tip, tix, t["Q"], t["K"], t["V"], fo, dO,
+                                                lse),
+        "bwd_ndh": lambda: gt.gt_sparse_mha_bwd_layout(t["indptr"], t["indices"], tip, tix, None, Qn, Kn, Vn, fon,
+                                                       dOn, lse, layout="ndh"),
     }
     res = {}
-    nbytes = algorithmic_bytes(w)
     for name, fn in calls.items():
+        nbytes = backward_bytes(w) if name.startswith("bwd") else algorithmic_bytes(w)
         for _ in range(warmup):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -317,8 +334,9 @@ def time_layout(gt, t, w, steps, warmup=3):
         ms = e0.elapsed_time(e1) / steps
         res[name + "_ms"] = ms
         res[name + "_GBps"] = nbytes / (ms * 1e-3) / 1e9
-    log("layout: [N][H][D] %.4f ms, [N][D][H] %.4f ms" % (res["nhd_ms"], res["ndh_ms"]))
-    del Qn, Kn, Vn, out, outn
+    log("layout: forward [N][H][D] %.4f ms, [N][D][H] %.4f ms; backward %.4f ms, %.4f ms" % (
+        res["nhd_ms"], res["ndh_ms"], res["bwd_nhd_ms"], res["bwd_ndh_ms"]))
+    del Qn, Kn, Vn, out, outn, tip, tix, dO, dOn, fo, fon, lse
     return res
 
 

@@ -694,16 +694,24 @@ int gt_sparse_mha_bwd_layout(const int64_t* indptr, const int32_t* indices, cons
     if (!indptr || !t_indptr || !Q || !K || !V || !out || !dout || !lse || !dQ || !dK || !dV)
         return fail(GT_EINVAL, "NULL array with N > 0");
     if (E > 0 && (!indices || !t_indices)) return fail(GT_EINVAL, "NULL indices with E > 0");
-    // through [N][H][D] copies: five inputs and three gradients after the
-    // backward's own part of the scratch
-    const size_t fb = align256((size_t)N * H * D * (dtype == GT_F32 ? 4 : 2));
-    const void* src[5] = {Q, K, V, out, dout};
-    void* cp[8];
     Args a, at;
-    // sized with placeholder (aligned) feature pointers: only the sizes matter here
     rc = bwd_args(a, at, indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, dQ, dK, dV, dbias,
                   dweight, N, N, E, H, D, dtype, opts);
     if (rc) return rc;
+    if (!extended(a) && choose_layout_ndh(a, {Q, K, V, out, dout, dQ, dK, dV})) {
+        at.vec = a.vec;
+        at.ndh = a.ndh;
+        at.lph = a.lph;
+        at.R = a.R;
+        at.G = a.G;
+        at.NC = a.NC;
+        return run_bwd(a, at, nullptr, nullptr, stream);
+    }
+    // other shapes and the logit options: through [N][H][D] copies, five
+    // inputs and three gradients after the backward's own part of the scratch
+    const size_t fb = align256((size_t)N * H * D * (dtype == GT_F32 ? 4 : 2));
+    const void* src[5] = {Q, K, V, out, dout};
+    void* cp[8];
     a.vec = at.vec = 1;  // the copies are aligned; only the dew scratch depends on it, sized below for both cases
     size_t bb = 0;
     rc = bwd_scratch_bytes(a, at, nullptr, nullptr, &bb);

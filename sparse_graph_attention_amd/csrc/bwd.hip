@@ -678,6 +678,188 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
     }
 }
 
+// ------------------------------------------------------------ head-innermost layout
+//
+// Features [N][D][H]: lane gl of a group holds vector gl of a row (d = gl /
+// HV, heads (gl % HV) * VN .. +VN-1), as in the forward's fused_ndh_kernel;
+// per-head sums run over the lanes with the same gl % HV.  Partials of split
+// rows keep the row's [D][H] order; the merge adds them elementwise.
+
+// Sum over the lanes of a group that hold the same heads.
+__device__ __forceinline__ float ndh_head_sum(float x, int HV, int G) {
+    for (int off = HV; off < G; off <<= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dq_ndh_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+    const int G = a.G, HV = a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const bool act = gl < a.R;
+    const int hg = gl & (HV - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    const U4 zero{0, 0, 0, 0};
+    float q[VN], g[VN], o[VN], dl[VN], ls[VN], acc[VN];
+    VT::unpack(act ? ld16((const char*)a.Q + row * rowbytes + gl * 16) : zero, q);
+    VT::unpack(act ? ld16((const char*)a.dO + row * rowbytes + gl * 16) : zero, g);
+    VT::unpack(act ? ld16((const char*)a.O + row * rowbytes + gl * 16) : zero, o);
+#pragma unroll
+    for (int k = 0; k < VN; ++k) {
+        dl[k] = ndh_head_sum(g[k] * o[k], HV, G);
+        ls[k] = a.lse_in[row * a.H + hg * VN + k] * kLog2e;
+        acc[k] = 0.0f;
+    }
+    const char* Kb = (const char*)a.K;
+    const char* Vb = (const char*)a.V;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        U4 kr[U], vr[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) kr[j] = (ok[j] && act) ? ld16(Kb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
+#pragma unroll
+        for (int j = 0; j < U; ++j) vr[j] = (ok[j] && act) ? ld16(Vb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float kf[VN], vf[VN];
+            VT::unpack(kr[j], kf);
+            VT::unpack(vr[j], vf);
+#pragma unroll
+            for (int k = 0; k < VN; ++k) {
+                const float sd = ndh_head_sum(q[k] * kf[k], HV, G) * a.qscale;
+                const float dd = ndh_head_sum(g[k] * vf[k], HV, G);
+                const float p = ok[j] ? exp2_(sd - ls[k]) : 0.0f;
+                acc[k] = __builtin_fmaf(p * (dd - dl[k]), kf[k], acc[k]);
+            }
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) acc[k] += __shfl_xor(acc[k], off, kWave);
+    if (grp != 0 || !act) return;
+    if (gl < HV)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) a.stats[row * a.H + hg * VN + k] = make_float2(ls[k], dl[k]);
+    if (it.slot < 0) {
+        float r[VN];
+#pragma unroll
+        for (int k = 0; k < VN; ++k) r[k] = acc[k] * a.kscale;
+        st16((char*)a.dQ + row * rowbytes + gl * 16, VT::pack(r));
+    } else {
+        float* pa = a.plan.pacc + it.slot * (int64_t)a.H * a.D + (int64_t)gl * VN;
+#pragma unroll
+        for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[k]));
+    }
+}
+
+template <int DT, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
+    using VT = Vec<DT>;
+    constexpr int VN = VT::n;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t src = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+    const int G = a.G, HV = a.lph;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const bool act = gl < a.R;
+    const int hg = gl & (HV - 1);
+    const int64_t rowbytes = (int64_t)a.R * 16;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    const U4 zero{0, 0, 0, 0};
+    float kk[VN], vv[VN], dk[VN], dv[VN];
+    VT::unpack(act ? ld16((const char*)a.K + src * rowbytes + gl * 16) : zero, kk);
+    VT::unpack(act ? ld16((const char*)a.V + src * rowbytes + gl * 16) : zero, vv);
+#pragma unroll
+    for (int k = 0; k < VN; ++k) dk[k] = dv[k] = 0.0f;
+    const char* Qb = (const char*)a.Q;
+    const char* Gb = (const char*)a.dO;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            u[j] = un[j];
+            ok[j] = eb + grp + (int64_t)j * epw < e1;
+        }
+        U4 qr[U], gr[U];
+        float2 st[U][VN];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const bool go = ok[j] && act;
+            qr[j] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
+            gr[j] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
+#pragma unroll
+            for (int k = 0; k < VN; ++k)
+                st[j][k] = ok[j] ? a.stats[(int64_t)u[j] * a.H + hg * VN + k] : make_float2(0.0f, 0.0f);
+        }
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            float qf[VN], gf[VN];
+            VT::unpack(qr[j], qf);
+            VT::unpack(gr[j], gf);
+#pragma unroll
+            for (int k = 0; k < VN; ++k) {
+                const float sd = ndh_head_sum(qf[k] * kk[k], HV, G) * a.qscale;
+                const float dd = ndh_head_sum(gf[k] * vv[k], HV, G);
+                const float p = ok[j] ? exp2_(sd - st[j][k].x) : 0.0f;
+                dv[k] = __builtin_fmaf(p, gf[k], dv[k]);
+                dk[k] = __builtin_fmaf(p * (dd - st[j][k].y), qf[k], dk[k]);
+            }
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+            dk[k] += __shfl_xor(dk[k], off, kWave);
+            dv[k] += __shfl_xor(dv[k], off, kWave);
+        }
+    if (grp != 0 || !act) return;
+    if (it.slot < 0) {
+        float r[VN];
+#pragma unroll
+        for (int k = 0; k < VN; ++k) r[k] = dk[k] * a.kscale;
+        st16((char*)a.dK + src * rowbytes + gl * 16, VT::pack(r));
+        st16((char*)a.dV + src * rowbytes + gl * 16, VT::pack(dv));
+    } else {
+        const int64_t HD = (int64_t)a.H * a.D;
+        float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)gl * VN;
+#pragma unroll
+        for (int k = 0; k < VN; k += 4) {
+            st16(pa + k, Vec<kF32>::pack(&dk[k]));
+            st16(pa + HD + k, Vec<kF32>::pack(&dv[k]));
+        }
+    }
+}
+
 // ------------------------------------------------------------ merges of split rows
 // Chunk partials of a heavy row are [chunk][width] with width = regions * HD;
 // region r of each is added over the row's chunks, in chunk order, and goes
@@ -760,7 +942,11 @@ template <int DT, int XL>
 static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
-    if (a0.vec) {
+    if (a0.vec == 2) {  // head-innermost layout (plain logits only)
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            bwd_dq_ndh_kernel<DT, DT == kF32 ? 4 : 2><<<dim3(gx), block, 0, s>>>(a);
+        });
+    } else if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
@@ -807,7 +993,11 @@ template <int DT, int XL>
 static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
-    if (a0.vec) {
+    if (a0.vec == 2) {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            bwd_dkv_ndh_kernel<DT, DT == kF32 ? 4 : 2><<<dim3(gx), block, 0, s>>>(a);
+        });
+    } else if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;

@@ -1,11 +1,13 @@
 """The head-innermost feature layout [N][D][H] ("Graph Transformer in a
 Nutshell", SparseMHA.forward reshapes q, k, v to [N, dh, nh]) on the GPU.
 
-* Shapes the head-innermost kernel takes (H a multiple of the 16-byte vector
+* Shapes the head-innermost kernels take (H a multiple of the 16-byte vector
   with a power-of-two quotient, D*H within 1 KB): out and lse against the
-  oracle with the forward tolerances, whole rows and split rows.
-* Other shapes, the logit options and the backward run the [N][H][D] kernels
-  on transposed copies: bit-identical to the [N][H][D] calls.
+  oracle with the forward tolerances, and dQ, dK, dV against the oracle with
+  the backward's bound tolerances, whole rows and split rows.
+* Other shapes and the logit options run the [N][H][D] kernels on transposed
+  copies: bit-identical to the [N][H][D] calls (and the backward of the other
+  shapes is held to the oracle as well).
 The oracle works on [N][H][D]; a layout is a permutation of each row, so the
 expected values are the oracle's, permuted.
 """
@@ -16,7 +18,7 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
-from tests.test_gpu_backward import check_lse, to_torch, with_grad
+from tests.test_gpu_backward import bound_dkv, bound_dq, btol_of, check_bound, check_lse, to_torch, with_grad
 from tests.test_gpu_parity import (assert_close, chunk_edges, custom, dev, host, oracle_inputs, random_graph, say,
                                    to_dev, tol_of, workload)
 
@@ -93,7 +95,77 @@ def test_ndh_zero_edges_and_hub_row():
         check_fwd(custom(N, src, np.full(E, 5), 8, 10, seed=3))
 
 
-def test_ndh_options_and_backward_are_the_nhd_calls():
+def check_bwd(w):
+    """GPU forward then backward in the head-innermost layout, against the
+    oracle's gradients (the backward consumes the GPU's own out and lse)."""
+    w = with_grad(w)
+    say("ndh bwd %s N=%d E=%d H=%d D=%d dtype=%d kernel=%s chunk=%d" % (
+        w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"], takes_kernel(w),
+        gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+    t = to_dev(w)
+    d = dev()
+    tip, tix = (torch.from_numpy(x).to(d) for x in (w["t_indptr"], w["t_indices"]))
+    out, lse = gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], ndh(t["Q"]), ndh(t["K"]), ndh(t["V"]),
+                                           layout="ndh", want_lse=True)
+    dq, dk, dv, _, _ = gt.gt_sparse_mha_bwd_layout(t["indptr"], t["indices"], tip, tix, None, ndh(t["Q"]),
+                                                   ndh(t["K"]), ndh(t["V"]), out, ndh(to_torch(w["dO"])), lse,
+                                                   layout="ndh")
+    torch.cuda.synchronize()
+    rq, rk, rv, rlse, _ = oracle.bwd(*oracle_inputs(w), w["dO"])
+    check_lse(host(lse), rlse, "ndh lse " + w["name"])
+    rout = oracle.fwd(*oracle_inputs(w))
+    allv = np.arange(w["N"])
+    BK, BV = bound_dkv(w, rlse, lambda v: rout[v], allv)
+    tol = btol_of(w)
+    check_bound(host(nhd(dq)), rq, bound_dq(w, rlse, lambda v: rout[v], allv), tol, "ndh dQ " + w["name"])
+    check_bound(host(nhd(dk)), rk, BK, tol, "ndh dK " + w["name"])
+    check_bound(host(nhd(dv)), rv, BV, tol, "ndh dV " + w["name"])
+
+
+@pytest.mark.parametrize("name", ["molecules", "tiny_random"])
+@pytest.mark.parametrize("chunk", [1024, 2, 5])
+def test_ndh_bwd_workloads(name, chunk):
+    with chunk_edges(chunk):
+        check_bwd(workload(name))
+
+
+def test_ndh_bwd_molecules_bf16():
+    w = dict(workload("molecules"))
+    w["dtype"] = gtgen.BF16
+    w["Q"], w["K"], w["V"] = gtgen.make_features(w["N"], w["H"], w["D"], gtgen.BF16, 0, 0.5)
+    for chunk in (1024, 3):
+        with chunk_edges(chunk):
+            check_bwd(w)
+
+
+@pytest.mark.parametrize("H,D", [(4, 16), (16, 4), (64, 1), (8, 8), (32, 2), (4, 1), (8, 10), (3, 5), (8, 64),
+                                 (12, 4)])
+@pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
+def test_ndh_bwd_shapes(H, D, dtype):
+    with chunk_edges(30):
+        check_bwd(random_graph(H * 41 + D, 80, 900, H, D, dtype))
+
+
+def test_ndh_bwd_zero_edges_and_hub_source():
+    w = with_grad(custom(20, [], [], 8, 10))
+    t = to_dev(w)
+    d = dev()
+    tip, tix = (torch.from_numpy(x).to(d) for x in (w["t_indptr"], w["t_indices"]))
+    lse = torch.full((20, 8), float("-inf"), device=d)
+    z = torch.zeros((20, 10, 8), device=d)
+    say("ndh bwd E=0")
+    g = gt.gt_sparse_mha_bwd_layout(t["indptr"], t["indices"], tip, tix, None, ndh(t["Q"]), ndh(t["K"]),
+                                    ndh(t["V"]), z, ndh(to_torch(w["dO"])), lse, layout="ndh")
+    torch.cuda.synchronize()
+    assert all(torch.all(x == 0) for x in g[:3])
+    # one source feeding every destination many times: a split source row
+    N, E = 40, 2000
+    dst = np.sort(gtgen.random_coo(5, N, E)[1])
+    with chunk_edges(64):
+        check_bwd(custom(N, np.full(E, 7), dst, 8, 10, seed=5))
+
+
+def test_ndh_options_are_the_nhd_calls():
     w = with_grad(workload("molecules"))
     t = to_dev(w)
     d = dev()
@@ -115,16 +187,11 @@ def test_ndh_options_and_backward_are_the_nhd_calls():
         ng = gt.gt_sparse_mha_bwd_layout(t["indptr"], t["indices"], tip, tix, tpm, ndh(t["Q"]), ndh(t["K"]),
                                          ndh(t["V"]), ndh(out), ndh(dO), lse, layout="ndh", want_dbias=True,
                                          want_dweight=True, **opts)
-        plain = gt.gt_sparse_mha_bwd(t["indptr"], t["indices"], tip, tix, t["Q"], t["K"], t["V"], out, dO, lse)
-        nplain = gt.gt_sparse_mha_bwd_layout(t["indptr"], t["indices"], tip, tix, None, ndh(t["Q"]), ndh(t["K"]),
-                                             ndh(t["V"]), ndh(out), ndh(dO), lse, layout="ndh")
         torch.cuda.synchronize()
     assert torch.equal(nhd(nout), out) and torch.equal(nlse, lse)
     for a, b in zip(ng[:3], g[:3]):
         assert torch.equal(nhd(a), b)
     assert torch.equal(ng[3], g[3]) and torch.equal(ng[4], g[4])
-    for a, b in zip(nplain[:3], plain):
-        assert torch.equal(nhd(a), b)
 
 
 def test_ndh_large_sampled():
