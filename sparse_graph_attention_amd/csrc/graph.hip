@@ -18,7 +18,10 @@
 //  3. radix_scatter_kernel: each wave ranks its keys in input order with a
 //     ballot multisplit (lanes with equal digits find each other through one
 //     ballot per key bit; the lowest such lane takes their slots with one LDS
-//     atomic), then adds the counts of earlier waves of its tile.
+//     atomic), then adds the counts of earlier waves of its tile; the tile is
+//     rearranged in LDS into (digit, input) order, and consecutive threads
+//     write consecutive keys, so each digit's run leaves as one contiguous
+//     stretch instead of one scattered 4-byte store per key.
 // Keys of equal digit keep their input order, so every pass is stable.
 #include "kernels.hpp"
 
@@ -27,9 +30,10 @@ namespace gt {
 namespace {
 
 constexpr int kSortWaves = 4;
-constexpr int kSortItems = 8;                               // 64-key chunks per wave
+constexpr int kSortItems = 16;                              // 64-key chunks per wave
 constexpr int kWaveSpan = kWave * kSortItems;               // keys per wave
 constexpr int64_t kSortTile = (int64_t)kSortWaves * kWaveSpan;  // keys per block
+static_assert(kSortWaves * kWave == 256, "one thread per 8-bit digit in the sort kernels");
 constexpr int kScanThreads = 256;
 constexpr int kScanItems = 16;
 constexpr int64_t kScanTile = (int64_t)kScanThreads * kScanItems;
@@ -73,10 +77,14 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
     uint32_t* __restrict__ vals_out, int64_t n, int shift, int bits, const uint32_t* __restrict__ first,
     int64_t ntiles) {
     __shared__ uint32_t cnt[kSortWaves][256];
+    __shared__ uint32_t wsum[kSortWaves];
+    __shared__ int64_t gbase[256];           // output slot of the tile's first key of each digit, minus its tile slot
+    __shared__ uint32_t sk[kSortTile], sv[kSortTile];  // the tile in (digit, input) order
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
     for (int j = 0; j < kSortWaves; ++j) cnt[j][t] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kSortTile + (int64_t)w * kWaveSpan;
+    const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;
+    const int64_t base = tile0 + (int64_t)w * kWaveSpan;
     const uint32_t mask = (1u << bits) - 1u;
     uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
 #pragma unroll
@@ -99,23 +107,44 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
         rank[i] = old + (uint32_t)__builtin_popcountll(peers & lanes_below(lane));
     }
     __syncthreads();
-    if (t <= (int)mask) {  // counts of earlier waves of the tile, per digit
-        uint32_t run = 0;
-        for (int j = 0; j < kSortWaves; ++j) {
-            const uint32_t c = cnt[j][t];
-            cnt[j][t] = run;
-            run += c;
-        }
+    // thread t = digit t: counts of earlier waves, then the digit's first slot in
+    // the tile (exclusive scan of the tile's digit totals over the 256 threads)
+    uint32_t tot = 0;
+    for (int j = 0; j < kSortWaves; ++j) {
+        const uint32_t c = cnt[j][t];
+        cnt[j][t] = tot;
+        tot += c;
     }
+    uint32_t inc = tot;
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t y = __shfl_up(inc, off, kWave);
+        if (lane >= off) inc += y;
+    }
+    if (lane == kWave - 1) wsum[w] = inc;
+    __syncthreads();
+    uint32_t start = inc - tot;
+    for (int j = 0; j < w; ++j) start += wsum[j];
+    for (int j = 0; j < kSortWaves; ++j) cnt[j][t] += start;
+    gbase[t] = t <= (int)mask ? (int64_t)first[(int64_t)t * ntiles + blockIdx.x] - start : 0;
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int64_t e = base + (int64_t)i * kWave + lane;
         if (e >= n) continue;
         const uint32_t d = (key[i] >> shift) & mask;
-        const int64_t pos = (int64_t)first[(int64_t)d * ntiles + blockIdx.x] + cnt[w][d] + rank[i];
-        keys_out[pos] = key[i];
-        vals_out[pos] = val[i];
+        const uint32_t slot = cnt[w][d] + rank[i];
+        sk[slot] = key[i];
+        sv[slot] = val[i];
+    }
+    __syncthreads();
+    // consecutive threads take consecutive slots: each digit's run goes out as
+    // one contiguous stretch
+    const int count = (int)(n - tile0 < kSortTile ? n - tile0 : kSortTile);
+    for (int j = t; j < count; j += kSortWaves * kWave) {
+        const uint32_t k = sk[j];
+        const int64_t pos = gbase[(k >> shift) & mask] + j;
+        keys_out[pos] = k;
+        vals_out[pos] = sv[j];
     }
 }
 
