@@ -765,13 +765,15 @@ int check_graph(int64_t n_dst, int64_t n_src, int64_t E) {
 // Groups E items by key (keys < nrows), stably: offsets[nrows + 1] from the
 // sorted keys, and out[j] = vals_src[position of the j-th item]; the sorted
 // positions go to perm when it is non-null.  `scratch` holds
-// sort_scratch_bytes(E).
+// sort_scratch_bytes(E, perm != nullptr).
 hipError_t group_by_key(const uint32_t* keys, const uint32_t* vals_src, int64_t E, int64_t nrows, int64_t* offsets,
                         uint32_t* out, uint32_t* perm, void* scratch, hipStream_t s) {
-    const uint32_t *ks = nullptr, *vs = nullptr;
-    hipError_t e = radix_sort_pairs(keys, nullptr, E, key_bits_for(nrows), scratch, perm, s, &ks, &vs);
+    const uint32_t *ks = nullptr, *vs = nullptr, *v2s = nullptr;
+    hipError_t e = perm ? radix_sort(keys, nullptr, vals_src, E, key_bits_for(nrows), scratch, perm, out, s, &ks, &vs,
+                                     &v2s)
+                        : radix_sort(keys, vals_src, nullptr, E, key_bits_for(nrows), scratch, out, nullptr, s, &ks,
+                                     &vs, nullptr);
     if (e == hipSuccess) e = launch_lower_bounds(ks, E, nrows, offsets, s);
-    if (e == hipSuccess) e = launch_gather_u32(vals_src, vs, out, E, s);
     return e;
 }
 
@@ -779,7 +781,7 @@ hipError_t group_by_key(const uint32_t* keys, const uint32_t* vals_src, int64_t 
 int build_transpose(gt_plan_s* P, hipStream_t stream) {
     void* base = nullptr;
     const size_t rows_bytes = align256(sizeof(uint32_t) * (size_t)P->E);
-    int rc = get_scratch(stream, rows_bytes + sort_scratch_bytes(P->E), &base);
+    int rc = get_scratch(stream, rows_bytes + sort_scratch_bytes(P->E, true), &base);
     if (rc) return rc;
     uint32_t* rows = (uint32_t*)base;
     hipError_t e = launch_row_of_position(P->indptr, P->n_dst, P->E, rows, stream);
@@ -885,7 +887,7 @@ int gt_coo_to_csr(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t
     if (!indptr) return fail(GT_EINVAL, "NULL indptr");
     if (E > 0 && (!src || !dst || !indices)) return fail(GT_EINVAL, "NULL COO or indices array with E > 0");
     void* base = nullptr;
-    rc = get_scratch(stream, sort_scratch_bytes(E), &base);
+    rc = get_scratch(stream, sort_scratch_bytes(E, perm != nullptr), &base);
     if (rc) return rc;
     hipError_t e = group_by_key((const uint32_t*)dst, (const uint32_t*)src, E, n_dst, indptr, (uint32_t*)indices,
                                 (uint32_t*)perm, base, stream);
@@ -927,7 +929,7 @@ int gt_plan_create_coo(const int32_t* src, const int32_t* dst, int64_t n_dst, in
     rc = alloc_plan(n_dst, n_src, E, flags, &P);
     if (rc) return rc;
     void* base = nullptr;
-    rc = get_scratch(stream, sort_scratch_bytes(E), &base);
+    rc = get_scratch(stream, sort_scratch_bytes(E, false), &base);
     if (!rc) {
         hipError_t e = group_by_key((const uint32_t*)dst, (const uint32_t*)src, E, n_dst, P->indptr,
                                     (uint32_t*)P->indices, nullptr, base, stream);

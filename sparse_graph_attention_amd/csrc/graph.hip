@@ -1,7 +1,7 @@
 // graph.hip -- graph construction on the device: a stable LSD radix sort of
-// 32-bit keys carrying 32-bit values, an exclusive scan, and the helpers that
-// turn sorted keys into a CSR (row offsets by binary search, row ids of CSR
-// positions, gathers).
+// 32-bit keys carrying one or two arrays of 32-bit values, an exclusive scan,
+// and the helpers that turn sorted keys into a CSR (row offsets by binary
+// search, the row of each CSR position).
 //
 // "Graph Transformer in a Nutshell", section "Graph Transformer Model":
 // GTModel.forward stacks the (src, dst) pairs of g.edges() into one sparse
@@ -11,7 +11,8 @@
 // source id) keeps each row's edges in their input order, so the result is
 // unique and bit-reproducible.
 //
-// Sort pass (8-bit digits, tiles of kSortTile keys per block of 4 waves):
+// Sort pass (8-bit digits, tiles of kSortTile keys per block of 4 waves; the
+// values, and an optional second value array, travel with the keys):
 //  1. radix_count_kernel: per-tile digit histogram -> hist[digit][tile];
 //  2. exclusive scan of hist in that digit-major order -> the first output
 //     slot of each (digit, tile);
@@ -71,28 +72,31 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_count_kernel(const u
     if (t <= (int)mask) hist[(int64_t)t * ntiles + blockIdx.x] = cnt[t];
 }
 
-template <bool IOTA>
+// IOTA: the values are the keys' input positions.  TWO: a second value array
+// travels with the first.
+template <bool IOTA, bool TWO>
 __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, uint32_t* __restrict__ keys_out,
-    uint32_t* __restrict__ vals_out, int64_t n, int shift, int bits, const uint32_t* __restrict__ first,
-    int64_t ntiles) {
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, const uint32_t* __restrict__ vals2_in,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ vals2_out, int64_t n,
+    int shift, int bits, const uint32_t* __restrict__ first, int64_t ntiles) {
     __shared__ uint32_t cnt[kSortWaves][256];
     __shared__ uint32_t wsum[kSortWaves];
     __shared__ int64_t gbase[256];           // output slot of the tile's first key of each digit, minus its tile slot
-    __shared__ uint32_t sk[kSortTile], sv[kSortTile];  // the tile in (digit, input) order
+    __shared__ uint32_t sk[kSortTile], sv[kSortTile], sv2[TWO ? kSortTile : 1];  // the tile in (digit, input) order
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
     for (int j = 0; j < kSortWaves; ++j) cnt[j][t] = 0;
     __syncthreads();
     const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;
     const int64_t base = tile0 + (int64_t)w * kWaveSpan;
     const uint32_t mask = (1u << bits) - 1u;
-    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+    uint32_t key[kSortItems], val[kSortItems], val2[TWO ? kSortItems : 1], rank[kSortItems];
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
         const int64_t e = base + (int64_t)i * kWave + lane;
         const bool valid = e < n;
         key[i] = valid ? keys_in[e] : 0u;
         val[i] = valid ? (IOTA ? (uint32_t)e : vals_in[e]) : 0u;
+        if constexpr (TWO) val2[i] = valid ? vals2_in[e] : 0u;
     }
 #pragma unroll
     for (int i = 0; i < kSortItems; ++i) {
@@ -135,6 +139,7 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
         const uint32_t slot = cnt[w][d] + rank[i];
         sk[slot] = key[i];
         sv[slot] = val[i];
+        if constexpr (TWO) sv2[slot] = val2[i];
     }
     __syncthreads();
     // consecutive threads take consecutive slots: each digit's run goes out as
@@ -145,6 +150,7 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
         const int64_t pos = gbase[(k >> shift) & mask] + j;
         keys_out[pos] = k;
         vals_out[pos] = sv[j];
+        if constexpr (TWO) vals2_out[pos] = sv2[j];
     }
 }
 
@@ -248,27 +254,40 @@ __global__ __launch_bounds__(256) void lower_bounds_kernel(const uint32_t* __res
     offsets[v] = lo;
 }
 
-// rows[p] = the row holding CSR position p (binary search in indptr).
-__global__ __launch_bounds__(256) void row_of_position_kernel(const int64_t* __restrict__ indptr, int64_t nrows,
-                                                               int64_t n, uint32_t* __restrict__ rows) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p >= n) return;
-    int64_t lo = 0, hi = nrows;  // last row r with indptr[r] <= p
-    while (hi - lo > 1) {
-        const int64_t mid = lo + ((hi - lo) >> 1);
+// rows[p] = the row holding CSR position p: the last row r with indptr[r] <= p.
+// A wave takes kRowSpan consecutive positions; it finds the rows of its first
+// and last position in all of indptr, then each position's row between
+// those two.
+constexpr int kRowItems = 16;
+constexpr int64_t kRowSpan = (int64_t)kWave * kRowItems;
+
+// Last r in [lo, hi] with indptr[r] <= p, given indptr[lo] <= p.
+__device__ __forceinline__ int64_t last_row_at_or_below(const int64_t* __restrict__ indptr, int64_t p, int64_t lo,
+                                                        int64_t hi) {
+    while (lo < hi) {
+        const int64_t mid = lo + ((hi - lo + 1) >> 1);
         if (indptr[mid] <= p)
             lo = mid;
         else
-            hi = mid;
+            hi = mid - 1;
     }
-    rows[p] = (uint32_t)lo;
+    return lo;
 }
 
-// out[p] = src[idx[p]].
-__global__ __launch_bounds__(256) void gather_kernel(const uint32_t* __restrict__ src, const uint32_t* __restrict__ idx,
-                                                      uint32_t* __restrict__ out, int64_t n) {
-    const int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (p < n) out[p] = src[idx[p]];
+__global__ __launch_bounds__(256) void row_of_position_kernel(const int64_t* __restrict__ indptr, int64_t nrows,
+                                                               int64_t n, uint32_t* __restrict__ rows) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
+    const int64_t p0 = wave * kRowSpan;
+    if (p0 >= n) return;
+    const int64_t p1 = (p0 + kRowSpan < n ? p0 + kRowSpan : n) - 1;
+    const int64_t r0 = last_row_at_or_below(indptr, p0, 0, nrows - 1);
+    const int64_t r1 = last_row_at_or_below(indptr, p1, r0, nrows - 1);
+#pragma unroll 4
+    for (int i = 0; i < kRowItems; ++i) {
+        const int64_t p = p0 + (int64_t)i * kWave + lane;
+        if (p < n) rows[p] = (uint32_t)last_row_at_or_below(indptr, p, r0, r1);
+    }
 }
 
 unsigned grid256(int64_t n) { return (unsigned)cdiv(n, 256); }
@@ -281,47 +300,63 @@ int key_bits_for(int64_t nkeys) {
     return b;
 }
 
-size_t sort_scratch_bytes(int64_t n) {
+size_t sort_scratch_bytes(int64_t n, bool two_values) {
     const int64_t tiles = cdiv(n > 0 ? n : 1, kSortTile);
-    return sizeof(uint32_t) * (size_t)(4 * n + 256 * tiles + scan_words(256 * tiles) + 1024);
+    return sizeof(uint32_t) * (size_t)((two_values ? 6 : 4) * n + 256 * tiles + scan_words(256 * tiles) + 1024);
 }
 
-hipError_t radix_sort_pairs(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int key_bits, void* scratch,
-                            uint32_t* vals_final, hipStream_t s, const uint32_t** keys_sorted,
-                            const uint32_t** vals_sorted) {
+hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const uint32_t* vals2_in, int64_t n,
+                      int key_bits, void* scratch, uint32_t* vals_final, uint32_t* vals2_final, hipStream_t s,
+                      const uint32_t** keys_sorted, const uint32_t** vals_sorted, const uint32_t** vals2_sorted) {
+    const bool two = vals2_in != nullptr;
     const int64_t tiles = cdiv(n > 0 ? n : 1, kSortTile);
-    uint32_t* kb[2] = {(uint32_t*)scratch, (uint32_t*)scratch + n};
-    uint32_t* vb[2] = {(uint32_t*)scratch + 2 * n, (uint32_t*)scratch + 3 * n};
-    uint32_t* hist = (uint32_t*)scratch + 4 * n;
+    uint32_t* w = (uint32_t*)scratch;
+    uint32_t* kb[2] = {w, w + n};
+    uint32_t* vb[2] = {w + 2 * n, w + 3 * n};
+    uint32_t* v2b[2] = {two ? w + 4 * n : nullptr, two ? w + 5 * n : nullptr};
+    uint32_t* hist = w + (two ? 6 : 4) * n;
     uint32_t* tmp = hist + 256 * tiles;
     const int passes = key_bits > 0 ? (key_bits + 7) / 8 : 1;
     const uint32_t* kin = keys_in;
     const uint32_t* vin = vals_in;
+    const uint32_t* v2in = vals2_in;
+    const unsigned grid = (unsigned)tiles;
+    const unsigned block = kSortWaves * kWave;
     for (int p = 0; p < passes; ++p) {
         const int shift = 8 * p;
         const int bits = key_bits - shift < 8 ? (key_bits - shift > 0 ? key_bits - shift : 1) : 8;
+        const bool last = p == passes - 1;
         uint32_t* kout = kb[p & 1];
-        uint32_t* vout = (p == passes - 1 && vals_final) ? vals_final : vb[p & 1];
+        uint32_t* vout = (last && vals_final) ? vals_final : vb[p & 1];
+        uint32_t* v2out = (last && vals2_final) ? vals2_final : v2b[p & 1];
         if (n > 0) {
-            radix_count_kernel<<<(unsigned)tiles, kSortWaves * kWave, 0, s>>>(kin, n, shift, bits, hist, tiles);
+            radix_count_kernel<<<grid, block, 0, s>>>(kin, n, shift, bits, hist, tiles);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
             err = scan_exclusive(hist, ((int64_t)1 << bits) * tiles, tmp, s);
             if (err != hipSuccess) return err;
-            if (vin)
-                radix_scatter_kernel<false><<<(unsigned)tiles, kSortWaves * kWave, 0, s>>>(kin, vin, kout, vout, n,
-                                                                                        shift, bits, hist, tiles);
+            if (!vin && two)
+                radix_scatter_kernel<true, true><<<grid, block, 0, s>>>(kin, nullptr, v2in, kout, vout, v2out, n,
+                                                                         shift, bits, hist, tiles);
+            else if (!vin)
+                radix_scatter_kernel<true, false><<<grid, block, 0, s>>>(kin, nullptr, nullptr, kout, vout, nullptr,
+                                                                          n, shift, bits, hist, tiles);
+            else if (two)
+                radix_scatter_kernel<false, true><<<grid, block, 0, s>>>(kin, vin, v2in, kout, vout, v2out, n, shift,
+                                                                          bits, hist, tiles);
             else
-                radix_scatter_kernel<true><<<(unsigned)tiles, kSortWaves * kWave, 0, s>>>(kin, nullptr, kout, vout, n,
-                                                                                       shift, bits, hist, tiles);
+                radix_scatter_kernel<false, false><<<grid, block, 0, s>>>(kin, vin, nullptr, kout, vout, nullptr, n,
+                                                                           shift, bits, hist, tiles);
             err = hipGetLastError();
             if (err != hipSuccess) return err;
         }
         kin = kout;
         vin = vout;
+        v2in = v2out;
     }
     *keys_sorted = kin;
     *vals_sorted = vin;
+    if (vals2_sorted) *vals2_sorted = v2in;
     return hipSuccess;
 }
 
@@ -332,13 +367,8 @@ hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, i
 
 hipError_t launch_row_of_position(const int64_t* indptr, int64_t nrows, int64_t n, uint32_t* rows, hipStream_t s) {
     if (n == 0) return hipSuccess;
-    row_of_position_kernel<<<grid256(n), 256, 0, s>>>(indptr, nrows, n, rows);
-    return hipGetLastError();
-}
-
-hipError_t launch_gather_u32(const uint32_t* src, const uint32_t* idx, uint32_t* out, int64_t n, hipStream_t s) {
-    if (n == 0) return hipSuccess;
-    gather_kernel<<<grid256(n), 256, 0, s>>>(src, idx, out, n);
+    const int64_t waves = cdiv(n, kRowSpan);
+    row_of_position_kernel<<<(unsigned)cdiv(waves * kWave, 256), 256, 0, s>>>(indptr, nrows, n, rows);
     return hipGetLastError();
 }
 

@@ -99,20 +99,20 @@ hipError_t launch_spmm(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dq(const Args& a, hipStream_t s);
 hipError_t launch_bwd_dkv(const Args& a, hipStream_t s);
 // Graph construction (graph.hip).  A stable LSD radix sort of n uint32 keys
-// below 2^key_bits carrying uint32 values (vals_in == nullptr: the key's
-// position); scratch holds sort_scratch_bytes(n) bytes; the sorted values
-// land in vals_final when it is non-null.
+// below 2^key_bits carrying uint32 values (vals_in == nullptr: each key's
+// input position) and, when vals2_in is non-null, a second value array.
+// scratch holds sort_scratch_bytes(n, vals2_in != nullptr) bytes; the sorted
+// values land in vals_final / vals2_final when those are non-null, else in
+// scratch; *keys_sorted etc. point at the results.
 int key_bits_for(int64_t nkeys);
-size_t sort_scratch_bytes(int64_t n);
-hipError_t radix_sort_pairs(const uint32_t* keys_in, const uint32_t* vals_in, int64_t n, int key_bits, void* scratch,
-                            uint32_t* vals_final, hipStream_t s, const uint32_t** keys_sorted,
-                            const uint32_t** vals_sorted);
+size_t sort_scratch_bytes(int64_t n, bool two_values);
+hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const uint32_t* vals2_in, int64_t n,
+                      int key_bits, void* scratch, uint32_t* vals_final, uint32_t* vals2_final, hipStream_t s,
+                      const uint32_t** keys_sorted, const uint32_t** vals_sorted, const uint32_t** vals2_sorted);
 // offsets[v] = number of sorted keys below v, v in [0, nrows].
 hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, int64_t* offsets, hipStream_t s);
 // rows[p] = the row of CSR position p.
 hipError_t launch_row_of_position(const int64_t* indptr, int64_t nrows, int64_t n, uint32_t* rows, hipStream_t s);
-// out[p] = src[idx[p]].
-hipError_t launch_gather_u32(const uint32_t* src, const uint32_t* idx, uint32_t* out, int64_t n, hipStream_t s);
 // CSR check: writes error flags into *flags (device memory, cleared first).
 hipError_t launch_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, uint32_t* flags,
                            hipStream_t s);
