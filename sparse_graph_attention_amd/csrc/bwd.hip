@@ -957,7 +957,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dq_vec_kernel<DT, 1, XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 1, XL == 2 ? GT_BWD_BF16_DQ_XL2_U : XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
@@ -1004,7 +1004,7 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dkv_vec_kernel<DT, 2, XL ? 2 : 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? GT_BWD_BF16_DKV_XL1_U : GT_BWD_BF16_DKV_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)
                 bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)

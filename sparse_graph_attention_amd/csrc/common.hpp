@@ -25,6 +25,18 @@
 #ifndef GT_BF16_D32_U
 #define GT_BF16_D32_U 8  // edges in flight per half-wave, bf16 rows of 8 heads x 32
 #endif
+#ifndef GT_BWD_BF16_DQ_XL2_U
+#define GT_BWD_BF16_DQ_XL2_U 4  // backward, bf16 8 x 32: destination pass with dropout
+#endif
+#ifndef GT_BWD_BF16_DKV_U
+#define GT_BWD_BF16_DKV_U 8  // source pass, plain logits
+#endif
+#ifndef GT_BWD_BF16_DKV_XL1_U
+#define GT_BWD_BF16_DKV_XL1_U 4  // source pass with bias or edge weights
+#endif
+#ifndef GT_BF16_D32_XL1_U
+#define GT_BF16_D32_XL1_U 4  // the same with bias or edge weights (keeps 4 waves per SIMD)
+#endif
 
 namespace gt {
 

@@ -160,10 +160,11 @@ def test_variants_small(variant, name, chunk):
 
 @pytest.mark.parametrize("H,D", [(8, 64), (3, 5), (4, 33), (2, 256), (16, 64), (8, 32), (64, 4)])
 @pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
-def test_variants_shapes(H, D, dtype):
+@pytest.mark.parametrize("p", [0.3, 0.0])  # the dropout kernels, and those of bias and weights alone
+def test_variants_shapes(H, D, dtype, p):
     w = with_grad(random_graph(H * 100 + D, 60, 800, H, D, dtype))
     with chunk_edges(40):
-        check_full(w, make_opts(w, H + D, bias=True, weights=True, p=0.3))
+        check_full(w, make_opts(w, H + D, bias=True, weights=True, p=p))
 
 
 def test_one_hub_row_and_source():
