@@ -953,7 +953,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             // streamed K/V gathers when K and V are far larger than the Infinity Cache
             const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv && XL == 0)
-                bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL, true><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 2, GT_BWD_F32_DQ_U, 64, 16, true, XL, true><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
@@ -1002,7 +1002,7 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = a.R == a.NC * a.G;
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
-                bwd_dkv_vec_kernel<DT, 2, XL ? 2 : 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 2, XL ? 2 : GT_BWD_F32_DKV_U, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? GT_BWD_BF16_DKV_XL1_U : GT_BWD_BF16_DKV_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 1)

@@ -25,6 +25,12 @@
 #ifndef GT_BF16_D32_U
 #define GT_BF16_D32_U 8  // edges in flight per half-wave, bf16 rows of 8 heads x 32
 #endif
+#ifndef GT_BWD_F32_DQ_U
+#define GT_BWD_F32_DQ_U 4  // backward, fp32 8 x 64: destination pass, plain logits
+#endif
+#ifndef GT_BWD_F32_DKV_U
+#define GT_BWD_F32_DKV_U 4  // source pass, plain logits
+#endif
 #ifndef GT_BWD_BF16_DQ_XL2_U
 #define GT_BWD_BF16_DQ_XL2_U 4  // backward, bf16 8 x 32: destination pass with dropout
 #endif
