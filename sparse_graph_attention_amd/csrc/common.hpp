@@ -25,6 +25,21 @@
 #ifndef GT_BF16_D32_U
 #define GT_BF16_D32_U 8  // edges in flight per half-wave, bf16 rows of 8 heads x 32
 #endif
+#ifndef GT_SDDMM_F32_U
+#define GT_SDDMM_F32_U 4  // unfused stages, fp32 8 x 64 and bf16 8 x 32 rows: edges in flight per group
+#endif
+#ifndef GT_SDDMM_BF16_U
+#define GT_SDDMM_BF16_U 8
+#endif
+#ifndef GT_SPMM_F32_U
+#define GT_SPMM_F32_U 4
+#endif
+#ifndef GT_SPMM_BF16_U
+#define GT_SPMM_BF16_U 4
+#endif
+#ifndef GT_UNFUSED_NTL
+#define GT_UNFUSED_NTL 0  // fp32 gathers of arrays over 1 GB with the non-temporal hint (measured slower)
+#endif
 #ifndef GT_BWD_F32_DQ_U
 #define GT_BWD_F32_DQ_U 4  // backward, fp32 8 x 64: destination pass, plain logits
 #endif

@@ -8,10 +8,19 @@
 
 namespace gt {
 
-template <int DT, int NC, int U>
+// G_ and LPH_ non-zero: a hot instance whose lane layout is known at compile
+// time, with every lane active (R == NC * G).  It reads a batch's weights
+// (epw * U edges x H heads, contiguous in [E][H]) as one run of 64 values
+// per load and hands each lane its weights by shuffles, instead of one
+// narrow load per (edge, block of heads).  NTL: V gathers with the
+// non-temporal hint.
+template <int DT, int NC, int U, int G_ = 0, int LPH_ = 0, bool NTL = false>
 __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
+    constexpr bool kHot = G_ > 0 && LPH_ > 0;
+    constexpr int kH = kHot ? NC * (G_ / LPH_) : 1;                    // heads
+    constexpr int kR = kHot ? ((kWave / G_) * U * kH + kWave - 1) / kWave : 1;  // loads of 64 weights per batch
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     Item it;
@@ -20,7 +29,7 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
     it.e0 = uniform64(it.e0);
     it.e1 = uniform64(it.e1);
 
-    const int G = a.G, lph = a.lph;
+    const int G = kHot ? G_ : a.G, lph = kHot ? LPH_ : a.lph;
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
@@ -32,7 +41,7 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = vi < a.R;
+        act[c] = kHot || vi < a.R;
         head[c] = act[c] ? vi / lph : 0;
 #pragma unroll
         for (int k = 0; k < VN; ++k) acc[c][k] = 0.0f;
@@ -51,14 +60,23 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
         }
         U4 vr[U][NC];
         float al[U][NC];
+        SlotBatch<kR> ab;
+        // weights past the item's last edge read as 0
+        if constexpr (kHot) slot_batch_load(ab, a.alpha_in, eb, e1, epw * U, kH, lane);
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const bool go = ok[j] && act[c];
-                vr[j][c] = go ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
-                al[j][c] = go ? a.alpha_in[(eb + grp + (int64_t)j * epw) * a.H + head[c]] : 0.0f;
+                const char* p = Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16;
+                vr[j][c] = go ? (NTL ? ld16_nt(p) : ld16(p)) : U4{0, 0, 0, 0};
+                if constexpr (!kHot) al[j][c] = go ? a.alpha_in[(eb + grp + (int64_t)j * epw) * a.H + head[c]] : 0.0f;
             }
+        if constexpr (kHot)
+#pragma unroll
+            for (int j = 0; j < U; ++j)
+#pragma unroll
+                for (int c = 0; c < NC; ++c) al[j][c] = slot_batch_get(ab, (grp + j * epw) * kH + head[c]);
         // the next batch's source ids load behind this batch's gathers
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(a.indices, nb, grp, epw, e1, un);
@@ -82,7 +100,12 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
         char* orow = (char*)a.out + it.row * rowbytes;
 #pragma unroll
         for (int c = 0; c < NC; ++c)
-            if (act[c]) st16(orow + (c * G + gl) * 16, VT::pack(acc[c]));
+            if (act[c]) {
+                if (kHot)
+                    st16_nt(orow + (c * G + gl) * 16, VT::pack(acc[c]));
+                else
+                    st16(orow + (c * G + gl) * 16, VT::pack(acc[c]));
+            }
     } else {
         const int64_t HD = (int64_t)a.H * a.D;
 #pragma unroll
@@ -179,6 +202,20 @@ static hipError_t launch_spmm_dt(const Args& a0, hipStream_t s) {
     if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
+            const bool full = a.R == a.NC * a.G;
+            // gathers streamed past the caches when V is far larger than the Infinity Cache
+            const bool stream_v = a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && a.H == 8 && full) {
+                if (stream_v && GT_UNFUSED_NTL)
+                    spmm_vec_kernel<DT, 2, GT_SPMM_F32_U, 64, 16, true><<<grid, block, 0, s>>>(a);
+                else
+                    spmm_vec_kernel<DT, 2, GT_SPMM_F32_U, 64, 16, false><<<grid, block, 0, s>>>(a);
+                return;
+            }
+            if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && a.H == 8 && full) {
+                spmm_vec_kernel<DT, 1, GT_SPMM_BF16_U, 32, 4, false><<<grid, block, 0, s>>>(a);
+                return;
+            }
             switch (a.NC) {
                 case 1: spmm_vec_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
                 case 2: spmm_vec_kernel<DT, 2, 4><<<grid, block, 0, s>>>(a); break;
