@@ -97,6 +97,10 @@ hipError_t launch_spmm(const Args& a, hipStream_t s);
 // Backward: dQ (and delta) over the destination-sorted graph, then dK and dV
 // over the source-sorted one (a.indptr/a.indices/a.plan describe that graph).
 hipError_t launch_bwd_dq(const Args& a, hipStream_t s);
+// Split rows whose chunk partials add up ([chunk][regions * H * D] floats in
+// a.plan.pacc): region r of the sum, times scale_r, goes to row hr.row of dst_r.
+hipError_t launch_sum_merge(const Args& a, int regions, void* dst0, float scale0, void* dst1, float scale1,
+                            hipStream_t s);
 hipError_t launch_bwd_dkv(const Args& a, hipStream_t s);
 // Graph construction (graph.hip).  A stable LSD radix sort of n uint32 keys
 // below 2^key_bits carrying uint32 values (vals_in == nullptr: each key's

@@ -3,7 +3,8 @@
 // "Graph Transformer in a Nutshell", section "Sparse Multi-head Attention"
 // (bspmm of the sparse attention matrix with V); the DGL builtin-operator
 // gist's u_mul_e_sum.  Same lane layouts and work items as the fused kernel.
-// Chunks of heavy rows leave partial sums; the merge adds them in chunk order.
+// Chunks of heavy rows leave partial sums; the merge (launch_sum_merge) adds
+// them in chunk order.
 #include "kernels.hpp"
 
 namespace gt {
@@ -181,21 +182,6 @@ __global__ __launch_bounds__(kBlock) void spmm_scalar_kernel(const Args a) {
 
 // One wave per heavy row: out = sum of the chunks' partial sums, in chunk order.
 template <int DT>
-__global__ __launch_bounds__(kBlock) void spmm_merge_kernel(const Args a) {
-    using VT = Vec<DT>;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
-    const HeavyRow hr = a.plan.heavy[hs];
-    const int64_t HD = (int64_t)a.H * a.D;
-    for (int64_t j = lane; j < HD; j += kWave) {
-        float A = 0.0f;
-        for (int i = 0; i < hr.nch; ++i) A += a.plan.pacc[(hr.base + i) * HD + j];
-        VT::store_scalar(a.out, (int64_t)hr.row * HD + j, A);
-    }
-}
-
-template <int DT>
 static hipError_t launch_spmm_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
@@ -234,10 +220,8 @@ static hipError_t launch_spmm_dt(const Args& a0, hipStream_t s) {
             }
         });
     }
-    if (err != hipSuccess || a0.plan.max_heavy == 0) return err;
-    return for_slices(a0, a0.plan.max_heavy, [&](const Args& a, unsigned gx) {
-        spmm_merge_kernel<DT><<<gx, block, 0, s>>>(a);
-    });
+    if (err != hipSuccess) return err;
+    return launch_sum_merge(a0, 1, a0.out, 1.0f, nullptr, 0.0f, s);
 }
 
 hipError_t launch_spmm(const Args& a, hipStream_t s) {
