@@ -389,6 +389,13 @@ def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
     dt = time.perf_counter() - t0
     g = out_gpu[rows].astype(np.float64)
     log("cpu baseline: %.2f s; GPU vs oracle on the sample: max abs err %.3e" % (dt, float(np.abs(g - ref).max())))
+    # one thread, on a tenth of that sample
+    rows1 = rows[::10]
+    edges1 = int((ip[rows1 + 1] - ip[rows1]).sum())
+    t0 = time.perf_counter()
+    oracle.fwd_rows(w["indptr"], w["indices"], w["Q"], w["K"], w["V"], rows1, nthreads=1)
+    dt1 = time.perf_counter() - t0
+    log("cpu baseline, 1 thread: %d rows (%d edges) in %.2f s" % (len(rows1), edges1, dt1))
     return {
         "value": edges * w["H"] / dt,
         "unit": "edge-heads/s",
@@ -396,6 +403,10 @@ def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
         "kind": "oracle",
         "sample": "%d%% of destination rows drawn uniformly (seed %d): %d rows, %d edges, %.1f s wall" % (
             round(fraction * 100), seed, len(rows), edges, dt),
+        "single_thread": {
+            "value": edges1 * w["H"] / dt1,
+            "sample": "every 10th row of that sample: %d rows, %d edges, %.1f s wall" % (len(rows1), edges1, dt1),
+        },
     }
 
 
