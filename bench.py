@@ -15,14 +15,16 @@ sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan] [--no-variants]
-                  [--no-layout]
+                  [--no-layout] [--no-ceiling]
                   [--calib-copy]
 
 Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM),
 the backward (gt_sparse_mha_bwd), graph construction (COO to CSR, a plan with
 its transpose, the forward on a plan), and the forward and backward with an
 additive bias, edge weights and attention dropout, each event-timed on the
-same inputs, and the forward with head-innermost [N][D][H] features.
+same inputs, and the forward with head-innermost [N][D][H] features; and the
+achievable ceiling: the K and V row gathers alone (gt_calib_gather) and a
+plain device copy.
 """
 import argparse
 import hashlib
@@ -342,6 +344,49 @@ def time_layout(gt, t, w, steps, warmup=3):
     return res
 
 
+def time_ceiling(gt, t, w, kern_ms, reps=10, copy_gib=1.0):
+    """Achievable rates beside the 8 TB/s peak, event-timed on the same inputs:
+    gt_calib_gather (the K and V row gathers of every edge, read as the fused
+    kernel reads them, and nothing else) and a plain device copy of copy_gib
+    GiB.  gather_frac: the fused kernel's K+V gather bytes per its time, over
+    the rate of the gathers alone."""
+    import torch
+
+    row_bytes = t["K"][0].numel() * t["K"].element_size()
+    if row_bytes not in (512, 1024, 2048):
+        return None
+    sink = torch.zeros(1, dtype=torch.int32, device=t["K"].device)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    g_ms = timed(lambda: gt.gt_calib_gather(t["indices"], t["K"], t["V"], checksum=sink))
+    g_bytes = 2 * w["E"] * row_bytes + 4 * w["E"]
+    n = int(copy_gib * (1 << 30)) // 4
+    a = torch.ones(n, dtype=torch.float32, device=t["K"].device)
+    b = torch.empty_like(a)
+    c_ms = timed(lambda: b.copy_(a))
+    del a, b
+    res = {
+        "gather_ms": g_ms,
+        "gather_GBps": g_bytes / (g_ms * 1e-3) / 1e9,
+        "gather_bytes": g_bytes,
+        "copy_GBps": 2 * n * 4 / (c_ms * 1e-3) / 1e9,
+        "gather_frac": (2 * w["E"] * row_bytes / (kern_ms * 1e-3)) / (g_bytes / (g_ms * 1e-3)),
+    }
+    log("ceiling: K+V gathers alone %.3f ms (%.0f GB/s), device copy %.0f GB/s; fused kernel's gathers at %.0f%% "
+        "of the gathers-alone rate" % (g_ms, res["gather_GBps"], res["copy_GBps"], 100 * res["gather_frac"]))
+    return res
+
+
 def time_calls(step, reps, flush_gib=1.0):
     """Per-call event times of step(): back to back, and with a write of a
     flush_gib GiB buffer between calls (evicting the L2 and the 256 MB
@@ -436,6 +481,7 @@ def main():
     ap.add_argument("--no-plan", action="store_true", help="skip timing graph construction and plans")
     ap.add_argument("--no-variants", action="store_true", help="skip timing the logit variants and dropout")
     ap.add_argument("--no-layout", action="store_true", help="skip timing the head-innermost layout")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the gathers-alone and copy rates")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -518,6 +564,7 @@ def main():
         },
         "cpu_baseline": None,
         "calls": time_calls(step, max(5, args.steps)),
+        "ceiling": None if args.no_ceiling else time_ceiling(gt, t, w, kern_avg_ms),
         "stages": None,
         "backward": None,
         "plan": None,

@@ -314,6 +314,25 @@ int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const voi
                            float* dweight, int32_t H, int32_t D, int32_t dtype, const gt_logit_opts* opts,
                            hipStream_t stream);
 
+/*
+ * Measurement aid, not part of the attention: the achievable rate of its
+ * gathers.  In "Graph Transformer in a Nutshell", section "Sparse Multi-head
+ * Attention", every nonzero (v, u) of the adjacency matrix reads row u of K
+ * (SDDMM) and row u of V (SpMM).  gt_calib_gather reads exactly those rows
+ * for the E edges of `indices` (int32 [E], values in [0, n_rows)), in CSR
+ * order, with the 16-byte loads and lane layout of the fused kernel, and
+ * does nothing else with them.  Every 32-bit word read is XOR-folded into
+ * *checksum (device memory owned by the caller, who sets it beforehand; 0
+ * for the checksum alone), so the result is the XOR over edges of the words
+ * of rows K[u] and V[u] and shows that each row was read whole.  K and V are
+ * n_rows rows of row_bytes bytes (512, 1024 or 2048: for example bf16 8 x 32,
+ * fp32 8 x 32, fp32 8 x 64), 16-byte aligned.  Asynchronous on `stream`.
+ * GT_EUNSUPPORTED for another row size or misaligned K or V, GT_EINVAL for
+ * negative sizes or a NULL array with E > 0.  Index values are not checked.
+ */
+int gt_calib_gather(const int32_t* indices, int64_t E, const void* K, const void* V, int64_t n_rows,
+                    int32_t row_bytes, uint32_t* checksum, hipStream_t stream);
+
 /* Static text for a status code. */
 const char* gt_status_string(int status);
 

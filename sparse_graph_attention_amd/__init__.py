@@ -17,6 +17,8 @@ The functions have the names of the C entry points declared in
 * ``gt_edge_softmax(indptr, scores, alpha=None)`` -- alpha [E][H] (fp32);
 * ``gt_spmm(indptr, indices, alpha, V, out=None)`` -- out [N][H][D];
 * ``gt_validate_csr(indptr, indices, N)`` -- device-side CSR check;
+* ``gt_calib_gather(indices, K, V)`` -- measurement aid: the K and V row
+  gathers of the attention alone, with their XOR checksum;
 * ``gt_sparse_mha_fwd_ex`` / ``gt_sparse_mha_bwd_ex`` -- with an additive
   logit bias [E][H], edge weights [E] and attention dropout (keyword
   arguments ``bias``, ``edge_weight``, ``dropout_p``, ``dropout_seed``);
@@ -57,6 +59,7 @@ EXPORTS = (
     "gt_edge_softmax",
     "gt_spmm",
     "gt_validate_csr",
+    "gt_calib_gather",
     "gt_coo_to_csr",
     "gt_plan_create",
     "gt_plan_create_coo",
@@ -111,6 +114,7 @@ def lib():
         L.gt_edge_softmax.argtypes = [_p, _p, _p, _i64, _i64, _i32, _p]
         L.gt_spmm.argtypes = [_p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_validate_csr.argtypes = [_p, _p, _i64, _i64, _p]
+        L.gt_calib_gather.argtypes = [_p, _i64, _p, _p, _i64, _i32, _p, _p]
         L.gt_coo_to_csr.argtypes = [_p, _p, _i64, _i64, _i64, _p, _p, _p, _p]
         L.gt_plan_create.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _p, ctypes.POINTER(_p)]
         L.gt_plan_create_coo.argtypes = [_p, _p, _i64, _i64, _i64, _i32, _p, ctypes.POINTER(_p)]
@@ -136,7 +140,7 @@ def lib():
                      "gt_sparse_mha_bwd_layout"):
             getattr(L, name).restype = ctypes.c_int
         for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
-                     "gt_config_set", "gt_profile_begin", "gt_profile_end"):
+                     "gt_calib_gather", "gt_config_set", "gt_profile_begin", "gt_profile_end"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -414,6 +418,25 @@ def gt_spmm(indptr, indices, alpha, V, out=None, stream=None):
     _check(lib().gt_spmm(_ptr(indptr), _ptr(indices), _ptr(alpha), _ptr(V), _ptr(out), N, E, H, D, _dtype_code(V),
                          _stream(stream)), "gt_spmm")
     return out
+
+
+def gt_calib_gather(indices, K, V, checksum=None, stream=None):
+    """Reads the K and V row of every edge's source as the fused kernel does and
+    nothing more (a measurement aid).  K and V are [n_rows][...] with rows of
+    512, 1024 or 2048 bytes; returns the int32 device tensor [1] holding the
+    XOR of all words read (XORed into `checksum` when one is given)."""
+    if indices.dtype != torch.int32 or indices.dim() != 1:
+        raise TypeError("indices must be a 1-D int32 tensor")
+    if K.shape != V.shape or K.dtype != V.dtype or not K.is_contiguous() or not V.is_contiguous():
+        raise ValueError("K and V must be contiguous tensors of one shape and dtype")
+    n_rows = K.shape[0]
+    row_bytes = K.numel() * K.element_size() // max(n_rows, 1)
+    if checksum is None:
+        checksum = torch.zeros(1, dtype=torch.int32, device=K.device)
+    _need_gpu(indices, K, V, checksum)
+    _check(lib().gt_calib_gather(_ptr(indices), indices.numel(), _ptr(K), _ptr(V), n_rows, row_bytes,
+                                 _ptr(checksum), _stream(stream)), "gt_calib_gather")
+    return checksum
 
 
 def gt_validate_csr(indptr, indices, N=None, stream=None):

@@ -1031,6 +1031,18 @@ int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     return run_bwd(a, at, &plan->tables, &plan->t_tables, stream);
 }
 
+int gt_calib_gather(const int32_t* indices, int64_t E, const void* K, const void* V, int64_t n_rows,
+                    int32_t row_bytes, uint32_t* checksum, hipStream_t stream) {
+    if (E < 0 || n_rows < 0) return fail(GT_EINVAL, "E and n_rows must be >= 0");
+    if (row_bytes != 512 && row_bytes != 1024 && row_bytes != 2048)
+        return fail(GT_EUNSUPPORTED, "row_bytes = %d: 512, 1024 or 2048 supported", row_bytes);
+    if (E == 0) return GT_OK;
+    if (!indices || !K || !V || !checksum) return fail(GT_EINVAL, "NULL array with E > 0");
+    if (!aligned16(K) || !aligned16(V)) return fail(GT_EUNSUPPORTED, "K and V must be 16-byte aligned");
+    hipError_t e = launch_calib_gather(indices, E, K, V, n_rows, row_bytes, checksum, stream);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "calibration gather launch");
+}
+
 int gt_validate_csr(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, hipStream_t stream) {
     if (N < 0 || E < 0) return fail(GT_EINVAL, "N and E must be >= 0");
     if (N >= ((int64_t)1 << 31)) return fail(GT_EINVAL, "N must be < 2^31");

@@ -117,6 +117,10 @@ hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const ui
 hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, int64_t* offsets, hipStream_t s);
 // rows[p] = the row of CSR position p.
 hipError_t launch_row_of_position(const int64_t* indptr, int64_t nrows, int64_t n, uint32_t* rows, hipStream_t s);
+// Measurement aid (calib.hip): the K and V rows of every edge, read as the
+// fused kernel reads them, XOR-folded into *sink.  row_bytes 512, 1024 or 2048.
+hipError_t launch_calib_gather(const int32_t* indices, int64_t E, const void* K, const void* V, int64_t n_rows,
+                               int row_bytes, uint32_t* sink, hipStream_t s);
 // CSR check: writes error flags into *flags (device memory, cleared first).
 hipError_t launch_validate(const int64_t* indptr, const int32_t* indices, int64_t N, int64_t E, uint32_t* flags,
                            hipStream_t s);

@@ -81,6 +81,17 @@ def test_unfused_reject():
     assert L.gt_edge_softmax(p, p, p, 4, 0, 8, S) == gt.GT_OK
 
 
+def test_calib_gather_rejects():
+    L = gt.lib()
+    p = ctypes.c_void_p(16)
+    assert L.gt_calib_gather(p, -1, p, p, 4, 2048, p, S) == gt.GT_EINVAL
+    assert L.gt_calib_gather(p, 4, p, p, 4, 100, p, S) == gt.GT_EUNSUPPORTED
+    assert L.gt_calib_gather(None, 4, p, p, 4, 2048, p, S) == gt.GT_EINVAL
+    assert L.gt_calib_gather(p, 4, p, p, 4, 2048, None, S) == gt.GT_EINVAL
+    assert L.gt_calib_gather(p, 4, ctypes.c_void_p(8), p, 4, 2048, p, S) == gt.GT_EUNSUPPORTED  # misaligned
+    assert L.gt_calib_gather(None, 0, None, None, 0, 512, None, S) == gt.GT_OK
+
+
 def test_config():
     old = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
     assert old == 512
