@@ -272,6 +272,16 @@ __device__ __forceinline__ int64_t drop_first_block(int64_t pos, int H, int hsel
     return hsel >= 0 ? (pos * H + hsel) / 4 : (pos * H) / 4;
 }
 
+// Batches whose keep bits one evaluation covers in a hot instance (edges per
+// wave epw, U per group, hc heads per edge), when a pass takes its edges in
+// consecutive positions: as many as fill one round of 64 lanes, so that the
+// wave's Philox work is not repeated for every batch with most lanes idle.
+constexpr int drop_batches_per_eval(int epw, int U, int hc) {
+    return 64 / (epw * U * (hc % 4 == 0 ? hc / 4 : (hc + 3) / 4 + 1)) > 1
+               ? 64 / (epw * U * (hc % 4 == 0 ? hc / 4 : (hc + 3) / 4 + 1))
+               : 1;
+}
+
 // Whether a batch fits the rounds (else each lane draws its own words).
 __device__ __forceinline__ bool drop_batched(int H, int hsel, int nslots) {
     return nslots * drop_bpe(H, hsel) <= 64 * kDropRounds;

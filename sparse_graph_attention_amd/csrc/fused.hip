@@ -46,6 +46,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     constexpr int kHc = (G_ && LPH_ && FULL) ? NC * G_ / LPH_ : 0;
     constexpr bool kBatched =
         kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * (kHc % 4 == 0 ? kHc / 4 : (kHc + 3) / 4 + 1) <= 64 * kDropRounds;
+    constexpr int kDropMB = kBatched ? drop_batches_per_eval(kWave / (G_ ? G_ : kWave), U, kHc) : 1;
     constexpr bool kSlots = kHc > 0 && (kWave / (G_ ? G_ : kWave)) * U * kHc <= 64 * kSlotRounds;
     // rounds of 64 values for a batch's bias and weights (exact for the hot instances)
     constexpr int kBR = kSlots ? ((kWave / G_) * U * kHc + 63) / 64 : kSlotRounds;
@@ -94,7 +95,9 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 
     const char* Kb = (const char*)a.K;
     const char* Vb = (const char*)a.V;
-    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+    DropBatch db;
+    int dph = 0;  // position of the batch among those its keep bits were drawn for
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U, dph = dph + 1 == kDropMB ? 0 : dph + 1) {
         int32_t u[U];
         bool ok[U];
 #pragma unroll
@@ -137,12 +140,12 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
-        DropBatch db;
         bool bdrop = false;
         if constexpr (XL) {
             bdrop = XL == 2 && (kBatched || drop_batched(a.H, -1, epw * U));
-            if (bdrop)
-                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, epw * U, lane,
+            // one evaluation covers kDropMB consecutive batches (consecutive edges)
+            if (bdrop && dph == 0)
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, kDropMB * epw * U, lane,
                                 [&](int k) { return eb + k; });
         }
 
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 float pv = p;  // dropout zeroes the weight, not its share of the normaliser
                 if constexpr (XL) {
                     if (XL == 2 && (kBatched || bdrop))
-                        pv = p * drop_mult(db, a.drop_scale, a.H, -1, grp + j * epw, ej(j), head[c]);
+                        pv = p * drop_mult(db, a.drop_scale, a.H, -1, dph * epw * U + grp + j * epw, ej(j), head[c]);
                     else if (XL == 2 && !kBatched)
                         pv = philox_hi32(a.drop_seed, (uint64_t)ej(j) * a.H + head[c]) >= a.drop_thresh
                                  ? p * a.drop_scale : 0.0f;
