@@ -385,8 +385,6 @@ int bwd_scratch_bytes(Args& a, Args& at, const Plan* tables, const Plan* t_table
     }
     bytes += partial_bytes(a.plan, a.H, HD) + partial_bytes(at.plan, a.H, 2 * HD);
     if (a.dew && !a.vec) bytes += align256(sizeof(float) * (size_t)a.E * a.H);
-    if (at.bias) bytes += align256(sizeof(float) * (size_t)a.E * a.H);  // bias in out-edge order
-    if (at.ew) bytes += align256(sizeof(float) * (size_t)a.E);           // weights in out-edge order
     *out = bytes;
     return GT_OK;
 }
@@ -418,17 +416,6 @@ int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStre
         a.dew_part = (float*)p;
         p += part_bytes;
     }
-    // the source pass reads bias and weights in its own edge order
-    float* bias_t = nullptr;
-    float* ew_t = nullptr;
-    if (at.bias) {
-        bias_t = (float*)p;
-        p += align256(sizeof(float) * (size_t)a.E * a.H);
-    }
-    if (at.ew) {
-        ew_t = (float*)p;
-        p += align256(sizeof(float) * (size_t)a.E);
-    }
     if (!tables) {
         p = carve_tables(p, a.plan);
         p = carve_tables(p, at.plan);
@@ -443,11 +430,6 @@ int run_bwd(Args& a, Args& at, const Plan* tables, const Plan* t_tables, hipStre
         if (e == hipSuccess) e = launch_plan(at, stream);
         if (e != hipSuccess) return hip_fail(e, "plan launch");
     }
-    if (bias_t) e = launch_permute_edges(at.t_perm, at.E, at.H, at.bias, bias_t, stream);
-    if (e == hipSuccess && ew_t) e = launch_permute_edges(at.t_perm, at.E, 1, at.ew, ew_t, stream);
-    if (e != hipSuccess) return hip_fail(e, "edge permutation launch");
-    at.bias_t = bias_t;
-    at.ew_t = ew_t;
     e = launch_bwd_dq(a, stream);
     if (e != hipSuccess) return hip_fail(e, "dQ kernel launch");
     e = launch_bwd_dkv(at, stream);

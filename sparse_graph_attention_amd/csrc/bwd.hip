@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     int32_t un[U], pn[U];  // destinations and (extended) their CSR positions
     if (e1 > e0) {
         load_ids<U>(idx, e0, grp, epw, e1, un);
-        if constexpr (XL == 2) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
+        if constexpr (XL) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
     }
 
     float kk[NC][VN], vv[NC][VN];
@@ -284,11 +284,12 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             u[j] = un[j];
-            if constexpr (XL == 2) ep[j] = pn[j];
+            if constexpr (XL) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
-        // per-edge inputs in out-edge order (copies made for this pass), so a
-        // batch's are contiguous like the destination pass's
+        // per-edge inputs at the out-edges' CSR positions ep (prefetched with
+        // the destinations): the batch's positions go round the lanes by
+        // shuffles, each lane loading one value per round
         float xw[U], xb[U][NC];
         SlotBatch<kBR> bb;
         SlotBatch<kWR> wb;
@@ -296,15 +297,24 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
         if constexpr (XL) {
             sb = kSlots || slot_batched(epw * U, a.H);
             if (sb) {
-                if (a.bias_t) slot_batch_load(bb, a.bias_t, eb, e1, epw * U, a.H, lane);
-                if (a.ew_t) slot_batch_load(wb, a.ew_t, eb, e1, epw * U, 1, lane);
+                auto pos_of = [&](int k) -> int64_t {  // slot k: ep[k / epw] of group k % epw
+                    int64_t r = 0;
+#pragma unroll
+                    for (int jj = 0; jj < U; ++jj) {
+                        const int v = __shfl(ep[jj], (k % epw) * G, kWave);
+                        if (jj == k / epw) r = v;
+                    }
+                    return r;
+                };
+                if (a.bias) slot_batch_load_at(bb, a.bias, e1 - eb, epw * U, a.H, lane, pos_of);
+                if (a.ew) slot_batch_load_at(wb, a.ew, e1 - eb, epw * U, 1, lane, pos_of);
             } else {
 #pragma unroll
-                for (int j = 0; j < U; ++j) {
-                    const int64_t jp = ok[j] ? eb + grp + (int64_t)j * epw : e0;
-                    xw[j] = a.ew_t ? a.ew_t[jp] : 1.0f;
+                for (int j = 0; j < U; ++j) {  // a clamped slot's ep is still a valid position
+                    xw[j] = a.ew ? a.ew[ep[j]] : 1.0f;
 #pragma unroll
-                    for (int c = 0; c < NC; ++c) xb[j][c] = a.bias_t ? a.bias_t[jp * a.H + head[c]] * kLog2e : 0.0f;
+                    for (int c = 0; c < NC; ++c)
+                        xb[j][c] = a.bias ? a.bias[(int64_t)ep[j] * a.H + head[c]] * kLog2e : 0.0f;
                 }
             }
         }
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) {
             load_ids<U>(idx, nb, grp, epw, e1, un);
-            if constexpr (XL == 2) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+            if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
         }
         bool bdrop = false;
         if constexpr (XL) {
@@ -365,8 +375,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
                 const float dlj = __shfl(st[j].y, gbase + head[c], kWave);
                 if constexpr (XL) {
                     const int k = grp + j * epw;
-                    const float w = sb ? (a.ew_t ? slot_batch_get(wb, k) : 1.0f) : xw[j];
-                    const float b = sb ? (a.bias_t ? slot_batch_get(bb, k * a.H + head[c]) * kLog2e : 0.0f) : xb[j][c];
+                    const float w = sb ? (a.ew ? slot_batch_get(wb, k) : 1.0f) : xw[j];
+                    const float b = sb ? (a.bias ? slot_batch_get(bb, k * a.H + head[c]) * kLog2e : 0.0f) : xb[j][c];
                     sd = __builtin_fmaf(sd, w, b);
                     const float p = ok[j] ? exp2_(sd - lsj) : 0.0f;
                     float keep = 1.0f;
@@ -570,7 +580,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
     int32_t un[U], pn[U];
     if (e1 > e0) {
         load_ids<U>(idx, e0, grp, epw, e1, un);
-        if constexpr (XL == 2) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
+        if constexpr (XL) load_ids<U>(a.t_perm, e0, grp, epw, e1, pn);
     }
     float kk[KD], vv[KD], dk[KD], dv[KD];
     bool act[KD];
@@ -588,16 +598,15 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
 #pragma unroll
         for (int j = 0; j < U; ++j) {
             u[j] = un[j];
-            if constexpr (XL == 2) ep[j] = pn[j];
+            if constexpr (XL) ep[j] = pn[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
         float xw[U], xb[U];
-        if constexpr (XL) {
+        if constexpr (XL) {  // per-edge inputs at the out-edges' CSR positions
 #pragma unroll
             for (int j = 0; j < U; ++j) {
-                const int64_t jp = ok[j] ? eb + grp + (int64_t)j * epw : e0;
-                xw[j] = a.ew_t ? a.ew_t[jp] : 1.0f;
-                xb[j] = a.bias_t ? a.bias_t[jp * a.H + h] * kLog2e : 0.0f;
+                xw[j] = a.ew ? a.ew[ep[j]] : 1.0f;
+                xb[j] = a.bias ? a.bias[(int64_t)ep[j] * a.H + h] * kLog2e : 0.0f;
             }
         }
         float qv[U][KD], gv[U][KD], ls[U], dl[U];
@@ -616,7 +625,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) {
             load_ids<U>(idx, nb, grp, epw, e1, un);
-            if constexpr (XL == 2) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
+            if constexpr (XL) load_ids<U>(a.t_perm, nb, grp, epw, e1, pn);
         }
         DropBatch db;
         bool bdrop = false;
@@ -870,22 +879,6 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
             st16(pa + HD + k, Vec<kF32>::pack(&dv[k]));
         }
     }
-}
-
-// Per-edge inputs in the source pass's order: dst[j][h] = src[perm[j]][h].
-__global__ __launch_bounds__(256) void permute_edges_kernel(const int32_t* __restrict__ perm, int64_t E, int H,
-                                                            const float* __restrict__ src, float* __restrict__ dst) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < E * H; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t j = i / H;
-        dst[i] = src[(int64_t)perm[j] * H + (i - j * H)];
-    }
-}
-
-hipError_t launch_permute_edges(const int32_t* perm, int64_t E, int H, const float* src, float* dst, hipStream_t s) {
-    if (E == 0) return hipSuccess;
-    const unsigned grid = (unsigned)std::min<int64_t>((E * H + 255) / 256, (int64_t)1 << 20);
-    permute_edges_kernel<<<grid, 256, 0, s>>>(perm, E, H, src, dst);
-    return hipGetLastError();
 }
 
 // dw[e] = sum over heads, in head order, of the per-head terms the scalar

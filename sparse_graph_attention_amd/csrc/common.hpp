@@ -361,6 +361,26 @@ __device__ __forceinline__ void slot_batch_load(SlotBatch<R>& b, const float* __
     }
 }
 
+// The same for slots at scattered edge positions: value (k, h) is
+// src[pos_of(k) * per + h] for the nvalid first slots (0 past them).
+// pos_of(k) must be called by every lane (it may use cross-lane shuffles).
+template <int R, typename PosOf>
+__device__ __forceinline__ void slot_batch_load_at(SlotBatch<R>& b, const float* __restrict__ src, int64_t nvalid,
+                                                   int nslots, int per, int lane, PosOf pos_of) {
+    b.rounds = (nslots * per + 63) >> 6;
+    const int64_t lim = nvalid * per;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        b.v[r] = 0.0f;
+        if (r < b.rounds) {
+            const int i = r * 64 + lane;
+            const int k = i / per;
+            const int64_t pos = pos_of(k < nslots ? k : 0);
+            if (i < lim) b.v[r] = src[pos * per + (i - k * per)];
+        }
+    }
+}
+
 // Value i = k * per + h of the batch; every lane must call it.
 template <int R>
 __device__ __forceinline__ float slot_batch_get(const SlotBatch<R>& b, int i) {

@@ -41,8 +41,6 @@ struct Args {
     uint32_t drop_thresh;   // keep iff the word's upper 32 bits >= this; 0: no dropout
     float drop_scale;       // 1 / (1 - p)
     const int32_t* t_perm;  // source pass: CSR position of each out-edge
-    const float* bias_t;    // source pass: bias in out-edge order ([E][H]), or nullptr
-    const float* ew_t;      // source pass: edge weights in out-edge order, or nullptr
     float* dbias;           // backward output [E][H] or nullptr
     float* dew;             // backward output [E] or nullptr
     float* dew_part;        // scratch [E][H]: per-head terms of dew (scalar layout)
@@ -63,8 +61,6 @@ struct Args {
 // Per node, src [A][B] -> dst [B][A] (elementwise; bf16 moved as 16-bit words).
 hipError_t launch_transpose_rows(const void* src, void* dst, int64_t N, int A, int B, int dtype, hipStream_t s);
 
-// dst[j][h] = src[perm[j]][h] for j < E, h < H.
-hipError_t launch_permute_edges(const int32_t* perm, int64_t E, int H, const float* src, float* dst, hipStream_t s);
 
 // Whether a launch needs the extended-logit kernels.
 inline bool extended(const Args& a) { return a.bias || a.ew || a.drop_thresh || a.dbias || a.dew; }
