@@ -220,12 +220,15 @@ int gt_sparse_mha_bwd_ex(const int64_t* indptr, const int32_t* indices, const in
  * dout, dQ, dK and dV; lse, bias and the other arrays are unchanged.
  * gt_sparse_mha_fwd_layout / gt_sparse_mha_bwd_layout are gt_sparse_mha_fwd_ex
  * / gt_sparse_mha_bwd_ex with a layout argument (GT_EINVAL for an unknown
- * one).  For GT_LAYOUT_NDH the forward and the backward without logit options
- * (and without dbias / dweight) run kernels of their own when H is a multiple
- * of the 16-byte vector (4 fp32 or 8 bf16 elements) with a power-of-two
- * quotient and D * H fits 64 vectors (1 KB); other shapes and the options go
- * through [N][H][D] copies in the per-stream scratch (transposed on the
- * device), with results bit-identical to the [N][H][D] calls.
+ * one).  For GT_LAYOUT_NDH, without logit options (and without dbias /
+ * dweight), kernels of their own serve shapes where H is a multiple of the
+ * 16-byte vector (4 fp32 or 8 bf16 elements) with a power-of-two quotient and
+ * a row fits 256 vectors (4 KB), when they are the faster route: always when
+ * a head of D elements is not a power-of-two number of 16-byte vectors, and
+ * for the forward also when a row's gathers are large against the cross-lane
+ * sums this layout needs.  Everything else goes through [N][H][D] copies in
+ * the per-stream scratch (transposed on the device), with results
+ * bit-identical to the [N][H][D] calls.
  *
  * (The tutorial also normalises along A[src, dst]'s rows, i.e. over each
  * source's out-edges with the source's query: that is these calls on the

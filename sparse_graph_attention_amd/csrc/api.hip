@@ -173,22 +173,45 @@ void choose_layout(Args& a, std::initializer_list<const void*> feats) {
     }
 }
 
-// The head-innermost kernel: a 16-byte vector holds VN heads of one d, the
-// vectors of a d are a power of two, and a row is at most 64 vectors.
+// The head-innermost kernels: a 16-byte vector holds VN heads of one d, the
+// vectors of a d are a power of two, and a row is at most 256 vectors (a
+// lane group of pow2ceil(R) lanes up to 64, then NC = ceil(R / 64) vectors
+// per lane of a 64-lane group).
 bool choose_layout_ndh(Args& a, std::initializer_list<const void*> feats) {
     const int vn = a.dtype == GT_F32 ? 4 : 8;
     if (a.H % vn != 0 || !pow2(a.H / vn)) return false;
     const int64_t R = (int64_t)a.D * (a.H / vn);
-    if (R > kWave) return false;
+    if (R > 4 * kWave) return false;
     for (const void* p : feats)
         if (!aligned16(p)) return false;
     a.vec = 2;
     a.ndh = 1;
     a.lph = a.H / vn;
     a.R = (int)R;
-    a.G = pow2ceil(R);
-    a.NC = 1;
+    a.G = R > kWave ? kWave : pow2ceil(R);
+    a.NC = (int)((R + a.G - 1) / a.G);
     return true;
+}
+
+// Whether the head-innermost kernels beat transposing into [N][H][D], run
+// with a layout chosen by choose_layout.  Their cost is the head sums: a lane
+// holds VN heads of one d, so each head's dot product takes VN * log2(G / HV)
+// cross-lane shuffles per edge, where [N][H][D] rows take a few DPP steps.
+// Measured: they win where [N][H][D] falls back to one wave per head (heads
+// not a power-of-two number of 16-byte vectors: fp32 8 x 10, 20 against 26 us
+// forward, 52 against 60 us backward); the forward also wins when a row's
+// gathers are large against its shuffles (fp32 8 x 64: 4 KB per edge for 20
+// shuffles, 12.2 against 16.9 ms), and loses when they are not (bf16 8 x 32:
+// 1 KB for 40 shuffles, 19.5 against 11 ms).  The backward, with two head
+// sums per edge in each pass, lost to the copies at both of those shapes.
+bool ndh_kernels_pay(const Args& a, bool forward) {
+    const int64_t hb = (int64_t)a.D * (a.dtype == GT_F32 ? 4 : 2);
+    if (!(hb % 16 == 0 && pow2(hb / 16) && (a.H * hb / 16 + kWave - 1) / kWave <= 4)) return true;
+    if (!forward) return false;
+    int steps = 0;
+    for (int64_t x = a.G / a.lph; x > 1; x >>= 1) ++steps;
+    const int shuffles = (a.dtype == GT_F32 ? 4 : 8) * steps;
+    return 2 * (int64_t)a.R * 16 >= 128 * (int64_t)shuffles;
 }
 
 int check_common(int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype) {
@@ -634,7 +657,9 @@ int gt_sparse_mha_fwd_layout(const int64_t* indptr, const int32_t* indices, cons
     set_scales(a);
     rc = set_options(a, opts);
     if (rc) return rc;
-    if (!extended(a) && choose_layout_ndh(a, {Q, K, V, out})) return run_fwd(a, nullptr, stream);
+    Args an = a;  // the head-innermost kernels' arguments, if they are used
+    if (!extended(a) && choose_layout_ndh(an, {Q, K, V, out}) && ndh_kernels_pay(an, true))
+        return run_fwd(an, nullptr, stream);
     // other shapes and the logit options: through [N][H][D] copies in scratch,
     // after the plan's part of it
     size_t pb = 0;
@@ -680,7 +705,9 @@ int gt_sparse_mha_bwd_layout(const int64_t* indptr, const int32_t* indices, cons
     rc = bwd_args(a, at, indptr, indices, t_indptr, t_indices, t_perm, Q, K, V, out, dout, lse, dQ, dK, dV, dbias,
                   dweight, N, N, E, H, D, dtype, opts);
     if (rc) return rc;
-    if (!extended(a) && choose_layout_ndh(a, {Q, K, V, out, dout, dQ, dK, dV})) {
+    Args an = a;  // the head-innermost kernels' arguments, if they are used
+    if (!extended(a) && choose_layout_ndh(an, {Q, K, V, out, dout, dQ, dK, dV}) && ndh_kernels_pay(an, false)) {
+        a = an;
         at.vec = a.vec;
         at.ndh = a.ndh;
         at.lph = a.lph;

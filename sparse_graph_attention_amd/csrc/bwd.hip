@@ -701,10 +701,11 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_scalar_kernel(const Args a) {
 
 // ------------------------------------------------------------ head-innermost layout
 //
-// Features [N][D][H]: lane gl of a group holds vector gl of a row (d = gl /
-// HV, heads (gl % HV) * VN .. +VN-1), as in the forward's fused_ndh_kernel;
-// per-head sums run over the lanes with the same gl % HV.  Partials of split
-// rows keep the row's [D][H] order; the merge adds them elementwise.
+// Features [N][D][H]: lane gl of a group holds vectors vi = c * G + gl, c <
+// NC, of a row (d = vi / HV, heads (vi % HV) * VN .. +VN-1), as in the
+// forward's fused_ndh_kernel; per-head sums add the lane's products over c,
+// then run over the lanes with the same gl % HV.  Partials of split rows keep
+// the row's [D][H] order; the merge adds them elementwise.
 
 // Sum over the lanes of a group that hold the same heads.
 __device__ __forceinline__ float ndh_head_sum(float x, int HV, int G) {
@@ -712,7 +713,7 @@ __device__ __forceinline__ float ndh_head_sum(float x, int HV, int G) {
     return x;
 }
 
-template <int DT, int U>
+template <int DT, int U, int NC>
 __global__ __launch_bounds__(kBlock) void bwd_dq_ndh_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -725,23 +726,36 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_ndh_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const bool act = gl < a.R;
     const int hg = gl & (HV - 1);
+    bool act[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) act[c] = c * G + gl < a.R;
     const int64_t rowbytes = (int64_t)a.R * 16;
     const int32_t* __restrict__ idx = a.indices;
 
     int32_t un[U];
     if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
     const U4 zero{0, 0, 0, 0};
-    float q[VN], g[VN], o[VN], dl[VN], ls[VN], acc[VN];
-    VT::unpack(act ? ld16((const char*)a.Q + row * rowbytes + gl * 16) : zero, q);
-    VT::unpack(act ? ld16((const char*)a.dO + row * rowbytes + gl * 16) : zero, g);
-    VT::unpack(act ? ld16((const char*)a.O + row * rowbytes + gl * 16) : zero, o);
+    float q[NC][VN], g[NC][VN], dl[VN], ls[VN], acc[NC][VN];
+#pragma unroll
+    for (int k = 0; k < VN; ++k) dl[k] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int64_t off = row * rowbytes + (c * G + gl) * 16;
+        float o[VN];
+        VT::unpack(act[c] ? ld16((const char*)a.Q + off) : zero, q[c]);
+        VT::unpack(act[c] ? ld16((const char*)a.dO + off) : zero, g[c]);
+        VT::unpack(act[c] ? ld16((const char*)a.O + off) : zero, o);
+#pragma unroll
+        for (int k = 0; k < VN; ++k) {
+            dl[k] = __builtin_fmaf(g[c][k], o[k], dl[k]);
+            acc[c][k] = 0.0f;
+        }
+    }
 #pragma unroll
     for (int k = 0; k < VN; ++k) {
-        dl[k] = ndh_head_sum(g[k] * o[k], HV, G);
+        dl[k] = ndh_head_sum(dl[k], HV, G);
         ls[k] = a.lse_in[row * a.H + hg * VN + k] * kLog2e;
-        acc[k] = 0.0f;
     }
     const char* Kb = (const char*)a.K;
     const char* Vb = (const char*)a.V;
@@ -753,47 +767,73 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_ndh_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
-        U4 kr[U], vr[U];
+        U4 kr[U][NC], vr[U][NC];
 #pragma unroll
-        for (int j = 0; j < U; ++j) kr[j] = (ok[j] && act) ? ld16(Kb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
+        for (int j = 0; j < U; ++j)
 #pragma unroll
-        for (int j = 0; j < U; ++j) vr[j] = (ok[j] && act) ? ld16(Vb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
+            for (int c = 0; c < NC; ++c)
+                kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : zero;
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : zero;
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            float kf[VN], vf[VN];
-            VT::unpack(kr[j], kf);
-            VT::unpack(vr[j], vf);
+            float kf[NC][VN], sd[VN], dd[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) sd[k] = dd[k] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float vf[VN];
+                VT::unpack(kr[j][c], kf[c]);
+                VT::unpack(vr[j][c], vf);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) {
+                    sd[k] = __builtin_fmaf(q[c][k], kf[c][k], sd[k]);
+                    dd[k] = __builtin_fmaf(g[c][k], vf[k], dd[k]);
+                }
+            }
 #pragma unroll
             for (int k = 0; k < VN; ++k) {
-                const float sd = ndh_head_sum(q[k] * kf[k], HV, G) * a.qscale;
-                const float dd = ndh_head_sum(g[k] * vf[k], HV, G);
-                const float p = ok[j] ? exp2_(sd - ls[k]) : 0.0f;
-                acc[k] = __builtin_fmaf(p * (dd - dl[k]), kf[k], acc[k]);
+                const float s2 = ndh_head_sum(sd[k], HV, G) * a.qscale;
+                const float da = ndh_head_sum(dd[k], HV, G);
+                const float p = ok[j] ? exp2_(s2 - ls[k]) : 0.0f;
+                const float ds = p * (da - dl[k]);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) acc[c][k] = __builtin_fmaf(ds, kf[c][k], acc[c][k]);
             }
         }
     }
     for (int off = G; off < kWave; off <<= 1)
 #pragma unroll
-        for (int k = 0; k < VN; ++k) acc[k] += __shfl_xor(acc[k], off, kWave);
-    if (grp != 0 || !act) return;
-    if (gl < HV)
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int k = 0; k < VN; ++k) acc[c][k] += __shfl_xor(acc[c][k], off, kWave);
+    if (grp != 0) return;
+    if (gl < HV)  // the lanes of d = 0 (in c = 0) carry each head's (lse, delta) once
 #pragma unroll
         for (int k = 0; k < VN; ++k) a.stats[row * a.H + hg * VN + k] = make_float2(ls[k], dl[k]);
-    if (it.slot < 0) {
-        float r[VN];
 #pragma unroll
-        for (int k = 0; k < VN; ++k) r[k] = acc[k] * a.kscale;
-        st16((char*)a.dQ + row * rowbytes + gl * 16, VT::pack(r));
-    } else {
-        float* pa = a.plan.pacc + it.slot * (int64_t)a.H * a.D + (int64_t)gl * VN;
+    for (int c = 0; c < NC; ++c) {
+        if (!act[c]) continue;
+        const int vi = c * G + gl;
+        if (it.slot < 0) {
+            float r[VN];
 #pragma unroll
-        for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[k]));
+            for (int k = 0; k < VN; ++k) r[k] = acc[c][k] * a.kscale;
+            st16((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(r));
+        } else {
+            float* pa = a.plan.pacc + it.slot * (int64_t)a.H * a.D + (int64_t)vi * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
+        }
     }
 }
 
-template <int DT, int U>
+template <int DT, int U, int NC>
 __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -806,19 +846,25 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const bool act = gl < a.R;
     const int hg = gl & (HV - 1);
+    bool act[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) act[c] = c * G + gl < a.R;
     const int64_t rowbytes = (int64_t)a.R * 16;
     const int32_t* __restrict__ idx = a.indices;
 
     int32_t un[U];
     if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
     const U4 zero{0, 0, 0, 0};
-    float kk[VN], vv[VN], dk[VN], dv[VN];
-    VT::unpack(act ? ld16((const char*)a.K + src * rowbytes + gl * 16) : zero, kk);
-    VT::unpack(act ? ld16((const char*)a.V + src * rowbytes + gl * 16) : zero, vv);
+    float kk[NC][VN], vv[NC][VN], dk[NC][VN], dv[NC][VN];
 #pragma unroll
-    for (int k = 0; k < VN; ++k) dk[k] = dv[k] = 0.0f;
+    for (int c = 0; c < NC; ++c) {
+        const int64_t off = src * rowbytes + (c * G + gl) * 16;
+        VT::unpack(act[c] ? ld16((const char*)a.K + off) : zero, kk[c]);
+        VT::unpack(act[c] ? ld16((const char*)a.V + off) : zero, vv[c]);
+#pragma unroll
+        for (int k = 0; k < VN; ++k) dk[c][k] = dv[c][k] = 0.0f;
+    }
     const char* Qb = (const char*)a.Q;
     const char* Gb = (const char*)a.dO;
     for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
@@ -829,54 +875,83 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
-        U4 qr[U], gr[U];
+        U4 qr[U][NC], gr[U][NC];
         float2 st[U][VN];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            const bool go = ok[j] && act;
-            qr[j] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
-            gr[j] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + gl * 16) : zero;
 #pragma unroll
-            for (int k = 0; k < VN; ++k)
-                st[j][k] = ok[j] ? a.stats[(int64_t)u[j] * a.H + hg * VN + k] : make_float2(0.0f, 0.0f);
+            for (int c = 0; c < NC; ++c) {
+                const bool go = ok[j] && act[c];
+                qr[j][c] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : zero;
+                gr[j][c] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : zero;
+            }
+            // the VN (lse, delta) pairs of the lane's heads are contiguous: 16-byte loads
+            const char* sp = (const char*)(a.stats + (int64_t)u[j] * a.H + hg * VN);
+#pragma unroll
+            for (int k = 0; k < VN; k += 2) {
+                const U4 t = ok[j] ? ld16(sp + k * 8) : U4{0, 0, 0, 0};
+                st[j][k] = make_float2(__uint_as_float(t.x), __uint_as_float(t.y));
+                st[j][k + 1] = make_float2(__uint_as_float(t.z), __uint_as_float(t.w));
+            }
         }
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            float qf[VN], gf[VN];
-            VT::unpack(qr[j], qf);
-            VT::unpack(gr[j], gf);
+            float qf[NC][VN], gf[NC][VN], sd[VN], dd[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) sd[k] = dd[k] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                VT::unpack(qr[j][c], qf[c]);
+                VT::unpack(gr[j][c], gf[c]);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) {
+                    sd[k] = __builtin_fmaf(qf[c][k], kk[c][k], sd[k]);
+                    dd[k] = __builtin_fmaf(gf[c][k], vv[c][k], dd[k]);
+                }
+            }
 #pragma unroll
             for (int k = 0; k < VN; ++k) {
-                const float sd = ndh_head_sum(qf[k] * kk[k], HV, G) * a.qscale;
-                const float dd = ndh_head_sum(gf[k] * vv[k], HV, G);
-                const float p = ok[j] ? exp2_(sd - st[j][k].x) : 0.0f;
-                dv[k] = __builtin_fmaf(p, gf[k], dv[k]);
-                dk[k] = __builtin_fmaf(p * (dd - st[j][k].y), qf[k], dk[k]);
+                const float s2 = ndh_head_sum(sd[k], HV, G) * a.qscale;
+                const float da = ndh_head_sum(dd[k], HV, G);
+                const float p = ok[j] ? exp2_(s2 - st[j][k].x) : 0.0f;
+                const float ds = p * (da - st[j][k].y);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    dv[c][k] = __builtin_fmaf(p, gf[c][k], dv[c][k]);
+                    dk[c][k] = __builtin_fmaf(ds, qf[c][k], dk[c][k]);
+                }
             }
         }
     }
     for (int off = G; off < kWave; off <<= 1)
 #pragma unroll
-        for (int k = 0; k < VN; ++k) {
-            dk[k] += __shfl_xor(dk[k], off, kWave);
-            dv[k] += __shfl_xor(dv[k], off, kWave);
-        }
-    if (grp != 0 || !act) return;
-    if (it.slot < 0) {
-        float r[VN];
+        for (int c = 0; c < NC; ++c)
 #pragma unroll
-        for (int k = 0; k < VN; ++k) r[k] = dk[k] * a.kscale;
-        st16((char*)a.dK + src * rowbytes + gl * 16, VT::pack(r));
-        st16((char*)a.dV + src * rowbytes + gl * 16, VT::pack(dv));
-    } else {
-        const int64_t HD = (int64_t)a.H * a.D;
-        float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)gl * VN;
+            for (int k = 0; k < VN; ++k) {
+                dk[c][k] += __shfl_xor(dk[c][k], off, kWave);
+                dv[c][k] += __shfl_xor(dv[c][k], off, kWave);
+            }
+    if (grp != 0) return;
+    const int64_t HD = (int64_t)a.H * a.D;
 #pragma unroll
-        for (int k = 0; k < VN; k += 4) {
-            st16(pa + k, Vec<kF32>::pack(&dk[k]));
-            st16(pa + HD + k, Vec<kF32>::pack(&dv[k]));
+    for (int c = 0; c < NC; ++c) {
+        if (!act[c]) continue;
+        const int vi = c * G + gl;
+        if (it.slot < 0) {
+            float r[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) r[k] = dk[c][k] * a.kscale;
+            st16((char*)a.dK + src * rowbytes + vi * 16, VT::pack(r));
+            st16((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
+        } else {
+            float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)vi * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) {
+                st16(pa + k, Vec<kF32>::pack(&dk[c][k]));
+                st16(pa + HD + k, Vec<kF32>::pack(&dv[c][k]));
+            }
         }
     }
 }
@@ -900,7 +975,12 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     hipError_t err;
     if (a0.vec == 2) {  // head-innermost layout (plain logits only)
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
-            bwd_dq_ndh_kernel<DT, DT == kF32 ? 4 : 2><<<dim3(gx), block, 0, s>>>(a);
+            switch (a.NC) {
+                case 1: bwd_dq_ndh_kernel<DT, DT == kF32 ? 4 : 2, 1><<<dim3(gx), block, 0, s>>>(a); break;
+                case 2: bwd_dq_ndh_kernel<DT, DT == kF32 ? 4 : 2, 2><<<dim3(gx), block, 0, s>>>(a); break;
+                case 3: bwd_dq_ndh_kernel<DT, 1, 3><<<dim3(gx), block, 0, s>>>(a); break;
+                default: bwd_dq_ndh_kernel<DT, 1, 4><<<dim3(gx), block, 0, s>>>(a); break;
+            }
         });
     } else if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
@@ -948,7 +1028,12 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     hipError_t err;
     if (a0.vec == 2) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
-            bwd_dkv_ndh_kernel<DT, DT == kF32 ? 4 : 2><<<dim3(gx), block, 0, s>>>(a);
+            switch (a.NC) {
+                case 1: bwd_dkv_ndh_kernel<DT, DT == kF32 ? 4 : 2, 1><<<dim3(gx), block, 0, s>>>(a); break;
+                case 2: bwd_dkv_ndh_kernel<DT, DT == kF32 ? 2 : 1, 2><<<dim3(gx), block, 0, s>>>(a); break;
+                case 3: bwd_dkv_ndh_kernel<DT, 1, 3><<<dim3(gx), block, 0, s>>>(a); break;
+                default: bwd_dkv_ndh_kernel<DT, 1, 4><<<dim3(gx), block, 0, s>>>(a); break;
+            }
         });
     } else if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {

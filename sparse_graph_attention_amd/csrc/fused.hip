@@ -396,14 +396,17 @@ __global__ __launch_bounds__(kBlock) void fused_scalar_kernel(const Args a) {
 // Features [N][D][H] ("Graph Transformer in a Nutshell", SparseMHA.forward:
 // q, k, v reshaped to [N, dh, nh]).  A 16-byte vector of a row then holds VN
 // consecutive heads of one d, so a lane group covers all heads of an edge at
-// once: lane gl holds vector gl (d = gl / HV, heads (gl % HV) * VN .. +VN-1,
-// HV = H / VN a power of two, R = D * HV <= 64 vectors, G = pow2ceil(R)).  A
-// head's dot product sums the lane products over the lanes with the same
-// gl % HV (xor offsets HV .. G/2); every lane keeps VN running softmax states,
-// one per head it holds.  For the tutorial's shape (H 8, D 10, fp32) a row is
-// 20 vectors, a group 32 lanes and a wave takes two edges at a time, where the
-// [N][H][D] layout needs one wave per head with 10-element heads.
-template <int DT, int U>
+// once: lane gl holds vectors vi = c * G + gl, c < NC (d = vi / HV, heads
+// (vi % HV) * VN .. +VN-1, HV = H / VN a power of two, R = D * HV <= 256
+// vectors; G = pow2ceil(R) when R <= 64, else 64 with NC = ceil(R / 64)).
+// Since G is a multiple of HV, a lane holds the same heads in every c.  A
+// head's dot product adds the lane's products over c, then over the lanes
+// with the same gl % HV (xor offsets HV .. G/2); every lane keeps VN running
+// softmax states, one per head it holds.  For the tutorial's shape (H 8,
+// D 10, fp32) a row is 20 vectors, a group 32 lanes and a wave takes two
+// edges at a time, where the [N][H][D] layout needs one wave per head with
+// 10-element heads.
+template <int DT, int U, int NC>
 __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
     using VT = Vec<DT>;
     constexpr int VN = VT::n;
@@ -417,21 +420,26 @@ __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const bool act = gl < a.R;
     const int hg = gl & (HV - 1);
+    bool act[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) act[c] = c * G + gl < a.R;
     const int64_t rowbytes = (int64_t)a.R * 16;
     const int32_t* __restrict__ idx = a.indices;
 
     int32_t un[U];
     if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
-    float q[VN];
-    VT::unpack(act ? ld16((const char*)a.Q + row * rowbytes + gl * 16) : U4{0, 0, 0, 0}, q);
-    float m[VN], l[VN], acc[VN];
+    float q[NC][VN];
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+        VT::unpack(act[c] ? ld16((const char*)a.Q + row * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0}, q[c]);
+    float m[VN], l[VN], acc[NC][VN];
 #pragma unroll
     for (int k = 0; k < VN; ++k) {
         m[k] = -INFINITY;
         l[k] = 0.0f;
-        acc[k] = 0.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c][k] = 0.0f;
     }
     const char* Kb = (const char*)a.K;
     const char* Vb = (const char*)a.V;
@@ -443,20 +451,31 @@ __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
             u[j] = un[j];
             ok[j] = eb + grp + (int64_t)j * epw < e1;
         }
-        U4 kr[U], vr[U];
+        U4 kr[U][NC], vr[U][NC];
 #pragma unroll
-        for (int j = 0; j < U; ++j) kr[j] = (ok[j] && act) ? ld16(Kb + (int64_t)u[j] * rowbytes + gl * 16) : U4{0, 0, 0, 0};
+        for (int j = 0; j < U; ++j)
 #pragma unroll
-        for (int j = 0; j < U; ++j) vr[j] = (ok[j] && act) ? ld16(Vb + (int64_t)u[j] * rowbytes + gl * 16) : U4{0, 0, 0, 0};
+            for (int c = 0; c < NC; ++c)
+                kr[j][c] = (ok[j] && act[c]) ? ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+#pragma unroll
+        for (int j = 0; j < U; ++j)
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+                vr[j][c] = (ok[j] && act[c]) ? ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
         float s[U][VN];
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            float kf[VN];
-            VT::unpack(kr[j], kf);
 #pragma unroll
-            for (int k = 0; k < VN; ++k) s[j][k] = q[k] * kf[k];
+            for (int k = 0; k < VN; ++k) s[j][k] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float kf[VN];
+                VT::unpack(kr[j][c], kf);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) s[j][k] = __builtin_fmaf(q[c][k], kf[k], s[j][k]);
+            }
             for (int off = HV; off < G; off <<= 1)
 #pragma unroll
                 for (int k = 0; k < VN; ++k) s[j][k] += __shfl_xor(s[j][k], off, kWave);
@@ -471,18 +490,24 @@ __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
             const float mn = fmaxf(m[k], mb);
             const float sc = rescale(m[k], mn);
             l[k] *= sc;
-            acc[k] *= sc;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) acc[c][k] *= sc;
             m[k] = mn;
         }
 #pragma unroll
         for (int j = 0; j < U; ++j) {
-            float vf[VN];
-            VT::unpack(vr[j], vf);
+            float p[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) {
-                const float p = ok[j] ? exp2_(s[j][k] - m[k]) : 0.0f;
-                l[k] += p;
-                acc[k] = __builtin_fmaf(p, vf[k], acc[k]);
+                p[k] = ok[j] ? exp2_(s[j][k] - m[k]) : 0.0f;
+                l[k] += p[k];
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                float vf[VN];
+                VT::unpack(vr[j][c], vf);
+#pragma unroll
+                for (int k = 0; k < VN; ++k) acc[c][k] = __builtin_fmaf(p[k], vf[k], acc[c][k]);
             }
         }
     }
@@ -491,21 +516,28 @@ __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
         for (int k = 0; k < VN; ++k) {
             const float mo = __shfl_xor(m[k], off, kWave);
             const float lo = __shfl_xor(l[k], off, kWave);
-            const float ao = __shfl_xor(acc[k], off, kWave);
             const float mn = fmaxf(m[k], mo);
             const float sa = rescale(m[k], mn), sb = rescale(mo, mn);
             l[k] = l[k] * sa + lo * sb;
-            acc[k] = acc[k] * sa + ao * sb;
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const float ao = __shfl_xor(acc[c][k], off, kWave);
+                acc[c][k] = acc[c][k] * sa + ao * sb;
+            }
             m[k] = mn;
         }
     }
-    if (grp != 0 || !act) return;
-    const bool first_d = gl < HV;  // the lanes of d = 0 carry each head's (m, l) once
+    if (grp != 0) return;
+    const bool first_d = gl < HV;  // the lanes of d = 0 (in c = 0) carry each head's (m, l) once
     if (it.slot < 0) {
-        float o[VN];
 #pragma unroll
-        for (int k = 0; k < VN; ++k) o[k] = l[k] > 0.0f ? acc[k] / l[k] : 0.0f;
-        st16_nt((char*)a.out + row * rowbytes + gl * 16, VT::pack(o));
+        for (int c = 0; c < NC; ++c) {
+            if (!act[c]) continue;
+            float o[VN];
+#pragma unroll
+            for (int k = 0; k < VN; ++k) o[k] = l[k] > 0.0f ? acc[c][k] / l[k] : 0.0f;
+            st16_nt((char*)a.out + row * rowbytes + (c * G + gl) * 16, VT::pack(o));
+        }
         if (a.lse_out && first_d)
 #pragma unroll
             for (int k = 0; k < VN; ++k) a.lse_out[row * a.H + hg * VN + k] = lse_of(m[k], l[k]);
@@ -517,9 +549,13 @@ __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
                 a.plan.pm[it.slot * a.H + hg * VN + k] = m[k];
                 a.plan.pl[it.slot * a.H + hg * VN + k] = l[k];
             }
-        float* pa = a.plan.pacc + it.slot * HD + (int64_t)gl * VN;
 #pragma unroll
-        for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[k]));
+        for (int c = 0; c < NC; ++c) {
+            if (!act[c]) continue;
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)(c * G + gl) * VN;
+#pragma unroll
+            for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
+        }
     }
 }
 
@@ -627,7 +663,12 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     if (a0.vec == 2) {  // head-innermost layout (plain logits only)
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
-            fused_ndh_kernel<DT, 4><<<dim3(gx), block, 0, s>>>(a);
+            switch (a.NC) {
+                case 1: fused_ndh_kernel<DT, 4, 1><<<dim3(gx), block, 0, s>>>(a); break;
+                case 2: fused_ndh_kernel<DT, DT == kF32 ? 4 : 2, 2><<<dim3(gx), block, 0, s>>>(a); break;
+                case 3: fused_ndh_kernel<DT, 2, 3><<<dim3(gx), block, 0, s>>>(a); break;
+                default: fused_ndh_kernel<DT, 2, 4><<<dim3(gx), block, 0, s>>>(a); break;
+            }
         });
     }
     if (a0.vec) {
