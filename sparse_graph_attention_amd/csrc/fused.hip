@@ -573,9 +573,84 @@ __global__ __launch_bounds__(256) void transpose_rows_kernel(const T* __restrict
     }
 }
 
+// The same through LDS, for nodes of a whole number of 16-byte vectors: a
+// block loads a tile of whole consecutive nodes with 16-byte loads, stores it
+// in LDS as [node][A][pitch] 32-bit words (pitch = B padded to an odd count,
+// against bank conflicts when read down a column), then writes the
+// transposed tile with 16-byte stores, so both sides are coalesced.
+constexpr int kTrTileWords = 8192;  // 32 KB of LDS per block
+
+template <typename T>
+__global__ __launch_bounds__(256) void transpose_tiles_kernel(const T* __restrict__ src, T* __restrict__ dst,
+                                                               int64_t N, int A, int B, int pitch, int npt) {
+    __shared__ uint32_t lds[kTrTileWords];
+    constexpr int VE = 16 / (int)sizeof(T);  // elements per 16-byte vector
+    const int64_t AB = (int64_t)A * B;
+    const int nodewords = A * pitch;
+    for (int64_t n0 = (int64_t)blockIdx.x * npt; n0 < N; n0 += (int64_t)gridDim.x * npt) {
+        const int nn = (int)(N - n0 < npt ? N - n0 : npt);
+        const int64_t nvec = nn * AB / VE;
+        const char* sp = (const char*)(src + n0 * AB);
+        for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x) {
+            const U4 w = ld16(sp + v * 16);
+            const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+            const int64_t e = v * VE;
+            const int nl = (int)(e / AB);
+            const int r = (int)(e - nl * AB);
+            int x = r / B, y = r - x * B;  // src [A][B]: row x, column y
+#pragma unroll
+            for (int i = 0; i < VE; ++i) {
+                const uint32_t bits = sizeof(T) == 4 ? wd[i] : (wd[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+                lds[nl * nodewords + x * pitch + y] = bits;
+                if (++y == B) {
+                    y = 0;
+                    ++x;
+                }
+            }
+        }
+        __syncthreads();
+        char* dp = (char*)(dst + n0 * AB);
+        for (int64_t v = threadIdx.x; v < nvec; v += blockDim.x) {
+            const int64_t o = v * VE;
+            const int nl = (int)(o / AB);
+            const int r = (int)(o - nl * AB);
+            int y = r / A, x = r - y * A;  // dst [B][A]: row y, column x
+            uint32_t wd[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < VE; ++i) {
+                const uint32_t bits = lds[nl * nodewords + x * pitch + y];
+                if (sizeof(T) == 4)
+                    wd[i] = bits;
+                else
+                    wd[i / 2] |= bits << (16 * (i & 1));
+                if (++x == A) {
+                    x = 0;
+                    ++y;
+                }
+            }
+            st16(dp + v * 16, U4{wd[0], wd[1], wd[2], wd[3]});
+        }
+        __syncthreads();
+    }
+}
+
 hipError_t launch_transpose_rows(const void* src, void* dst, int64_t N, int A, int B, int dtype, hipStream_t s) {
     const int64_t n = N * A * B;
     if (n == 0) return hipSuccess;
+    const int esize = dtype == kF32 ? 4 : 2;
+    const int pitch = B % 2 == 0 ? B + 1 : B + 2;
+    const bool tiled = ((int64_t)A * B * esize) % 16 == 0 && ((uintptr_t)src & 15) == 0 && ((uintptr_t)dst & 15) == 0 &&
+                       (int64_t)A * pitch <= kTrTileWords;
+    if (tiled) {
+        const int npt = kTrTileWords / (A * pitch);
+        const unsigned grid = (unsigned)std::min<int64_t>((N + npt - 1) / npt, (int64_t)1 << 16);
+        if (dtype == kF32)
+            transpose_tiles_kernel<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, N, A, B, pitch, npt);
+        else
+            transpose_tiles_kernel<uint16_t><<<grid, 256, 0, s>>>((const uint16_t*)src, (uint16_t*)dst, N, A, B, pitch,
+                                                                  npt);
+        return hipGetLastError();
+    }
     const unsigned grid = (unsigned)std::min<int64_t>((n + 255) / 256, (int64_t)1 << 20);
     if (dtype == kF32)
         transpose_rows_kernel<float><<<grid, 256, 0, s>>>((const float*)src, (float*)dst, n, A, B);
