@@ -1,13 +1,13 @@
 """The head-innermost feature layout [N][D][H] ("Graph Transformer in a
 Nutshell", SparseMHA.forward reshapes q, k, v to [N, dh, nh]) on the GPU.
 
-* Shapes the head-innermost kernels take (H a multiple of the 16-byte vector
-  with a power-of-two quotient, D*H within 4 KB): out and lse against the
-  oracle with the forward tolerances, and dQ, dK, dV against the oracle with
-  the backward's bound tolerances, whole rows and split rows.
-* Other shapes and the logit options run the [N][H][D] kernels on transposed
-  copies: bit-identical to the [N][H][D] calls (and the backward of the other
-  shapes is held to the oracle as well).
+* Every shape: out and lse against the oracle with the forward tolerances,
+  and dQ, dK, dV against the oracle with the backward's bound tolerances,
+  whole rows and split rows.  Shapes the head-innermost kernels can take (H a
+  multiple of the 16-byte vector with a power-of-two quotient, D*H within
+  4 KB) run them or the copies route, whichever the library's cost rule picks.
+* Shapes outside that range and the logit options always run the [N][H][D]
+  kernels on transposed copies: bit-identical to the [N][H][D] calls.
 The oracle works on [N][H][D]; a layout is a permutation of each row, so the
 expected values are the oracle's, permuted.
 """
