@@ -558,6 +558,8 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
+            # HBM bytes counted by rocprofv3 over the same kernel's live average duration
+            "traffic_GBps": None if traffic is None else traffic / (kern_avg_ms * 1e-3) / 1e9,
             "kernel": "fused attention kernel",
             "kernel_ms": kern_avg_ms,
             "algorithmic_bytes": alg,
