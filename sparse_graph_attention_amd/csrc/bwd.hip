@@ -205,7 +205,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
             float o[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * a.kscale;
-            st16((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(o));
+            st16_nt((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(o));
         } else {
             float* pa = a.plan.pacc + it.slot * HD + (int64_t)vi * VN;
 #pragma unroll
@@ -420,8 +420,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
             float o[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = dk[c][k] * a.kscale;
-            st16((char*)a.dK + src * rowbytes + vi * 16, VT::pack(o));
-            st16((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
+            st16_nt((char*)a.dK + src * rowbytes + vi * 16, VT::pack(o));
+            st16_nt((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
         } else {
             float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)vi * VN;
 #pragma unroll
@@ -824,7 +824,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_ndh_kernel(const Args a) {
             float r[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) r[k] = acc[c][k] * a.kscale;
-            st16((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(r));
+            st16_nt((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(r));
         } else {
             float* pa = a.plan.pacc + it.slot * (int64_t)a.H * a.D + (int64_t)vi * VN;
 #pragma unroll
@@ -943,8 +943,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
             float r[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) r[k] = dk[c][k] * a.kscale;
-            st16((char*)a.dK + src * rowbytes + vi * 16, VT::pack(r));
-            st16((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
+            st16_nt((char*)a.dK + src * rowbytes + vi * 16, VT::pack(r));
+            st16_nt((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
         } else {
             float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)vi * VN;
 #pragma unroll
