@@ -418,6 +418,9 @@ __device__ __forceinline__ U4 ld16_nt(const void* p) {
     return U4{v.x, v.y, v.z, v.w};
 }
 
+// One float with the non-temporal hint (streamed output, not re-read soon).
+__device__ __forceinline__ void st_nt(float* p, float v) { __builtin_nontemporal_store(v, p); }
+
 __device__ __forceinline__ void st16_nt(void* p, U4 v) {
     u32x4 w = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));

@@ -92,7 +92,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
                 // every lane of the head's segment ends with the same sum
                 dd[j][c] = kHot ? seg_sum_c<LPH_>(d) : seg_sum(d, lph);
                 if (!kHot && ok[j] && writer[c])
-                    a.scores_out[(eb + grp + (int64_t)j * epw) * a.H + head[c]] = dd[j][c] * a.qscale;
+                    st_nt(&a.scores_out[(eb + grp + (int64_t)j * epw) * a.H + head[c]], dd[j][c] * a.qscale);
             }
         if constexpr (kHot) {
             // pack: in each (group, head) segment, the lane at position k holds
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
                     const float t = __shfl(x[p], src, kWave);
                     if (p == i / LPH_) val = t;
                 }
-                if (s < kS && s < lim) a.scores_out[eb * kH + s] = val * a.qscale;
+                if (s < kS && s < lim) st_nt(&a.scores_out[eb * kH + s], val * a.qscale);
             }
         }
     }
@@ -174,7 +174,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_scalar_kernel(const Args a) {
 #pragma unroll
             for (int k = 0; k < KD; ++k) d = __builtin_fmaf(q[k], kv[j][k], d);
             d = seg_sum(d, G);
-            if (ok[j] && gl == 0) a.scores_out[(e + (int64_t)j * epw) * a.H + h] = d * a.qscale;
+            if (ok[j] && gl == 0) st_nt(&a.scores_out[(e + (int64_t)j * epw) * a.H + h], d * a.qscale);
         }
     }
 }
