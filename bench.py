@@ -15,7 +15,7 @@ sample of the same workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan] [--no-variants]
-                  [--no-layout] [--no-ceiling]
+                  [--no-layout] [--no-ceiling] [--no-shards]
                   [--calib-copy]
 
 Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM),
@@ -24,7 +24,8 @@ its transpose, the forward on a plan), and the forward and backward with an
 additive bias, edge weights and attention dropout, each event-timed on the
 same inputs, and the forward with head-innermost [N][D][H] features; and the
 achievable ceiling: the K and V row gathers alone (gt_calib_gather) and a
-plain device copy.
+plain device copy; and one GPU's share of an 8-way row-sharded run (each
+shard's forward and backward on a plan with all N nodes as sources).
 """
 import argparse
 import hashlib
@@ -387,6 +388,59 @@ def time_ceiling(gt, t, w, kern_ms, reps=10, copy_gib=1.0):
     return res
 
 
+def time_shards(gt, t, w, parts=8, reps=5):
+    """One GPU's share of a row-sharded run: the rows cut into `parts` ranges of
+    about E/parts edges each; every shard's plan has its rows as destinations
+    and all N nodes as sources (K and V whole, as after an all-gather), and its
+    forward (gt_sparse_mha_fwd_plan) and backward (gt_sparse_mha_bwd_plan) are
+    event-timed on this GPU at that shape.  The exchange of K/V and of the
+    dK/dV shares between GPUs is not included."""
+    import numpy as np
+    import torch
+
+    import gtgen
+
+    dev = t["Q"].device
+    N, E = w["N"], w["E"]
+    ip = w["indptr"]
+    cuts = np.searchsorted(ip, np.linspace(0, E, parts + 1)[1:-1])
+    bounds = [0, *cuts.tolist(), N]
+    g = gtgen.make_grad(N, w["H"], w["D"], w["dtype"], seed=11)
+    dO = (torch.from_numpy(g.view(np.int16)).to(dev).view(torch.bfloat16) if g.dtype == np.uint16
+          else torch.from_numpy(g).to(dev))
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    fwd, bwd, edges = [], [], []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        sip = torch.from_numpy(ip[a:b + 1] - ip[a]).to(dev)
+        six = torch.from_numpy(np.ascontiguousarray(w["indices"][ip[a]:ip[b]])).to(dev)
+        plan = gt.gt_plan_create(sip, six, n_src=N, transpose=True)
+        Qs, dOs = t["Q"][a:b], dO[a:b]
+        out, lse = gt.gt_sparse_mha_fwd_plan(plan, Qs, t["K"], t["V"], want_lse=True)
+        fwd.append(timed(lambda: gt.gt_sparse_mha_fwd_plan(plan, Qs, t["K"], t["V"], out=out, lse=lse)))
+        bwd.append(timed(lambda: gt.gt_sparse_mha_bwd_plan(plan, Qs, t["K"], t["V"], out, dOs, lse)))
+        edges.append(int(ip[b] - ip[a]))
+        plan.destroy()
+        del sip, six, out, lse
+    res = {"parts": parts, "edges_per_shard_max": max(edges), "fwd_ms_max": max(fwd), "fwd_ms_mean": sum(fwd) / parts,
+           "bwd_ms_max": max(bwd), "bwd_ms_mean": sum(bwd) / parts,
+           "fwd_edge_heads_per_s_per_gpu": max(edges) * w["H"] / (max(fwd) * 1e-3)}
+    log("shards: %d row ranges of <= %d edges; forward %.3f ms (slowest), backward %.3f ms (slowest)"
+        % (parts, max(edges), res["fwd_ms_max"], res["bwd_ms_max"]))
+    del dO
+    return res
+
+
 def time_calls(step, reps, flush_gib=1.0):
     """Per-call event times of step(): back to back, and with a write of a
     flush_gib GiB buffer between calls (evicting the L2 and the 256 MB
@@ -482,6 +536,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip timing the logit variants and dropout")
     ap.add_argument("--no-layout", action="store_true", help="skip timing the head-innermost layout")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the gathers-alone and copy rates")
+    ap.add_argument("--no-shards", action="store_true", help="skip timing one GPU's share of 8 row shards")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -572,6 +627,7 @@ def main():
         "plan": None,
         "variants": None,
         "layout": None,
+        "shards": None,
     }
     out_host = out.float().cpu().numpy() if out.dtype == torch.bfloat16 else out.cpu().numpy()
     if not args.no_stages:
@@ -584,6 +640,8 @@ def main():
         line["variants"] = time_variants(gt, t, w, max(3, args.steps // 4))
     if not args.no_layout:
         line["layout"] = time_layout(gt, t, w, 200 if w["E"] < 10 ** 6 else max(3, args.steps // 4))
+    if not args.no_shards:
+        line["shards"] = time_shards(gt, t, w)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, out_host)
     print(json.dumps(line), flush=True)
