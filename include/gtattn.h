@@ -1,6 +1,8 @@
 /*
- * gtattn.h -- C ABI of libgtattn: sparse multi-head graph attention forward
- * on one AMD Instinct MI355X (gfx950).
+ * gtattn.h -- C ABI of libgtattn: sparse multi-head graph attention on one
+ * AMD Instinct MI355X (gfx950): the fused forward and its unfused stages, the
+ * backward, logit options (bias, edge weights, dropout), the head-innermost
+ * feature layout, and graph construction and plans on the device.
  *
  * The operation.  For a directed graph stored as a destination-sorted CSR and
  * per-node features Q, K, V of H heads x D dims, every edge u->v and head h
