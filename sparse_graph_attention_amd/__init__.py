@@ -1,4 +1,4 @@
-"""Python binding of libgtattn: sparse multi-head graph attention forward on MI355X.
+"""Python binding of libgtattn: sparse multi-head graph attention on MI355X.
 
 Argument marshalling only.  Every step of the computation runs in the HIP
 kernels of ``libgtattn.so`` (built from ``csrc/`` for gfx950); PyTorch
