@@ -16,7 +16,7 @@ sample of the same workload.
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan] [--no-variants]
                   [--no-layout] [--no-ceiling] [--no-shards]
-                  [--calib-copy]
+                  [--calib-copy] [--calib-windows]
 
 Also reported beside the step: the unfused stages (SDDMM, edge softmax, SpMM),
 the backward (gt_sparse_mha_bwd), graph construction (COO to CSR, a plan with
@@ -522,6 +522,44 @@ def calib_copy(gib=1.0, reps=5):
     print(json.dumps({"calib_copy_bytes_read": n * 4, "calib_copy_bytes_written": n * 4, "reps": reps}), flush=True)
 
 
+def calib_windows(E=16_000_000, N=1_000_000, reps=5):
+    """The K and V row gathers alone (gt_calib_gather, fp32 rows of 8 x 64,
+    2 KB) over E edges whose uniform sources lie in a window of W nodes, for
+    K+V footprints from 4 GB down to 4 MB: one JSON line of event-timed rates.
+    Under rocprofv3 --pmc FETCH_SIZE the dispatches of each window follow in
+    this order (1 warm-up + reps each), which shows whether reads served by the
+    Infinity Cache are counted as fetched bytes."""
+    import torch
+
+    import sparse_graph_attention_amd as gt
+
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    K = torch.randn(N, 512, device=dev)
+    V = torch.randn(N, 512, device=dev)
+    res = []
+    for W in (N, 65536, 16384, 1024):
+        gen.manual_seed(W)
+        idx = torch.randint(0, W, (E,), device=dev, dtype=torch.int32, generator=gen)
+        Kw, Vw = K[:W], V[:W]
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        gt.gt_calib_gather(idx, Kw, Vw, checksum=sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            gt.gt_calib_gather(idx, Kw, Vw, checksum=sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        nbytes = 2 * E * 2048 + 4 * E
+        res.append({"window_nodes": W, "footprint_bytes": 2 * W * 2048, "ms": ms, "GBps": nbytes / (ms * 1e-3) / 1e9,
+                    "gather_bytes": nbytes})
+        log("window %d nodes (K+V %.1f MB): %.3f ms, %.0f GB/s" % (W, 2 * W * 2048 / 1e6, ms, res[-1]["GBps"]))
+        del idx
+    print(json.dumps({"calib_windows": res, "reps": reps, "E": E}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -530,6 +568,8 @@ def main():
     ap.add_argument("--workload", default="powerlaw", choices=sorted(DESCRIPTIONS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calib-copy", action="store_true")
+    ap.add_argument("--calib-windows", action="store_true",
+                    help="only the K/V gathers alone over source windows of 4 GB .. 4 MB")
     ap.add_argument("--no-stages", action="store_true", help="skip timing the unfused stages")
     ap.add_argument("--no-backward", action="store_true", help="skip timing the backward")
     ap.add_argument("--no-plan", action="store_true", help="skip timing graph construction and plans")
@@ -545,6 +585,9 @@ def main():
         sys.exit(2)
     if args.calib_copy:
         calib_copy()
+        return
+    if args.calib_windows:
+        calib_windows()
         return
 
     import numpy as np
