@@ -46,14 +46,18 @@
  * work enqueued on `stream` has finished.  The library keeps no caller
  * pointer after a call returns.  It owns its internal scratch (work lists
  * and the partial results of split rows): one buffer per (device, stream),
- * grown on demand; growing it synchronises that stream once.
+ * grown on demand; growing it synchronises that stream once and frees the
+ * old buffer.  The buffer stays allocated until gt_scratch_release.
  *
  * Execution.  Calls enqueue kernels on `stream` (NULL = the null stream) and
  * return without waiting for them; gt_validate_csr is the exception.  Every
  * element of every output is written, including the zeros of destinations
  * without in-edges, so outputs need no clearing.  Results are deterministic:
  * two calls on the same inputs give bit-identical outputs.  Calls on
- * different streams may run concurrently.
+ * different streams may run concurrently, from any host threads.  Calls on
+ * one stream share its scratch and must not be made from several host
+ * threads at once: one call growing the buffer would free it under another
+ * call that is still enqueuing work on it.
  *
  * Errors.  Arguments are checked before anything is enqueued; on a non-OK
  * status nothing was launched.  No exception or abort crosses the ABI.
@@ -354,6 +358,19 @@ const char* gt_last_error(void);
 typedef enum { GT_CFG_CHUNK_EDGES = 0 } gt_config_key;
 int gt_config_set(int32_t key, int64_t value);
 int64_t gt_config_get(int32_t key);
+
+/*
+ * The scratch buffer of `stream` on the current device: gt_scratch_release
+ * waits for the stream, frees the buffer and forgets it (the next call on the
+ * stream allocates afresh); GT_OK also when the stream has none.  Call it
+ * before destroying a stream that the library has used, or to return the
+ * memory (up to 8 feature arrays' worth for the head-innermost backward).
+ * gt_scratch_bytes gives the buffer's current size (0 if none, -1 if the
+ * current device cannot be read).  The same threading rule as for the other
+ * calls on a stream applies.
+ */
+int gt_scratch_release(hipStream_t stream);
+int64_t gt_scratch_bytes(hipStream_t stream);
 
 /*
  * Kernel timing for measurement.  gt_profile_begin(capacity) makes the next

@@ -72,6 +72,8 @@ EXPORTS = (
     "gt_last_error",
     "gt_config_set",
     "gt_config_get",
+    "gt_scratch_release",
+    "gt_scratch_bytes",
     "gt_profile_begin",
     "gt_profile_end",
 )
@@ -130,6 +132,10 @@ def lib():
         L.gt_config_set.argtypes = [_i32, _i64]
         L.gt_config_get.restype = _i64
         L.gt_config_get.argtypes = [_i32]
+        L.gt_scratch_release.argtypes = [_p]
+        L.gt_scratch_release.restype = ctypes.c_int
+        L.gt_scratch_bytes.argtypes = [_p]
+        L.gt_scratch_bytes.restype = _i64
         L.gt_profile_begin.argtypes = [_i32]
         L.gt_profile_end.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double),
                                      ctypes.POINTER(_i64)]
@@ -595,6 +601,20 @@ def gt_config_set(key, value):
 
 def gt_config_get(key):
     return lib().gt_config_get(key)
+
+
+def gt_scratch_release(stream=None):
+    """Waits for `stream` (default: torch's current stream), then frees the
+    library's scratch buffer for it on the current device."""
+    _check(lib().gt_scratch_release(_stream(stream)), "gt_scratch_release")
+
+
+def gt_scratch_bytes(stream=None):
+    """Size of the library's scratch buffer for `stream` (0 if none)."""
+    n = lib().gt_scratch_bytes(_stream(stream))
+    if n < 0:
+        raise GtError(GT_EHIP, "gt_scratch_bytes")
+    return n
 
 
 def gt_profile_begin(capacity):

@@ -268,6 +268,28 @@ int gt_config_set(int32_t key, int64_t value) {
 
 int64_t gt_config_get(int32_t key) { return key == GT_CFG_CHUNK_EDGES ? g_chunk.load() : -1; }
 
+int gt_scratch_release(hipStream_t stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch.find({dev, (uintptr_t)stream});
+    if (it == g_scratch.end()) return GT_OK;
+    e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    e = hipFree(it->second.ptr);
+    g_scratch.erase(it);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "hipFree");
+}
+
+int64_t gt_scratch_bytes(hipStream_t stream) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    auto it = g_scratch.find({dev, (uintptr_t)stream});
+    return it == g_scratch.end() ? 0 : (int64_t)it->second.bytes;
+}
+
 int gt_profile_begin(int32_t capacity) {
     if (capacity < 1) return fail(GT_EINVAL, "profile capacity must be >= 1");
     release_profile();

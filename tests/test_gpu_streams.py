@@ -5,7 +5,7 @@ different streams may run concurrently.  The kernels are deterministic, so
 every result must equal the same call's on the default stream bit for bit:
 forward with lse and backward (split rows included), two graphs of different
 shapes and dtypes in flight together, and a plan built on one stream and used
-on another after a stream wait.
+on another after a stream wait; and the release of a stream's scratch.
 """
 import pytest
 import torch
@@ -68,3 +68,23 @@ def test_plan_built_on_one_stream_used_on_another():
         torch.cuda.synchronize()
         gt.gt_plan_destroy(plan)
     assert torch.equal(out, ref_out) and torch.equal(lse, ref_lse)
+
+
+def test_scratch_release_and_reuse():
+    """gt_scratch_release frees a stream's buffer; the next call allocates a
+    new one and gives the same results bit for bit."""
+    _, t = inputs(14, 20000, 400000, 8, 64, gtgen.F32)
+    s = torch.cuda.Stream()
+    with chunk_edges(64), torch.cuda.stream(s):
+        say("streams: scratch release")
+        ref = run(t)
+        assert gt.gt_scratch_bytes(s) > 0
+        gt.gt_scratch_release(s)
+        assert gt.gt_scratch_bytes(s) == 0
+        gt.gt_scratch_release(s)  # nothing left to free: still OK
+        got = run(t)
+        assert gt.gt_scratch_bytes(s) > 0
+        gt.gt_scratch_release(s)
+    torch.cuda.synchronize()
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b), "result after a scratch release differs"
