@@ -500,6 +500,7 @@ def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
         "unit": "edge-heads/s",
         "cores": threads,
         "kind": "oracle",
+        "host": {"cpu_model": cpu_model(), "logical_cpus": os.cpu_count()},
         "sample": "%d%% of destination rows drawn uniformly (seed %d): %d rows, %d edges, %.1f s wall" % (
             round(fraction * 100), seed, len(rows), edges, dt),
         "single_thread": {
@@ -507,6 +508,17 @@ def cpu_baseline(w, out_gpu, fraction=0.5, seed=0):
             "sample": "every 10th row of that sample: %d rows, %d edges, %.1f s wall" % (len(rows1), edges1, dt1),
         },
     }
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def calib_copy(gib=1.0, reps=5):
