@@ -11,44 +11,75 @@ __global__ void reset_kernel(PlanCounters* c) {
     }
 }
 
-// One thread per row.  A row with more than `chunk` in-edges gets a slot in
-// the heavy-row list and a contiguous range of chunk item ids; the chunk
-// table maps each id back to (row, chunk index, heavy slot).  Slot order
-// depends on scheduling, but each chunk's result does not, and the merges
-// read a row's chunks in chunk order, so outputs are deterministic.
-// The wave adds up its heavy rows and chunks with a prefix scan and takes
-// its ranges with one atomic per counter (64x fewer atomics on two hot words).
-__global__ __launch_bounds__(256) void plan_kernel(const int64_t* __restrict__ indptr, int64_t N, Plan p) {
-    const int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    const int lane = threadIdx.x & 63;
-    const int64_t deg = v < N ? indptr[v + 1] - indptr[v] : 0;
-    const bool heavy = deg > p.chunk;
-    const int64_t nch = heavy ? (deg + p.chunk - 1) / p.chunk : 0;
-    uint32_t hin = heavy ? 1u : 0u, cin = (uint32_t)nch;  // inclusive prefix sums over the wave
-    for (int off = 1; off < 64; off <<= 1) {
-        const uint32_t h = __shfl_up(hin, off, 64), c = __shfl_up(cin, off, 64);
+// A row with more than `chunk` in-edges gets a slot in the heavy-row list and
+// a contiguous range of chunk item ids; the chunk table maps each id back to
+// (row, chunk index, heavy slot).  Slot order depends on scheduling, but each
+// chunk's result does not, and the merges read a row's chunks in chunk order,
+// so outputs are deterministic.  A block takes kPlanThreads * kPlanRows rows
+// (each thread kPlanRows of them, kPlanThreads apart, so that loads
+// coalesce), adds up its heavy rows and chunks with a block-wide prefix scan
+// and takes its ranges with one atomic per counter.  The counters are hot
+// words that every block updates at the coherent memory side, so the fewer
+// the atomics the better: one pair per 8,192 rows.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanRows = 8;
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ indptr, int64_t N, Plan p) {
+    constexpr int kWaves = kPlanThreads / kWave;
+    __shared__ uint32_t s_h[kWaves], s_c[kWaves], s_base[2];
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    const int64_t v0 = (int64_t)blockIdx.x * kPlanThreads * kPlanRows + threadIdx.x;
+    uint32_t nch[kPlanRows];
+    uint32_t hcnt = 0, ccnt = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k) {
+        const int64_t v = v0 + (int64_t)k * kPlanThreads;
+        const int64_t deg = v < N ? indptr[v + 1] - indptr[v] : 0;
+        nch[k] = deg > p.chunk ? (uint32_t)((deg + p.chunk - 1) / p.chunk) : 0u;
+        hcnt += nch[k] ? 1u : 0u;
+        ccnt += nch[k];
+    }
+    uint32_t hin = hcnt, cin = ccnt;  // inclusive prefix sums over the wave
+    for (int off = 1; off < kWave; off <<= 1) {
+        const uint32_t h = __shfl_up(hin, off, kWave), c = __shfl_up(cin, off, kWave);
         if (lane >= off) {
             hin += h;
             cin += c;
         }
     }
-    const uint32_t htot = __shfl(hin, 63, 64), ctot = __shfl(cin, 63, 64);
-    if (htot == 0) return;
-    uint32_t hb = 0, cb = 0;
-    if (lane == 0) {
-        hb = atomicAdd(&p.counters->nheavy, htot);
-        cb = atomicAdd(&p.counters->nchunks, ctot);
+    if (lane == kWave - 1) {
+        s_h[wid] = hin;
+        s_c[wid] = cin;
     }
-    hb = __shfl(hb, 0, 64);
-    cb = __shfl(cb, 0, 64);
-    if (!heavy) return;
-    const uint32_t hs = hb + hin - 1;
-    const uint32_t base = cb + cin - (uint32_t)nch;
-    // a valid CSR never trips these (the host sizes both tables for it); a
-    // malformed one must not write past them
-    if ((int64_t)hs >= p.max_heavy || (int64_t)base + nch > p.max_chunks) return;
-    p.heavy[hs] = HeavyRow{(int32_t)v, (int32_t)nch, (int64_t)base};
-    for (int64_t i = 0; i < nch; ++i) p.chunks[base + i] = ChunkRef{(int32_t)v, (int32_t)i, (int32_t)hs, 0};
+    __syncthreads();
+    if (threadIdx.x == 0) {  // exclusive prefix over the waves, then the block's ranges
+        uint32_t ht = 0, ct = 0;
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t h = s_h[w], c = s_c[w];
+            s_h[w] = ht;
+            s_c[w] = ct;
+            ht += h;
+            ct += c;
+        }
+        s_base[0] = ht ? atomicAdd(&p.counters->nheavy, ht) : 0u;
+        s_base[1] = ht ? atomicAdd(&p.counters->nchunks, ct) : 0u;
+    }
+    __syncthreads();
+    if (hcnt == 0) return;
+    uint32_t hs = s_base[0] + s_h[wid] + hin - hcnt;
+    uint32_t cb = s_base[1] + s_c[wid] + cin - ccnt;
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k) {
+        if (!nch[k]) continue;
+        // a valid CSR never trips this (the host sizes both tables for it); a
+        // malformed one must not write past them
+        if ((int64_t)hs >= p.max_heavy || (int64_t)cb + nch[k] > p.max_chunks) return;
+        const int32_t v = (int32_t)(v0 + (int64_t)k * kPlanThreads);
+        p.heavy[hs] = HeavyRow{v, (int32_t)nch[k], (int64_t)cb};
+        for (uint32_t i = 0; i < nch[k]; ++i) p.chunks[cb + i] = ChunkRef{v, (int32_t)i, (int32_t)hs, 0};
+        ++hs;
+        cb += nch[k];
+    }
 }
 
 hipError_t launch_plan(const Args& a, hipStream_t s) {
@@ -56,7 +87,8 @@ hipError_t launch_plan(const Args& a, hipStream_t s) {
     reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    plan_kernel<<<(unsigned)((a.N + 255) / 256), 256, 0, s>>>(a.indptr, a.N, a.plan);
+    const int64_t per_block = (int64_t)kPlanThreads * kPlanRows;
+    plan_kernel<<<(unsigned)((a.N + per_block - 1) / per_block), kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
     return hipGetLastError();
 }
 
