@@ -198,8 +198,8 @@ bool choose_layout_ndh(Args& a, std::initializer_list<const void*> feats) {
 // holds VN heads of one d, so each head's dot product takes VN * log2(G / HV)
 // cross-lane shuffles per edge, where [N][H][D] rows take a few DPP steps.
 // Measured: they win where [N][H][D] falls back to one wave per head (heads
-// not a power-of-two number of 16-byte vectors: fp32 8 x 10, 20 against 26 us
-// forward, 52 against 60 us backward); the forward also wins when a row's
+// not a power-of-two number of 16-byte vectors: fp32 8 x 10, 16 against 25 us
+// forward, 50 against 59 us backward); the forward also wins when a row's
 // gathers are large against its shuffles (fp32 8 x 64: 4 KB per edge for 20
 // shuffles, 12.2 against 16.9 ms), and loses when they are not (bf16 8 x 32:
 // 1 KB for 40 shuffles, 19.5 against 11 ms).  The backward, with two head

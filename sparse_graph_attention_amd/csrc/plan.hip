@@ -20,7 +20,9 @@ __global__ void reset_kernel(PlanCounters* c) {
 // coalesce), adds up its heavy rows and chunks with a block-wide prefix scan
 // and takes its ranges with one atomic per counter.  The counters are hot
 // words that every block updates at the coherent memory side, so the fewer
-// the atomics the better: one pair per 8,192 rows.
+// the atomics the better: one pair per 8,192 rows.  A graph of at most that
+// many rows has one block, which writes the counters itself, so small graphs
+// need no reset launch before it.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanRows = 8;
 
@@ -61,8 +63,14 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
             ht += h;
             ct += c;
         }
-        s_base[0] = ht ? atomicAdd(&p.counters->nheavy, ht) : 0u;
-        s_base[1] = ht ? atomicAdd(&p.counters->nchunks, ct) : 0u;
+        if (gridDim.x == 1) {  // the only block: it sets the counters (no reset ran)
+            p.counters->nheavy = ht;
+            p.counters->nchunks = ct;
+            s_base[0] = s_base[1] = 0u;
+        } else {
+            s_base[0] = ht ? atomicAdd(&p.counters->nheavy, ht) : 0u;
+            s_base[1] = ht ? atomicAdd(&p.counters->nchunks, ct) : 0u;
+        }
     }
     __syncthreads();
     if (hcnt == 0) return;
@@ -84,10 +92,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
 
 hipError_t launch_plan(const Args& a, hipStream_t s) {
     if (a.plan.max_heavy == 0) return hipSuccess;  // no row can be split: nothing to list
-    reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
     const int64_t per_block = (int64_t)kPlanThreads * kPlanRows;
+    if (a.N > per_block) {  // several blocks add to the counters: clear them first
+        reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
+        hipError_t err = hipGetLastError();
+        if (err != hipSuccess) return err;
+    }
     plan_kernel<<<(unsigned)((a.N + per_block - 1) / per_block), kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
     return hipGetLastError();
 }
