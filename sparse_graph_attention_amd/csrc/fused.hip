@@ -675,17 +675,12 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
-// One wave per (heavy row, head h = blockIdx.y).  The chunk loop is unrolled
-// so that eight partial rows are in flight per lane.
+// Merges head h of one heavy row (one wave).  The chunk loop is unrolled so
+// that eight partial rows are in flight per lane.
 template <int DT, int T>
-__global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
+__device__ __forceinline__ void merge_row(const Args& a, const HeavyRow hr, int h, int lane) {
     using VT = Vec<DT>;
     constexpr int UN = 8;
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int h = blockIdx.y;
-    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
-    const HeavyRow hr = a.plan.heavy[hs];
     const int H = a.H, D = a.D, nch = hr.nch;
     const int64_t HD = (int64_t)H * D;
     const float* pm = a.plan.pm + hr.base * H + h;
@@ -729,6 +724,21 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
         const int d = lane + t * kWave;
         if (d < D) VT::store_scalar(a.out, (int64_t)hr.row * HD + hoff + d * dstride, A[t] / L);
     }
+}
+
+// A wave per (heavy row, head h = blockIdx.y) at a time, striding over the
+// heavy rows listed by the plan.  The grid is capped (kMergeGridX blocks in
+// x): the host sizes it for the upper bound of heavy rows, E / (chunk + 1),
+// which can be ten times the rows the plan lists, and a wave per bound would
+// spend the kernel's time launching waves that exit at once.
+template <int DT, int T>
+__global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int h = blockIdx.y;
+    const int64_t nheavy = min(a.plan.max_heavy, (int64_t)a.plan.counters->nheavy);
+    for (int64_t hs = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         hs < nheavy; hs += (int64_t)gridDim.x * kWavesPerBlock)
+        merge_row<DT, T>(a, a.plan.heavy[hs], h, lane);
 }
 
 // ------------------------------------------------------------ launchers
@@ -796,17 +806,17 @@ hipError_t launch_fused(const Args& a, hipStream_t s, hipEvent_t ev0, hipEvent_t
 
 hipError_t launch_fused_merge(const Args& a, hipStream_t s) {
     const dim3 block(kBlock);
-    return for_slices(a, a.plan.max_heavy, [&](const Args& as, unsigned gx) {
-        const dim3 grid(gx, a.H);
-        const int T = (a.D + kWave - 1) / kWave;
-        if (a.dtype == kF32) {
-            if (T == 1) fused_merge_kernel<kF32, 1><<<grid, block, 0, s>>>(as);
-            else fused_merge_kernel<kF32, 4><<<grid, block, 0, s>>>(as);
-        } else {
-            if (T == 1) fused_merge_kernel<kBF16, 1><<<grid, block, 0, s>>>(as);
-            else fused_merge_kernel<kBF16, 4><<<grid, block, 0, s>>>(as);
-        }
-    });
+    const dim3 grid((unsigned)std::min<int64_t>((a.plan.max_heavy + kWavesPerBlock - 1) / kWavesPerBlock, kMergeGridX),
+                    a.H);
+    const int T = (a.D + kWave - 1) / kWave;
+    if (a.dtype == kF32) {
+        if (T == 1) fused_merge_kernel<kF32, 1><<<grid, block, 0, s>>>(a);
+        else fused_merge_kernel<kF32, 4><<<grid, block, 0, s>>>(a);
+    } else {
+        if (T == 1) fused_merge_kernel<kBF16, 1><<<grid, block, 0, s>>>(a);
+        else fused_merge_kernel<kBF16, 4><<<grid, block, 0, s>>>(a);
+    }
+    return hipGetLastError();
 }
 
 }  // namespace gt

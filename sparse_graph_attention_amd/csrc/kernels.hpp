@@ -65,6 +65,9 @@ hipError_t launch_transpose_rows(const void* src, void* dst, int64_t N, int A, i
 // Whether a launch needs the extended-logit kernels.
 inline bool extended(const Args& a) { return a.bias || a.ew || a.drop_thresh || a.dbias || a.dew; }
 
+// Blocks in x of the merges of split rows, which stride over the heavy rows.
+constexpr int64_t kMergeGridX = 1024;
+
 // Items per launch slice: keeps gridDim.x * blockDim.x below 2^32.
 constexpr int64_t kSliceItems = (int64_t)1 << 24;
 

@@ -1,5 +1,7 @@
 // plan.hip -- device-side work list (heavy rows and their chunks) and the
 // CSR validity check.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace gt {
@@ -106,9 +108,9 @@ hipError_t launch_plan(const Args& a, hipStream_t s) {
 // (the unfused SpMM and both passes of the backward)
 // Chunk partials of a heavy row are [chunk][width] with width = regions * HD;
 // region r of each is added over the row's chunks, in chunk order, and goes
-// to dst_r scaled by scale_r.  One wave per (heavy row, slice of kMergeCols
-// columns); chunks are read kMergeUnroll at a time so that many loads are in
-// flight (one wave walks up to E / chunk partials of a hub row).
+// to dst_r scaled by scale_r.  A wave per (heavy row, slice of kMergeCols
+// columns) at a time; chunks are read kMergeUnroll at a time so that many
+// loads are in flight (one wave walks up to E / chunk partials of a hub row).
 constexpr int kMergeCols = kWave * 4;
 constexpr int kMergeUnroll = 8;
 
@@ -117,13 +119,10 @@ __global__ __launch_bounds__(kBlock) void sum_merge_kernel(const Args a, int reg
                                                            void* dst1, float scale1) {
     using VT = Vec<DT>;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy) return;
-    const HeavyRow hr = a.plan.heavy[hs];
+    const int64_t nheavy = min(a.plan.max_heavy, (int64_t)a.plan.counters->nheavy);
     const int64_t HD = (int64_t)a.H * a.D;
     const int64_t width = HD * regions;
     const int64_t j0 = (int64_t)blockIdx.y * kMergeCols;
-    const float* pa = a.plan.pacc + hr.base * width;
     int64_t col[4];
     bool in[4];
 #pragma unroll
@@ -131,35 +130,43 @@ __global__ __launch_bounds__(kBlock) void sum_merge_kernel(const Args a, int reg
         col[t] = j0 + lane + t * kWave;
         in[t] = col[t] < width;
     }
-    float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int i0 = 0; i0 < hr.nch; i0 += kMergeUnroll) {
-        float x[kMergeUnroll][4];
+    for (int64_t hs = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         hs < nheavy; hs += (int64_t)gridDim.x * kWavesPerBlock) {
+        const HeavyRow hr = a.plan.heavy[hs];
+        const float* pa = a.plan.pacc + hr.base * width;
+        float A[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        for (int i0 = 0; i0 < hr.nch; i0 += kMergeUnroll) {
+            float x[kMergeUnroll][4];
 #pragma unroll
-        for (int i = 0; i < kMergeUnroll; ++i)
+            for (int i = 0; i < kMergeUnroll; ++i)
 #pragma unroll
-            for (int t = 0; t < 4; ++t)
-                x[i][t] = (i0 + i < hr.nch && in[t]) ? pa[(int64_t)(i0 + i) * width + col[t]] : 0.0f;
+                for (int t = 0; t < 4; ++t)
+                    x[i][t] = (i0 + i < hr.nch && in[t]) ? pa[(int64_t)(i0 + i) * width + col[t]] : 0.0f;
 #pragma unroll
-        for (int i = 0; i < kMergeUnroll; ++i)
+            for (int i = 0; i < kMergeUnroll; ++i)
 #pragma unroll
-            for (int t = 0; t < 4; ++t) A[t] += x[i][t];
-    }
+                for (int t = 0; t < 4; ++t) A[t] += x[i][t];
+        }
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        if (!in[t]) continue;
-        const int r = col[t] >= HD;  // regions <= 2
-        VT::store_scalar(r ? dst1 : dst0, (int64_t)hr.row * HD + col[t] - r * HD, A[t] * (r ? scale1 : scale0));
+        for (int t = 0; t < 4; ++t) {
+            if (!in[t]) continue;
+            const int r = col[t] >= HD;  // regions <= 2
+            VT::store_scalar(r ? dst1 : dst0, (int64_t)hr.row * HD + col[t] - r * HD, A[t] * (r ? scale1 : scale0));
+        }
     }
 }
 
+// The grid strides over the heavy rows listed by the plan, capped at
+// kMergeGridX blocks in x, as in the forward's merge.
 template <int DT>
-static hipError_t launch_sum_merge_dt(const Args& a0, int regions, void* dst0, float scale0, void* dst1, float scale1,
+static hipError_t launch_sum_merge_dt(const Args& a, int regions, void* dst0, float scale0, void* dst1, float scale1,
                                       hipStream_t s) {
-    if (a0.plan.max_heavy == 0) return hipSuccess;
-    return for_slices(a0, a0.plan.max_heavy, [&](const Args& a, unsigned gx) {
-        const unsigned gy = (unsigned)((regions * (int64_t)a.H * a.D + kMergeCols - 1) / kMergeCols);
-        sum_merge_kernel<DT><<<dim3(gx, gy), dim3(kBlock), 0, s>>>(a, regions, dst0, scale0, dst1, scale1);
-    });
+    if (a.plan.max_heavy == 0) return hipSuccess;
+    const unsigned gx =
+        (unsigned)std::min<int64_t>((a.plan.max_heavy + kWavesPerBlock - 1) / kWavesPerBlock, kMergeGridX);
+    const unsigned gy = (unsigned)((regions * (int64_t)a.H * a.D + kMergeCols - 1) / kMergeCols);
+    sum_merge_kernel<DT><<<dim3(gx, gy), dim3(kBlock), 0, s>>>(a, regions, dst0, scale0, dst1, scale1);
+    return hipGetLastError();
 }
 
 hipError_t launch_sum_merge(const Args& a, int regions, void* dst0, float scale0, void* dst1, float scale1,
