@@ -158,7 +158,8 @@ def test_variants_small(variant, name, chunk):
         check_full(w, make_opts(w, 5, **VARIANTS[variant]))
 
 
-@pytest.mark.parametrize("H,D", [(8, 64), (3, 5), (4, 33), (2, 256), (16, 64), (8, 32), (64, 4)])
+@pytest.mark.parametrize("H,D", [(8, 64), (3, 5), (4, 33), (2, 256), (16, 64), (8, 32), (64, 4), (12, 64),
+                                 (24, 64)])
 @pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
 @pytest.mark.parametrize("p", [0.3, 0.0])  # the dropout kernels, and those of bias and weights alone
 def test_variants_shapes(H, D, dtype, p):
