@@ -164,6 +164,9 @@ def _ptr(t):
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
+    elif stream.device.index != torch.cuda.current_device():
+        raise ValueError("the stream is on cuda:%d but the current device is cuda:%d" % (
+            stream.device.index, torch.cuda.current_device()))
     return ctypes.c_void_p(stream.cuda_stream)
 
 
@@ -176,11 +179,24 @@ def _dtype_code(t):
 
 
 def _need_gpu(*ts):
+    """Every tensor on the GPU, contiguous, and on the current device: the
+    library launches on the current device, where another device's pointers
+    would not be valid."""
+    dev = None
     for t in ts:
-        if t is not None and not t.is_cuda:
+        if t is None:
+            continue
+        if not t.is_cuda:
             raise ValueError("libgtattn works on GPU tensors only; got a %s tensor" % t.device)
-        if t is not None and not t.is_contiguous():
+        if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+        if dev is None:
+            dev = t.device.index
+        elif t.device.index != dev:
+            raise ValueError("tensors on several devices (cuda:%d and cuda:%d)" % (dev, t.device.index))
+    if dev is not None and dev != torch.cuda.current_device():
+        raise ValueError("tensors are on cuda:%d but the current device is cuda:%d; call inside "
+                         "torch.cuda.device(%d)" % (dev, torch.cuda.current_device(), dev))
 
 
 def _csr(indptr, indices):
