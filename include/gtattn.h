@@ -128,8 +128,9 @@ int gt_sparse_mha_fwd_lse(const int64_t* indptr, const int32_t* indices, const v
  * element written (zeros for nodes without in- or out-edges).  All feature
  * arrays share dtype; accumulation is fp32.  The transpose is trusted like
  * the CSR: that it matches (indptr, indices) is not checked.  No atomics:
- * results are deterministic.  Scratch: the per-stream buffer also holds an
- * fp32 [N][H] delta.  Errors as for gt_sparse_mha_fwd.
+ * results are deterministic.  Scratch: the per-stream buffer also holds,
+ * per (destination, head), delta and lse in the base-2 scale (two floats,
+ * 8 * N * H bytes).  Errors as for gt_sparse_mha_fwd.
  */
 int gt_sparse_mha_bwd(const int64_t* indptr, const int32_t* indices, const int64_t* t_indptr, const int32_t* t_indices,
                       const void* Q, const void* K, const void* V, const void* out, const void* dout, const float* lse,
