@@ -9,6 +9,8 @@
 // item's scores (max, sum of exponentials, weights).  A chunk of a heavy row
 // only leaves its (max, sum); the row's chunks are merged in chunk order and
 // a last pass over the chunks writes the weights.
+#include <algorithm>
+
 #include "kernels.hpp"
 
 namespace gt {
@@ -125,7 +127,10 @@ __device__ __forceinline__ void softmax_wave(const Args& a, int64_t e0, int64_t 
 }
 
 // Rows of at most this many in-edges are done by one lane per (row, head).
-constexpr int kSmallDeg = 32;
+#ifndef GT_SOFTMAX_SMALL_DEG
+#define GT_SOFTMAX_SMALL_DEG 32
+#endif
+constexpr int kSmallDeg = GT_SOFTMAX_SMALL_DEG;
 
 // Chunks of heavy rows: their statistics only (one wave per chunk item).
 __global__ __launch_bounds__(kBlock) void softmax_chunk_kernel(const Args a) {
@@ -191,20 +196,46 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(const Args a) {
     }
 }
 
-// One wave per heavy row, lane h < H per head: merge the chunks' (max, sum) in chunk order.
+// The chunks' (max, sum) of each heavy row, merged per head.  A wave per
+// heavy row at a time, striding over the rows the plan lists (the grid is
+// capped at kMergeGridX blocks; the host only knows an upper bound of heavy
+// rows).  When H divides 64, lane j takes head j % H of chunks j / H,
+// j / H + 64 / H, ... and the lanes of a head combine their partial (max, sum)
+// by xor shuffles, in a fixed order; otherwise lane h < H walks its head's
+// chunks in order.
 __global__ __launch_bounds__(kBlock) void softmax_merge_kernel(const Args a) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t hs = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H;
-    if (hs >= a.plan.max_heavy || hs >= (int64_t)a.plan.counters->nheavy || lane >= H) return;
-    const HeavyRow hr = a.plan.heavy[hs];
-    float M = -INFINITY;
-    for (int i = 0; i < hr.nch; ++i) M = fmaxf(M, a.plan.pm[(hr.base + i) * H + lane]);
-    float L = 0.0f;
-    for (int i = 0; i < hr.nch; ++i)
-        L += a.plan.pl[(hr.base + i) * H + lane] * expd(a.plan.pm[(hr.base + i) * H + lane], M);
-    a.plan.hstat[(hs * H + lane) * 2 + 0] = M;
-    a.plan.hstat[(hs * H + lane) * 2 + 1] = L;
+    const int64_t nheavy = min(a.plan.max_heavy, (int64_t)a.plan.counters->nheavy);
+    for (int64_t hs = (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+         hs < nheavy; hs += (int64_t)gridDim.x * kWavesPerBlock) {
+        const HeavyRow hr = a.plan.heavy[hs];
+        const float* pm = a.plan.pm + hr.base * H;
+        const float* pl = a.plan.pl + hr.base * H;
+        if ((kWave % H) == 0) {
+            const int h = lane % H, cpw = kWave / H;
+            float m = -INFINITY, l = 0.0f;
+            for (int i = lane / H; i < hr.nch; i += cpw) {  // every chunk has edges: its max is finite
+                const float mi = pm[(int64_t)i * H + h], li = pl[(int64_t)i * H + h];
+                const float mn = fmaxf(m, mi);
+                l = l * (m == -INFINITY ? 0.0f : expd(m, mn)) + li * expd(mi, mn);
+                m = mn;
+            }
+            const float M = wave_max_stride(m, H);
+            const float L = wave_sum_stride(m == -INFINITY ? 0.0f : l * expd(m, M), H);
+            if (lane < H) {
+                a.plan.hstat[(hs * H + h) * 2 + 0] = M;
+                a.plan.hstat[(hs * H + h) * 2 + 1] = L;
+            }
+        } else if (lane < H) {
+            float M = -INFINITY;
+            for (int i = 0; i < hr.nch; ++i) M = fmaxf(M, pm[(int64_t)i * H + lane]);
+            float L = 0.0f;
+            for (int i = 0; i < hr.nch; ++i) L += pl[(int64_t)i * H + lane] * expd(pm[(int64_t)i * H + lane], M);
+            a.plan.hstat[(hs * H + lane) * 2 + 0] = M;
+            a.plan.hstat[(hs * H + lane) * 2 + 1] = L;
+        }
+    }
 }
 
 // One wave per chunk item: weights from the merged statistics of its row.
@@ -249,9 +280,10 @@ hipError_t launch_softmax(const Args& a, hipStream_t s) {
         softmax_chunk_kernel<<<gx, block, 0, s>>>(as);
     });
     if (err != hipSuccess) return err;
-    err = for_slices(a, a.plan.max_heavy, [&](const Args& as, unsigned gx) {
-        softmax_merge_kernel<<<gx, block, 0, s>>>(as);
-    });
+    softmax_merge_kernel<<<(unsigned)std::min<int64_t>((a.plan.max_heavy + kWavesPerBlock - 1) / kWavesPerBlock,
+                                                        kMergeGridX),
+                           block, 0, s>>>(a);
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
     return for_slices(a, a.plan.max_chunks, [&](const Args& as, unsigned gx) {
         softmax_chunk_norm_kernel<<<gx, block, 0, s>>>(as);
