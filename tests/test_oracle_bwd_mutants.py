@@ -32,6 +32,7 @@ def workdir():
         yield d
 
 
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")  # a planted mistake may make non-finite values
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_bwd_mutant_is_caught(name, workdir):
     old, new = MUTANTS[name]
