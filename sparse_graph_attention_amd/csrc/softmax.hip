@@ -168,7 +168,9 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(const Args a) {
         e = a.indptr[r + 1];
     }
     const int64_t deg = e - b;
-    if (deg > 0 && deg <= kSmallDeg) {
+    // rows above the split threshold belong to the chunk kernels: in place,
+    // writing their weights here would overwrite scores those kernels read
+    if (deg > 0 && deg <= kSmallDeg && deg <= a.plan.chunk) {
         // the lane's (row, head) scores in registers: one read with all loads in flight
         const float* s = a.scores_in;  // may alias alpha_out (in place)
         float v[kSmallDeg];

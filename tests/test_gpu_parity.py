@@ -364,9 +364,12 @@ def test_unfused_large_sampled(name):
 
 @pytest.mark.parametrize("H", [1, 4, 8, 16, 64])
 @pytest.mark.parametrize("in_place", [False, True])
-def test_softmax_row_blocks(H, in_place):
-    # degrees around the lane/wave cut (32) and the split threshold (512 by default)
-    degs = [0, 1, 2, 31, 32, 33, 100, 511, 512, 513, 1300, 0, 5, 64, 65, 7]
+@pytest.mark.parametrize("chunk", [512, 20])
+def test_softmax_row_blocks(H, in_place, chunk):
+    # degrees around the lane/wave cut (32) and the split threshold (512 by
+    # default; 20 splits rows that the per-lane path could otherwise take, which
+    # in place must not be overwritten before their chunks are read)
+    degs = [0, 1, 2, 19, 20, 21, 31, 32, 33, 100, 511, 512, 513, 1300, 0, 5, 64, 65, 7]
     N = len(degs) + 3
     dst = np.concatenate([np.full(d, v) for v, d in enumerate(degs)])
     src = gtgen.random_coo(41, N, len(dst))[0]
@@ -376,7 +379,8 @@ def test_softmax_row_blocks(H, in_place):
     ref = oracle.edge_softmax(indptr, sc.astype(np.float64))
     ip = torch.from_numpy(indptr).to(dev())
     buf = torch.from_numpy(sc).to(dev())
-    say("softmax row blocks H=%d in_place=%s" % (H, in_place))
-    a = gt.gt_edge_softmax(ip, buf, alpha=buf if in_place else None)
-    torch.cuda.synchronize()
+    say("softmax row blocks H=%d in_place=%s chunk=%d" % (H, in_place, chunk))
+    with chunk_edges(chunk):
+        a = gt.gt_edge_softmax(ip, buf, alpha=buf if in_place else None)
+        torch.cuda.synchronize()
     assert_close(host(a), ref, F32_TOL, "edge_softmax H=%d" % H)
