@@ -497,6 +497,7 @@ class GtPlan:
 
     def __init__(self, handle):
         self.handle = handle
+        self.info = None  # the plan's sizes, read once (a plan never changes)
 
     def destroy(self):
         if self.handle:
@@ -537,11 +538,13 @@ def gt_plan_destroy(plan):
 
 def gt_plan_info(plan):
     """dict(n_dst, n_src, E, transpose): the plan's sizes."""
-    n = [_i64() for _ in range(3)]
-    tptr = _p()
-    _check(lib().gt_plan_info(plan.handle, *[ctypes.byref(x) for x in n], None, None, ctypes.byref(tptr), None, None),
-           "gt_plan_info")
-    return dict(n_dst=n[0].value, n_src=n[1].value, E=n[2].value, transpose=bool(tptr.value))
+    if plan.info is None:
+        n = [_i64() for _ in range(3)]
+        tptr = _p()
+        _check(lib().gt_plan_info(plan.handle, *[ctypes.byref(x) for x in n], None, None, ctypes.byref(tptr), None,
+                                  None), "gt_plan_info")
+        plan.info = dict(n_dst=n[0].value, n_src=n[1].value, E=n[2].value, transpose=bool(tptr.value))
+    return dict(plan.info)
 
 
 def gt_plan_copy_graph(plan, device=None, stream=None):
