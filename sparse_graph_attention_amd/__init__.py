@@ -28,7 +28,13 @@ The functions have the names of the C entry points declared in
 * ``gt_plan_create(indptr, indices)`` / ``gt_plan_create_coo(src, dst, n_dst)``
   -- a reusable graph plan (``GtPlan``), ``gt_plan_destroy``, ``gt_plan_info``,
   ``gt_plan_copy_graph``;
-* ``gt_sparse_mha_fwd_plan(plan, Q, K, V)`` / ``gt_sparse_mha_bwd_plan(plan, ...)``.
+* ``gt_sparse_mha_fwd_plan(plan, Q, K, V)`` / ``gt_sparse_mha_bwd_plan(plan, ...)``;
+* ``gt_scratch_release(stream=None)`` / ``gt_scratch_bytes(stream=None)`` -- the
+  library's per-stream work buffer;
+* ``gt_config_set`` / ``gt_config_get``, ``gt_profile_begin`` / ``gt_profile_end``.
+
+Every tensor must be contiguous and on the current device; calls are
+asynchronous on ``stream`` (default: torch's current stream).
 
 Graphs are destination-sorted CSR: ``indptr`` int64 [N+1], ``indices`` int32
 [E] holding the source of each in-edge.  Features are [N][H][D] tensors of
