@@ -22,6 +22,8 @@
 // Chunks of split rows leave partial sums that a merge adds in chunk order.
 #include <algorithm>
 
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace gt {
@@ -969,6 +971,63 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
 
 // ------------------------------------------------------------ launchers
 
+// Whole rows of 32, 64 or 128 vectors with the head width known at compile
+// time (plain logits), for head splits besides the two tuned shapes.  The
+// run-time layout works out each item's lane groups and heads with integer
+// divisions and masks every vector; these instances do not, which the two
+// passes feel more than the forward does (power-law graph: fp32 4x128
+// 21.1 -> 18.3 ms, 8x32 11.2 -> 9.0 ms; bf16 8x64 13.3 -> 9.9 ms, 16x64
+// 36.2 -> 19.5 ms).  F(NC, U, G, LPH) launches one instance; false when
+// none fits.
+template <typename F>
+static bool launch_fixed_layout(const Args& a, F&& f) {
+    if (a.R != a.NC * a.G) return false;
+    if (a.G == 64 && a.NC == 2) {
+        switch (a.lph) {
+            case 8: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 8>{}); return true;
+            case 16: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 16>{}); return true;
+            case 32: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 32>{}); return true;
+            case 64: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 64>{}); return true;
+            default: return false;
+        }
+    }
+    if (a.G == 64 && a.NC == 1) {
+        switch (a.lph) {
+            case 4: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 4>{}); return true;
+            case 8: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 8>{}); return true;
+            case 16: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 16>{}); return true;
+            case 32: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 32>{}); return true;
+            default: return false;
+        }
+    }
+    if (a.G == 32 && a.NC == 1) {
+        switch (a.lph) {
+            case 4: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 32>{}, std::integral_constant<int, 4>{}); return true;
+            case 8: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 32>{}, std::integral_constant<int, 8>{}); return true;
+            case 16: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 32>{}, std::integral_constant<int, 16>{}); return true;
+            default: return false;
+        }
+    }
+    return false;
+}
+
+template <int DT>
+static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
+    return launch_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+        if (DT == kF32 && nc == 2 && ntl)
+            bwd_dq_vec_kernel<DT, nc, u, g, lph, true, 0, true><<<grid, block, 0, s>>>(a);
+        else
+            bwd_dq_vec_kernel<DT, nc, u, g, lph, true, 0><<<grid, block, 0, s>>>(a);
+    });
+}
+
+template <int DT>
+static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s) {
+    return launch_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+        bwd_dkv_vec_kernel<DT, nc, u, g, lph, true, 0><<<grid, block, 0, s>>>(a);
+    });
+}
+
 template <int DT, int XL>
 static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
@@ -994,6 +1053,8 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
                 bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 bwd_dq_vec_kernel<DT, 1, XL == 2 ? GT_BWD_BF16_DQ_XL2_U : XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+            else if (XL == 0 && launch_dq_fixed<DT>(a, grid, block, s, stream_kv))
+                ;
             else if (a.NC == 1)
                 bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
@@ -1043,6 +1104,8 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
                 bwd_dkv_vec_kernel<DT, 2, XL ? 2 : GT_BWD_F32_DKV_U, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? GT_BWD_BF16_DKV_XL1_U : GT_BWD_BF16_DKV_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+            else if (XL == 0 && launch_dkv_fixed<DT>(a, grid, block, s))
+                ;
             else if (a.NC == 1)
                 bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
             else if (a.NC == 2)
