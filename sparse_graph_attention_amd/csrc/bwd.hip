@@ -22,8 +22,6 @@
 // Chunks of split rows leave partial sums that a merge adds in chunk order.
 #include <algorithm>
 
-#include <type_traits>
-
 #include "kernels.hpp"
 
 namespace gt {
@@ -971,49 +969,13 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
 
 // ------------------------------------------------------------ launchers
 
-// Whole rows of 32, 64 or 128 vectors with the head width known at compile
-// time (plain logits), for head splits besides the two tuned shapes.  The
-// run-time layout works out each item's lane groups and heads with integer
-// divisions and masks every vector; these instances do not, which the two
-// passes feel more than the forward does (power-law graph: fp32 4x128
-// 21.1 -> 18.3 ms, 8x32 11.2 -> 9.0 ms; bf16 8x64 13.3 -> 9.9 ms, 16x64
-// 36.2 -> 19.5 ms).  F(NC, U, G, LPH) launches one instance; false when
-// none fits.
-template <typename F>
-static bool launch_fixed_layout(const Args& a, F&& f) {
-    if (a.R != a.NC * a.G) return false;
-    if (a.G == 64 && a.NC == 2) {
-        switch (a.lph) {
-            case 8: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 8>{}); return true;
-            case 16: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 16>{}); return true;
-            case 32: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 32>{}); return true;
-            case 64: f(std::integral_constant<int, 2>{}, std::integral_constant<int, 4>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 64>{}); return true;
-            default: return false;
-        }
-    }
-    if (a.G == 64 && a.NC == 1) {
-        switch (a.lph) {
-            case 4: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 4>{}); return true;
-            case 8: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 8>{}); return true;
-            case 16: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 16>{}); return true;
-            case 32: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 64>{}, std::integral_constant<int, 32>{}); return true;
-            default: return false;
-        }
-    }
-    if (a.G == 32 && a.NC == 1) {
-        switch (a.lph) {
-            case 4: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 32>{}, std::integral_constant<int, 4>{}); return true;
-            case 8: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 32>{}, std::integral_constant<int, 8>{}); return true;
-            case 16: f(std::integral_constant<int, 1>{}, std::integral_constant<int, 8>{}, std::integral_constant<int, 32>{}, std::integral_constant<int, 16>{}); return true;
-            default: return false;
-        }
-    }
-    return false;
-}
-
+// The compile-time layouts (for_fixed_layout) with plain logits.  The
+// run-time layout costs the two passes more than it costs the forward
+// (power-law graph: fp32 4x128 21.1 -> 18.3 ms, 8x32 11.2 -> 9.0 ms; bf16
+// 8x64 13.3 -> 9.9 ms, 16x64 36.2 -> 19.5 ms).
 template <int DT>
 static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
-    return launch_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+    return for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         if (DT == kF32 && nc == 2 && ntl)
             bwd_dq_vec_kernel<DT, nc, u, g, lph, true, 0, true><<<grid, block, 0, s>>>(a);
         else
@@ -1023,7 +985,7 @@ static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s,
 
 template <int DT>
 static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s) {
-    return launch_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+    return for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         bwd_dkv_vec_kernel<DT, nc, u, g, lph, true, 0><<<grid, block, 0, s>>>(a);
     });
 }

@@ -743,53 +743,17 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 
 // ------------------------------------------------------------ launchers
 
-// Whole rows with the lane layout known at compile time (plain logits): the
-// two tuned shapes' instances, for other head splits of rows of 32, 64 or 128
-// vectors.  Against the run-time layout they save the per-item index
-// arithmetic and the lane masks: 4-6% on the power-law graph (fp32 4x128,
-// 16x32, 8x32, 2x256; bf16 8x64, 16x64, 8x128).  False when none fits.
-template <int DT, int NC, int G, int LPH>
-static void launch_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
-    constexpr int U = NC == 1 ? 8 : 4;
-    if constexpr (DT == kF32 && NC == 2) {
-        if (ntl) {
-            fused_vec_kernel<DT, NC, U, G, LPH, true, true, 0><<<grid, block, 0, s>>>(a);
-            return;
-        }
-    }
-    fused_vec_kernel<DT, NC, U, G, LPH, true, false, 0><<<grid, block, 0, s>>>(a);
-}
-
+// The compile-time layouts (for_fixed_layout) with plain logits: 4-6% on
+// the power-law graph against the run-time layout (fp32 4x128, 16x32, 8x32,
+// 2x256; bf16 8x64, 16x64, 8x128).  NTL as for the tuned fp32 instance.
 template <int DT>
 static bool launch_fixed_lph(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
-    if (a.R != a.NC * a.G) return false;
-    if (a.G == 64 && a.NC == 2) {
-        switch (a.lph) {
-            case 8: launch_fixed<DT, 2, 64, 8>(a, grid, block, s, ntl); return true;
-            case 16: launch_fixed<DT, 2, 64, 16>(a, grid, block, s, ntl); return true;
-            case 32: launch_fixed<DT, 2, 64, 32>(a, grid, block, s, ntl); return true;
-            case 64: launch_fixed<DT, 2, 64, 64>(a, grid, block, s, ntl); return true;
-            default: return false;
-        }
-    }
-    if (a.G == 64 && a.NC == 1) {
-        switch (a.lph) {
-            case 4: launch_fixed<DT, 1, 64, 4>(a, grid, block, s, false); return true;
-            case 8: launch_fixed<DT, 1, 64, 8>(a, grid, block, s, false); return true;
-            case 16: launch_fixed<DT, 1, 64, 16>(a, grid, block, s, false); return true;
-            case 32: launch_fixed<DT, 1, 64, 32>(a, grid, block, s, false); return true;
-            default: return false;
-        }
-    }
-    if (a.G == 32 && a.NC == 1) {
-        switch (a.lph) {
-            case 4: launch_fixed<DT, 1, 32, 4>(a, grid, block, s, false); return true;
-            case 8: launch_fixed<DT, 1, 32, 8>(a, grid, block, s, false); return true;
-            case 16: launch_fixed<DT, 1, 32, 16>(a, grid, block, s, false); return true;
-            default: return false;
-        }
-    }
-    return false;
+    return for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+        if (DT == kF32 && nc == 2 && ntl)
+            fused_vec_kernel<DT, nc, u, g, lph, true, true, 0><<<grid, block, 0, s>>>(a);
+        else
+            fused_vec_kernel<DT, nc, u, g, lph, true, false, 0><<<grid, block, 0, s>>>(a);
+    });
 }
 
 template <int DT, int XL>

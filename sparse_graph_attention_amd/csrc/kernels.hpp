@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace gt {
@@ -82,6 +84,52 @@ inline hipError_t for_slices(Args a, int64_t items, F fn) {
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
+}
+
+// Whole rows of 32, 64 or 128 vectors (R == NC * G) get kernel instances
+// with the lane layout known at compile time for every head width: the
+// run-time layout works out each item's lane groups and heads with integer
+// divisions and masks every vector.  Calls f(NC, U, G, LPH) with
+// std::integral_constant arguments (U: edges in flight per lane group) and
+// returns true, or returns false when the layout has no such instance.
+template <typename F>
+inline bool for_fixed_layout(const Args& a, F&& f) {
+    using std::integral_constant;
+    if (a.R != a.NC * a.G) return false;
+    if (a.G == 64 && a.NC == 2) {
+        using N = integral_constant<int, 2>;
+        using U = integral_constant<int, 4>;
+        using G = integral_constant<int, 64>;
+        switch (a.lph) {
+            case 8: f(N{}, U{}, G{}, integral_constant<int, 8>{}); return true;
+            case 16: f(N{}, U{}, G{}, integral_constant<int, 16>{}); return true;
+            case 32: f(N{}, U{}, G{}, integral_constant<int, 32>{}); return true;
+            case 64: f(N{}, U{}, G{}, integral_constant<int, 64>{}); return true;
+            default: return false;
+        }
+    }
+    if (a.NC == 1 && (a.G == 64 || a.G == 32)) {
+        using N = integral_constant<int, 1>;
+        using U = integral_constant<int, 8>;
+        if (a.G == 64) {
+            using G = integral_constant<int, 64>;
+            switch (a.lph) {
+                case 4: f(N{}, U{}, G{}, integral_constant<int, 4>{}); return true;
+                case 8: f(N{}, U{}, G{}, integral_constant<int, 8>{}); return true;
+                case 16: f(N{}, U{}, G{}, integral_constant<int, 16>{}); return true;
+                case 32: f(N{}, U{}, G{}, integral_constant<int, 32>{}); return true;
+                default: return false;
+            }
+        }
+        using G = integral_constant<int, 32>;
+        switch (a.lph) {
+            case 4: f(N{}, U{}, G{}, integral_constant<int, 4>{}); return true;
+            case 8: f(N{}, U{}, G{}, integral_constant<int, 8>{}); return true;
+            case 16: f(N{}, U{}, G{}, integral_constant<int, 16>{}); return true;
+            default: return false;
+        }
+    }
+    return false;
 }
 
 // Plan: clears the counters and lists heavy rows and their chunks.

@@ -199,6 +199,10 @@ static hipError_t launch_sddmm_dt(const Args& a0, hipStream_t s) {
                 sddmm_vec_kernel<DT, 1, GT_SDDMM_BF16_U, 32, 4, false><<<grid, block, 0, s>>>(a);
                 return;
             }
+            if (for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+                    sddmm_vec_kernel<DT, nc, u, g, lph, false><<<grid, block, 0, s>>>(a);
+                }))
+                return;
             switch (a.NC) {
                 case 1: sddmm_vec_kernel<DT, 1, 8><<<grid, block, 0, s>>>(a); break;
                 case 2: sddmm_vec_kernel<DT, 2, 4><<<grid, block, 0, s>>>(a); break;

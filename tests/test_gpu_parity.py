@@ -344,6 +344,15 @@ def test_unfused_split_rows(dtype, D):
         check_stages(custom(N, src, dst, 6 if D == 10 else 8, D, dtype, seed=21))
 
 
+@pytest.mark.parametrize("H,D", [(8, 64), (2, 256), (16, 32), (4, 128), (8, 32), (16, 16), (8, 16), (4, 32), (2, 64),
+                                 (8, 128), (4, 256), (4, 64), (2, 128), (3, 128), (5, 16)])
+@pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
+def test_unfused_shapes(H, D, dtype):
+    # every compile-time lane layout of the SDDMM and SpMM, and run-time ones
+    with chunk_edges(40):
+        check_stages(random_graph(H * 500 + D, 70, 900, H, D, dtype))
+
+
 def test_softmax_in_place_and_odd_heads():
     w = random_graph(31, 50, 700, 3, 8)
     t = to_dev(w)
