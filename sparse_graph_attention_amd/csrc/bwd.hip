@@ -973,20 +973,28 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
 // run-time layout costs the two passes more than it costs the forward
 // (power-law graph: fp32 4x128 21.1 -> 18.3 ms, 8x32 11.2 -> 9.0 ms; bf16
 // 8x64 13.3 -> 9.9 ms, 16x64 36.2 -> 19.5 ms).
-template <int DT>
+// With logit options the heads per edge are then known too, so bias and
+// weights load as batches and dropout draws its keep bits per batch, as in
+// the tuned instances (without, a shape off them ran 2-6 times slower: bf16
+// 8x64 with dropout 56.9 ms against 9.8 ms plain).  These instances keep
+// fewer edges in flight, like the tuned ones: 4 per lane group (2 in the
+// source pass of rows of 128 vectors).
+template <int DT, int XL>
 static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
     return for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-        if (DT == kF32 && nc == 2 && ntl)
-            bwd_dq_vec_kernel<DT, nc, u, g, lph, true, 0, true><<<grid, block, 0, s>>>(a);
+        constexpr int U = XL ? 4 : decltype(u)::value;
+        if (XL == 0 && DT == kF32 && nc == 2 && ntl)
+            bwd_dq_vec_kernel<DT, nc, U, g, lph, true, XL, true><<<grid, block, 0, s>>>(a);
         else
-            bwd_dq_vec_kernel<DT, nc, u, g, lph, true, 0><<<grid, block, 0, s>>>(a);
+            bwd_dq_vec_kernel<DT, nc, U, g, lph, true, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
-template <int DT>
+template <int DT, int XL>
 static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s) {
     return for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-        bwd_dkv_vec_kernel<DT, nc, u, g, lph, true, 0><<<grid, block, 0, s>>>(a);
+        constexpr int U = XL ? (decltype(nc)::value == 2 ? 2 : 4) : decltype(u)::value;
+        bwd_dkv_vec_kernel<DT, nc, U, g, lph, true, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
@@ -1015,7 +1023,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
                 bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 bwd_dq_vec_kernel<DT, 1, XL == 2 ? GT_BWD_BF16_DQ_XL2_U : XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
-            else if (XL == 0 && launch_dq_fixed<DT>(a, grid, block, s, stream_kv))
+            else if (launch_dq_fixed<DT, XL>(a, grid, block, s, stream_kv))
                 ;
             else if (a.NC == 1)
                 bwd_dq_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);
@@ -1066,7 +1074,7 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
                 bwd_dkv_vec_kernel<DT, 2, XL ? 2 : GT_BWD_F32_DKV_U, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? GT_BWD_BF16_DKV_XL1_U : GT_BWD_BF16_DKV_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
-            else if (XL == 0 && launch_dkv_fixed<DT>(a, grid, block, s))
+            else if (launch_dkv_fixed<DT, XL>(a, grid, block, s))
                 ;
             else if (a.NC == 1)
                 bwd_dkv_vec_kernel<DT, 1, 8, 0, 0, false, XL><<<grid, block, 0, s>>>(a);

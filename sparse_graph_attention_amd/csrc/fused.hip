@@ -746,13 +746,17 @@ __global__ __launch_bounds__(kBlock) void fused_merge_kernel(const Args a) {
 // The compile-time layouts (for_fixed_layout) with plain logits: 4-6% on
 // the power-law graph against the run-time layout (fp32 4x128, 16x32, 8x32,
 // 2x256; bf16 8x64, 16x64, 8x128).  NTL as for the tuned fp32 instance.
-template <int DT>
+// With logit options the heads per edge are known at compile time too, so
+// bias and weights load as batches and dropout draws its keep bits per
+// batch, as in the tuned instances; 4 edges in flight per lane group.
+template <int DT, int XL>
 static bool launch_fixed_lph(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
     return for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-        if (DT == kF32 && nc == 2 && ntl)
-            fused_vec_kernel<DT, nc, u, g, lph, true, true, 0><<<grid, block, 0, s>>>(a);
+        constexpr int U = XL ? 4 : decltype(u)::value;
+        if (XL == 0 && DT == kF32 && nc == 2 && ntl)
+            fused_vec_kernel<DT, nc, U, g, lph, true, true, XL><<<grid, block, 0, s>>>(a);
         else
-            fused_vec_kernel<DT, nc, u, g, lph, true, false, 0><<<grid, block, 0, s>>>(a);
+            fused_vec_kernel<DT, nc, U, g, lph, true, false, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
@@ -783,7 +787,7 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 // the extended kernel keeps per-edge inputs live: fewer edges in flight
                 fused_vec_kernel<DT, 1, XL == 2 ? 4 : XL == 1 ? GT_BF16_D32_XL1_U : GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
-            else if (XL == 0 && launch_fixed_lph<DT>(a, grid, block, s, DT == kF32 && stream_kv))
+            else if (launch_fixed_lph<DT, XL>(a, grid, block, s, DT == kF32 && stream_kv))
                 ;
             else if (a.NC == 1)
                 fused_vec_kernel<DT, 1, 8, 0, 0, false, false, XL><<<grid, block, 0, s>>>(a);
