@@ -145,16 +145,21 @@ int pow2ceil(int64_t x) {
 }
 bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
 
-// Vector layout when every head is a power-of-two number of 16-byte vectors,
-// the row fits in four vectors per lane and the feature arrays are aligned;
-// the scalar layout otherwise.
+// Vector layout when every head is a whole number of 16-byte vectors, the
+// row fits in four lane slots per lane and the feature arrays are aligned;
+// the scalar layout otherwise.  A head of vph vectors takes lph =
+// pow2ceil(vph) lane slots, so that head sums stay within aligned lane
+// segments; the slots past vph idle (for example fp32 D = 48: 12 vectors in
+// 16 slots).
 void choose_layout(Args& a, std::initializer_list<const void*> feats) {
     const int bytes = a.dtype == GT_F32 ? 4 : 2;
     const int64_t hb = (int64_t)a.D * bytes;
-    bool vec = hb % 16 == 0 && pow2(hb / 16);
+    bool vec = hb % 16 == 0;
     for (const void* p : feats) vec = vec && aligned16(p);
     if (vec) {
-        a.lph = (int)(hb / 16);
+        a.vph = (int)(hb / 16);
+        a.lph = pow2ceil(a.vph);
+        a.Rm = a.H * a.vph;
         a.R = a.H * a.lph;
         if (a.R >= kWave) {
             a.G = kWave;
@@ -169,7 +174,7 @@ void choose_layout(Args& a, std::initializer_list<const void*> feats) {
     if (!vec) {
         a.G = std::min(kWave, pow2ceil(a.D));
         a.KD = (a.D + a.G - 1) / a.G;
-        a.lph = a.R = a.NC = 0;
+        a.lph = a.R = a.NC = a.vph = a.Rm = 0;
     }
 }
 
@@ -186,8 +191,8 @@ bool choose_layout_ndh(Args& a, std::initializer_list<const void*> feats) {
         if (!aligned16(p)) return false;
     a.vec = 2;
     a.ndh = 1;
-    a.lph = a.H / vn;
-    a.R = (int)R;
+    a.lph = a.vph = a.H / vn;
+    a.R = a.Rm = (int)R;
     a.G = R > kWave ? kWave : pow2ceil(R);
     a.NC = (int)((R + a.G - 1) / a.G);
     return true;
@@ -206,7 +211,7 @@ bool choose_layout_ndh(Args& a, std::initializer_list<const void*> feats) {
 // sums per edge in each pass, lost to the copies at both of those shapes.
 bool ndh_kernels_pay(const Args& a, bool forward) {
     const int64_t hb = (int64_t)a.D * (a.dtype == GT_F32 ? 4 : 2);
-    if (!(hb % 16 == 0 && pow2(hb / 16) && (a.H * hb / 16 + kWave - 1) / kWave <= 4)) return true;
+    if (!(hb % 16 == 0 && (a.H * (int64_t)pow2ceil(hb / 16) + kWave - 1) / kWave <= 4)) return true;
     if (!forward) return false;
     int steps = 0;
     for (int64_t x = a.G / a.lph; x > 1; x >>= 1) ++steps;
@@ -733,7 +738,9 @@ int gt_sparse_mha_bwd_layout(const int64_t* indptr, const int32_t* indices, cons
         at.vec = a.vec;
         at.ndh = a.ndh;
         at.lph = a.lph;
+        at.vph = a.vph;
         at.R = a.R;
+        at.Rm = a.Rm;
         at.G = a.G;
         at.NC = a.NC;
         return run_bwd(a, at, nullptr, nullptr, stream);

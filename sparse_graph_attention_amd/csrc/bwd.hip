@@ -52,7 +52,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const int64_t rowbytes = (int64_t)a.R * 16;
+    // FULL: no idle lane slots (heads of a power of two of vectors)
+    const int vph = FULL ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(FULL ? a.R : a.Rm) * 16;
     const int64_t HD = (int64_t)a.H * a.D;
     const int32_t* __restrict__ idx = a.indices;
 
@@ -62,25 +64,27 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     // row data: q, dO, and per head delta = dO . out and lse (log2 units)
     float q[NC][VN], g[NC][VN], dl[NC], ls[NC];
     bool act[NC];
-    int head[NC];
+    int head[NC], moff[NC];  // moff: byte offset of the lane slot's vector in a row
     const char* qrow = (const char*)a.Q + row * rowbytes;
     const char* grow = (const char*)a.dO + row * rowbytes;
     const char* orow = (const char*)a.O + row * rowbytes;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = FULL || vi < a.R;
-        head[c] = act[c] ? vi / lph : 0;
+        const bool in_row = FULL || vi < a.R;  // a slot of some head (it may idle)
+        act[c] = in_row && (vi & (lph - 1)) < vph;
+        head[c] = in_row ? vi / lph : 0;
+        moff[c] = FULL ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         const U4 zero{0, 0, 0, 0};
-        VT::unpack(act[c] ? ld16(qrow + vi * 16) : zero, q[c]);
-        VT::unpack(act[c] ? ld16(grow + vi * 16) : zero, g[c]);
+        VT::unpack(act[c] ? ld16(qrow + moff[c]) : zero, q[c]);
+        VT::unpack(act[c] ? ld16(grow + moff[c]) : zero, g[c]);
         float o[VN];
-        VT::unpack(act[c] ? ld16(orow + vi * 16) : zero, o);
+        VT::unpack(act[c] ? ld16(orow + moff[c]) : zero, o);
         float d = 0.0f;
 #pragma unroll
         for (int k = 0; k < VN; ++k) d = __builtin_fmaf(g[c][k], o[k], d);
         dl[c] = LPH_ ? seg_sum_c<LPH_>(d) : seg_sum(d, lph);
-        ls[c] = act[c] ? a.lse_in[row * a.H + vi / lph] * kLog2e : 0.0f;
+        ls[c] = in_row ? a.lse_in[row * a.H + vi / lph] * kLog2e : 0.0f;
     }
     float acc[NC][VN];
 #pragma unroll
@@ -124,12 +128,12 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
+                kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Kb + (int64_t)u[j] * rowbytes + moff[c]) : ld16(Kb + (int64_t)u[j] * rowbytes + moff[c])) : U4{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
+                vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + moff[c]) : ld16(Vb + (int64_t)u[j] * rowbytes + moff[c])) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
         bool bdrop = false;
@@ -205,9 +209,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
             float o[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * a.kscale;
-            st16_nt((char*)a.dQ + row * rowbytes + vi * 16, VT::pack(o));
+            st16_nt((char*)a.dQ + row * rowbytes + moff[c], VT::pack(o));
         } else {
-            float* pa = a.plan.pacc + it.slot * HD + (int64_t)vi * VN;
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)(moff[c] / 16) * VN;
 #pragma unroll
             for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
         }
@@ -242,7 +246,9 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const int64_t rowbytes = (int64_t)a.R * 16;
+    // FULL: no idle lane slots (heads of a power of two of vectors)
+    const int vph = FULL ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(FULL ? a.R : a.Rm) * 16;
     const int64_t HD = (int64_t)a.H * a.D;
     const int32_t* __restrict__ idx = a.indices;
 
@@ -254,15 +260,17 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 
     float kk[NC][VN], vv[NC][VN];
     bool act[NC];
-    int head[NC];
+    int head[NC], moff[NC];  // moff: byte offset of the lane slot's vector in a row
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = FULL || vi < a.R;
-        head[c] = act[c] ? vi / lph : 0;
+        const bool in_row = FULL || vi < a.R;  // a slot of some head (it may idle)
+        act[c] = in_row && (vi & (lph - 1)) < vph;
+        head[c] = in_row ? vi / lph : 0;
+        moff[c] = FULL ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         const U4 zero{0, 0, 0, 0};
-        VT::unpack(act[c] ? ld16((const char*)a.K + src * rowbytes + vi * 16) : zero, kk[c]);
-        VT::unpack(act[c] ? ld16((const char*)a.V + src * rowbytes + vi * 16) : zero, vv[c]);
+        VT::unpack(act[c] ? ld16((const char*)a.K + src * rowbytes + moff[c]) : zero, kk[c]);
+        VT::unpack(act[c] ? ld16((const char*)a.V + src * rowbytes + moff[c]) : zero, vv[c]);
     }
     float dk[NC][VN], dv[NC][VN];
 #pragma unroll
@@ -325,8 +333,8 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const bool go = ok[j] && act[c];
-                qr[j][c] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
-                gr[j][c] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : U4{0, 0, 0, 0};
+                qr[j][c] = go ? ld16(Qb + (int64_t)u[j] * rowbytes + moff[c]) : U4{0, 0, 0, 0};
+                gr[j][c] = go ? ld16(Gb + (int64_t)u[j] * rowbytes + moff[c]) : U4{0, 0, 0, 0};
             }
             st[j] = ok[j] ? a.stats[(int64_t)u[j] * a.H + hsrc] : make_float2(0.0f, 0.0f);
         }
@@ -420,10 +428,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
             float o[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = dk[c][k] * a.kscale;
-            st16_nt((char*)a.dK + src * rowbytes + vi * 16, VT::pack(o));
-            st16_nt((char*)a.dV + src * rowbytes + vi * 16, VT::pack(dv[c]));
+            st16_nt((char*)a.dK + src * rowbytes + moff[c], VT::pack(o));
+            st16_nt((char*)a.dV + src * rowbytes + moff[c], VT::pack(dv[c]));
         } else {
-            float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)vi * VN;
+            float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)(moff[c] / 16) * VN;
 #pragma unroll
             for (int k = 0; k < VN; k += 4) {
                 st16(pa + k, Vec<kF32>::pack(&dk[c][k]));
@@ -1014,9 +1022,9 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     } else if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
-            const bool full = a.R == a.NC * a.G;
+            const bool full = full_rows(a);
             // streamed K/V gathers when K and V are far larger than the Infinity Cache
-            const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            const bool stream_kv = 2 * a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv && XL == 0)
                 bwd_dq_vec_kernel<DT, 2, GT_BWD_F32_DQ_U, 64, 16, true, XL, true><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
@@ -1069,7 +1077,7 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     } else if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
-            const bool full = a.R == a.NC * a.G;
+            const bool full = full_rows(a);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dkv_vec_kernel<DT, 2, XL ? 2 : GT_BWD_F32_DKV_U, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)

@@ -63,7 +63,9 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const int64_t rowbytes = (int64_t)a.R * 16;
+    // FULL: no idle lane slots (heads of a power of two of vectors)
+    const int vph = FULL ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(FULL ? a.R : a.Rm) * 16;
     const int32_t* __restrict__ idx = a.indices;
 
     int32_t un[U];
@@ -71,16 +73,18 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
 
     float q[NC][VN];
     bool act[NC];
-    int head[NC];
+    int head[NC], moff[NC];  // moff: byte offset of the lane slot's vector in a row
     const char* qrow = (const char*)a.Q + row * rowbytes;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = FULL || vi < a.R;
-        head[c] = act[c] ? vi / lph : 0;
+        const bool in_row = FULL || vi < a.R;  // a slot of some head (it may idle)
+        act[c] = in_row && (vi & (lph - 1)) < vph;
+        head[c] = in_row ? vi / lph : 0;
+        moff[c] = FULL ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         // unscaled: the scale goes on the reduced score, so nothing waits for Q
         // before the first gathers are issued
-        const U4 r = act[c] ? ld16(qrow + vi * 16) : U4{0, 0, 0, 0};
+        const U4 r = act[c] ? ld16(qrow + moff[c]) : U4{0, 0, 0, 0};
         VT::unpack(r, q[c]);
     }
 
@@ -132,12 +136,12 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
+                kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Kb + (int64_t)u[j] * rowbytes + moff[c]) : ld16(Kb + (int64_t)u[j] * rowbytes + moff[c])) : U4{0, 0, 0, 0};
 #pragma unroll
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c)
-                vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16) : ld16(Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16)) : U4{0, 0, 0, 0};
+                vr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(Vb + (int64_t)u[j] * rowbytes + moff[c]) : ld16(Vb + (int64_t)u[j] * rowbytes + moff[c])) : U4{0, 0, 0, 0};
         const int64_t nb = eb + (int64_t)epw * U;
         if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
         bool bdrop = false;
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
             float o[VN];
 #pragma unroll
             for (int k = 0; k < VN; ++k) o[k] = acc[c][k] * inv;
-            st16_nt(orow + (c * G + gl) * 16, VT::pack(o));
+            st16_nt(orow + moff[c], VT::pack(o));
             const int vi = c * G + gl;
             if (a.lse_out && (vi & (lph - 1)) == 0) a.lse_out[row * a.H + vi / lph] = lse_of(m[c], l[c]);
         }
@@ -243,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
                 a.plan.pm[h] = m[c];
                 a.plan.pl[h] = l[c];
             }
-            float* pa = a.plan.pacc + it.slot * HD + (int64_t)vi * VN;
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)(moff[c] / 16) * VN;
 #pragma unroll
             for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
         }
@@ -776,10 +780,10 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     if (a0.vec) {
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
-            const bool full = a.R == a.NC * a.G;
+            const bool full = full_rows(a);
             // Streaming K/V gathers pay off only when K and V are far larger than
             // the 256 MB Infinity Cache; smaller ones are partly served from it.
-            const bool stream_kv = 2 * a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            const bool stream_kv = 2 * a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv)
                 fused_vec_kernel<DT, 2, XL == 2 ? 4 : GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)

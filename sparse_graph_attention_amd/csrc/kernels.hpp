@@ -51,7 +51,9 @@ struct Args {
     int vec;       // 1: 16-byte vector layout, 0: scalar layout
     int G;         // lanes per edge group
     int lph;       // vector layout: lanes per head
-    int R;         // vector layout: 16-byte vectors per node row
+    int R;         // vector layout: lane slots per node row (H * lph)
+    int vph;       // vector layout: 16-byte vectors per head in memory (lph = pow2ceil(vph))
+    int Rm;        // vector layout: 16-byte vectors per node row in memory (H * vph)
     int NC;        // vector layout: vectors per lane
     int KD;        // scalar layout: elements per lane
     int ndh;       // features are [N][D][H] (head innermost); vec = 2 selects fused_ndh_kernel
@@ -92,10 +94,14 @@ inline hipError_t for_slices(Args a, int64_t items, F fn) {
 // divisions and masks every vector.  Calls f(NC, U, G, LPH) with
 // std::integral_constant arguments (U: edges in flight per lane group) and
 // returns true, or returns false when the layout has no such instance.
+// Every lane slot of a row holds a vector: no lane idles past the row's end,
+// and heads are a power of two of vectors (no padding slots).
+inline bool full_rows(const Args& a) { return a.R == a.NC * a.G && a.vph == a.lph; }
+
 template <typename F>
 inline bool for_fixed_layout(const Args& a, F&& f) {
     using std::integral_constant;
-    if (a.R != a.NC * a.G) return false;
+    if (!full_rows(a)) return false;
     if (a.G == 64 && a.NC == 2) {
         using N = integral_constant<int, 2>;
         using U = integral_constant<int, 4>;

@@ -37,20 +37,23 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const int64_t rowbytes = (int64_t)a.R * 16;
+    // hot instances have no idle lane slots (heads of a power of two of vectors)
+    const int vph = kHot ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(kHot ? a.R : a.Rm) * 16;
 
     float q[NC][VN];
     bool act[NC], writer[NC];
-    int head[NC];
+    int head[NC], moff[NC];  // moff: byte offset of the lane slot's vector in a row
     const char* qrow = (const char*)a.Q + it.row * rowbytes;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = kHot || vi < a.R;
+        act[c] = kHot || (vi < a.R && (vi & (lph - 1)) < vph);
         writer[c] = act[c] && (vi & (lph - 1)) == 0;
         head[c] = vi / lph;
+        moff[c] = kHot ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         if (act[c]) {
-            VT::unpack(ld16(qrow + vi * 16), q[c]);
+            VT::unpack(ld16(qrow + moff[c]), q[c]);
         } else {
 #pragma unroll
             for (int k = 0; k < VN; ++k) q[c][k] = 0.0f;
@@ -73,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void sddmm_vec_kernel(const Args a) {
         for (int j = 0; j < U; ++j)
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const char* p = Kb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16;
+                const char* p = Kb + (int64_t)u[j] * rowbytes + moff[c];
                 kr[j][c] = (ok[j] && act[c]) ? (NTL ? ld16_nt(p) : ld16(p)) : U4{0, 0, 0, 0};
             }
         // the next batch's source ids load behind this batch's gathers
@@ -185,9 +188,9 @@ static hipError_t launch_sddmm_dt(const Args& a0, hipStream_t s) {
     if (a0.vec) {
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
-            const bool full = a.R == a.NC * a.G;
+            const bool full = full_rows(a);
             // gathers streamed past the caches when K is far larger than the Infinity Cache
-            const bool stream_k = a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            const bool stream_k = a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && a.H == 8 && full) {
                 if (stream_k && GT_UNFUSED_NTL)
                     sddmm_vec_kernel<DT, 2, GT_SDDMM_F32_U, 64, 16, true><<<grid, block, 0, s>>>(a);

@@ -34,16 +34,20 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    const int64_t rowbytes = (int64_t)a.R * 16;
+    // hot instances have no idle lane slots (heads of a power of two of vectors)
+    const int vph = kHot ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(kHot ? a.R : a.Rm) * 16;
 
     bool act[NC];
-    int head[NC];
+    int head[NC], moff[NC];  // moff: byte offset of the lane slot's vector in a row
     float acc[NC][VN];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int vi = c * G + gl;
-        act[c] = kHot || vi < a.R;
-        head[c] = act[c] ? vi / lph : 0;
+        const bool in_row = kHot || vi < a.R;  // a slot of some head (it may idle)
+        act[c] = in_row && (vi & (lph - 1)) < vph;
+        head[c] = in_row ? vi / lph : 0;
+        moff[c] = kHot ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
 #pragma unroll
         for (int k = 0; k < VN; ++k) acc[c][k] = 0.0f;
     }
@@ -69,7 +73,7 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const bool go = ok[j] && act[c];
-                const char* p = Vb + (int64_t)u[j] * rowbytes + (c * G + gl) * 16;
+                const char* p = Vb + (int64_t)u[j] * rowbytes + moff[c];
                 vr[j][c] = go ? (NTL ? ld16_nt(p) : ld16(p)) : U4{0, 0, 0, 0};
                 if constexpr (!kHot) al[j][c] = go ? a.alpha_in[(eb + grp + (int64_t)j * epw) * a.H + head[c]] : 0.0f;
             }
@@ -103,16 +107,16 @@ __global__ __launch_bounds__(kBlock) void spmm_vec_kernel(const Args a) {
         for (int c = 0; c < NC; ++c)
             if (act[c]) {
                 if (kHot)
-                    st16_nt(orow + (c * G + gl) * 16, VT::pack(acc[c]));
+                    st16_nt(orow + moff[c], VT::pack(acc[c]));
                 else
-                    st16(orow + (c * G + gl) * 16, VT::pack(acc[c]));
+                    st16(orow + moff[c], VT::pack(acc[c]));
             }
     } else {
         const int64_t HD = (int64_t)a.H * a.D;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             if (!act[c]) continue;
-            float* pa = a.plan.pacc + it.slot * HD + (int64_t)(c * G + gl) * VN;
+            float* pa = a.plan.pacc + it.slot * HD + (int64_t)(moff[c] / 16) * VN;
 #pragma unroll
             for (int k = 0; k < VN; k += 4) st16(pa + k, Vec<kF32>::pack(&acc[c][k]));
         }
@@ -188,9 +192,9 @@ static hipError_t launch_spmm_dt(const Args& a0, hipStream_t s) {
     if (a0.vec) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             const dim3 grid(gx);
-            const bool full = a.R == a.NC * a.G;
+            const bool full = full_rows(a);
             // gathers streamed past the caches when V is far larger than the Infinity Cache
-            const bool stream_v = a.N * (int64_t)a.R * 16 > ((int64_t)1 << 30);
+            const bool stream_v = a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && a.H == 8 && full) {
                 if (stream_v && GT_UNFUSED_NTL)
                     spmm_vec_kernel<DT, 2, GT_SPMM_F32_U, 64, 16, true><<<grid, block, 0, s>>>(a);

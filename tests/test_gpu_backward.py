@@ -210,7 +210,8 @@ def test_bwd_regular16_sampled():
 @pytest.mark.parametrize("H,D", [(1, 1), (3, 5), (2, 7), (1, 64), (4, 33), (8, 100), (2, 256), (16, 64),
                                  (5, 16), (64, 4), (3, 128), (12, 64), (3, 256), (24, 64),
                                  (1, 4), (1, 8), (2, 4), (16, 32), (4, 128), (8, 32), (16, 16), (8, 16), (4, 32),
-                                 (2, 64), (8, 64), (8, 128), (4, 256), (4, 64), (2, 128)])
+                                 (2, 64), (8, 64), (8, 128), (4, 256), (4, 64), (2, 128),
+                                 (8, 48), (8, 40), (4, 24), (3, 12), (2, 80), (16, 48), (8, 96)])
 @pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
 def test_bwd_shapes(H, D, dtype):
     with chunk_edges(40):

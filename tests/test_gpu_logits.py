@@ -160,7 +160,8 @@ def test_variants_small(variant, name, chunk):
 
 @pytest.mark.parametrize("H,D", [(8, 64), (3, 5), (4, 33), (2, 256), (16, 64), (8, 32), (64, 4), (12, 64),
                                  (24, 64), (16, 32), (4, 128), (8, 16), (4, 64), (2, 64), (16, 16), (8, 128),
-                                 (4, 256), (2, 128)])
+                                 (4, 256), (2, 128),
+                                 (8, 48), (8, 40), (4, 24), (3, 12), (2, 80), (16, 48), (8, 96)])
 @pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
 @pytest.mark.parametrize("p", [0.3, 0.0])  # the dropout kernels, and those of bias and weights alone
 def test_variants_shapes(H, D, dtype, p):
