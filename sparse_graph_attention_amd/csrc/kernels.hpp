@@ -98,10 +98,10 @@ inline hipError_t for_slices(Args a, int64_t items, F fn) {
 // and heads are a power of two of vectors (no padding slots).
 inline bool full_rows(const Args& a) { return a.R == a.NC * a.G && a.vph == a.lph; }
 
+// The table of compile-time lane layouts (see for_fixed_layout).
 template <typename F>
-inline bool for_fixed_layout(const Args& a, F&& f) {
+inline bool fixed_layout_table(const Args& a, F&& f) {
     using std::integral_constant;
-    if (!full_rows(a)) return false;
     if (a.G == 64 && a.NC == 2) {
         using N = integral_constant<int, 2>;
         using U = integral_constant<int, 4>;
@@ -136,6 +136,20 @@ inline bool for_fixed_layout(const Args& a, F&& f) {
         }
     }
     return false;
+}
+
+template <typename F>
+inline bool for_fixed_layout(const Args& a, F&& f) {
+    return full_rows(a) && fixed_layout_table(a, f);
+}
+
+// The same table for rows whose lane slots are all in use but whose heads
+// are padded (vph < lph): the instances keep the run-time masks of idle
+// slots and the true row stride, with lane groups and head widths known at
+// compile time.
+template <typename F>
+inline bool for_fixed_padded_layout(const Args& a, F&& f) {
+    return a.R == a.NC * a.G && a.vph != a.lph && fixed_layout_table(a, f);
 }
 
 // Plan: clears the counters and lists heavy rows and their chunks.
