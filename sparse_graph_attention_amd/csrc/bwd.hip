@@ -990,14 +990,14 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
 template <int DT, int XL>
 static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
     if (for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-            constexpr int U = XL ? 4 : decltype(u)::value;
+            constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
             if (XL == 0 && DT == kF32 && nc == 2 && ntl)
                 bwd_dq_vec_kernel<DT, nc, U, g, lph, true, XL, true><<<grid, block, 0, s>>>(a);
             else
                 bwd_dq_vec_kernel<DT, nc, U, g, lph, true, XL><<<grid, block, 0, s>>>(a);
         }))
         return true;
-    return XL == 0 && for_fixed_padded_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+    return XL == 0 && for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         bwd_dq_vec_kernel<DT, nc, u, g, lph, false, 0><<<grid, block, 0, s>>>(a);
     });
 }
@@ -1005,11 +1005,11 @@ static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s,
 template <int DT, int XL>
 static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s) {
     if (for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-            constexpr int U = XL ? (decltype(nc)::value == 2 ? 2 : 4) : decltype(u)::value;
+            constexpr int U = XL ? (decltype(nc)::value >= 2 ? 2 : 4) : decltype(u)::value;
             bwd_dkv_vec_kernel<DT, nc, U, g, lph, true, XL><<<grid, block, 0, s>>>(a);
         }))
         return true;
-    return XL == 0 && for_fixed_padded_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+    return XL == 0 && for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         bwd_dkv_vec_kernel<DT, nc, u, g, lph, false, 0><<<grid, block, 0, s>>>(a);
     });
 }

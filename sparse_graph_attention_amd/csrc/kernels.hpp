@@ -88,7 +88,7 @@ inline hipError_t for_slices(Args a, int64_t items, F fn) {
     return hipSuccess;
 }
 
-// Whole rows of 32, 64 or 128 vectors (R == NC * G) get kernel instances
+// Whole rows of 32 to 256 vectors (R == NC * G) get kernel instances
 // with the lane layout known at compile time for every head width: the
 // run-time layout works out each item's lane groups and heads with integer
 // divisions and masks every vector.  Calls f(NC, U, G, LPH) with
@@ -102,6 +102,20 @@ inline bool full_rows(const Args& a) { return a.R == a.NC * a.G && a.vph == a.lp
 template <typename F>
 inline bool fixed_layout_table(const Args& a, F&& f) {
     using std::integral_constant;
+    if (a.G == 64 && (a.NC == 3 || a.NC == 4)) {  // rows of up to 192 or 256 vectors
+        using U = integral_constant<int, 2>;
+        using G = integral_constant<int, 64>;
+        auto go = [&](auto nc) {
+            switch (a.lph) {
+                case 8: f(nc, U{}, G{}, integral_constant<int, 8>{}); return true;
+                case 16: f(nc, U{}, G{}, integral_constant<int, 16>{}); return true;
+                case 32: f(nc, U{}, G{}, integral_constant<int, 32>{}); return true;
+                case 64: f(nc, U{}, G{}, integral_constant<int, 64>{}); return true;
+                default: return false;
+            }
+        };
+        return a.NC == 3 ? go(integral_constant<int, 3>{}) : go(integral_constant<int, 4>{});
+    }
     if (a.G == 64 && a.NC == 2) {
         using N = integral_constant<int, 2>;
         using U = integral_constant<int, 4>;
@@ -143,13 +157,13 @@ inline bool for_fixed_layout(const Args& a, F&& f) {
     return full_rows(a) && fixed_layout_table(a, f);
 }
 
-// The same table for rows whose lane slots are all in use but whose heads
-// are padded (vph < lph): the instances keep the run-time masks of idle
+// The same table for the other rows: lane slots past the row's end, or
+// padded heads (vph < lph).  The instances keep the run-time masks of idle
 // slots and the true row stride, with lane groups and head widths known at
 // compile time.
 template <typename F>
-inline bool for_fixed_padded_layout(const Args& a, F&& f) {
-    return a.R == a.NC * a.G && a.vph != a.lph && fixed_layout_table(a, f);
+inline bool for_fixed_partial_layout(const Args& a, F&& f) {
+    return !full_rows(a) && fixed_layout_table(a, f);
 }
 
 // Plan: clears the counters and lists heavy rows and their chunks.
