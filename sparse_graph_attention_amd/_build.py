@@ -9,8 +9,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgtattn.so")
 OBJDIR = os.path.join(ROOT, "_build")
-SOURCES = ["api.hip", "plan.hip", "fused.hip", "sddmm.hip", "softmax.hip", "spmm.hip", "bwd.hip", "graph.hip",
-           "calib.hip"]
+# bwd.hip is built as its two passes (bwd_dq.hip, bwd_dkv.hip include it)
+SOURCES = ["api.hip", "plan.hip", "fused.hip", "sddmm.hip", "softmax.hip", "spmm.hip", "bwd_dq.hip", "bwd_dkv.hip",
+           "graph.hip", "calib.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

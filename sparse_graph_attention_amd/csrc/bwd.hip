@@ -24,6 +24,13 @@
 
 #include "kernels.hpp"
 
+// The two passes' launchers compile as separate objects (bwd_dq.hip and
+// bwd_dkv.hip include this file with GT_BWD_PART 1 and 2) so that their many
+// kernel instances build in parallel; 0 compiles both.
+#ifndef GT_BWD_PART
+#define GT_BWD_PART 0
+#endif
+
 namespace gt {
 
 // ------------------------------------------------------------ dQ, vector layout
@@ -423,7 +430,6 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         if (!act[c]) continue;
-        const int vi = c * G + gl;
         if (it.slot < 0) {
             float o[VN];
 #pragma unroll
@@ -964,6 +970,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
     }
 }
 
+#if GT_BWD_PART != 2
 // dw[e] = sum over heads, in head order, of the per-head terms the scalar
 // layout's one-head waves left in part[e][h].
 __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict__ part, int64_t E, int H,
@@ -974,6 +981,8 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
     for (int h = 0; h < H; ++h) t += part[e * H + h];
     dw[e] = t;
 }
+
+#endif
 
 // ------------------------------------------------------------ launchers
 
@@ -987,6 +996,7 @@ __global__ __launch_bounds__(256) void sum_heads_kernel(const float* __restrict_
 // 8x64 with dropout 56.9 ms against 9.8 ms plain).  These instances keep
 // fewer edges in flight, like the tuned ones: 4 per lane group (2 in the
 // source pass of rows of 128 vectors).
+#if GT_BWD_PART != 2
 template <int DT, int XL>
 static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s, bool ntl) {
     if (for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
@@ -997,11 +1007,15 @@ static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s,
                 bwd_dq_vec_kernel<DT, nc, U, g, lph, true, XL><<<grid, block, 0, s>>>(a);
         }))
         return true;
-    return XL == 0 && for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-        bwd_dq_vec_kernel<DT, nc, u, g, lph, false, 0><<<grid, block, 0, s>>>(a);
+    return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+        constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
+        bwd_dq_vec_kernel<DT, nc, U, g, lph, false, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
+#endif
+
+#if GT_BWD_PART != 1
 template <int DT, int XL>
 static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s) {
     if (for_fixed_layout(a, [&](auto nc, auto u, auto g, auto lph) {
@@ -1009,11 +1023,15 @@ static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s
             bwd_dkv_vec_kernel<DT, nc, U, g, lph, true, XL><<<grid, block, 0, s>>>(a);
         }))
         return true;
-    return XL == 0 && for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-        bwd_dkv_vec_kernel<DT, nc, u, g, lph, false, 0><<<grid, block, 0, s>>>(a);
+    return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+        constexpr int U = XL ? (decltype(nc)::value >= 2 ? 2 : 4) : decltype(u)::value;
+        bwd_dkv_vec_kernel<DT, nc, U, g, lph, false, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
+#endif
+
+#if GT_BWD_PART != 2
 template <int DT, int XL>
 static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
@@ -1069,6 +1087,9 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     return launch_sum_merge(a0, 1, a0.dQ, a0.kscale, nullptr, 0.0f, s);
 }
 
+#endif
+
+#if GT_BWD_PART != 1
 template <int DT, int XL>
 static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
@@ -1116,9 +1137,12 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     return launch_sum_merge(a0, 2, a0.dK, a0.kscale, a0.dV, 1.0f, s);
 }
 
-// 0: plain logits; 1: bias, edge weights, dbias or dweight; 2: with dropout
-static int xl_level(const Args& a) { return extended(a) ? (a.drop_thresh ? 2 : 1) : 0; }
+#endif
 
+// 0: plain logits; 1: bias, edge weights, dbias or dweight; 2: with dropout
+[[maybe_unused]] static int xl_level(const Args& a) { return extended(a) ? (a.drop_thresh ? 2 : 1) : 0; }
+
+#if GT_BWD_PART != 2
 hipError_t launch_bwd_dq(const Args& a, hipStream_t s) {
     const int xl = xl_level(a);
     if (a.dtype == kF32)
@@ -1126,11 +1150,15 @@ hipError_t launch_bwd_dq(const Args& a, hipStream_t s) {
     return xl == 0 ? launch_dq_dt<kBF16, 0>(a, s) : xl == 1 ? launch_dq_dt<kBF16, 1>(a, s) : launch_dq_dt<kBF16, 2>(a, s);
 }
 
+#endif
+
+#if GT_BWD_PART != 1
 hipError_t launch_bwd_dkv(const Args& a, hipStream_t s) {
     const int xl = xl_level(a);
     if (a.dtype == kF32)
         return xl == 0 ? launch_dkv_dt<kF32, 0>(a, s) : xl == 1 ? launch_dkv_dt<kF32, 1>(a, s) : launch_dkv_dt<kF32, 2>(a, s);
     return xl == 0 ? launch_dkv_dt<kBF16, 0>(a, s) : xl == 1 ? launch_dkv_dt<kBF16, 1>(a, s) : launch_dkv_dt<kBF16, 2>(a, s);
 }
+#endif
 
 }  // namespace gt

@@ -766,9 +766,10 @@ static bool launch_fixed_lph(const Args& a, dim3 grid, dim3 block, hipStream_t s
                 fused_vec_kernel<DT, nc, U, g, lph, true, false, XL><<<grid, block, 0, s>>>(a);
         }))
         return true;
-    // rows with idle lane slots (plain logits)
-    return XL == 0 && for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
-        fused_vec_kernel<DT, nc, u, g, lph, false, false, 0><<<grid, block, 0, s>>>(a);
+    // rows with idle lane slots
+    return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
+        constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
+        fused_vec_kernel<DT, nc, U, g, lph, false, false, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
