@@ -34,7 +34,7 @@
 namespace gt {
 
 // ------------------------------------------------------------ dQ, vector layout
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, int XL, bool NTL = false>
+template <int DT, int NC, int U, int G_, int LPH_, int FULL, int XL, bool NTL = false>
 __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     // hot instances: the heads per edge are known, so the batched dropout
@@ -59,9 +59,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    // FULL: no idle lane slots (heads of a power of two of vectors)
-    const int vph = FULL ? lph : a.vph;
-    const int64_t rowbytes = (int64_t)(FULL ? a.R : a.Rm) * 16;
+    // FULL 1: no idle lane slots; 2: every slot in a head, heads padded (vph < lph);
+    // 0: slots past the row's end too
+    const int vph = FULL == 1 ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(FULL == 1 ? a.R : a.Rm) * 16;
     const int64_t HD = (int64_t)a.H * a.D;
     const int32_t* __restrict__ idx = a.indices;
 
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
         const bool in_row = FULL || vi < a.R;  // a slot of some head (it may idle)
         act[c] = in_row && (vi & (lph - 1)) < vph;
         head[c] = in_row ? vi / lph : 0;
-        moff[c] = FULL ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
+        moff[c] = FULL == 1 ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         const U4 zero{0, 0, 0, 0};
         VT::unpack(act[c] ? ld16(qrow + moff[c]) : zero, q[c]);
         VT::unpack(act[c] ? ld16(grow + moff[c]) : zero, g[c]);
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
 // ------------------------------------------------------------ dK, dV, vector layout
 // a.indptr / a.indices are the source-sorted graph: item rows are sources u,
 // "edges" are their out-edges with the destination v in a.indices.
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, int XL>
+template <int DT, int NC, int U, int G_, int LPH_, int FULL, int XL>
 __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     // hot instances: the heads per edge are known, so the batched dropout
@@ -253,9 +254,10 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    // FULL: no idle lane slots (heads of a power of two of vectors)
-    const int vph = FULL ? lph : a.vph;
-    const int64_t rowbytes = (int64_t)(FULL ? a.R : a.Rm) * 16;
+    // FULL 1: no idle lane slots; 2: every slot in a head, heads padded (vph < lph);
+    // 0: slots past the row's end too
+    const int vph = FULL == 1 ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(FULL == 1 ? a.R : a.Rm) * 16;
     const int64_t HD = (int64_t)a.H * a.D;
     const int32_t* __restrict__ idx = a.indices;
 
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_vec_kernel(const Args a) {
         const bool in_row = FULL || vi < a.R;  // a slot of some head (it may idle)
         act[c] = in_row && (vi & (lph - 1)) < vph;
         head[c] = in_row ? vi / lph : 0;
-        moff[c] = FULL ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
+        moff[c] = FULL == 1 ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         const U4 zero{0, 0, 0, 0};
         VT::unpack(act[c] ? ld16((const char*)a.K + src * rowbytes + moff[c]) : zero, kk[c]);
         VT::unpack(act[c] ? ld16((const char*)a.V + src * rowbytes + moff[c]) : zero, vv[c]);
@@ -1009,7 +1011,10 @@ static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s,
         return true;
     return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
-        bwd_dq_vec_kernel<DT, nc, U, g, lph, false, XL><<<grid, block, 0, s>>>(a);
+        if (a.R == a.NC * a.G)  // padded heads filling the lane groups: heads per edge known
+            bwd_dq_vec_kernel<DT, nc, U, g, lph, 2, XL><<<grid, block, 0, s>>>(a);
+        else
+            bwd_dq_vec_kernel<DT, nc, U, g, lph, 0, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
@@ -1025,7 +1030,10 @@ static bool launch_dkv_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s
         return true;
     return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         constexpr int U = XL ? (decltype(nc)::value >= 2 ? 2 : 4) : decltype(u)::value;
-        bwd_dkv_vec_kernel<DT, nc, U, g, lph, false, XL><<<grid, block, 0, s>>>(a);
+        if (a.R == a.NC * a.G)  // padded heads filling the lane groups: heads per edge known
+            bwd_dkv_vec_kernel<DT, nc, U, g, lph, 2, XL><<<grid, block, 0, s>>>(a);
+        else
+            bwd_dkv_vec_kernel<DT, nc, U, g, lph, 0, XL><<<grid, block, 0, s>>>(a);
     });
 }
 

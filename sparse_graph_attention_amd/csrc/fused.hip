@@ -38,7 +38,7 @@ namespace gt {
 // G_ and LPH_ are compile-time lane-group and lanes-per-head sizes when
 // nonzero, else read from the arguments.  FULL: the row is exactly NC*G
 // vectors (no idle lanes).  U edges per group are in flight.
-template <int DT, int NC, int U, int G_, int LPH_, bool FULL, bool NTL, int XL>
+template <int DT, int NC, int U, int G_, int LPH_, int FULL, bool NTL, int XL>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     using VT = Vec<DT>;
     // hot instances: the heads per edge are known, so the batched dropout
@@ -63,9 +63,10 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     const int epw = kWave / G;
     const int grp = lane / G;
     const int gl = lane & (G - 1);
-    // FULL: no idle lane slots (heads of a power of two of vectors)
-    const int vph = FULL ? lph : a.vph;
-    const int64_t rowbytes = (int64_t)(FULL ? a.R : a.Rm) * 16;
+    // FULL 1: no idle lane slots; 2: every slot in a head, heads padded (vph < lph);
+    // 0: slots past the row's end too
+    const int vph = FULL == 1 ? lph : a.vph;
+    const int64_t rowbytes = (int64_t)(FULL == 1 ? a.R : a.Rm) * 16;
     const int32_t* __restrict__ idx = a.indices;
 
     int32_t un[U];
@@ -81,7 +82,7 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
         const bool in_row = FULL || vi < a.R;  // a slot of some head (it may idle)
         act[c] = in_row && (vi & (lph - 1)) < vph;
         head[c] = in_row ? vi / lph : 0;
-        moff[c] = FULL ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
+        moff[c] = FULL == 1 ? vi * 16 : (head[c] * vph + (vi & (lph - 1))) * 16;
         // unscaled: the scale goes on the reduced score, so nothing waits for Q
         // before the first gathers are issued
         const U4 r = act[c] ? ld16(qrow + moff[c]) : U4{0, 0, 0, 0};
@@ -769,7 +770,10 @@ static bool launch_fixed_lph(const Args& a, dim3 grid, dim3 block, hipStream_t s
     // rows with idle lane slots
     return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
-        fused_vec_kernel<DT, nc, U, g, lph, false, false, XL><<<grid, block, 0, s>>>(a);
+        if (a.R == a.NC * a.G)  // padded heads filling the lane groups: heads per edge known
+            fused_vec_kernel<DT, nc, U, g, lph, 2, false, XL><<<grid, block, 0, s>>>(a);
+        else
+            fused_vec_kernel<DT, nc, U, g, lph, 0, false, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
