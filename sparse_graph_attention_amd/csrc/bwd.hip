@@ -34,6 +34,7 @@
 namespace gt {
 
 // ------------------------------------------------------------ dQ, vector layout
+// Template parameters as for the forward's fused_vec_kernel (G_, LPH_, FULL).
 template <int DT, int NC, int U, int G_, int LPH_, int FULL, int XL, bool NTL = false>
 __global__ __launch_bounds__(kBlock) void bwd_dq_vec_kernel(const Args a) {
     using VT = Vec<DT>;

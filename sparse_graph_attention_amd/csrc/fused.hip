@@ -36,8 +36,10 @@ namespace gt {
 // ------------------------------------------------------------ vector layout
 //
 // G_ and LPH_ are compile-time lane-group and lanes-per-head sizes when
-// nonzero, else read from the arguments.  FULL: the row is exactly NC*G
-// vectors (no idle lanes).  U edges per group are in flight.
+// nonzero, else read from the arguments.  FULL 1: the row is exactly NC*G
+// vectors (no idle lane slot); 2: every slot belongs to a head, but heads
+// are padded (vph < lph slots hold vectors); 0: slots may also lie past the
+// row's end.  U edges per group are in flight.
 template <int DT, int NC, int U, int G_, int LPH_, int FULL, bool NTL, int XL>
 __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     using VT = Vec<DT>;
