@@ -254,39 +254,26 @@ __global__ __launch_bounds__(256) void lower_bounds_kernel(const uint32_t* __res
     offsets[v] = lo;
 }
 
-// rows[p] = the row holding CSR position p: the last row r with indptr[r] <= p.
-// A wave takes kRowSpan consecutive positions; it finds the rows of its first
-// and last position in all of indptr, then each position's row between
-// those two.
-constexpr int kRowItems = 16;
-constexpr int64_t kRowSpan = (int64_t)kWave * kRowItems;
+// rows[p] = the row holding CSR position p.  A wave takes kFillRows
+// consecutive rows, lane j loading the offset of row r0 + j (kFillRows + 1
+// offsets fit the wave), and its lanes write each row's positions in turn,
+// 64 at a time.  Every position is written once, by coalesced stores.  A
+// binary search per position, which cost each one a chain of dependent
+// loads, took 34 us on a 4k-node molecule batch against 12 us here; on the
+// power-law graph, where one wave fills a 50,000-edge row alone, 59 against
+// 69 us.
+constexpr int kFillRows = kWave - 1;
 
-// Last r in [lo, hi] with indptr[r] <= p, given indptr[lo] <= p.
-__device__ __forceinline__ int64_t last_row_at_or_below(const int64_t* __restrict__ indptr, int64_t p, int64_t lo,
-                                                        int64_t hi) {
-    while (lo < hi) {
-        const int64_t mid = lo + ((hi - lo + 1) >> 1);
-        if (indptr[mid] <= p)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
-__global__ __launch_bounds__(256) void row_of_position_kernel(const int64_t* __restrict__ indptr, int64_t nrows,
-                                                               int64_t n, uint32_t* __restrict__ rows) {
+__global__ __launch_bounds__(256) void fill_rows_kernel(const int64_t* __restrict__ indptr, int64_t nrows,
+                                                        uint32_t* __restrict__ rows) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t wave = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave;
-    const int64_t p0 = wave * kRowSpan;
-    if (p0 >= n) return;
-    const int64_t p1 = (p0 + kRowSpan < n ? p0 + kRowSpan : n) - 1;
-    const int64_t r0 = last_row_at_or_below(indptr, p0, 0, nrows - 1);
-    const int64_t r1 = last_row_at_or_below(indptr, p1, r0, nrows - 1);
-#pragma unroll 4
-    for (int i = 0; i < kRowItems; ++i) {
-        const int64_t p = p0 + (int64_t)i * kWave + lane;
-        if (p < n) rows[p] = (uint32_t)last_row_at_or_below(indptr, p, r0, r1);
+    const int64_t r0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kWave * kFillRows;
+    if (r0 >= nrows) return;
+    const int nr = (int)(nrows - r0 < kFillRows ? nrows - r0 : kFillRows);
+    const int64_t off = lane <= nr ? indptr[r0 + lane] : 0;
+    for (int j = 0; j < nr; ++j) {
+        const int64_t b = __shfl(off, j, kWave), e = __shfl(off, j + 1, kWave);
+        for (int64_t p = b + lane; p < e; p += kWave) rows[p] = (uint32_t)(r0 + j);
     }
 }
 
@@ -366,9 +353,9 @@ hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, i
 }
 
 hipError_t launch_row_of_position(const int64_t* indptr, int64_t nrows, int64_t n, uint32_t* rows, hipStream_t s) {
-    if (n == 0) return hipSuccess;
-    const int64_t waves = cdiv(n, kRowSpan);
-    row_of_position_kernel<<<(unsigned)cdiv(waves * kWave, 256), 256, 0, s>>>(indptr, nrows, n, rows);
+    if (n == 0 || nrows == 0) return hipSuccess;
+    const int64_t waves = cdiv(nrows, kFillRows);
+    fill_rows_kernel<<<(unsigned)cdiv(waves * kWave, 256), 256, 0, s>>>(indptr, nrows, rows);
     return hipGetLastError();
 }
 
