@@ -26,8 +26,8 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
-from tests.test_gpu_parity import (chunk_edges, custom, dev, host, oracle_inputs, random_graph, sample_rows, say,
-                                   to_dev, workload)
+from tests.test_gpu_parity import (check_fused_full, chunk_edges, custom, dev, host, oracle_inputs, random_graph,
+                                   sample_rows, say, to_dev, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -307,3 +307,20 @@ def test_bwd_deterministic():
 @pytest.mark.parametrize("name", ["powerlaw", "lognormal"])
 def test_bwd_large_sampled(name):
     check_bwd_sampled(with_grad(workload(name)))
+
+
+@pytest.mark.parametrize("H,D,dtype", [(8, 48, gtgen.F32), (8, 96, gtgen.BF16), (6, 64, gtgen.F32), (3, 128, gtgen.F32),
+                                       (16, 64, gtgen.F32), (16, 128, gtgen.BF16), (24, 64, gtgen.BF16),
+                                       (8, 64, gtgen.F32), (8, 32, gtgen.BF16)])
+def test_split_rows_every_layout(H, D, dtype):
+    # a hub destination and a hub source split into chunks, for padded heads,
+    # rows that end before their last lane group and wide rows: the chunk
+    # partials are indexed by memory position, not lane slot
+    N, E = 60, 1500
+    src, dst = gtgen.random_coo(H * 100 + D, N, E)
+    dst = np.where(np.arange(E) < 500, 5, dst)
+    src = np.where((np.arange(E) >= 500) & (np.arange(E) < 900), 9, src)
+    w = custom(N, src, dst, H, D, dtype, seed=H + D)
+    with chunk_edges(37):
+        check_fused_full(w)
+        check_bwd_full(with_grad(w))

@@ -294,3 +294,20 @@ def test_variants_large_sampled(name, p):
         BV[i] = (ac[:, :, None] * Ga[dst]).sum(0)
     check_bound(dk[srcs], rk, BK, btol, "dK %s (%d sources)" % (name, len(srcs)))
     check_bound(dv[srcs], rv, BV, btol, "dV %s (%d sources)" % (name, len(srcs)))
+
+
+@pytest.mark.parametrize("H,D,dtype", [(8, 48, gtgen.F32), (8, 96, gtgen.BF16), (6, 64, gtgen.F32), (16, 64, gtgen.F32),
+                                       (16, 128, gtgen.BF16), (4, 128, gtgen.F32)])
+@pytest.mark.parametrize("p", [0.3, 0.0])
+def test_split_rows_every_layout(H, D, dtype, p):
+    # a hub destination and a hub source split into chunks, with bias, weights
+    # and dropout, for padded heads, rows that end before their last lane
+    # group, wide rows and a compile-time layout
+    from tests.test_gpu_parity import custom
+    N, E = 60, 1500
+    src, dst = gtgen.random_coo(H * 10 + D, N, E)
+    dst = np.where(np.arange(E) < 500, 5, dst)
+    src = np.where((np.arange(E) >= 500) & (np.arange(E) < 900), 9, src)
+    w = with_grad(custom(N, src, dst, H, D, dtype, seed=H * D))
+    with chunk_edges(37):
+        check_full(w, make_opts(w, H + 2 * D, bias=True, weights=True, p=p))
