@@ -355,6 +355,18 @@ def test_unfused_shapes(H, D, dtype):
         check_stages(random_graph(H * 500 + D, 70, 900, H, D, dtype))
 
 
+@pytest.mark.parametrize("H,D,dtype", [(8, 48, gtgen.F32), (8, 96, gtgen.BF16), (6, 64, gtgen.F32), (16, 64, gtgen.F32),
+                                       (8, 64, gtgen.F32), (4, 64, gtgen.BF16)])
+def test_unfused_split_rows_every_layout(H, D, dtype):
+    # a hub row split into chunks: the SpMM's chunk partials are indexed by
+    # memory position (padded heads, early-ending and wide rows)
+    N, E = 60, 1500
+    src, dst = gtgen.random_coo(H * 7 + D, N, E)
+    dst = np.where(np.arange(E) < 500, 5, dst)
+    with chunk_edges(37):
+        check_stages(custom(N, src, dst, H, D, dtype, seed=D))
+
+
 def test_softmax_in_place_and_odd_heads():
     w = random_graph(31, 50, 700, 3, 8)
     t = to_dev(w)
