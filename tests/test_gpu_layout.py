@@ -74,7 +74,7 @@ def test_ndh_molecules_bf16():
 
 
 @pytest.mark.parametrize("H,D", [(4, 16), (16, 4), (64, 1), (8, 8), (32, 2), (4, 1), (8, 10), (3, 5), (2, 7),
-                                 (8, 64), (12, 4), (16, 64), (4, 100), (32, 32), (8, 200), (64, 16)])
+                                 (8, 64), (12, 4), (16, 64), (4, 100), (32, 32), (8, 200), (64, 16), (8, 48), (8, 96)])
 @pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
 def test_ndh_shapes(H, D, dtype):
     with chunk_edges(30):
@@ -139,7 +139,7 @@ def test_ndh_bwd_molecules_bf16():
 
 
 @pytest.mark.parametrize("H,D", [(4, 16), (16, 4), (64, 1), (8, 8), (32, 2), (4, 1), (8, 10), (3, 5), (8, 64),
-                                 (12, 4), (16, 64), (4, 100), (32, 32), (8, 200), (64, 16)])
+                                 (12, 4), (16, 64), (4, 100), (32, 32), (8, 200), (64, 16), (8, 48), (8, 96)])
 @pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
 def test_ndh_bwd_shapes(H, D, dtype):
     with chunk_edges(30):
