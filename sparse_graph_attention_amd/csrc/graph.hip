@@ -23,7 +23,8 @@
 //     rearranged in LDS into (digit, input) order, and consecutive threads
 //     write consecutive keys, so each digit's run leaves as one contiguous
 //     stretch instead of one scattered 4-byte store per key.
-// Keys of equal digit keep their input order, so every pass is stable.
+// Keys of equal digit keep their input order, so every pass is stable.  At
+// most 16,384 keys take one launch per pass (radix_pass_small_kernel).
 #include "kernels.hpp"
 
 namespace gt {
@@ -151,6 +152,87 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
         keys_out[pos] = k;
         vals_out[pos] = sv[j];
         if constexpr (TWO) vals2_out[pos] = sv2[j];
+    }
+}
+
+// A whole pass in one block of kSmallWaves waves for at most kSmallSortKeys
+// keys: a small graph (a batch of molecules) otherwise pays three dependent
+// launches per pass, each a few memory round trips long.  Wave w takes keys
+// [w * kWaveSpan, (w + 1) * kWaveSpan), the same span as in the tiled kernels.
+//  1. every wave ranks its keys within their digit and counts the digits
+//     into cnt[wave][digit];
+//  2. thread t = digit t (the first four waves) turns the counts into first
+//     slots: the counts of the waves before, plus the keys of lower digits;
+//  3. every key goes straight to its output slot: its digit's first slot for
+//     its wave plus its rank among the wave's keys of that digit, which step 1
+//     found with the tiled kernels' ballot multisplit and kept in registers.
+// Equal digits keep their input order: slots grow with (wave, item, lane).
+constexpr int kSmallWaves = 16;
+constexpr int64_t kSmallSortKeys = (int64_t)kSmallWaves * kWaveSpan;
+
+template <bool IOTA, bool TWO>
+__global__ __launch_bounds__(kSmallWaves * kWave) void radix_pass_small_kernel(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, const uint32_t* __restrict__ vals2_in,
+    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ vals2_out, int n,
+    int shift, int bits) {
+    __shared__ uint32_t cnt[kSmallWaves][256];
+    __shared__ uint32_t wsum[4];
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
+    const uint32_t mask = (1u << bits) - 1u;
+    for (int k = t; k < kSmallWaves * 256; k += kSmallWaves * kWave) (&cnt[0][0])[k] = 0;
+    const int base = w * kWaveSpan;
+    uint32_t key[kSortItems], val[kSortItems], val2[TWO ? kSortItems : 1];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const int e = base + i * kWave + lane;
+        const bool valid = e < n;
+        key[i] = valid ? keys_in[e] : 0u;
+        val[i] = valid ? (IOTA ? (uint32_t)e : vals_in[e]) : 0u;
+        if constexpr (TWO) val2[i] = valid ? vals2_in[e] : 0u;
+    }
+    __syncthreads();
+    uint32_t rank[kSortItems];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const bool valid = base + i * kWave + lane < n;
+        const uint32_t d = (key[i] >> shift) & mask;
+        const uint64_t peers = digit_peers(d, bits, valid);
+        const int leader = valid ? (int)__builtin_ctzll(peers) : lane;
+        uint32_t old = 0;
+        if (valid && leader == lane) old = atomicAdd(&cnt[w][d], (uint32_t)__builtin_popcountll(peers));
+        old = __shfl(old, leader, kWave);
+        rank[i] = old + (uint32_t)__builtin_popcountll(peers & lanes_below(lane));
+    }
+    __syncthreads();
+    uint32_t tot = 0, inc = 0;
+    if (t < 256) {
+        for (int j = 0; j < kSmallWaves; ++j) {
+            const uint32_t c = cnt[j][t];
+            cnt[j][t] = tot;
+            tot += c;
+        }
+        inc = tot;
+        for (int off = 1; off < kWave; off <<= 1) {
+            const uint32_t y = __shfl_up(inc, off, kWave);
+            if (lane >= off) inc += y;
+        }
+        if (lane == kWave - 1) wsum[w] = inc;
+    }
+    __syncthreads();
+    if (t < 256) {
+        uint32_t start = inc - tot;
+        for (int j = 0; j < w; ++j) start += wsum[j];
+        for (int j = 0; j < kSmallWaves; ++j) cnt[j][t] += start;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        if (base + i * kWave + lane < n) {
+            const uint32_t slot = cnt[w][(key[i] >> shift) & mask] + rank[i];
+            keys_out[slot] = key[i];
+            vals_out[slot] = val[i];
+            if constexpr (TWO) vals2_out[slot] = val2[i];
+        }
     }
 }
 
@@ -316,7 +398,22 @@ hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const ui
         uint32_t* kout = kb[p & 1];
         uint32_t* vout = (last && vals_final) ? vals_final : vb[p & 1];
         uint32_t* v2out = (last && vals2_final) ? vals2_final : v2b[p & 1];
-        if (n > 0) {
+        if (n > 0 && n <= kSmallSortKeys) {
+            if (!vin && two)
+                radix_pass_small_kernel<true, true><<<1, kSmallWaves * kWave, 0, s>>>(kin, nullptr, v2in, kout, vout, v2out, (int)n,
+                                                                         shift, bits);
+            else if (!vin)
+                radix_pass_small_kernel<true, false><<<1, kSmallWaves * kWave, 0, s>>>(kin, nullptr, nullptr, kout, vout, nullptr,
+                                                                          (int)n, shift, bits);
+            else if (two)
+                radix_pass_small_kernel<false, true><<<1, kSmallWaves * kWave, 0, s>>>(kin, vin, v2in, kout, vout, v2out, (int)n,
+                                                                          shift, bits);
+            else
+                radix_pass_small_kernel<false, false><<<1, kSmallWaves * kWave, 0, s>>>(kin, vin, nullptr, kout, vout, nullptr,
+                                                                           (int)n, shift, bits);
+            const hipError_t err = hipGetLastError();
+            if (err != hipSuccess) return err;
+        } else if (n > 0) {
             radix_count_kernel<<<grid, block, 0, s>>>(kin, n, shift, bits, hist, tiles);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;

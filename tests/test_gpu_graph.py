@@ -45,7 +45,7 @@ def check_coo(src, dst, n_dst, n_src=None, what=""):
 
 
 @pytest.mark.parametrize("case", ["tiny_random", "molecules", "one_row", "single_node", "empty", "n256", "n257",
-                                  "rectangular"])
+                                  "rectangular", "e4096", "e4097", "e16384", "e16385"])
 def test_coo_to_csr_small(case):
     rng = np.random.default_rng(7)
     n_src = None
@@ -68,6 +68,13 @@ def test_coo_to_csr_small(case):
     elif case == "n257":  # 9-bit keys: a second pass of 1 bit
         n = 257
         src, dst = gtgen.random_coo(2, n, 20000)
+    elif case.startswith("e"):
+        # edge counts around the one-launch sort pass (at most 16,384 keys) and
+        # the tiled passes above it; 17-bit ids: three passes, the last of one bit
+        n, E = 70000, int(case[1:])
+        src = rng.integers(0, n, E).astype(np.int32)
+        dst = rng.integers(0, n, E).astype(np.int32)
+        dst[: E // 3] = dst[0]  # a long run of one key: stability across waves and tiles
     else:
         n, n_src = 1000, 70000
         src = rng.integers(0, n_src, 50000).astype(np.int32)
