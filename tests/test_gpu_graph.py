@@ -138,6 +138,26 @@ def test_plan_graph_matches_oracle(name):
     plan.destroy()
 
 
+@pytest.mark.parametrize("n,E", [(300, 16384), (300, 16385), (70000, 12000), (70000, 16385)])
+def test_plan_arrays_around_the_one_launch_sort(n, E):
+    # both sorts of a plan (by destination from COO, by source for the
+    # transpose) on either side of the one-launch sort pass's 16,384-key limit
+    rng = np.random.default_rng(n + E)
+    src = rng.integers(0, n, E).astype(np.int32)
+    dst = rng.integers(0, n, E).astype(np.int32)
+    src[: E // 4] = src[0]  # a long run of one source: the transpose's stability
+    say("plan arrays n=%d E=%d" % (n, E))
+    d = dev()
+    plan = gt.gt_plan_create_coo(torch.from_numpy(src).to(d), torch.from_numpy(dst).to(d), n)
+    p = plan_arrays(plan)
+    rip, rix, _ = oracle.coo_to_csr(n, src, dst)
+    assert np.array_equal(p["indptr"], rip) and np.array_equal(p["indices"], rix)
+    tip, tix, tpm = oracle.source_sorted(rip, rix, want_perm=True)
+    assert np.array_equal(p["t_indptr"], tip) and np.array_equal(p["t_indices"], tix)
+    assert np.array_equal(p["t_perm"], tpm)
+    plan.destroy()
+
+
 @pytest.mark.parametrize("name,chunk", [("tiny_random", 3), ("molecules", 2), ("regular16", 5), ("powerlaw", 512),
                                         ("lognormal", 512)])
 def test_plan_attention_is_bitwise_the_plain_call(name, chunk):
