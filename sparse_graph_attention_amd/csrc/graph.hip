@@ -163,9 +163,11 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
 //     into cnt[wave][digit];
 //  2. thread t = digit t (the first four waves) turns the counts into first
 //     slots: the counts of the waves before, plus the keys of lower digits;
-//  3. every key goes straight to its output slot: its digit's first slot for
-//     its wave plus its rank among the wave's keys of that digit, which step 1
-//     found with the tiled kernels' ballot multisplit and kept in registers.
+//  3. every key takes its output slot: its digit's first slot for its wave
+//     plus its rank among the wave's keys of that digit, which step 1 found
+//     with the tiled kernels' ballot multisplit and kept in registers.  Keys
+//     and values are placed in LDS and leave with coalesced stores (a second
+//     value array, for which LDS has no room, is stored to its slot directly).
 // Equal digits keep their input order: slots grow with (wave, item, lane).
 constexpr int kSmallWaves = 16;
 constexpr int64_t kSmallSortKeys = (int64_t)kSmallWaves * kWaveSpan;
@@ -177,6 +179,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void radix_pass_small_kernel(
     int shift, int bits) {
     __shared__ uint32_t cnt[kSmallWaves][256];
     __shared__ uint32_t wsum[4];
+    __shared__ uint32_t sk[kSmallSortKeys], sv[kSmallSortKeys];  // the pass's output, in slot order
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
     const uint32_t mask = (1u << bits) - 1u;
     for (int k = t; k < kSmallWaves * 256; k += kSmallWaves * kWave) (&cnt[0][0])[k] = 0;
@@ -229,10 +232,15 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void radix_pass_small_kernel(
     for (int i = 0; i < kSortItems; ++i) {
         if (base + i * kWave + lane < n) {
             const uint32_t slot = cnt[w][(key[i] >> shift) & mask] + rank[i];
-            keys_out[slot] = key[i];
-            vals_out[slot] = val[i];
+            sk[slot] = key[i];
+            sv[slot] = val[i];
             if constexpr (TWO) vals2_out[slot] = val2[i];
         }
+    }
+    __syncthreads();
+    for (int j = t; j < n; j += kSmallWaves * kWave) {
+        keys_out[j] = sk[j];
+        vals_out[j] = sv[j];
     }
 }
 
