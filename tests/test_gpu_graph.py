@@ -17,6 +17,7 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
+from tests.bounds import OutTable, sub_graph
 from tests.test_gpu_backward import (bound_dkv, btol_of, check_bound, run_gpu, to_torch, widen, with_grad)
 from tests.test_gpu_parity import chunk_edges, custom, dev, host, oracle_inputs, say, to_dev, workload
 
@@ -215,10 +216,8 @@ def test_row_shards(name, parts):
                                     srcs)
     else:
         rk, rv = rk[srcs], rv[srcs]
-    need = np.unique(np.concatenate([w["t_indices"][w["t_indptr"][u]:w["t_indptr"][u + 1]] for u in srcs]))
-    rout = oracle.fwd_rows(*oracle_inputs(w), need.astype(np.int64))
-    pos = {int(v): i for i, v in enumerate(need)}
-    BK, BV = bound_dkv(w, rlse, lambda v: rout[pos[int(v)]], srcs)
+    need = np.unique(sub_graph(w["t_indptr"], w["t_indices"], srcs)[1]).astype(np.int64)
+    BK, BV = bound_dkv(w, rlse, OutTable(oracle.fwd_rows(*oracle_inputs(w), need), need), srcs)
     check_bound(dk_sum, rk, BK, btol_of(w), "sum of shard dK " + name)
     check_bound(dv_sum, rv, BV, btol_of(w), "sum of shard dV " + name)
 

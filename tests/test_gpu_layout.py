@@ -18,9 +18,10 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
+from tests.bounds import OutTable
 from tests.test_gpu_backward import bound_dkv, bound_dq, btol_of, check_bound, check_lse, to_torch, with_grad
 from tests.test_gpu_parity import (assert_close, chunk_edges, custom, dev, host, oracle_inputs, random_graph,
-                                   sample_rows, say, to_dev, tol_of, workload)
+                                   sample_rows, say, say_split, to_dev, tol_of, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -113,11 +114,11 @@ def check_bwd(w):
     torch.cuda.synchronize()
     rq, rk, rv, rlse, _ = oracle.bwd(*oracle_inputs(w), w["dO"])
     check_lse(host(lse), rlse, "ndh lse " + w["name"])
-    rout = oracle.fwd(*oracle_inputs(w))
+    outs = OutTable(oracle.fwd(*oracle_inputs(w)))
     allv = np.arange(w["N"])
-    BK, BV = bound_dkv(w, rlse, lambda v: rout[v], allv)
+    BK, BV = bound_dkv(w, rlse, outs, allv)
     tol = btol_of(w)
-    check_bound(host(nhd(dq)), rq, bound_dq(w, rlse, lambda v: rout[v], allv), tol, "ndh dQ " + w["name"])
+    check_bound(host(nhd(dq)), rq, bound_dq(w, rlse, outs, allv), tol, "ndh dQ " + w["name"])
     check_bound(host(nhd(dk)), rk, BK, tol, "ndh dK " + w["name"])
     check_bound(host(nhd(dv)), rv, BV, tol, "ndh dV " + w["name"])
 
@@ -203,7 +204,9 @@ def test_ndh_large_sampled():
     out, lse = gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], ndh(t["Q"]), ndh(t["K"]), ndh(t["V"]),
                                            want_lse=True)
     torch.cuda.synchronize()
-    rows = sample_rows(w["indptr"], gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES), n_random=400)
+    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    rows = sample_rows(w["indptr"], chunk, n_random=400)
+    say_split(w["indptr"], rows, chunk, "ndh powerlaw")
     rows_t = torch.from_numpy(rows).to(dev())
     rout = oracle.fwd_rows(*oracle_inputs(w), rows)
     assert_close(host(nhd(out[rows_t])), rout, tol_of(w), "ndh powerlaw out (%d sampled rows)" % len(rows))

@@ -26,9 +26,10 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
-from tests.test_gpu_backward import check_bound, check_lse, to_torch, widen, with_grad
+from tests.bounds import OutTable, dest_bounds, source_bounds, sub_graph
+from tests.test_gpu_backward import check_bound, check_lse, to_torch, with_grad
 from tests.test_gpu_parity import (BF16_TOL, F32_TOL, assert_close, chunk_edges, dev, host, oracle_inputs,
-                                   random_graph, sample_rows, say, to_dev, workload)
+                                   random_graph, sample_rows, say, say_split, to_dev, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -88,26 +89,12 @@ def run_ex(w, o, t=None):
     return (out, lse) + tuple(res)
 
 
-def edge_bounds(w, o, lse, out_of, e_dst, e_src, e_ids):
-    """alpha*c [n][H] and the weight alpha (c |da| + |dO_v|.|out_v|) [n][H] of the listed edges."""
-    Q, K, V, G = (widen(w[k][idx]) for k, idx in (("Q", e_dst), ("K", e_src), ("V", e_src), ("dO", e_dst)))
-    dot = np.einsum("ehd,ehd->eh", Q, K) / math.sqrt(w["D"])
-    s = dot * (o["ew"][e_ids][:, None] if o["ew"] is not None else 1.0)
-    if o["bias"] is not None:
-        s = s + o["bias"][e_ids]
-    alpha = np.exp(s - lse[e_dst])
-    if o["drop_p"]:
-        if "c_all" not in o:
-            o["c_all"] = keep_mask(o["seed"], w["E"], w["H"], o["drop_p"])
-        c = o["c_all"][e_ids].astype(np.float64)
-    else:
-        c = np.ones_like(alpha)
-    da = np.einsum("ehd,ehd->eh", np.abs(G), np.abs(V))  # bounds |dO.v| and its rounding
-    outs = np.stack([out_of(v) for v in e_dst]) if len(e_dst) else np.zeros((0, w["H"], w["D"]))
-    dabs = np.einsum("ehd,ehd->eh", np.abs(G), np.abs(outs))
-    wt = alpha * (c * da + dabs)
-    absdot = np.einsum("ehd,ehd->eh", np.abs(Q), np.abs(K)) / math.sqrt(w["D"])
-    return alpha * c, wt, absdot
+def bound_opts(w, o):
+    """The options as the bounds take them (tests.bounds), with the dropout
+    multipliers of every edge drawn from numpy's Philox stream."""
+    if o["drop_p"] and "c_all" not in o:
+        o["c_all"] = keep_mask(o["seed"], w["E"], w["H"], o["drop_p"])
+    return dict(ew=o["ew"], bias=o["bias"], c_all=o.get("c_all") if o["drop_p"] else None)
 
 
 def check_full(w, o):
@@ -121,24 +108,17 @@ def check_full(w, o):
     assert_close(host(out), rout, ftol, "out " + w["name"])
     check_lse(host(lse), rlse, "lse " + w["name"])
     g = oracle.bwd_ex(*oracle_inputs(w), w["dO"], **kw)
-    N, H, D = w["N"], w["H"], w["D"]
-    e_dst = np.repeat(np.arange(N), np.diff(w["indptr"]))
-    e_src = w["indices"].astype(np.int64)
-    e_ids = np.arange(w["E"])
-    ac, wt, absdot = edge_bounds(w, o, g["lse"], lambda v: rout[v], e_dst, e_src, e_ids)
-    ww = (o["ew"][:, None, None] if o["ew"] is not None else 1.0)
-    Qa, Ka, Ga = (np.abs(widen(w[k])) for k in ("Q", "K", "dO"))
-    BQ = np.zeros((N, H, D))
-    BK = np.zeros((N, H, D))
-    BV = np.zeros((N, H, D))
-    np.add.at(BQ, e_dst, wt[:, :, None] * ww * Ka[e_src] / math.sqrt(D))
-    np.add.at(BK, e_src, wt[:, :, None] * ww * Qa[e_dst] / math.sqrt(D))
-    np.add.at(BV, e_src, ac[:, :, None] * Ga[e_dst])
-    check_bound(host(dq), g["dq"], BQ, btol, "dQ " + w["name"])
+    bopts = bound_opts(w, o)
+    outs = OutTable(rout)
+    allv = np.arange(w["N"])
+    tip, tix, tpm = gtgen.source_sorted(w["indptr"], w["indices"], want_perm=True)
+    rb = dest_bounds(w, g["lse"], outs, allv, opts=bopts)
+    BK, BV = source_bounds(dict(w, t_indptr=tip, t_indices=tix), g["lse"], outs, allv, opts=bopts, t_perm=tpm)
+    check_bound(host(dq), g["dq"], rb["dq"], btol, "dQ " + w["name"])
     check_bound(host(dk), g["dk"], BK, btol, "dK " + w["name"])
     check_bound(host(dv), g["dv"], BV, btol, "dV " + w["name"])
-    check_bound(host(dbias), g["dbias"], wt, btol, "dbias " + w["name"])
-    check_bound(host(dw), g["dw"], (wt * absdot).sum(1), btol, "dweight " + w["name"])
+    check_bound(host(dbias)[rb["sel"]], g["dbias"][rb["sel"]], rb["db"], btol, "dbias " + w["name"])
+    check_bound(host(dw)[rb["sel"]], g["dw"][rb["sel"]], rb["dw"], btol, "dweight " + w["name"])
 
 
 VARIANTS = {
@@ -247,51 +227,26 @@ def test_variants_large_sampled(name, p):
     kw = oracle_opts(o)
     chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
     rows = sample_rows(w["indptr"], chunk, n_random=600)
+    say_split(w["indptr"], rows, chunk, "ex destinations " + name)
     rlse, rdelta = oracle.row_stats_ex(*oracle_inputs(w), w["dO"], **kw)
     check_lse(lse, rlse, "lse " + name)
     tip, tix, tpm = gtgen.source_sorted(w["indptr"], w["indices"], want_perm=True)
     srcs = sample_rows(tip, chunk, n_random=600, seed=1)
-    need = np.unique(np.concatenate([rows] + [tix[tip[u]:tip[u + 1]] for u in srcs]).astype(np.int64))
-    rout = oracle.fwd_ex(*oracle_inputs(w), rows=need, **kw)
-    pos = {int(v): i for i, v in enumerate(need)}
-    out_of = lambda v: rout[pos[int(v)]]  # noqa: E731
-    assert_close(out[rows], np.stack([out_of(v) for v in rows]), ftol, "out %s" % name)
-    H, D, ip = w["H"], w["D"], w["indptr"]
-    rdb = np.zeros((w["E"], H))
+    say_split(tip, srcs, chunk, "ex sources " + name)
+    need = np.union1d(rows, sub_graph(tip, tix, srcs)[1])
+    outs = OutTable(oracle.fwd_ex(*oracle_inputs(w), rows=need, **kw), need)
+    assert_close(out[rows], outs.take(rows), ftol, "out %s" % name)
+    rdb = np.zeros((w["E"], w["H"]))
     rdw = np.zeros(w["E"])
     rq = oracle.dq_rows_ex(*oracle_inputs(w), w["dO"], rlse, rdelta, rows, dbias=rdb, dw=rdw, **kw)
-    Ka, Qa, Ga = (np.abs(widen(w[k])) for k in ("K", "Q", "dO"))
-    BQ = np.zeros((len(rows), H, D))
-    eds = []
-    Bdb = []
-    Bdw = []
-    for i, v in enumerate(rows):
-        e_ids = np.arange(ip[v], ip[v + 1])
-        if not len(e_ids):
-            continue
-        src = w["indices"][e_ids].astype(np.int64)
-        dst = np.full(len(e_ids), v)
-        ac, wt, absdot = edge_bounds(w, o, rlse, out_of, dst, src, e_ids)
-        BQ[i] = (wt[:, :, None] * o["ew"][e_ids][:, None, None] * Ka[src]).sum(0) / math.sqrt(D)
-        eds.append(e_ids)
-        Bdb.append(wt)
-        Bdw.append((wt * absdot).sum(1))
-    check_bound(dq[rows], rq, BQ, btol, "dQ %s (%d rows)" % (name, len(rows)))
-    eds = np.concatenate(eds)
-    check_bound(dbias[eds], rdb[eds], np.concatenate(Bdb), btol, "dbias %s" % name)
-    check_bound(dw[eds], rdw[eds], np.concatenate(Bdw), btol, "dweight %s" % name)
+    bopts = bound_opts(w, o)
+    rb = dest_bounds(w, rlse, outs, rows, opts=bopts)
+    check_bound(dq[rows], rq, rb["dq"], btol, "dQ %s (%d rows)" % (name, len(rows)))
+    eds = rb["sel"]
+    check_bound(dbias[eds], rdb[eds], rb["db"], btol, "dbias %s" % name)
+    check_bound(dw[eds], rdw[eds], rb["dw"], btol, "dweight %s" % name)
     rk, rv = oracle.dkv_sources_ex(tip, tix, tpm, w["Q"], w["K"], w["V"], w["dO"], rlse, rdelta, srcs, **kw)
-    BK = np.zeros((len(srcs), H, D))
-    BV = np.zeros((len(srcs), H, D))
-    for i, u in enumerate(srcs):
-        js = np.arange(tip[u], tip[u + 1])
-        if not len(js):
-            continue
-        dst = tix[js].astype(np.int64)
-        e_ids = tpm[js].astype(np.int64)
-        ac, wt, _ = edge_bounds(w, o, rlse, out_of, dst, np.full(len(js), u), e_ids)
-        BK[i] = (wt[:, :, None] * o["ew"][e_ids][:, None, None] * Qa[dst]).sum(0) / math.sqrt(D)
-        BV[i] = (ac[:, :, None] * Ga[dst]).sum(0)
+    BK, BV = source_bounds(dict(w, t_indptr=tip, t_indices=tix), rlse, outs, srcs, opts=bopts, t_perm=tpm)
     check_bound(dk[srcs], rk, BK, btol, "dK %s (%d sources)" % (name, len(srcs)))
     check_bound(dv[srcs], rv, BV, btol, "dV %s (%d sources)" % (name, len(srcs)))
 

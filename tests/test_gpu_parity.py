@@ -7,7 +7,8 @@ Tolerances, elementwise |gpu - oracle| <= atol + rtol * |oracle|:
 * scores and alpha from the unfused stages use the fp32 bounds.
 Small workloads are compared in full; the million-node workloads on sampled
 destination rows (every split row, rows at the chunk threshold, empty rows
-and a random sample), which the oracle computes one by one.
+and a random sample), which the oracle computes one by one; each such test
+prints how many split rows it checked against the graph's count.
 """
 import math
 import sys
@@ -19,6 +20,7 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
+from tests.bounds import sub_graph
 
 pytestmark = pytest.mark.gpu
 
@@ -131,16 +133,28 @@ def workload(name):
 
 
 def sample_rows(indptr, chunk, n_random=1500, seed=0):
+    """Rows checked on the million-node workloads: every split row (more than
+    `chunk` in-edges), rows at and around the split threshold, rows without
+    in-edges, the first and last row, and a uniform random sample."""
     deg = np.diff(indptr)
     N = len(deg)
     rng = np.random.default_rng(seed)
     heavy = np.nonzero(deg > chunk)[0]
-    top = np.argsort(deg)[-64:]
     near = np.nonzero(np.isin(deg, [chunk - 1, chunk, chunk + 1, 2 * chunk, 2 * chunk + 1]))[0][:64]
     empty = np.nonzero(deg == 0)[0][:200]
     rand = rng.choice(N, size=min(n_random, N), replace=False)
-    rows = np.unique(np.concatenate([heavy[:400], top, near, empty, rand, [0, N - 1]]))
+    rows = np.unique(np.concatenate([heavy, near, empty, rand, [0, N - 1]]))
     return rows.astype(np.int64)
+
+
+def say_split(indptr, rows, chunk, what):
+    """Prints how many split rows the sample holds, against all split rows of the graph."""
+    deg = np.diff(indptr)
+    n_split = int((deg > chunk).sum())
+    in_sample = int((deg[rows] > chunk).sum())
+    say("%s: %d sampled rows, %d of the graph's %d split rows (%d edges in split rows)" % (
+        what, len(rows), in_sample, n_split, int(deg[deg > chunk].sum())))
+    assert in_sample == n_split, "every split row must be checked"
 
 
 # ------------------------------------------------------------------ fused, whole outputs
@@ -161,7 +175,9 @@ def test_fused_large_sampled(name):
     w = workload(name)
     say("fused %s sampled rows, N=%d E=%d" % (name, w["N"], w["E"]))
     out = host(run_fused(w))
-    rows = sample_rows(w["indptr"], gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES))
+    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    rows = sample_rows(w["indptr"], chunk)
+    say_split(w["indptr"], rows, chunk, "fused " + name)
     ref = oracle.fwd_rows(*oracle_inputs(w), rows)
     assert_close(out[rows], ref, tol_of(w), "fused %s (%d sampled rows)" % (name, len(rows)))
     deg = np.diff(w["indptr"])
@@ -318,11 +334,10 @@ def check_stages(w, rows=None):
         assert_close(comp, oracle.fwd(*oracle_inputs(w)), tol, "sddmm->softmax->spmm")
     else:
         ref, rs, _ = oracle.fwd_rows(*oracle_inputs(w), rows, want_edges=True)
-        sel = np.concatenate([np.arange(indptr[r], indptr[r + 1]) for r in rows])
+        # softmax and SpMM of independent inputs on the same rows, as a sub-CSR of those rows
+        sub_indptr, _, sel = sub_graph(indptr, indices, rows)
         assert_close(s[sel], rs, F32_TOL, "sddmm (sampled)")
         assert_close(comp[rows], ref, tol, "sddmm->softmax->spmm (sampled)")
-        # softmax and SpMM of independent inputs on the same rows, as a sub-CSR of those rows
-        sub_indptr = np.concatenate([[0], np.cumsum(indptr[rows + 1] - indptr[rows])]).astype(np.int64)
         assert_close(a[sel], oracle.edge_softmax(sub_indptr, sc[sel].astype(np.float64)), F32_TOL,
                      "edge_softmax (sampled)")
         ref_o = oracle.spmm(sub_indptr, indices[sel], al[sel].astype(np.float64), w["V"])
@@ -383,7 +398,9 @@ def test_softmax_in_place_and_odd_heads():
 @pytest.mark.parametrize("name", ["powerlaw", "lognormal"])
 def test_unfused_large_sampled(name):
     w = workload(name)
-    rows = sample_rows(w["indptr"], gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES), n_random=500)
+    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    rows = sample_rows(w["indptr"], chunk, n_random=500)
+    say_split(w["indptr"], rows, chunk, "unfused " + name)
     check_stages(w, rows)
 
 

@@ -16,6 +16,7 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
+from tests.bounds import OutTable, sub_graph
 from tests.test_gpu_backward import F32_BTOL, bound_dkv, bound_dq, check_bound, check_lse
 from tests.test_gpu_parity import F32_TOL, assert_close, dev, host, say
 
@@ -72,7 +73,7 @@ def test_more_items_than_one_slice():
     alpha = gt.gt_edge_softmax(tip, scores)
     out2 = gt.gt_spmm(tip, tix, alpha, tv)
     torch.cuda.synchronize()
-    sel = np.concatenate([np.arange(indptr[r], indptr[r + 1]) for r in rows])
+    sel = sub_graph(indptr, indices, rows)[2]
     sel_t = torch.from_numpy(sel).to(d)
     assert_close(host(scores[sel_t]), rs, F32_TOL, "scores of the sampled rows")
     assert_close(host(alpha[sel_t]), ra, F32_TOL, "alpha of the sampled rows")
@@ -89,14 +90,12 @@ def test_more_items_than_one_slice():
     # sources: the same boundary for the source pass (its chunk bound differs), and random ones
     t_heavy = min(N, E // (chunk + 1))
     srcs = sampled(E // chunk + t_heavy, N, rng)
-    need = np.unique(np.concatenate([rows] + [t_ix[t_ip[u]:t_ip[u + 1]] for u in srcs]).astype(np.int64))
-    nout = oracle.fwd_rows(indptr, indices, Q, K, V, need)
-    pos = {int(v): i for i, v in enumerate(need)}
-    out_of = lambda v: nout[pos[int(v)]]  # noqa: E731
+    need = np.union1d(rows, sub_graph(t_ip, t_ix, srcs)[1])
+    outs = OutTable(oracle.fwd_rows(indptr, indices, Q, K, V, need), need)
     rq = oracle.dq_rows(indptr, indices, Q, K, V, dO, rlse, rdelta, rows)
-    check_bound(host(dq[rows_t]), rq, bound_dq(w, rlse, out_of, rows), F32_BTOL, "dQ around the slice boundary")
+    check_bound(host(dq[rows_t]), rq, bound_dq(w, rlse, outs, rows), F32_BTOL, "dQ around the slice boundary")
     rk, rv = oracle.dkv_sources(t_ip, t_ix, Q, K, V, dO, rlse, rdelta, srcs)
-    BK, BV = bound_dkv(w, rlse, out_of, srcs)
+    BK, BV = bound_dkv(w, rlse, outs, srcs)
     srcs_t = torch.from_numpy(srcs).to(d)
     check_bound(host(dk[srcs_t]), rk, BK, F32_BTOL, "dK around the slice boundary")
     check_bound(host(dv[srcs_t]), rv, BV, F32_BTOL, "dV around the slice boundary")
