@@ -46,8 +46,10 @@
  * work enqueued on `stream` has finished.  The library keeps no caller
  * pointer after a call returns.  It owns its internal scratch (work lists
  * and the partial results of split rows): one buffer per (device, stream),
- * grown on demand; growing it synchronises that stream once and frees the
- * old buffer.  The buffer stays allocated until gt_scratch_release.
+ * grown on demand in the stream's order (the old buffer released with
+ * hipFreeAsync and the new one taken with hipMallocAsync on that stream,
+ * from the device's default memory pool), so no call waits for the device.
+ * The buffer stays allocated until gt_scratch_release.
  *
  * Execution.  Calls enqueue kernels on `stream` (NULL = the null stream) and
  * return without waiting for them; gt_validate_csr is the exception.  Every
@@ -65,7 +67,10 @@
  *                  alpha), N < 0, E < 0, H < 1, D < 1, N >= 2^31, or an
  *                  invalid configuration value;
  *  GT_EUNSUPPORTED an unknown dtype, H > 64 or D > 256;
- *  GT_ENOMEM       the scratch buffer could not be allocated;
+ *  GT_ENOMEM       the scratch buffer (or a plan) could not be allocated;
+ *                  also every allocation while the environment variable
+ *                  GT_TEST_FAIL_ALLOC is set to a value other than "" or
+ *                  "0" (a test hook: the call returns before any HIP call);
  *  GT_EHIP         a HIP runtime or launch error (gt_last_error() has it).
  * Special sizes: N = 0 is a no-op returning GT_OK; E = 0 writes zeros.
  * The CSR's contents are not checked on the hot path (a malformed CSR is
@@ -283,13 +288,20 @@ int gt_coo_to_csr(const int32_t* src, const int32_t* dst, int64_t n_dst, int64_t
  *
  * gt_plan_create copies a caller CSR; gt_plan_create_coo builds it from COO
  * arrays as gt_coo_to_csr does.  Both allocate the plan's device memory with
- * hipMalloc (so they are not for graph capture), enqueue the construction on
- * `stream` and return without waiting: the plan is ready for work on
- * `stream`, and for other streams once they are ordered after it.  The
- * library keeps no caller pointer.  gt_plan_destroy waits for the device to
- * finish queued work, then frees the plan.  gt_plan_info returns the plan's
- * sizes and device arrays (owned by the plan; t_* are NULL without
- * GT_PLAN_TRANSPOSE); any output pointer may be NULL.  gt_plan_copy_graph
+ * hipMallocAsync on `stream` (so they are not for graph capture), enqueue
+ * the construction on `stream` and return without waiting: the plan is ready
+ * for work on `stream`, and for other streams once they are ordered after
+ * it.  The library keeps no caller pointer.  Every call on a plan records an
+ * event on its stream; gt_plan_destroy releases the plan's memory in stream
+ * order behind all of them (the null stream waits for those events, then
+ * hipFreeAsync), without waiting on the host.  Work of the caller's own that
+ * reads arrays taken from gt_plan_info must therefore be finished, or be
+ * enqueued before a library call on the plan on the same stream, when the
+ * plan is destroyed; and since the release goes on the null stream,
+ * gt_plan_destroy must not be called while a stream capture is under way.
+ * gt_plan_info returns the plan's sizes and device arrays (owned by the
+ * plan; t_* are NULL without GT_PLAN_TRANSPOSE); any output pointer may be
+ * NULL.  gt_plan_copy_graph
  * copies the plan's graph into caller device arrays of those sizes (any may
  * be NULL; asking for t_* of a plan without a transpose is GT_EINVAL),
  * enqueued on `stream`.
@@ -362,10 +374,11 @@ int64_t gt_config_get(int32_t key);
 
 /*
  * The scratch buffer of `stream` on the current device: gt_scratch_release
- * waits for the stream, frees the buffer and forgets it (the next call on the
- * stream allocates afresh); GT_OK also when the stream has none.  Call it
- * before destroying a stream that the library has used, or to return the
- * memory (up to 8 feature arrays' worth for the head-innermost backward).
+ * releases it in the stream's order (hipFreeAsync on `stream`, after the
+ * work already enqueued there) and forgets it (the next call on the stream
+ * allocates afresh); GT_OK also when the stream has none.  Call it before
+ * destroying a stream that the library has used, or to return the memory
+ * (up to 8 feature arrays' worth for the head-innermost backward).
  * gt_scratch_bytes gives the buffer's current size (0 if none, -1 if the
  * current device cannot be read).  The same threading rule as for the other
  * calls on a stream applies.

@@ -498,8 +498,22 @@ def gt_coo_to_csr(src, dst, n_dst, n_src=None, want_perm=False, stream=None):
     return (indptr, indices, perm) if want_perm else (indptr, indices)
 
 
+# Plans collected by the garbage collector while a stream capture was under
+# way: gt_plan_destroy enqueues the plan's release on the null stream, which a
+# capture must not see, so they are destroyed at the next plan call instead.
+_deferred = []
+
+
+def _destroy_deferred():
+    if _deferred and not torch.cuda.is_current_stream_capturing():
+        while _deferred:
+            lib().gt_plan_destroy(_deferred.pop())
+
+
 class GtPlan:
-    """Owner of a gt_plan handle; destroy() (or garbage collection) frees it."""
+    """Owner of a gt_plan handle; destroy() (or garbage collection) frees it.
+    The release is stream-ordered: it waits on the device, not on the host,
+    for the work already enqueued on the plan."""
 
     def __init__(self, handle):
         self.handle = handle
@@ -507,7 +521,11 @@ class GtPlan:
 
     def destroy(self):
         if self.handle:
-            lib().gt_plan_destroy(self.handle)
+            if torch.cuda.is_current_stream_capturing():
+                _deferred.append(self.handle)
+            else:
+                _destroy_deferred()
+                lib().gt_plan_destroy(self.handle)
             self.handle = None
 
     def __del__(self):
@@ -518,6 +536,7 @@ class GtPlan:
 
 
 def gt_plan_create(indptr, indices, n_src=None, transpose=True, stream=None):
+    _destroy_deferred()
     n_dst, E = _csr(indptr, indices)
     n_src = n_dst if n_src is None else n_src
     _need_gpu(indptr, indices)
@@ -529,6 +548,7 @@ def gt_plan_create(indptr, indices, n_src=None, transpose=True, stream=None):
 
 
 def gt_plan_create_coo(src, dst, n_dst, n_src=None, transpose=True, stream=None):
+    _destroy_deferred()
     E = _coo(src, dst)
     n_src = n_dst if n_src is None else n_src
     _need_gpu(src, dst)

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <map>
 #include <new>
 #include <mutex>
@@ -38,6 +39,15 @@ int hip_fail(hipError_t e, const char* what) {
 
 // ---------------------------------------------------------------- scratch
 
+// Test hook: with GT_TEST_FAIL_ALLOC set to anything but "" or "0", every
+// device allocation the library would make (scratch growth, plans) fails as
+// if the device were out of memory: the call returns GT_ENOMEM before any
+// HIP call, so nothing is enqueued.
+bool alloc_refused() {
+    const char* v = getenv("GT_TEST_FAIL_ALLOC");
+    return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
 struct Scratch {
     void* ptr = nullptr;
     size_t bytes = 0;
@@ -45,9 +55,13 @@ struct Scratch {
 std::mutex g_scratch_mu;
 std::map<std::pair<int, uintptr_t>, Scratch> g_scratch;
 
-// A buffer of at least `bytes` for `stream` on the current device.  Growing it
-// waits for the stream (its old buffer may still be in use by queued work).
+// A buffer of at least `bytes` for `stream` on the current device.  Growth
+// is stream-ordered: the old buffer goes back to the device's memory pool
+// after the work already queued on `stream` (hipFreeAsync), and the new one
+// is allocated in the stream's order (hipMallocAsync), so no call waits for
+// the device.
 int get_scratch(hipStream_t stream, size_t bytes, void** out) {
+    if (alloc_refused()) return fail(GT_ENOMEM, "scratch allocation refused (GT_TEST_FAIL_ALLOC is set)");
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -55,18 +69,17 @@ int get_scratch(hipStream_t stream, size_t bytes, void** out) {
     Scratch& s = g_scratch[{dev, (uintptr_t)stream}];
     if (s.bytes < bytes) {
         if (s.ptr) {
-            e = hipStreamSynchronize(stream);
-            if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-            (void)hipFree(s.ptr);
+            e = hipFreeAsync(s.ptr, stream);
+            if (e != hipSuccess) return hip_fail(e, "hipFreeAsync of the old scratch");
             s.ptr = nullptr;
             s.bytes = 0;
         }
         size_t want = bytes + bytes / 4;  // headroom against frequent regrowth
-        e = hipMalloc(&s.ptr, want);
+        e = hipMallocAsync(&s.ptr, want, stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             s.ptr = nullptr;
-            return fail(GT_ENOMEM, "hipMalloc of %zu scratch bytes failed: %s", want, hipGetErrorString(e));
+            return fail(GT_ENOMEM, "hipMallocAsync of %zu scratch bytes failed: %s", want, hipGetErrorString(e));
         }
         s.bytes = want;
     }
@@ -80,12 +93,13 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 // and partials (per-chunk results, sized by the features: per call).
 // Sizes the tables for a graph of N rows and E edges at the current split
 // threshold.
-void size_plan(int64_t N, int64_t E, Plan& p) {
-    const int64_t C = g_chunk.load();
+void size_plan_at(int64_t N, int64_t E, int64_t C, Plan& p) {
     p.chunk = C;
     p.max_heavy = std::min<int64_t>(N, E / (C + 1));
     p.max_chunks = p.max_heavy ? E / C + p.max_heavy : 0;
 }
+
+void size_plan(int64_t N, int64_t E, Plan& p) { size_plan_at(N, E, g_chunk.load(), p); }
 
 size_t table_bytes(const Plan& p) {
     return align256(sizeof(PlanCounters)) + align256(sizeof(HeavyRow) * p.max_heavy) +
@@ -280,11 +294,9 @@ int gt_scratch_release(hipStream_t stream) {
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     auto it = g_scratch.find({dev, (uintptr_t)stream});
     if (it == g_scratch.end()) return GT_OK;
-    e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
-    e = hipFree(it->second.ptr);
+    e = it->second.ptr ? hipFreeAsync(it->second.ptr, stream) : hipSuccess;
     g_scratch.erase(it);
-    return e == hipSuccess ? GT_OK : hip_fail(e, "hipFree");
+    return e == hipSuccess ? GT_OK : hip_fail(e, "hipFreeAsync");
 }
 
 int64_t gt_scratch_bytes(hipStream_t stream) {
@@ -404,6 +416,7 @@ int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, cons
     a.out = out;
     a.lse_out = lse;
     a.N = N;
+    a.n_gather = N;
     a.E = E;
     a.H = H;
     a.D = D;
@@ -508,6 +521,7 @@ int bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, c
     a.dK = dK;
     a.dV = dV;
     a.N = n_dst;
+    a.n_gather = n_src;
     a.E = E;
     a.H = H;
     a.D = D;
@@ -521,6 +535,7 @@ int bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, c
     at.indices = t_indices;
     at.t_perm = t_perm;
     at.N = n_src;
+    at.n_gather = n_dst;
     // the destination pass writes the per-edge gradients; the source pass
     // needs the CSR positions of its out-edges only for per-edge inputs
     a.dbias = dbias;
@@ -600,6 +615,7 @@ int gt_sddmm(const int64_t* indptr, const int32_t* indices, const void* Q, const
     a.K = K;
     a.scores_out = scores;
     a.N = N;
+    a.n_gather = N;
     a.E = E;
     a.H = H;
     a.D = D;
@@ -647,6 +663,7 @@ int gt_spmm(const int64_t* indptr, const int32_t* indices, const float* alpha, c
     a.V = V;
     a.out = out;
     a.N = N;
+    a.n_gather = N;
     a.E = E;
     a.H = H;
     a.D = D;
@@ -677,6 +694,7 @@ int gt_sparse_mha_fwd_layout(const int64_t* indptr, const int32_t* indices, cons
     a.out = out;
     a.lse_out = lse;
     a.N = N;
+    a.n_gather = N;
     a.E = E;
     a.H = H;
     a.D = D;
@@ -789,6 +807,11 @@ struct gt_plan_s {
     int32_t* t_perm = nullptr;  // CSR position of each out-edge of the transpose
     Plan tables{};    // split rows of the destination-sorted graph
     Plan t_tables{};  // split rows of the source-sorted graph
+    // The streams the plan's memory is used on, each with an event recorded
+    // after the last work enqueued there; destruction releases the memory in
+    // stream order behind all of them.
+    std::mutex mu;
+    std::vector<std::pair<hipStream_t, hipEvent_t>> uses;
 };
 
 namespace {
@@ -830,9 +853,11 @@ int build_transpose(gt_plan_s* P, hipStream_t stream) {
 }
 
 // Allocates a plan for (n_dst, n_src, E): CSR, transpose (with
-// GT_PLAN_TRANSPOSE) and the split-row tables, in one device allocation.
-int alloc_plan(int64_t n_dst, int64_t n_src, int64_t E, int32_t flags, gt_plan_s** out) {
+// GT_PLAN_TRANSPOSE) and the split-row tables, in one device allocation
+// ordered on `stream`.
+int alloc_plan(int64_t n_dst, int64_t n_src, int64_t E, int32_t flags, hipStream_t stream, gt_plan_s** out) {
     if (flags & ~GT_PLAN_TRANSPOSE) return fail(GT_EINVAL, "unknown plan flags 0x%x", flags);
+    if (alloc_refused()) return fail(GT_ENOMEM, "plan allocation refused (GT_TEST_FAIL_ALLOC is set)");
     auto* P = new (std::nothrow) gt_plan_s;
     if (!P) return fail(GT_ENOMEM, "host allocation of a plan failed");
     P->n_dst = n_dst;
@@ -852,11 +877,11 @@ int alloc_plan(int64_t n_dst, int64_t n_src, int64_t E, int32_t flags, gt_plan_s
                              : 0) +
                          table_bytes(P->tables) + table_bytes(P->t_tables);
     if (!rc) {
-        e = hipMalloc(&P->mem, bytes);
+        e = hipMallocAsync(&P->mem, bytes, stream);
         if (e != hipSuccess) {
             (void)hipGetLastError();
             P->mem = nullptr;
-            rc = fail(GT_ENOMEM, "hipMalloc of %zu plan bytes failed: %s", bytes, hipGetErrorString(e));
+            rc = fail(GT_ENOMEM, "hipMallocAsync of %zu plan bytes failed: %s", bytes, hipGetErrorString(e));
         }
     }
     if (rc) {
@@ -896,11 +921,32 @@ int finish_plan(gt_plan_s* P, hipStream_t stream) {
     return e == hipSuccess ? GT_OK : hip_fail(e, "plan launch");
 }
 
+// Records that `stream` has work on the plan's memory enqueued up to now.
+int note_use(gt_plan_s* P, hipStream_t stream) {
+    std::lock_guard<std::mutex> lock(P->mu);
+    hipEvent_t ev = nullptr;
+    for (auto& u : P->uses)
+        if (u.first == stream) ev = u.second;
+    if (!ev) {
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e != hipSuccess) return hip_fail(e, "hipEventCreateWithFlags");
+        P->uses.emplace_back(stream, ev);
+    }
+    hipError_t e = hipEventRecord(ev, stream);
+    return e == hipSuccess ? GT_OK : hip_fail(e, "hipEventRecord");
+}
+
+// Stream-ordered release: the null stream waits for the last recorded work
+// of every stream that used the plan, then returns its memory to the pool.
+// The host does not wait.
 void free_plan(gt_plan_s* P) {
     if (!P) return;
-    if (P->mem) {
-        (void)hipDeviceSynchronize();  // no queued kernel may still read it
-        (void)hipFree(P->mem);
+    {
+        std::lock_guard<std::mutex> lock(P->mu);
+        for (auto& u : P->uses) (void)hipStreamWaitEvent(nullptr, u.second, 0);
+        if (P->mem) (void)hipFreeAsync(P->mem, nullptr);
+        for (auto& u : P->uses) (void)hipEventDestroy(u.second);
+        P->uses.clear();
     }
     delete P;
 }
@@ -941,13 +987,15 @@ int gt_plan_create(const int64_t* indptr, const int32_t* indices, int64_t n_dst,
     if (!indptr) return fail(GT_EINVAL, "NULL indptr");
     if (E > 0 && !indices) return fail(GT_EINVAL, "NULL indices with E > 0");
     gt_plan_s* P = nullptr;
-    rc = alloc_plan(n_dst, n_src, E, flags, &P);
+    rc = alloc_plan(n_dst, n_src, E, flags, stream, &P);
     if (rc) return rc;
     hipError_t e = hipMemcpyAsync(P->indptr, indptr, sizeof(int64_t) * (size_t)(n_dst + 1), hipMemcpyDeviceToDevice,
                                   stream);
     if (e == hipSuccess && E > 0)
         e = hipMemcpyAsync(P->indices, indices, sizeof(int32_t) * (size_t)E, hipMemcpyDeviceToDevice, stream);
     rc = e == hipSuccess ? finish_plan(P, stream) : hip_fail(e, "CSR copy");
+    const int urc = note_use(P, stream);
+    if (!rc) rc = urc;
     if (rc) {
         free_plan(P);
         return rc;
@@ -964,7 +1012,7 @@ int gt_plan_create_coo(const int32_t* src, const int32_t* dst, int64_t n_dst, in
     if (rc) return rc;
     if (E > 0 && (!src || !dst)) return fail(GT_EINVAL, "NULL COO array with E > 0");
     gt_plan_s* P = nullptr;
-    rc = alloc_plan(n_dst, n_src, E, flags, &P);
+    rc = alloc_plan(n_dst, n_src, E, flags, stream, &P);
     if (rc) return rc;
     void* base = nullptr;
     rc = get_scratch(stream, sort_scratch_bytes(E, false), &base);
@@ -973,6 +1021,8 @@ int gt_plan_create_coo(const int32_t* src, const int32_t* dst, int64_t n_dst, in
                                     (uint32_t*)P->indices, nullptr, base, stream);
         rc = e == hipSuccess ? finish_plan(P, stream) : hip_fail(e, "COO to CSR launch");
     }
+    const int urc = note_use(P, stream);
+    if (!rc) rc = urc;
     if (rc) {
         free_plan(P);
         return rc;
@@ -1019,9 +1069,12 @@ int gt_plan_copy_graph(gt_plan plan, int64_t* indptr, int32_t* indices, int64_t*
     for (const Item& it : items) {
         if (!it.dst || it.bytes == 0) continue;
         hipError_t e = hipMemcpyAsync(it.dst, it.src, it.bytes, hipMemcpyDeviceToDevice, stream);
-        if (e != hipSuccess) return hip_fail(e, "plan graph copy");
+        if (e != hipSuccess) {
+            (void)note_use(plan, stream);
+            return hip_fail(e, "plan graph copy");
+        }
     }
-    return GT_OK;
+    return note_use(plan, stream);
 }
 
 int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, void* out, float* lse,
@@ -1040,6 +1093,7 @@ int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     a.out = out;
     a.lse_out = lse;
     a.N = plan->n_dst;
+    a.n_gather = plan->n_src;
     a.E = plan->E;
     a.H = H;
     a.D = D;
@@ -1048,7 +1102,9 @@ int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     rc = set_options(a, opts);
     if (rc) return rc;
     choose_layout(a, {Q, K, V, out});
-    return run_fwd(a, &plan->tables, stream);
+    rc = run_fwd(a, &plan->tables, stream);
+    const int urc = note_use(plan, stream);
+    return rc ? rc : urc;
 }
 
 int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const void* V, const void* out,
@@ -1066,7 +1122,9 @@ int gt_sparse_mha_bwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     rc = bwd_args(a, at, plan->indptr, plan->indices, plan->t_indptr, plan->t_indices, plan->t_perm, Q, K, V, out,
                   dout, lse, dQ, dK, dV, dbias, dweight, plan->n_dst, plan->n_src, plan->E, H, D, dtype, opts);
     if (rc) return rc;
-    return run_bwd(a, at, &plan->tables, &plan->t_tables, stream);
+    rc = run_bwd(a, at, &plan->tables, &plan->t_tables, stream);
+    const int urc = note_use(plan, stream);
+    return rc ? rc : urc;
 }
 
 int gt_calib_gather(const int32_t* indices, int64_t E, const void* K, const void* V, int64_t n_rows,

@@ -1059,7 +1059,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = full_rows(a);
             // streamed K/V gathers when K and V are far larger than the Infinity Cache
-            const bool stream_kv = 2 * a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
+            const bool stream_kv = 2 * a.n_gather * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv && XL == 0)
                 bwd_dq_vec_kernel<DT, 2, GT_BWD_F32_DQ_U, 64, 16, true, XL, true><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)

@@ -798,7 +798,7 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
             const bool full = full_rows(a);
             // Streaming K/V gathers pay off only when K and V are far larger than
             // the 256 MB Infinity Cache; smaller ones are partly served from it.
-            const bool stream_kv = 2 * a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
+            const bool stream_kv = 2 * a.n_gather * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full && stream_kv)
                 fused_vec_kernel<DT, 2, XL == 2 ? 4 : GT_F32_D64_U, 64, 16, true, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)

@@ -23,6 +23,7 @@ struct Args {
     const float* alpha_in;
     float* alpha_out;
     int64_t N, E;
+    int64_t n_gather;  // rows of the arrays the pass gathers by index (K and V: the source count)
     int H, D, dtype;
     float qscale;  // fused and backward: log2(e)/sqrt(D); SDDMM: 1/sqrt(D)
     float kscale;  // backward: 1/sqrt(D)

@@ -190,7 +190,7 @@ static hipError_t launch_sddmm_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = full_rows(a);
             // gathers streamed past the caches when K is far larger than the Infinity Cache
-            const bool stream_k = a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
+            const bool stream_k = a.n_gather * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && a.H == 8 && full) {
                 if (stream_k && GT_UNFUSED_NTL)
                     sddmm_vec_kernel<DT, 2, GT_SDDMM_F32_U, 64, 16, true><<<grid, block, 0, s>>>(a);

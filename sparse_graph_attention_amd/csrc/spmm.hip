@@ -194,7 +194,7 @@ static hipError_t launch_spmm_dt(const Args& a0, hipStream_t s) {
             const dim3 grid(gx);
             const bool full = full_rows(a);
             // gathers streamed past the caches when V is far larger than the Infinity Cache
-            const bool stream_v = a.N * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
+            const bool stream_v = a.n_gather * (int64_t)a.Rm * 16 > ((int64_t)1 << 30);
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && a.H == 8 && full) {
                 if (stream_v && GT_UNFUSED_NTL)
                     spmm_vec_kernel<DT, 2, GT_SPMM_F32_U, 64, 16, true><<<grid, block, 0, s>>>(a);

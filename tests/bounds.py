@@ -25,6 +25,10 @@ import numpy as np
 
 import oracle
 
+# Lines that the test session's summary prints (how many split rows each
+# large test checked); filled by tests that sample rows.
+REPORT = []
+
 
 def absf(x):
     """|x| elementwise, exactly, in x's own storage type (float32, float64 or bf16 bits)."""

@@ -161,3 +161,43 @@ def test_layout_reject():
     assert L.gt_sparse_mha_bwd_layout(p, p, p, p, None, p, p, p, p, p, p, p, p, p, None, None, 4, 4, 8, 64, 0, 5,
                                       None, S) == gt.GT_EINVAL
     assert L.gt_sparse_mha_fwd_layout(p, p, p, p, p, p, None, 0, 0, 8, 64, 0, 1, None, S) == gt.GT_OK
+
+
+class fail_alloc:
+    """Sets the GT_TEST_FAIL_ALLOC test hook for the duration of a block."""
+
+    def __enter__(self):
+        self.old = os.environ.get("GT_TEST_FAIL_ALLOC")
+        os.environ["GT_TEST_FAIL_ALLOC"] = "1"
+
+    def __exit__(self, *a):
+        if self.old is None:
+            del os.environ["GT_TEST_FAIL_ALLOC"]
+        else:
+            os.environ["GT_TEST_FAIL_ALLOC"] = self.old
+
+
+def test_allocation_failure_hook_returns_enomem_before_any_hip_call():
+    # with the hook set, the calls that take scratch or allocate a plan stop
+    # at the allocation, which comes before every HIP call (there is no device
+    # here: a HIP call would fail with GT_EHIP instead), so nothing is enqueued
+    L = gt.lib()
+    p = ctypes.c_void_p(256)
+    with fail_alloc():
+        assert fwd(ptr=256) == gt.GT_ENOMEM
+        assert "GT_TEST_FAIL_ALLOC" in gt.gt_last_error()
+        assert L.gt_sparse_mha_fwd_lse(p, p, p, p, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_ENOMEM
+        assert L.gt_sddmm(p, p, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_ENOMEM
+        assert L.gt_edge_softmax(p, p, p, 4, 4, 8, S) == gt.GT_ENOMEM
+        assert L.gt_spmm(p, p, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_ENOMEM
+        assert L.gt_sparse_mha_bwd(p, p, p, p, p, p, p, p, p, p, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_ENOMEM
+        assert L.gt_coo_to_csr(p, p, 4, 4, 4, p, p, None, S) == gt.GT_ENOMEM
+        h = ctypes.c_void_p()
+        assert L.gt_plan_create(p, p, 4, 4, 4, gt.GT_PLAN_TRANSPOSE, S, ctypes.byref(h)) == gt.GT_ENOMEM
+        assert h.value is None
+        assert L.gt_plan_create_coo(p, p, 4, 4, 4, 0, S, ctypes.byref(h)) == gt.GT_ENOMEM
+        assert "plan allocation refused" in gt.gt_last_error()
+        # argument errors still come first
+        assert fwd(H=0, ptr=256) == gt.GT_EINVAL
+    assert gt.gt_status_string(gt.GT_ENOMEM) == "out of device memory"
+

@@ -22,6 +22,7 @@ from scipy.special import logsumexp
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
+from tests.bounds import OutTable
 from tests.test_gpu_backward import bound_dkv, bound_dq, check_bound, F32_BTOL
 from tests.test_gpu_parity import F32_TOL, assert_close, dev, host, say
 
@@ -111,7 +112,7 @@ def test_more_than_2_31_feature_elements():
     w["t_indptr"], w["t_indices"] = gtgen.source_sorted(lip, lix)
     rq, rk, rv, olse, _ = oracle.bwd(lip, lix, lQ, lK, lV, ldO)
     full_out = oracle.fwd(lip, lix, lQ, lK, lV)
-    out_of = lambda v: full_out[v]  # noqa: E731
+    out_of = OutTable(full_out)
     check_bound(host(dq[sam_t]), rq[rows], bound_dq(w, olse, out_of, rows), F32_BTOL, "dQ of the sampled rows")
     top_local = np.array([np.nonzero(nodes == g)[0][0] for g in TOP])
     BK, BV = bound_dkv(w, olse, out_of, top_local)

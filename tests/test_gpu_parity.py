@@ -20,6 +20,7 @@ import torch
 import gtgen
 import oracle
 import sparse_graph_attention_amd as gt
+from tests import bounds
 from tests.bounds import sub_graph
 
 pytestmark = pytest.mark.gpu
@@ -152,8 +153,10 @@ def say_split(indptr, rows, chunk, what):
     deg = np.diff(indptr)
     n_split = int((deg > chunk).sum())
     in_sample = int((deg[rows] > chunk).sum())
-    say("%s: %d sampled rows, %d of the graph's %d split rows (%d edges in split rows)" % (
-        what, len(rows), in_sample, n_split, int(deg[deg > chunk].sum())))
+    line = "%s: %d sampled rows, %d of the graph's %d split rows (%d edges in split rows)" % (
+        what, len(rows), in_sample, n_split, int(deg[deg > chunk].sum()))
+    say(line)
+    bounds.REPORT.append(line)
     assert in_sample == n_split, "every split row must be checked"
 
 

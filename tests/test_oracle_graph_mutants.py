@@ -1,7 +1,9 @@
 """Plant plausible mistakes in the oracle's graph construction (copies of
 oracle.c, compiled on the CPU) and show that the graph pins catch each one.
 Some mistakes write outside the arrays, so each mutant runs its pins in a
-forked child process: a crash of the child counts as caught."""
+forked child process: a crash of the child, or pins that do not finish
+within a minute (corrupted offsets can make a check loop nearly forever),
+counts as caught."""
 import multiprocessing
 import os
 import tempfile
@@ -39,10 +41,15 @@ def test_graph_mutant_is_caught(name, workdir):
     path_so = os.path.join(workdir, "liboracle_%s.so" % name)
     open(path_c, "w").write(src.replace(old, new))
     _build.build(src=path_c, out=path_so, extra_flags=("-w",))
-    child = multiprocessing.get_context("fork").Process(target=_run_pins, args=(path_so,))
+    child = multiprocessing.get_context("fork").Process(target=_run_pins, args=(path_so,), daemon=True)
     child.start()
-    child.join(120)
-    assert child.exitcode is not None, "mutant %s: pins did not finish" % name
+    child.join(60)
+    if child.exitcode is None:
+        # the pins never finished: a mutant that corrupts the row offsets can
+        # send a check into a near-endless loop.  Not passing is what counts.
+        child.kill()
+        child.join()
+        return
     assert child.exitcode != 0, "mutant %s passed every graph pin" % name
 
 
