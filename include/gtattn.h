@@ -104,6 +104,29 @@ int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void*
                       void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype, hipStream_t stream);
 
 /*
+ * gt_sparse_mha_fwd for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same arguments and result, with no hipMalloc, hipFree or
+ * other allocating call.  The split-row work lists and partial results go to
+ * a file-scope device array of 160 MiB, which every GPU the library runs on
+ * holds until the process ends, instead of the per-stream scratch.  The split
+ * threshold is the configured one (GT_CFG_CHUNK_EDGES), doubled, up to 64
+ * times, until the work lists and partials fit; while it is unchanged, out is
+ * bit-identical to gt_sparse_mha_fwd's (at the default 512: up to about
+ * 19.8M edges for 8 heads of 64 features, 37.5M for 8 heads of 32; each
+ * doubling about doubles that).  Inputs that do not fit
+ * even at 64 times the threshold return GT_EUNSUPPORTED, before anything is
+ * enqueued (gt_last_error() gives the bytes needed).  All calls on one GPU
+ * share the array, which keeps the last call's contents; nothing in it needs
+ * clearing (each call resets its work-list counters with a kernel).  Calls
+ * that overlap on one GPU (several streams, or several host threads) race
+ * for the array: the caller must order them.
+ */
+int gt_sparse_mha_fwd_noalloc(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K,
+                              const void* V, void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                              hipStream_t stream);
+
+/*
  * Fused forward that also saves, for the backward, the natural-log
  * log-sum-exp of every destination's scores:
  *     lse[v][h] = log sum over in-edges of exp(s)    (float32 [N][H]),

@@ -9,6 +9,8 @@ The functions have the names of the C entry points declared in
 ``include/gtattn.h`` and follow their contracts:
 
 * ``gt_sparse_mha_fwd(indptr, indices, Q, K, V, out=None)`` -- fused forward;
+* ``gt_sparse_mha_fwd_noalloc(indptr, indices, Q, K, V, out)`` -- the same with
+  no device allocation (for callers that cannot allocate);
 * ``gt_sparse_mha_fwd_lse(indptr, indices, Q, K, V, out=None, lse=None)`` --
   fused forward that also returns the per-destination log-sum-exp [N][H];
 * ``gt_sparse_mha_bwd(indptr, indices, t_indptr, t_indices, Q, K, V, out, dout,
@@ -55,6 +57,7 @@ GT_LAYOUT_NHD, GT_LAYOUT_NDH = 0, 1
 
 EXPORTS = (
     "gt_sparse_mha_fwd",
+    "gt_sparse_mha_fwd_noalloc",
     "gt_sparse_mha_fwd_lse",
     "gt_sparse_mha_bwd",
     "gt_sparse_mha_fwd_ex",
@@ -111,6 +114,7 @@ def lib():
             _build.build()
         L = ctypes.CDLL(_build.LIB)
         L.gt_sparse_mha_fwd.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
+        L.gt_sparse_mha_fwd_noalloc.argtypes = [_p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_sparse_mha_fwd_lse.argtypes = [_p, _p, _p, _p, _p, _p, _p, _i64, _i64, _i32, _i32, _i32, _p]
         L.gt_sparse_mha_bwd.argtypes = [_p] * 13 + [_i64, _i64, _i32, _i32, _i32, _p]
         _o = ctypes.POINTER(LogitOpts)
@@ -151,7 +155,7 @@ def lib():
         for name in ("gt_sparse_mha_fwd_ex", "gt_sparse_mha_bwd_ex", "gt_sparse_mha_fwd_layout",
                      "gt_sparse_mha_bwd_layout"):
             getattr(L, name).restype = ctypes.c_int
-        for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
+        for name in ("gt_sparse_mha_fwd", "gt_sparse_mha_fwd_noalloc", "gt_sparse_mha_fwd_lse", "gt_sparse_mha_bwd", "gt_sddmm", "gt_edge_softmax", "gt_spmm", "gt_validate_csr",
                      "gt_calib_gather", "gt_config_set", "gt_profile_begin", "gt_profile_end"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
@@ -225,6 +229,23 @@ def gt_sparse_mha_fwd(indptr, indices, Q, K, V, out=None, stream=None):
     H, D = Q.shape[1], Q.shape[2]
     _check(lib().gt_sparse_mha_fwd(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), N, E, H, D,
                                    _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd")
+    return out
+
+
+def gt_sparse_mha_fwd_noalloc(indptr, indices, Q, K, V, out, stream=None):
+    """The fused forward into the caller's `out`, with no device allocation: its
+    work lists and split-row partials live in the library's static device array."""
+    N, E = _csr(indptr, indices)
+    if Q.dim() != 3 or Q.shape[0] != N or K.shape != Q.shape or V.shape != Q.shape:
+        raise ValueError("Q, K, V must all be [N][H][D] with N = len(indptr) - 1")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    if out is None or out.shape != Q.shape or out.dtype != Q.dtype:
+        raise ValueError("out must be given and match Q in shape and dtype")
+    _need_gpu(indptr, indices, Q, K, V, out)
+    H, D = Q.shape[1], Q.shape[2]
+    _check(lib().gt_sparse_mha_fwd_noalloc(_ptr(indptr), _ptr(indices), _ptr(Q), _ptr(K), _ptr(V), _ptr(out), N, E, H,
+                                           D, _dtype_code(Q), _stream(stream)), "gt_sparse_mha_fwd_noalloc")
     return out
 
 

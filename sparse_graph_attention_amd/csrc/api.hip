@@ -791,6 +791,108 @@ int gt_sparse_mha_bwd_layout(const int64_t* indptr, const int32_t* indices, cons
     return e == hipSuccess ? GT_OK : hip_fail(e, "layout transpose");
 }
 
+// ------------------------------------------------------------------ allocation-free forward
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of gt_sparse_mha_fwd_noalloc: one file-scope device array, which
+// each GPU the library runs on holds until the process ends.  In host code
+// `scratch` names a host-side stand-in, never the device memory: the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is handed to kernels.
+constexpr size_t kStaticScratchBytes = (size_t)160 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_static_mu;
+std::map<int, void*> g_static_ptr;  // device -> address of its `scratch`
+
+int static_scratch(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    std::lock_guard<std::mutex> lock(g_static_mu);
+    auto it = g_static_ptr.find(dev);
+    if (it == g_static_ptr.end()) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) return hip_fail(e, "hipGetSymbolAddress of the static scratch");
+        it = g_static_ptr.emplace(dev, p).first;
+    }
+    *out = it->second;
+    return GT_OK;
+}
+
+// The split threshold may grow to this multiple of the configured one so that
+// a plan fits the static scratch.
+constexpr int64_t kNoallocChunkGrowth = 64;
+
+}  // namespace
+
+extern "C" {
+
+int gt_sparse_mha_fwd_noalloc(const int64_t* indptr, const int32_t* indices, const void* Q, const void* K,
+                              const void* V, void* out, int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype,
+                              hipStream_t stream) {
+    int rc = check_common(N, E, H, D, dtype);
+    if (rc) return rc;
+    if (N == 0) return GT_OK;
+    if (!indptr || !Q || !K || !V || !out) return fail(GT_EINVAL, "NULL array with N > 0");
+    if (E > 0 && !indices) return fail(GT_EINVAL, "NULL indices with E > 0");
+    // the configured split threshold, doubled until the plan's tables and
+    // partials fit the static scratch
+    const int64_t HD = (int64_t)H * D;
+    const int64_t C0 = g_chunk.load();
+    Plan p{};
+    size_t need = 0;
+    for (int64_t C = C0;; C *= 2) {
+        size_plan_at(N, E, C, p);
+        need = table_bytes(p) + partial_bytes(p, H, HD);
+        if (need <= kStaticScratchBytes || C >= C0 * kNoallocChunkGrowth || C >= ((int64_t)1 << 30)) break;
+    }
+    if (need > kStaticScratchBytes)
+        return fail(GT_EUNSUPPORTED,
+                    "N = %lld, E = %lld, H x D = %lld need %zu bytes of scratch at a split threshold of %lld "
+                    "edges; the allocation-free forward has %zu",
+                    (long long)N, (long long)E, (long long)HD, need, (long long)p.chunk, kStaticScratchBytes);
+    rc = check_plan(p);
+    if (rc) return rc;
+    void* base = nullptr;
+    rc = static_scratch(&base);
+    if (rc) return rc;
+    Args a{};
+    a.indptr = indptr;
+    a.indices = indices;
+    a.Q = Q;
+    a.K = K;
+    a.V = V;
+    a.out = out;
+    a.N = N;
+    a.n_gather = N;
+    a.E = E;
+    a.H = H;
+    a.D = D;
+    a.dtype = dtype;
+    set_scales(a);
+    choose_layout(a, {Q, K, V, out});
+    a.plan = p;
+    carve_partials(carve_tables((char*)base, a.plan), H, HD, a.plan);
+    a.items = a.plan.max_chunks + N;
+    // launch_plan clears the counters with a kernel when several blocks add
+    // to them, or its one block writes them: nothing carries over from the
+    // last call's contents
+    hipError_t e = launch_plan(a, stream);
+    if (e != hipSuccess) return hip_fail(e, "plan launch");
+    e = launch_fused(a, stream, nullptr, nullptr);
+    if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
+    if (a.plan.max_heavy) {
+        e = launch_fused_merge(a, stream);
+        if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
+    }
+    return GT_OK;
+}
+
 // ------------------------------------------------------------------ graph plans
 
 }  // extern "C"

@@ -201,3 +201,13 @@ def test_allocation_failure_hook_returns_enomem_before_any_hip_call():
         assert fwd(H=0, ptr=256) == gt.GT_EINVAL
     assert gt.gt_status_string(gt.GT_ENOMEM) == "out of device memory"
 
+
+def test_noalloc_rejects_what_its_static_scratch_cannot_hold():
+    # sizes are checked before any HIP call: far too many edges for the static
+    # array even at 64 times the split threshold
+    L = gt.lib()
+    p = ctypes.c_void_p(256)
+    assert L.gt_sparse_mha_fwd_noalloc(p, p, p, p, p, p, 1000, 1 << 40, 8, 64, 0, S) == gt.GT_EUNSUPPORTED
+    assert "allocation-free forward" in gt.gt_last_error()
+    assert L.gt_sparse_mha_fwd_noalloc(p, None, p, p, p, p, 4, 4, 8, 64, 0, S) == gt.GT_EINVAL
+    assert L.gt_sparse_mha_fwd_noalloc(None, None, None, None, None, None, 0, 0, 8, 64, 0, S) == gt.GT_OK
