@@ -4,12 +4,19 @@ import subprocess
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
-LIB = os.path.join(HERE, "liboracle.so")
+# GT_SANITIZE=1: an AddressSanitizer + UndefinedBehaviorSanitizer build of the
+# oracle (a library of its own, loaded instead of the plain one).  The process
+# must preload gcc's libasan; see the design doc for the command.
+SANITIZE = os.environ.get("GT_SANITIZE", "") not in ("", "0")
+SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
+LIB = os.path.join(HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 
 
 def build(src: str = SRC, out: str = LIB, extra_flags=(), verbose: bool = False) -> str:
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", *extra_flags, "-o", tmp, src, "-lm"]
+    san = SAN_FLAGS if SANITIZE and out == LIB else []  # planted mutants are built plain
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-fPIC", "-shared", "-Wall", *san, *extra_flags, "-o", tmp, src,
+           "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -7,8 +7,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-LIB = os.path.join(HERE, "libgtattn.so")
-OBJDIR = os.path.join(ROOT, "_build")
+# GT_SANITIZE=1: the host code built with AddressSanitizer and
+# UndefinedBehaviorSanitizer (device code unchanged), as a library of its own
+# for CPU tests of the argument checks; the process must preload clang's ASan
+# runtime (see the design doc for the command).  Never used on a GPU.
+SANITIZE = os.environ.get("GT_SANITIZE", "") not in ("", "0")
+LIB = os.path.join(HERE, "libgtattn_san.so" if SANITIZE else "libgtattn.so")
+OBJDIR = os.path.join(ROOT, "_build_san" if SANITIZE else "_build")
+HOST_SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
+                  "-Xarch_host -fno-omit-frame-pointer -Xarch_host -shared-libsan").split()
 # bwd.hip is built as its two passes (bwd_dq.hip, bwd_dkv.hip include it)
 SOURCES = ["api.hip", "plan.hip", "fused.hip", "sddmm.hip", "softmax.hip", "spmm.hip", "bwd_dq.hip", "bwd_dkv.hip",
            "graph.hip", "calib.hip"]
@@ -29,7 +36,8 @@ FLAGS = [
 
 def _compile(src, verbose, objdir, extra):
     obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
+    san = HOST_SAN_FLAGS if SANITIZE else []
+    cmd = [HIPCC, *FLAGS, *san, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,7 +57,8 @@ def build(verbose: bool = False, out: str = LIB, extra_flags=(), objdir: str = O
             if lines:
                 print("\n".join(lines))
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
+    san = HOST_SAN_FLAGS if SANITIZE else []
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *san, "-o", tmp, *[o for o, _ in results]]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
