@@ -7,11 +7,12 @@ D=64, fp32; inputs resident in HBM before timing starts.
 
 Prints one JSON line: edge-heads/s of the whole call (and per-call median and
 minimum event times, back to back and after an L2 / Infinity Cache flush), the roofline of the
-dominant kernel (the fused attention kernel, timed with HIP events on its own
-stream over the timed region) against MI355X's 8 TB/s HBM peak, the HBM
-traffic counted by rocprofv3 (from the committed counter summary, when it
-matches the current kernel source), and the CPU oracle timed on a bounded
-sample of the same workload.
+dominant kernels (the fused attention kernel and the merge of split rows, which
+writes those rows' outputs, timed with HIP events on their own stream over the
+timed region) against MI355X's 8 TB/s HBM peak, the HBM traffic counted by
+rocprofv3 (from the committed counter summary, when it matches the current
+kernel source), and the CPU oracle timed on a bounded sample of the same
+workload.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                   [--no-cpu-baseline] [--no-stages] [--no-backward] [--no-plan] [--no-variants]
@@ -42,6 +43,10 @@ HBM_PEAK_GBS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fused_fwd_powerlaw_1M.traffic.txt")
 KERNEL_SOURCES = ["sparse_graph_attention_amd/csrc/fused.hip", "sparse_graph_attention_amd/csrc/common.hpp",
                   "sparse_graph_attention_amd/csrc/kernels.hpp"]
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "bwd_powerlaw_1M.traffic.txt")
+BWD_SOURCES = ["sparse_graph_attention_amd/csrc/bwd.hip", "sparse_graph_attention_amd/csrc/bwd_dq.hip",
+               "sparse_graph_attention_amd/csrc/bwd_dkv.hip", "sparse_graph_attention_amd/csrc/plan.hip",
+               "sparse_graph_attention_amd/csrc/common.hpp", "sparse_graph_attention_amd/csrc/kernels.hpp"]
 
 DESCRIPTIONS = {
     "powerlaw": "power-law graph: N=1,000,000, E=16,000,000, in-degree Zipf(1.8) clipped at 50,000, "
@@ -57,28 +62,32 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
-def kernel_source_sha():
+def kernel_source_sha(sources=KERNEL_SOURCES):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in sources:
         h.update(open(os.path.join(ROOT, p), "rb").read())
     return h.hexdigest()
 
 
-def load_traffic():
-    """HBM bytes per launch of the fused kernel from the committed counter summary, or None."""
-    if not os.path.exists(TRAFFIC_FILE):
+def load_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+    """HBM bytes per call of the timed kernels from a committed counter summary
+    (rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch, summed over the call's
+    kernels and scaled by what the counters read for a plain copy), or None when
+    the summary is missing or the kernel sources changed since it was taken."""
+    if not os.path.exists(path):
         return None, "no counter summary"
     kv = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         line = line.strip()
         if line and not line.startswith("#") and "=" in line:
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_sha():
+    if kv.get("kernel_source_sha256") != kernel_source_sha(sources):
         return None, "kernel changed since the counters were taken"
-    fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_scale"])
-    write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_scale"])
-    return fetch + write, "rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by a plain copy"
+    fetch = float(kv["fetch_kib_per_call"]) * 1024 * float(kv["copy_fetch_scale"])
+    write = float(kv["write_kib_per_call"]) * 1024 * float(kv["copy_write_scale"])
+    return fetch + write, "stored rocprofv3 FETCH_SIZE + WRITE_SIZE (%s), scaled by a plain copy" % (
+        os.path.relpath(path, ROOT))
 
 
 def algorithmic_bytes(w):
@@ -185,11 +194,20 @@ def time_backward(gt, t, w, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     nbytes = backward_bytes(w)
-    res = {"ms": ms, "edge_heads_per_s": w["E"] * w["H"] / (ms * 1e-3), "algorithmic_bytes": nbytes,
-           "GBps": nbytes / (ms * 1e-3) / 1e9, "frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
-    # frac can pass 1 on graphs whose popular destinations the source pass re-reads from cache
-    log("backward: %.3f ms, %.0f GB/s algorithmic (algorithmic bytes at %.0f%% of HBM peak)" % (
-        ms, res["GBps"], 100 * res["frac"]))
+    traffic, note = (load_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES) if w.get("name") == "powerlaw"
+                     else (None, "counters are for the power-law workload"))
+    res = {"ms": ms, "edge_heads_per_s": w["E"] * w["H"] / (ms * 1e-3),
+           # the method's bytes over the call time: can pass the HBM peak, since the
+           # source pass re-reads popular destinations' rows from cache
+           "algorithmic_bytes": nbytes, "algorithmic_GBps": nbytes / (ms * 1e-3) / 1e9,
+           "algorithmic_rate_over_peak": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+           # HBM bytes counted per call (both passes, merges and work lists) over the call time
+           "traffic": traffic, "traffic_source": note,
+           "GBps": None if traffic is None else traffic / (ms * 1e-3) / 1e9,
+           "frac": None if traffic is None else traffic / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+    log("backward: %.3f ms, %.0f GB/s algorithmic; counted traffic: %s" % (
+        ms, res["algorithmic_GBps"], "%.0f GB/s (%.0f%% of HBM peak)" % (res["GBps"], 100 * res["frac"])
+        if traffic is not None else note))
     del grads, out, lse, dO, tip, tix
     return res
 
@@ -643,7 +661,7 @@ def main():
     alg = algorithmic_bytes(w)
     achieved = alg / (kern_avg_ms * 1e-3) / 1e9
     traffic, traffic_note = load_traffic() if args.workload == "powerlaw" else (None, "counters are for powerlaw")
-    log("ms/step %.3f (event-timed call %.3f ms, fused kernel %.3f ms); algorithmic %.2f GB -> %.0f GB/s"
+    log("ms/step %.3f (event-timed call %.3f ms, fused kernel + merge %.3f ms); algorithmic %.2f GB -> %.0f GB/s"
         % (ms_per_step, call_ms / calls, kern_avg_ms, alg / 1e9, achieved))
     log("traffic: %s" % traffic_note)
 
@@ -668,9 +686,10 @@ def main():
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBS,
             "traffic": traffic,
-            # HBM bytes counted by rocprofv3 over the same kernel's live average duration
+            "traffic_source": traffic_note,
+            # HBM bytes counted by rocprofv3 over the same kernels' live average duration
             "traffic_GBps": None if traffic is None else traffic / (kern_avg_ms * 1e-3) / 1e9,
-            "kernel": "fused attention kernel",
+            "kernel": "fused attention kernel + merge of split rows",
             "kernel_ms": kern_avg_ms,
             "algorithmic_bytes": alg,
         },

@@ -412,8 +412,10 @@ int64_t gt_scratch_bytes(hipStream_t stream);
 /*
  * Kernel timing for measurement.  gt_profile_begin(capacity) makes the next
  * `capacity` calls of gt_sparse_mha_fwd record HIP events, on the stream they
- * launch on, around their attention kernel and around the whole call.
- * gt_profile_end waits for those events and returns the summed kernel time,
+ * launch on, around their attention kernels (the fused kernel and the merge
+ * of split rows, which writes those rows' outputs) and around the whole call
+ * (with the work-list kernel).  gt_profile_end waits for those events and
+ * returns the summed kernel time,
  * the summed call time (milliseconds) and the number of calls recorded, then
  * stops recording.  Not for concurrent use from several threads.
  */

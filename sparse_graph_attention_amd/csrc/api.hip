@@ -247,7 +247,7 @@ int check_common(int64_t N, int64_t E, int32_t H, int32_t D, int32_t dtype) {
 
 struct Profile {
     bool on = false;
-    std::vector<hipEvent_t> ev;  // 4 per call: call start, kernel start, kernel end, call end
+    std::vector<hipEvent_t> ev;  // 4 per call: call start, kernels start, kernels end, call end
     int capacity = 0;
     int used = 0;
 };
@@ -371,12 +371,15 @@ int run_fwd(Args& a, const Plan* tables, hipStream_t stream) {
         rc = make_plan(a.indptr, a.N, a.E, a.H, a.D, stream, a);
         if (rc) return rc;
     }
-    hipError_t e = launch_fused(a, stream, ev ? ev[1] : nullptr, ev ? ev[2] : nullptr);
+    // the attention kernels: the fused kernel and the merge of split rows,
+    // which writes those rows' outputs
+    hipError_t e = launch_fused(a, stream, ev ? ev[1] : nullptr, nullptr);
     if (e != hipSuccess) return hip_fail(e, "fused kernel launch");
     if (a.plan.max_heavy) {
         e = launch_fused_merge(a, stream);
         if (e != hipSuccess) return hip_fail(e, "merge kernel launch");
     }
+    if (ev) (void)hipEventRecord(ev[2], stream);
     if (ev) (void)hipEventRecord(ev[3], stream);
     return GT_OK;
 }

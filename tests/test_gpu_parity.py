@@ -429,3 +429,50 @@ def test_softmax_row_blocks(H, in_place, chunk):
         a = gt.gt_edge_softmax(ip, buf, alpha=buf if in_place else None)
         torch.cuda.synchronize()
     assert_close(host(a), ref, F32_TOL, "edge_softmax H=%d" % H)
+
+
+@pytest.mark.parametrize("H", [4, 8, 16])
+@pytest.mark.parametrize("in_place", [False, True])
+def test_softmax_row_lengths(H, in_place):
+    # rows of many lengths (powers of two and one past them, up to the split
+    # threshold and far past it, where rows are cut into chunks whose
+    # statistics are merged), for 4, 8 and 16 heads, and then a graph of more
+    # rows than one plan block lists (8,192), so that several blocks add to the
+    # split-row lists
+    degs = [1, 7, 8, 9, 31, 32, 33, 127, 128, 129, 255, 256, 257, 300, 511, 512, 513, 0, 2, 1000,
+            1024, 1025, 2048, 2049, 4096, 4097, 8192, 8193, 20000]
+    N = len(degs) + 2
+    dst = np.concatenate([np.full(d, v) for v, d in enumerate(degs)])
+    src = gtgen.random_coo(43, N, len(dst))[0]
+    cases = [gtgen.coo_to_csr(N, src, dst)]
+    rng = np.random.default_rng(H)
+    deg2 = rng.choice([0, 1, 3, 8, 9, 20, 33, 70, 130, 260, 400, 520], size=20000)
+    dst2 = np.repeat(np.arange(20000), deg2).astype(np.int32)
+    cases.append(gtgen.coo_to_csr(20000, rng.integers(0, 20000, len(dst2)).astype(np.int32), dst2))
+    for indptr, indices in cases:
+        E = len(indices)
+        sc = gtgen.normal_f32(47, 7, (E, H), 3.0)
+        ref = oracle.edge_softmax(indptr, sc.astype(np.float64))
+        ip = torch.from_numpy(indptr).to(dev())
+        buf = torch.from_numpy(sc).to(dev())
+        say("softmax row lengths H=%d N=%d E=%d in_place=%s" % (H, len(indptr) - 1, E, in_place))
+        a = gt.gt_edge_softmax(ip, buf, alpha=buf if in_place else None)
+        torch.cuda.synchronize()
+        assert_close(host(a), ref, F32_TOL, "edge_softmax row lengths H=%d" % H)
+
+
+def test_softmax_misaligned_scores():
+    # scores 4 bytes into a buffer (not 16-byte aligned), a split row included
+    degs = [3, 40, 200, 600, 0, 9]
+    N = len(degs)
+    dst = np.concatenate([np.full(d, v) for v, d in enumerate(degs)])
+    indptr, _ = gtgen.coo_to_csr(N, gtgen.random_coo(44, N, len(dst))[0], dst)
+    E, H = len(dst), 8
+    sc = gtgen.normal_f32(48, 7, (E, H), 3.0)
+    big = torch.empty(E * H + 1, dtype=torch.float32, device=dev())
+    view = big[1:].view(E, H)
+    view.copy_(torch.from_numpy(sc).to(dev()))
+    say("softmax misaligned scores")
+    a = gt.gt_edge_softmax(torch.from_numpy(indptr).to(dev()), view)
+    torch.cuda.synchronize()
+    assert_close(host(a), oracle.edge_softmax(indptr, sc.astype(np.float64)), F32_TOL, "misaligned softmax")
