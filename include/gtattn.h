@@ -112,9 +112,9 @@ int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void*
  * holds until the process ends, instead of the per-stream scratch.  The split
  * threshold is the configured one (GT_CFG_CHUNK_EDGES), doubled, up to 64
  * times, until the work lists and partials fit; while it is unchanged, out is
- * bit-identical to gt_sparse_mha_fwd's (at the default 512: up to about
- * 19.8M edges for 8 heads of 64 features, 37.5M for 8 heads of 32; each
- * doubling about doubles that).  Inputs that do not fit
+ * bit-identical to gt_sparse_mha_fwd's (at the default 512 and 16 in-edges
+ * per node on average: up to about 19M edges for 8 heads of 64 features,
+ * 35M for 8 heads of 32; each doubling about doubles that).  Inputs that do not fit
  * even at 64 times the threshold return GT_EUNSUPPORTED, before anything is
  * enqueued (gt_last_error() gives the bytes needed).  All calls on one GPU
  * share the array, which keeps the last call's contents; nothing in it needs

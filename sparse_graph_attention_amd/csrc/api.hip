@@ -97,13 +97,16 @@ void size_plan_at(int64_t N, int64_t E, int64_t C, Plan& p) {
     p.chunk = C;
     p.max_heavy = std::min<int64_t>(N, E / (C + 1));
     p.max_chunks = p.max_heavy ? E / C + p.max_heavy : 0;
+    // the row order by degree bin comes with the plan kernel, which runs when
+    // a row can be split (for smaller graphs rows go in index order)
+    p.n_order = p.max_heavy ? N : 0;
 }
 
 void size_plan(int64_t N, int64_t E, Plan& p) { size_plan_at(N, E, g_chunk.load(), p); }
 
 size_t table_bytes(const Plan& p) {
     return align256(sizeof(PlanCounters)) + align256(sizeof(HeavyRow) * p.max_heavy) +
-           align256(sizeof(ChunkRef) * p.max_chunks);
+           align256(sizeof(ChunkRef) * p.max_chunks) + align256(sizeof(int32_t) * p.n_order);
 }
 
 // Partials of chunks `accw` floats wide.
@@ -116,6 +119,7 @@ char* carve_tables(char* b, Plan& p) {
     p.counters = (PlanCounters*)b;               b += align256(sizeof(PlanCounters));
     p.heavy = (HeavyRow*)b;                      b += align256(sizeof(HeavyRow) * p.max_heavy);
     p.chunks = (ChunkRef*)b;                     b += align256(sizeof(ChunkRef) * p.max_chunks);
+    p.order = p.n_order ? (int32_t*)b : nullptr; b += align256(sizeof(int32_t) * p.n_order);
     return b;
 }
 

@@ -9,7 +9,8 @@
 // (no host synchronisation); kernels are launched over an upper bound of the
 // item count and surplus waves exit at once.  Item ids [0, max_chunks) are
 // chunks, dispatched first so the longest work starts first; item ids
-// [max_chunks, max_chunks + N) are rows.
+// [max_chunks, max_chunks + N) are rows, taken through the plan's row order
+// (rows grouped by degree bin, longest first) when the plan made one.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -67,10 +68,20 @@ constexpr int kBlock = kWave * kWavesPerBlock;
 
 enum : int { kF32 = 0, kBF16 = 1 };
 
+// Degree bins of the row order, longest rows first: (256, chunk], (64, 256],
+// (16, 64], (4, 16], [1, 4], and rows without in-edges.  Waves that take rows
+// of like length run together, the write-heavy short and empty rows last.
+constexpr int kOrderBins = 6;
+__device__ __forceinline__ int order_bin(int64_t deg) {
+    return deg > 256 ? 0 : deg > 64 ? 1 : deg > 16 ? 2 : deg > 4 ? 3 : deg > 0 ? 4 : 5;
+}
+
 struct PlanCounters {
-    uint32_t nheavy;     // heavy rows listed
-    uint32_t nchunks;    // chunk items listed
-    uint32_t pad[62];    // keep the following arrays 256-byte aligned
+    uint32_t nheavy;                  // heavy rows listed
+    uint32_t nchunks;                 // chunk items listed
+    uint32_t bin_total[kOrderBins];   // unsplit rows of each degree bin
+    uint32_t bin_cursor[kOrderBins];  // rows placed in each bin's part of the order so far
+    uint32_t pad[64 - 2 - 2 * kOrderBins];  // keep the following arrays 256-byte aligned
 };
 
 struct HeavyRow {
@@ -95,6 +106,8 @@ struct Plan {
     float* pl;           // [max_chunks][H] sum of exponentials of a chunk
     float* pacc;         // [max_chunks][H*D] unnormalised weighted sum of a chunk
     float* hstat;        // [max_heavy][H][2] merged (max, sum) of a heavy row
+    int32_t* order;      // [n_order] the unsplit rows by degree bin (nullptr: rows in index order)
+    int64_t n_order;     // N when the plan orders the rows, else 0
     int64_t max_heavy;
     int64_t max_chunks;
     int64_t chunk;       // edges per chunk; rows with more edges are split
@@ -130,7 +143,16 @@ __device__ __forceinline__ bool resolve_item(const Plan& p, const int64_t* __res
         return true;
     }
     int64_t row = item - p.max_chunks;
-    if (row >= N) return false;
+    if (p.order) {  // rows by degree bin; the list holds every row that is not split
+        const PlanCounters* c = p.counters;
+        int64_t listed = 0;
+#pragma unroll
+        for (int b = 0; b < kOrderBins; ++b) listed += c->bin_total[b];
+        if (row >= listed) return false;
+        row = p.order[row];
+    } else if (row >= N) {
+        return false;
+    }
     it.row = row;
     it.e0 = indptr[row];
     it.e1 = indptr[row + 1];

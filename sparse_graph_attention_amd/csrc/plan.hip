@@ -7,84 +7,138 @@
 namespace gt {
 
 __global__ void reset_kernel(PlanCounters* c) {
-    if (threadIdx.x == 0) {
-        c->nheavy = 0;
-        c->nchunks = 0;
-    }
+    if (threadIdx.x < 64) reinterpret_cast<uint32_t*>(c)[threadIdx.x] = 0;
 }
 
 // A row with more than `chunk` in-edges gets a slot in the heavy-row list and
 // a contiguous range of chunk item ids; the chunk table maps each id back to
-// (row, chunk index, heavy slot).  Slot order depends on scheduling, but each
-// chunk's result does not, and the merges read a row's chunks in chunk order,
-// so outputs are deterministic.  A block takes kPlanThreads * kPlanRows rows
-// (each thread kPlanRows of them, kPlanThreads apart, so that loads
-// coalesce), adds up its heavy rows and chunks with a block-wide prefix scan
-// and takes its ranges with one atomic per counter.  The counters are hot
-// words that every block updates at the coherent memory side, so the fewer
-// the atomics the better: one pair per 8,192 rows.  A graph of at most that
-// many rows has one block, which writes the counters itself, so small graphs
-// need no reset launch before it.
+// (row, chunk index, heavy slot).  Every other row goes into the row order, by
+// degree bin (order_bin), each bin's rows in index order within a block.
+// Slot and block order depend on scheduling, but no result does: each row and
+// chunk is computed on its own, and the merges read a row's chunks in chunk
+// order.  A block takes kPlanThreads * kPlanRows consecutive rows (each thread
+// kPlanRows consecutive ones), adds up its heavy rows, chunks and bin counts
+// with a block-wide prefix scan and takes its ranges with one atomic per
+// counter.  The counters are hot words that every block updates at the
+// coherent memory side, so the fewer the atomics the better.  A graph of at
+// most kPlanThreads * kPlanRows rows has one block, which writes the counters
+// and the row order itself, so small graphs need neither a reset launch nor
+// the ordering launch.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanRows = 8;
+constexpr int kPlanWaves = kPlanThreads / kWave;
+constexpr int kPlanCounts = 2 + kOrderBins;  // heavy rows, chunks, rows of each bin
+
+// The degrees of the thread's rows (-1 past the end).
+__device__ __forceinline__ void plan_degrees(const int64_t* __restrict__ indptr, int64_t N, int64_t v0,
+                                             int64_t (&deg)[kPlanRows]) {
+    int64_t ip[kPlanRows + 1];
+#pragma unroll
+    for (int k = 0; k <= kPlanRows; ++k) ip[k] = v0 + k <= N ? indptr[v0 + k] : 0;
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k) deg[k] = v0 + k < N ? ip[k + 1] - ip[k] : -1;
+}
+
+// Exclusive block-wide prefix of the thread's counts: out[i] is the sum of
+// cnt[i] over the threads before this one; tot[i] the block's total.
+__device__ __forceinline__ void block_prefix(const uint32_t (&cnt)[kPlanCounts], uint32_t (&out)[kPlanCounts],
+                                             uint32_t (&tot)[kPlanCounts], uint32_t (*s_w)[kPlanCounts]) {
+    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
+    uint32_t inc[kPlanCounts];
+#pragma unroll
+    for (int i = 0; i < kPlanCounts; ++i) inc[i] = cnt[i];
+    for (int off = 1; off < kWave; off <<= 1) {
+#pragma unroll
+        for (int i = 0; i < kPlanCounts; ++i) {
+            const uint32_t x = __shfl_up(inc[i], off, kWave);
+            if (lane >= off) inc[i] += x;
+        }
+    }
+    if (lane == kWave - 1)
+#pragma unroll
+        for (int i = 0; i < kPlanCounts; ++i) s_w[wid][i] = inc[i];
+    __syncthreads();
+    if (threadIdx.x < kPlanCounts) {  // exclusive prefix over the waves, kept in place; the total at the end
+        const int i = threadIdx.x;
+        uint32_t t = 0;
+        for (int w = 0; w < kPlanWaves; ++w) {
+            const uint32_t c = s_w[w][i];
+            s_w[w][i] = t;
+            t += c;
+        }
+        s_w[kPlanWaves][i] = t;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kPlanCounts; ++i) {
+        out[i] = s_w[wid][i] + inc[i] - cnt[i];
+        tot[i] = s_w[kPlanWaves][i];
+    }
+}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __restrict__ indptr, int64_t N, Plan p) {
-    constexpr int kWaves = kPlanThreads / kWave;
-    __shared__ uint32_t s_h[kWaves], s_c[kWaves], s_base[2];
-    const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x >> 6;
-    const int64_t v0 = (int64_t)blockIdx.x * kPlanThreads * kPlanRows + threadIdx.x;
-    uint32_t nch[kPlanRows];
-    uint32_t hcnt = 0, ccnt = 0;
+    __shared__ uint32_t s_w[kPlanWaves + 1][kPlanCounts], s_base[kPlanCounts];
+    const int64_t v0 = ((int64_t)blockIdx.x * kPlanThreads + threadIdx.x) * kPlanRows;
+    int64_t deg[kPlanRows];
+    plan_degrees(indptr, N, v0, deg);
+    uint32_t nch[kPlanRows], cnt[kPlanCounts];
+#pragma unroll
+    for (int i = 0; i < kPlanCounts; ++i) cnt[i] = 0;
 #pragma unroll
     for (int k = 0; k < kPlanRows; ++k) {
-        const int64_t v = v0 + (int64_t)k * kPlanThreads;
-        const int64_t deg = v < N ? indptr[v + 1] - indptr[v] : 0;
-        nch[k] = deg > p.chunk ? (uint32_t)((deg + p.chunk - 1) / p.chunk) : 0u;
-        hcnt += nch[k] ? 1u : 0u;
-        ccnt += nch[k];
+        nch[k] = deg[k] > p.chunk ? (uint32_t)((deg[k] + p.chunk - 1) / p.chunk) : 0u;
+        cnt[0] += nch[k] ? 1u : 0u;
+        cnt[1] += nch[k];
+        if (deg[k] >= 0 && !nch[k])
+#pragma unroll
+            for (int b = 0; b < kOrderBins; ++b) cnt[2 + b] += order_bin(deg[k]) == b ? 1u : 0u;
     }
-    uint32_t hin = hcnt, cin = ccnt;  // inclusive prefix sums over the wave
-    for (int off = 1; off < kWave; off <<= 1) {
-        const uint32_t h = __shfl_up(hin, off, kWave), c = __shfl_up(cin, off, kWave);
-        if (lane >= off) {
-            hin += h;
-            cin += c;
-        }
-    }
-    if (lane == kWave - 1) {
-        s_h[wid] = hin;
-        s_c[wid] = cin;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {  // exclusive prefix over the waves, then the block's ranges
-        uint32_t ht = 0, ct = 0;
-        for (int w = 0; w < kWaves; ++w) {
-            const uint32_t h = s_h[w], c = s_c[w];
-            s_h[w] = ht;
-            s_c[w] = ct;
-            ht += h;
-            ct += c;
-        }
-        if (gridDim.x == 1) {  // the only block: it sets the counters (no reset ran)
-            p.counters->nheavy = ht;
-            p.counters->nchunks = ct;
-            s_base[0] = s_base[1] = 0u;
+    uint32_t pre[kPlanCounts], tot[kPlanCounts];
+    block_prefix(cnt, pre, tot, s_w);
+    const bool single = gridDim.x == 1;
+    if (threadIdx.x < kPlanCounts) {
+        const int i = threadIdx.x;
+        uint32_t* ctr = i == 0 ? &p.counters->nheavy : i == 1 ? &p.counters->nchunks : &p.counters->bin_total[i - 2];
+        if (single) {  // the only block: it sets the counters (no reset ran)
+            *ctr = tot[i];
+            if (i >= 2) p.counters->bin_cursor[i - 2] = tot[i];
+            s_base[i] = 0u;
         } else {
-            s_base[0] = ht ? atomicAdd(&p.counters->nheavy, ht) : 0u;
-            s_base[1] = ht ? atomicAdd(&p.counters->nchunks, ct) : 0u;
+            s_base[i] = tot[i] && i < 2 ? atomicAdd(ctr, tot[i]) : 0u;
+            if (i >= 2 && tot[i]) atomicAdd(ctr, tot[i]);
         }
     }
     __syncthreads();
-    if (hcnt == 0) return;
-    uint32_t hs = s_base[0] + s_h[wid] + hin - hcnt;
-    uint32_t cb = s_base[1] + s_c[wid] + cin - ccnt;
+    uint32_t hs = s_base[0] + pre[0];
+    uint32_t cb = s_base[1] + pre[1];
+    // one block: the row order too, each bin's part after the longer bins'
+    uint32_t ob[kOrderBins];
+    if (single && p.order) {
+        uint32_t start = 0;
+#pragma unroll
+        for (int b = 0; b < kOrderBins; ++b) {
+            ob[b] = start + pre[2 + b];
+            start += tot[2 + b];
+        }
+    }
 #pragma unroll
     for (int k = 0; k < kPlanRows; ++k) {
-        if (!nch[k]) continue;
+        if (deg[k] < 0) continue;
+        const int32_t v = (int32_t)(v0 + k);
+        if (!nch[k]) {
+            if (single && p.order) {
+                const int b = order_bin(deg[k]);
+                uint32_t pos = 0;
+#pragma unroll
+                for (int c = 0; c < kOrderBins; ++c)
+                    if (c == b) pos = ob[c]++;
+                if ((int64_t)pos < p.n_order) p.order[pos] = v;
+            }
+            continue;
+        }
         // a valid CSR never trips this (the host sizes both tables for it); a
         // malformed one must not write past them
         if ((int64_t)hs >= p.max_heavy || (int64_t)cb + nch[k] > p.max_chunks) return;
-        const int32_t v = (int32_t)(v0 + (int64_t)k * kPlanThreads);
         p.heavy[hs] = HeavyRow{v, (int32_t)nch[k], (int64_t)cb};
         for (uint32_t i = 0; i < nch[k]; ++i) p.chunks[cb + i] = ChunkRef{v, (int32_t)i, (int32_t)hs, 0};
         ++hs;
@@ -92,15 +146,59 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
     }
 }
 
+// Several blocks: the row order, once plan_kernel has counted every bin.
+// Each block places its rows of bin b at the bin's start (the rows of the
+// longer bins) plus what the blocks before it in this launch placed.
+__global__ __launch_bounds__(kPlanThreads) void order_kernel(const int64_t* __restrict__ indptr, int64_t N, Plan p) {
+    __shared__ uint32_t s_w[kPlanWaves + 1][kPlanCounts], s_base[kPlanCounts];
+    const int64_t v0 = ((int64_t)blockIdx.x * kPlanThreads + threadIdx.x) * kPlanRows;
+    int64_t deg[kPlanRows];
+    plan_degrees(indptr, N, v0, deg);
+    uint32_t cnt[kPlanCounts];
+#pragma unroll
+    for (int i = 0; i < kPlanCounts; ++i) cnt[i] = 0;
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k)
+        if (deg[k] >= 0 && deg[k] <= p.chunk)
+#pragma unroll
+            for (int b = 0; b < kOrderBins; ++b) cnt[2 + b] += order_bin(deg[k]) == b ? 1u : 0u;
+    uint32_t pre[kPlanCounts], tot[kPlanCounts];
+    block_prefix(cnt, pre, tot, s_w);
+    if (threadIdx.x < kOrderBins) {
+        const int b = threadIdx.x;
+        uint32_t start = 0;
+        for (int c = 0; c < b; ++c) start += p.counters->bin_total[c];
+        s_base[2 + b] = start + (tot[2 + b] ? atomicAdd(&p.counters->bin_cursor[b], tot[2 + b]) : 0u);
+    }
+    __syncthreads();
+    uint32_t ob[kOrderBins];
+#pragma unroll
+    for (int b = 0; b < kOrderBins; ++b) ob[b] = s_base[2 + b] + pre[2 + b];
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k) {
+        if (deg[k] < 0 || deg[k] > p.chunk) continue;
+        const int b = order_bin(deg[k]);
+        uint32_t pos = 0;
+#pragma unroll
+        for (int c = 0; c < kOrderBins; ++c)
+            if (c == b) pos = ob[c]++;
+        if ((int64_t)pos < p.n_order) p.order[pos] = (int32_t)(v0 + k);
+    }
+}
+
 hipError_t launch_plan(const Args& a, hipStream_t s) {
-    if (a.plan.max_heavy == 0) return hipSuccess;  // no row can be split: nothing to list
+    if (a.plan.max_heavy == 0) return hipSuccess;  // no row can be split: nothing to list, rows in index order
     const int64_t per_block = (int64_t)kPlanThreads * kPlanRows;
-    if (a.N > per_block) {  // several blocks add to the counters: clear them first
+    const unsigned blocks = (unsigned)((a.N + per_block - 1) / per_block);
+    if (blocks > 1) {  // several blocks add to the counters: clear them first
         reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
-    plan_kernel<<<(unsigned)((a.N + per_block - 1) / per_block), kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
+    plan_kernel<<<blocks, kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || blocks == 1 || !a.plan.order) return err;
+    order_kernel<<<blocks, kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
     return hipGetLastError();
 }
 
