@@ -196,6 +196,46 @@ void choose_layout(Args& a, std::initializer_list<const void*> feats) {
     }
 }
 
+// Word layout for plain logits when choose_layout fell back to one wave per
+// head: every head a whole number vph of 8-byte (else 4-byte) words, in lph =
+// pow2ceil(vph) <= 32 lane slots, all H heads of an edge in one lane group of
+// G = pow2ceil(H * lph) <= 64 lanes, the feature arrays aligned to the word.  The
+// shape it is for: fp32 heads of 10 elements (five 8-byte words), 8 heads in
+// 64 lanes; a wave then takes 1 (row) instead of 8 (row, head) items with
+// 4-byte loads.  word_bytes: the word for heads of hb bytes with arrays
+// aligned to `align` bytes, 0 if none fits.
+int word_bytes(int64_t H, int64_t hb, int align) {
+    for (int w : {8, 4})
+        if (w <= align && hb % w == 0 && pow2ceil(hb / w) <= 32 && H * pow2ceil(hb / w) <= kWave) return w;
+    return 0;
+}
+
+bool choose_word_layout(Args& a, std::initializer_list<const void*> feats) {
+    if (a.vec || extended(a)) return false;
+    const int64_t hb = (int64_t)a.D * (a.dtype == GT_F32 ? 4 : 2);
+    uintptr_t bits = 0;
+    for (const void* p : feats) bits |= (uintptr_t)p;
+    const int wb = word_bytes(a.H, hb, bits % 8 == 0 ? 8 : bits % 4 == 0 ? 4 : 0);
+    if (!wb) return false;
+    const int64_t vph = hb / wb;
+    const int lph = pow2ceil(vph);
+    a.vec = 3;
+    a.wb = wb;
+    a.vph = (int)vph;
+    a.lph = lph;
+    a.R = a.Rm = a.H * (int)vph;
+    a.G = pow2ceil((int64_t)a.H * lph);
+    a.NC = 1;
+    a.KD = 0;
+    return true;
+}
+
+// The forward's layout over [N][H][D] rows: vector, else word, else scalar.
+void choose_fwd_layout(Args& a, std::initializer_list<const void*> feats) {
+    choose_layout(a, feats);
+    choose_word_layout(a, feats);
+}
+
 // The head-innermost kernels: a 16-byte vector holds VN heads of one d, the
 // vectors of a d are a power of two, and a row is at most 256 vectors (a
 // lane group of pow2ceil(R) lanes up to 64, then NC = ceil(R / 64) vectors
@@ -217,19 +257,31 @@ bool choose_layout_ndh(Args& a, std::initializer_list<const void*> feats) {
 }
 
 // Whether the head-innermost kernels beat transposing into [N][H][D], run
-// with a layout chosen by choose_layout.  Their cost is the head sums: a lane
-// holds VN heads of one d, so each head's dot product takes VN * log2(G / HV)
-// cross-lane shuffles per edge, where [N][H][D] rows take a few DPP steps.
-// Measured: they win where [N][H][D] falls back to one wave per head (heads
-// not a power-of-two number of 16-byte vectors: fp32 8 x 10, 16 against 25 us
-// forward, 50 against 59 us backward); the forward also wins when a row's
-// gathers are large against its shuffles (fp32 8 x 64: 4 KB per edge for 20
-// shuffles, 12.2 against 16.9 ms), and loses when they are not (bf16 8 x 32:
-// 1 KB for 40 shuffles, 19.5 against 11 ms).  The backward, with two head
-// sums per edge in each pass, lost to the copies at both of those shapes.
+// with a layout chosen by choose_fwd_layout.  Their cost is the head sums: a
+// lane holds VN heads of one d, so each head's dot product takes VN *
+// log2(G / HV) cross-lane shuffles per edge, where [N][H][D] rows sum a head
+// in a few DPP steps; the copies cost five transposes in and three out (one
+// in and one out for the forward), each a launch.  Measured:
+// - heads that [N][H][D] serves only one wave per head: the native kernels;
+// - heads that take the word layout in [N][H][D] (fp32 8 x 10): the native
+//   forward (molecule batch 17 against 43 us, power-law graph 2.30 against
+//   2.65 ms); the backward through copies on large graphs (power-law 5.6
+//   against 13.7 ms), natively on small ones, where the launches of the
+//   copies outweigh the head sums (molecule batch, 8.5 K edges: 61 against
+//   93 us);
+// - heads of 16-byte vectors: the forward natively when a row's gathers are
+//   large against its shuffles (fp32 8 x 64: 4 KB per edge for 20 shuffles,
+//   12.2 against 16.9 ms), through copies when they are not (bf16 8 x 32: 1 KB
+//   for 40 shuffles, 19.5 against 11 ms); the backward, with two head sums
+//   per edge in each pass, through copies at both of those shapes.
+constexpr int64_t kNdhBwdCopiesMinEdges = 1 << 16;
+
 bool ndh_kernels_pay(const Args& a, bool forward) {
     const int64_t hb = (int64_t)a.D * (a.dtype == GT_F32 ? 4 : 2);
-    if (!(hb % 16 == 0 && (a.H * (int64_t)pow2ceil(hb / 16) + kWave - 1) / kWave <= 4)) return true;
+    if (!(hb % 16 == 0 && (a.H * (int64_t)pow2ceil(hb / 16) + kWave - 1) / kWave <= 4)) {
+        if (!word_bytes(a.H, hb, 8)) return true;
+        return forward || a.E < kNdhBwdCopiesMinEdges;
+    }
     if (!forward) return false;
     int steps = 0;
     for (int64_t x = a.G / a.lph; x > 1; x >>= 1) ++steps;
@@ -431,7 +483,7 @@ int fused_fwd(const int64_t* indptr, const int32_t* indices, const void* Q, cons
     set_scales(a);
     rc = set_options(a, opts);
     if (rc) return rc;
-    choose_layout(a, {Q, K, V, out});
+    choose_fwd_layout(a, {Q, K, V, out});
     return run_fwd(a, nullptr, stream);
 }
 
@@ -547,6 +599,17 @@ int bwd_args(Args& a, Args& at, const int64_t* indptr, const int32_t* indices, c
     // needs the CSR positions of its out-edges only for per-edge inputs
     a.dbias = dbias;
     a.dew = dew;
+    if (choose_word_layout(a, {Q, K, V, out, dout, dQ, dK, dV})) {
+        at.vec = a.vec;
+        at.wb = a.wb;
+        at.vph = a.vph;
+        at.lph = a.lph;
+        at.R = a.R;
+        at.Rm = a.Rm;
+        at.G = a.G;
+        at.NC = a.NC;
+        at.KD = a.KD;
+    }
     if (extended(at) && E > 0 && !t_perm)
         return fail(GT_EINVAL, "bias, edge weights or dropout need the transpose's CSR positions (t_perm)");
     return GT_OK;
@@ -731,7 +794,7 @@ int gt_sparse_mha_fwd_layout(const int64_t* indptr, const int32_t* indices, cons
     a.K = Kt;
     a.V = Vt;
     a.out = Ot;
-    choose_layout(a, {Qt, Kt, Vt, Ot});
+    choose_fwd_layout(a, {Qt, Kt, Vt, Ot});
     rc = run_fwd(a, nullptr, stream);
     if (rc) return rc;
     e = launch_transpose_rows(Ot, out, N, H, D, dtype, stream);
@@ -882,7 +945,7 @@ int gt_sparse_mha_fwd_noalloc(const int64_t* indptr, const int32_t* indices, con
     a.D = D;
     a.dtype = dtype;
     set_scales(a);
-    choose_layout(a, {Q, K, V, out});
+    choose_fwd_layout(a, {Q, K, V, out});
     a.plan = p;
     carve_partials(carve_tables((char*)base, a.plan), H, HD, a.plan);
     a.items = a.plan.max_chunks + N;
@@ -1210,7 +1273,7 @@ int gt_sparse_mha_fwd_plan(gt_plan plan, const void* Q, const void* K, const voi
     set_scales(a);
     rc = set_options(a, opts);
     if (rc) return rc;
-    choose_layout(a, {Q, K, V, out});
+    choose_fwd_layout(a, {Q, K, V, out});
     rc = run_fwd(a, &plan->tables, stream);
     const int urc = note_use(plan, stream);
     return rc ? rc : urc;

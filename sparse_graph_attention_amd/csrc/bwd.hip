@@ -973,6 +973,199 @@ __global__ __launch_bounds__(kBlock) void bwd_dkv_ndh_kernel(const Args a) {
     }
 }
 
+// ------------------------------------------------------------ word layout
+//
+// [N][H][D] rows whose heads are whole 8- or 4-byte words but not 16-byte
+// vectors (fp32 heads of 10 elements: five 8-byte words), laid out as in the
+// forward's fused_word_kernel: head h, word j of an edge sit in lane slot
+// h * LPH + j of a G-lane group, a per-head sum is a DPP sum over an aligned
+// LPH-lane segment, and the 64 / G groups of a wave take different edges.
+// Partials of split rows keep the row's [H][D] order.
+template <int DT, int WB, int LPH, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dq_word_kernel(const Args a) {
+    constexpr int EW = Word<DT, WB>::EW;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+    const int G = a.G;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int head = gl / LPH, j = gl % LPH;
+    const bool hv = head < a.H;
+    const bool act = hv && j < a.vph;
+    const int64_t rowbytes = (int64_t)a.H * a.vph * WB;
+    const int moff = (head * a.vph + j) * WB;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    float q[EW], g[EW], o[EW], acc[EW];
+    {
+        const int64_t off = row * rowbytes + moff;
+        unpack_word<DT, WB>(act ? ldw<DT, WB>((const char*)a.Q + off) : zero_word<DT, WB>(), q);
+        unpack_word<DT, WB>(act ? ldw<DT, WB>((const char*)a.dO + off) : zero_word<DT, WB>(), g);
+        unpack_word<DT, WB>(act ? ldw<DT, WB>((const char*)a.O + off) : zero_word<DT, WB>(), o);
+    }
+    float dl = 0.0f;
+#pragma unroll
+    for (int k = 0; k < EW; ++k) {
+        dl = __builtin_fmaf(g[k], o[k], dl);
+        acc[k] = 0.0f;
+    }
+    dl = seg_sum_c<LPH>(dl);
+    const float ls = hv ? a.lse_in[row * a.H + head] * kLog2e : 0.0f;
+    const char* Kb = (const char*)a.K;
+    const char* Vb = (const char*)a.V;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            u[jj] = un[jj];
+            ok[jj] = eb + grp + (int64_t)jj * epw < e1;
+        }
+        Word<DT, WB> kr[U], vr[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj)
+            kr[jj] = (ok[jj] && act) ? ldw<DT, WB>(Kb + (int64_t)u[jj] * rowbytes + moff) : zero_word<DT, WB>();
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj)
+            vr[jj] = (ok[jj] && act) ? ldw<DT, WB>(Vb + (int64_t)u[jj] * rowbytes + moff) : zero_word<DT, WB>();
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            float kf[EW], vf[EW];
+            unpack_word<DT, WB>(kr[jj], kf);
+            unpack_word<DT, WB>(vr[jj], vf);
+            float sd = 0.0f, dd = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EW; ++k) {
+                sd = __builtin_fmaf(q[k], kf[k], sd);
+                dd = __builtin_fmaf(g[k], vf[k], dd);
+            }
+            const float s2 = seg_sum_c<LPH>(sd) * a.qscale;
+            const float da = seg_sum_c<LPH>(dd);
+            const float p = ok[jj] ? exp2_(s2 - ls) : 0.0f;
+            const float ds = p * (da - dl);
+#pragma unroll
+            for (int k = 0; k < EW; ++k) acc[k] = __builtin_fmaf(ds, kf[k], acc[k]);
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < EW; ++k) acc[k] += __shfl_xor(acc[k], off, kWave);
+    if (grp != 0) return;
+    if (hv && j == 0) a.stats[row * a.H + head] = make_float2(ls, dl);  // once per head
+    if (!act) return;
+    if (it.slot < 0) {
+        float r[EW];
+#pragma unroll
+        for (int k = 0; k < EW; ++k) r[k] = acc[k] * a.kscale;
+        stw_nt<DT, WB>((char*)a.dQ + row * rowbytes + moff, r);
+    } else {
+        float* pa = a.plan.pacc + it.slot * (int64_t)a.H * a.D + (int64_t)head * a.D + j * EW;
+#pragma unroll
+        for (int k = 0; k < EW; ++k) pa[k] = acc[k];
+    }
+}
+
+template <int DT, int WB, int LPH, int U>
+__global__ __launch_bounds__(kBlock) void bwd_dkv_word_kernel(const Args a) {
+    constexpr int EW = Word<DT, WB>::EW;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t src = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+    const int G = a.G;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int head = gl / LPH, j = gl % LPH;
+    const bool hv = head < a.H;
+    const bool act = hv && j < a.vph;
+    const int64_t rowbytes = (int64_t)a.H * a.vph * WB;
+    const int moff = (head * a.vph + j) * WB;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    float kk[EW], vv[EW], dk[EW], dv[EW];
+    unpack_word<DT, WB>(act ? ldw<DT, WB>((const char*)a.K + src * rowbytes + moff) : zero_word<DT, WB>(), kk);
+    unpack_word<DT, WB>(act ? ldw<DT, WB>((const char*)a.V + src * rowbytes + moff) : zero_word<DT, WB>(), vv);
+#pragma unroll
+    for (int k = 0; k < EW; ++k) dk[k] = dv[k] = 0.0f;
+    const char* Qb = (const char*)a.Q;
+    const char* Gb = (const char*)a.dO;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            u[jj] = un[jj];
+            ok[jj] = eb + grp + (int64_t)jj * epw < e1;
+        }
+        Word<DT, WB> qr[U], gr[U];
+        float2 st[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            const bool go = ok[jj] && act;
+            qr[jj] = go ? ldw<DT, WB>(Qb + (int64_t)u[jj] * rowbytes + moff) : zero_word<DT, WB>();
+            gr[jj] = go ? ldw<DT, WB>(Gb + (int64_t)u[jj] * rowbytes + moff) : zero_word<DT, WB>();
+            st[jj] = (ok[jj] && hv) ? a.stats[(int64_t)u[jj] * a.H + head] : make_float2(0.0f, 0.0f);
+        }
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            float qf[EW], gf[EW];
+            unpack_word<DT, WB>(qr[jj], qf);
+            unpack_word<DT, WB>(gr[jj], gf);
+            float sd = 0.0f, dd = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EW; ++k) {
+                sd = __builtin_fmaf(qf[k], kk[k], sd);
+                dd = __builtin_fmaf(gf[k], vv[k], dd);
+            }
+            const float s2 = seg_sum_c<LPH>(sd) * a.qscale;
+            const float da = seg_sum_c<LPH>(dd);
+            const float p = ok[jj] ? exp2_(s2 - st[jj].x) : 0.0f;
+            const float ds = p * (da - st[jj].y);
+#pragma unroll
+            for (int k = 0; k < EW; ++k) {
+                dv[k] = __builtin_fmaf(p, gf[k], dv[k]);
+                dk[k] = __builtin_fmaf(ds, qf[k], dk[k]);
+            }
+        }
+    }
+    for (int off = G; off < kWave; off <<= 1)
+#pragma unroll
+        for (int k = 0; k < EW; ++k) {
+            dk[k] += __shfl_xor(dk[k], off, kWave);
+            dv[k] += __shfl_xor(dv[k], off, kWave);
+        }
+    if (grp != 0 || !act) return;
+    if (it.slot < 0) {
+        float r[EW];
+#pragma unroll
+        for (int k = 0; k < EW; ++k) r[k] = dk[k] * a.kscale;
+        stw_nt<DT, WB>((char*)a.dK + src * rowbytes + moff, r);
+        stw_nt<DT, WB>((char*)a.dV + src * rowbytes + moff, dv);
+    } else {
+        const int64_t HD = (int64_t)a.H * a.D;
+        float* pa = a.plan.pacc + it.slot * 2 * HD + (int64_t)head * a.D + j * EW;
+#pragma unroll
+        for (int k = 0; k < EW; ++k) {
+            pa[k] = dk[k];
+            pa[HD + k] = dv[k];
+        }
+    }
+}
+
 #if GT_BWD_PART != 2
 // dw[e] = sum over heads, in head order, of the per-head terms the scalar
 // layout's one-head waves left in part[e][h].
@@ -1045,7 +1238,13 @@ template <int DT, int XL>
 static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
-    if (a0.vec == 2) {  // head-innermost layout (plain logits only)
+    if (a0.vec == 3) {  // word layout (plain logits only)
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            for_word_layout(a, [&](auto wb, auto lph) {
+                bwd_dq_word_kernel<DT, wb, lph, 4><<<dim3(gx), block, 0, s>>>(a);
+            });
+        });
+    } else if (a0.vec == 2) {  // head-innermost layout (plain logits only)
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             switch (a.NC) {
                 case 1: bwd_dq_ndh_kernel<DT, DT == kF32 ? 4 : 2, 1><<<dim3(gx), block, 0, s>>>(a); break;
@@ -1103,7 +1302,13 @@ template <int DT, int XL>
 static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
     hipError_t err;
-    if (a0.vec == 2) {
+    if (a0.vec == 3) {
+        err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            for_word_layout(a, [&](auto wb, auto lph) {
+                bwd_dkv_word_kernel<DT, wb, lph, 4><<<dim3(gx), block, 0, s>>>(a);
+            });
+        });
+    } else if (a0.vec == 2) {
         err = for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             switch (a.NC) {
                 case 1: bwd_dkv_ndh_kernel<DT, DT == kF32 ? 4 : 2, 1><<<dim3(gx), block, 0, s>>>(a); break;

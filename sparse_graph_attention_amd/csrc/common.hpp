@@ -495,6 +495,65 @@ struct Vec<kBF16> {
     }
 };
 
+// Lane words of 8 or 4 bytes (the word layout: heads that are a whole number
+// of such words but not of 16-byte vectors, e.g. fp32 heads of 10 elements).
+template <int DT, int WB>
+struct Word {
+    static constexpr int NW = WB / 4;                      // 32-bit parts
+    static constexpr int EW = DT == kF32 ? NW : 2 * NW;   // elements
+    uint32_t w[NW];
+};
+
+template <int DT, int WB>
+__device__ __forceinline__ Word<DT, WB> ldw(const char* p) {
+    Word<DT, WB> r;
+    if constexpr (WB == 8) {
+        const uint2 v = *reinterpret_cast<const uint2*>(p);
+        r.w[0] = v.x;
+        r.w[1] = v.y;
+    } else {
+        r.w[0] = *reinterpret_cast<const uint32_t*>(p);
+    }
+    return r;
+}
+
+template <int DT, int WB>
+__device__ __forceinline__ Word<DT, WB> zero_word() {
+    Word<DT, WB> r;
+#pragma unroll
+    for (int i = 0; i < Word<DT, WB>::NW; ++i) r.w[i] = 0;
+    return r;
+}
+
+template <int DT, int WB>
+__device__ __forceinline__ void unpack_word(const Word<DT, WB>& x, float* f) {
+#pragma unroll
+    for (int i = 0; i < Word<DT, WB>::NW; ++i) {
+        if constexpr (DT == kF32) {
+            f[i] = __uint_as_float(x.w[i]);
+        } else {
+            f[2 * i] = bf16_lo(x.w[i]);
+            f[2 * i + 1] = bf16_hi(x.w[i]);
+        }
+    }
+}
+
+// Stores EW elements with the non-temporal hint (rows written once).
+template <int DT, int WB>
+__device__ __forceinline__ void stw_nt(char* p, const float* f) {
+    uint32_t w[Word<DT, WB>::NW];
+#pragma unroll
+    for (int i = 0; i < Word<DT, WB>::NW; ++i)
+        w[i] = DT == kF32 ? __float_as_uint(f[i]) : (bf16_bits(f[2 * i]) | (bf16_bits(f[2 * i + 1]) << 16));
+    if constexpr (WB == 8) {
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        u32x2 v = {w[0], w[1]};
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x2*>(p));
+    } else {
+        __builtin_nontemporal_store(w[0], reinterpret_cast<uint32_t*>(p));
+    }
+}
+
 // ---------------------------------------------------------------- lane layouts
 //
 // Vector layout: a node row of H*D elements is R = H*D*bytes/16 vectors of

@@ -566,6 +566,129 @@ __global__ __launch_bounds__(kBlock) void fused_ndh_kernel(const Args a) {
     }
 }
 
+// ------------------------------------------------------------ word layout
+//
+// [N][H][D] rows whose heads are a whole number of 8- or 4-byte words but not
+// of 16-byte vectors, such as the tutorial's molecule shape (H 8, D 10, fp32:
+// 40-byte heads, five 8-byte words).  A head of vph words takes LPH =
+// pow2ceil(vph) lane slots, so its dot product is a DPP sum within an aligned
+// LPH-lane segment (the slots past vph idle with zeros), and a lane group of
+// G = pow2ceil(H * LPH) <= 64 lanes covers all heads of an edge: one wave per
+// row, 64 / G edges per step, where the scalar layout takes a wave per
+// (row, head) with 4-byte loads.  Plain logits only.
+template <int DT, int WB, int LPH, int U>
+__global__ __launch_bounds__(kBlock) void fused_word_kernel(const Args a) {
+    using W = Word<DT, WB>;
+    constexpr int EW = W::EW;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t item = a.item_base + (int64_t)blockIdx.x * kWavesPerBlock + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    Item it;
+    if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
+    const int64_t row = uniform64(it.row), e0 = uniform64(it.e0), e1 = uniform64(it.e1);
+
+    const int G = a.G;
+    const int epw = kWave / G;
+    const int grp = lane / G;
+    const int gl = lane & (G - 1);
+    const int head = gl / LPH, j = gl % LPH;
+    const bool act = head < a.H && j < a.vph;
+    const int64_t rowbytes = (int64_t)a.H * a.vph * WB;
+    const int moff = (head * a.vph + j) * WB;
+    const int32_t* __restrict__ idx = a.indices;
+
+    int32_t un[U];
+    if (e1 > e0) load_ids<U>(idx, e0, grp, epw, e1, un);
+    float q[EW];
+    unpack_word<DT, WB>(act ? ldw<DT, WB>((const char*)a.Q + row * rowbytes + moff) : zero_word<DT, WB>(), q);
+    float m = -INFINITY, l = 0.0f, acc[EW];
+#pragma unroll
+    for (int k = 0; k < EW; ++k) acc[k] = 0.0f;
+    const char* Kb = (const char*)a.K;
+    const char* Vb = (const char*)a.V;
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U) {
+        int32_t u[U];
+        bool ok[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            u[jj] = un[jj];
+            ok[jj] = eb + grp + (int64_t)jj * epw < e1;
+        }
+        Word<DT, WB> kr[U], vr[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj)
+            kr[jj] = (ok[jj] && act) ? ldw<DT, WB>(Kb + (int64_t)u[jj] * rowbytes + moff) : zero_word<DT, WB>();
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj)
+            vr[jj] = (ok[jj] && act) ? ldw<DT, WB>(Vb + (int64_t)u[jj] * rowbytes + moff) : zero_word<DT, WB>();
+        const int64_t nb = eb + (int64_t)epw * U;
+        if (nb < e1) load_ids<U>(idx, nb, grp, epw, e1, un);
+        float sc[U];
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            float kf[EW];
+            unpack_word<DT, WB>(kr[jj], kf);
+            float d = 0.0f;
+#pragma unroll
+            for (int k = 0; k < EW; ++k) d = __builtin_fmaf(q[k], kf[k], d);
+            d = seg_sum_c<LPH>(d) * a.qscale;
+            sc[jj] = ok[jj] ? d : -INFINITY;
+        }
+        float mb = sc[0];
+#pragma unroll
+        for (int jj = 1; jj < U; ++jj) mb = fmaxf(mb, sc[jj]);
+        const float mn = fmaxf(m, mb);
+        const float r = rescale(m, mn);
+        l *= r;
+#pragma unroll
+        for (int k = 0; k < EW; ++k) acc[k] *= r;
+#pragma unroll
+        for (int jj = 0; jj < U; ++jj) {
+            const float p = ok[jj] ? exp2_(sc[jj] - mn) : 0.0f;
+            l += p;
+            float vf[EW];
+            unpack_word<DT, WB>(vr[jj], vf);
+#pragma unroll
+            for (int k = 0; k < EW; ++k) acc[k] = __builtin_fmaf(p, vf[k], acc[k]);
+        }
+        m = mn;
+    }
+    // fold the edge groups of the wave together
+    for (int off = G; off < kWave; off <<= 1) {
+        const float mo = __shfl_xor(m, off, kWave);
+        const float lo = __shfl_xor(l, off, kWave);
+        const float mn = fmaxf(m, mo);
+        const float sa = rescale(m, mn), sb = rescale(mo, mn);
+        l = l * sa + lo * sb;
+#pragma unroll
+        for (int k = 0; k < EW; ++k) {
+            const float ao = __shfl_xor(acc[k], off, kWave);
+            acc[k] = acc[k] * sa + ao * sb;
+        }
+        m = mn;
+    }
+    if (grp != 0) return;
+    const bool first = j == 0 && head < a.H;  // one lane per head carries its (m, l)
+    if (it.slot < 0) {
+        if (act) {
+            float o[EW];
+#pragma unroll
+            for (int k = 0; k < EW; ++k) o[k] = l > 0.0f ? acc[k] / l : 0.0f;
+            stw_nt<DT, WB>((char*)a.out + row * rowbytes + moff, o);
+        }
+        if (a.lse_out && first) a.lse_out[row * a.H + head] = lse_of(m, l);
+    } else {
+        if (first) {
+            a.plan.pm[it.slot * a.H + head] = m;
+            a.plan.pl[it.slot * a.H + head] = l;
+        }
+        if (act) {
+            float* pa = a.plan.pacc + it.slot * (int64_t)a.H * a.D + (int64_t)head * a.D + j * EW;
+#pragma unroll
+            for (int k = 0; k < EW; ++k) pa[k] = acc[k];
+        }
+    }
+}
+
 // Per node, src [A][B] -> dst [B][A]; grid-stride over the elements, reads
 // coalesced.
 template <typename T>
@@ -782,6 +905,13 @@ static bool launch_fixed_lph(const Args& a, dim3 grid, dim3 block, hipStream_t s
 template <int DT, int XL>
 static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
     const dim3 block(kBlock);
+    if (a0.vec == 3) {  // word layout (plain logits only)
+        return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
+            for_word_layout(a, [&](auto wb, auto lph) {
+                fused_word_kernel<DT, wb, lph, 4><<<dim3(gx), block, 0, s>>>(a);
+            });
+        });
+    }
     if (a0.vec == 2) {  // head-innermost layout (plain logits only)
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             switch (a.NC) {

@@ -58,6 +58,7 @@ struct Args {
     int NC;        // vector layout: vectors per lane
     int KD;        // scalar layout: elements per lane
     int ndh;       // features are [N][D][H] (head innermost); vec = 2 selects fused_ndh_kernel
+    int wb;        // word layout (vec = 3): bytes per lane word (4 or 8); vph words per head
     // grid
     int64_t items;      // max_chunks + N
     int64_t item_base;  // first item of the current launch slice
@@ -66,6 +67,25 @@ struct Args {
 // Per node, src [A][B] -> dst [B][A] (elementwise; bf16 moved as 16-bit words).
 hipError_t launch_transpose_rows(const void* src, void* dst, int64_t N, int A, int B, int dtype, hipStream_t s);
 
+
+// Calls f(wb, lph) with std::integral_constant arguments for the word layout's
+// instances (vec = 3): lane words of 8 or 4 bytes, 1 .. 32 lane slots per head.
+template <typename F>
+inline bool for_word_layout(const Args& a, F&& f) {
+    using std::integral_constant;
+    auto go = [&](auto wb) {
+        switch (a.lph) {
+            case 1: f(wb, integral_constant<int, 1>{}); return true;
+            case 2: f(wb, integral_constant<int, 2>{}); return true;
+            case 4: f(wb, integral_constant<int, 4>{}); return true;
+            case 8: f(wb, integral_constant<int, 8>{}); return true;
+            case 16: f(wb, integral_constant<int, 16>{}); return true;
+            case 32: f(wb, integral_constant<int, 32>{}); return true;
+            default: return false;
+        }
+    };
+    return a.wb == 8 ? go(integral_constant<int, 8>{}) : a.wb == 4 ? go(integral_constant<int, 4>{}) : false;
+}
 
 // Whether a launch needs the extended-logit kernels.
 inline bool extended(const Args& a) { return a.bias || a.ew || a.drop_thresh || a.dbias || a.dew; }

@@ -28,8 +28,8 @@ import oracle
 import sparse_graph_attention_amd as gt
 from tests import bounds
 from tests.bounds import OutTable, sub_graph
-from tests.test_gpu_parity import (check_fused_full, chunk_edges, custom, dev, host, oracle_inputs, random_graph,
-                                   sample_rows, say, say_split, to_dev, workload)
+from tests.test_gpu_parity import (WORD_SHAPES, check_fused_full, chunk_edges, custom, dev, host, hub_graph,
+                                   oracle_inputs, random_graph, sample_rows, say, say_split, to_dev, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -267,6 +267,45 @@ def test_bwd_misaligned_features_use_the_scalar_layout():
     check_bound(host(views["dV"]), rv, BV, F32_BTOL, "misaligned dV")
     # and the aligned run (vector layout) too
     check_bwd_full(w)
+
+
+@pytest.mark.parametrize("H,D,dtype", WORD_SHAPES)
+@pytest.mark.parametrize("chunk", [512, 37])
+def test_bwd_word_layout_shapes(H, D, dtype, chunk):
+    # both passes in the word layout, with a destination hub and a source hub
+    # split into chunks at chunk 37
+    with chunk_edges(chunk):
+        check_bwd_full(with_grad(hub_graph(H, D, dtype, H * 100 + D)))
+
+
+@pytest.mark.parametrize("H,D,shift", [(2, 64, 2), (4, 10, 1), (8, 10, 2)])
+def test_bwd_misaligned_word_layout(H, D, shift):
+    w = with_grad(hub_graph(H, D, gtgen.F32, 7 * shift + D))
+    t = to_dev(w)
+    t["dO"] = to_torch(w["dO"])
+    shape = t["Q"].shape
+    names = ("Q", "K", "V", "dO", "out", "dQ", "dK", "dV")
+    bufs = {k: torch.empty(t["Q"].numel() + shift, dtype=torch.float32, device=dev()) for k in names}
+    views = {k: bufs[k][shift:].view(shape) for k in names}
+    for k in ("Q", "K", "V", "dO"):
+        views[k].copy_(t[k])
+    tip = torch.from_numpy(w["t_indptr"]).to(dev())
+    tix = torch.from_numpy(w["t_indices"]).to(dev())
+    with chunk_edges(37):
+        say("bwd misaligned by %d elements H=%d D=%d" % (shift, H, D))
+        _, lse = gt.gt_sparse_mha_fwd_lse(t["indptr"], t["indices"], views["Q"], views["K"], views["V"],
+                                          out=views["out"])
+        gt.gt_sparse_mha_bwd(t["indptr"], t["indices"], tip, tix, views["Q"], views["K"], views["V"],
+                             views["out"], views["dO"], lse, views["dQ"], views["dK"], views["dV"])
+        torch.cuda.synchronize()
+    rq, rk, rv, rlse, _ = oracle.bwd(*oracle_inputs(w), w["dO"])
+    check_lse(host(lse), rlse, "misaligned lse")
+    outs = OutTable(oracle.fwd(*oracle_inputs(w)))
+    allv = np.arange(w["N"])
+    BK, BV = bound_dkv(w, rlse, outs, allv)
+    check_bound(host(views["dQ"]), rq, bound_dq(w, rlse, outs, allv), F32_BTOL, "misaligned dQ")
+    check_bound(host(views["dK"]), rk, BK, F32_BTOL, "misaligned dK")
+    check_bound(host(views["dV"]), rv, BV, F32_BTOL, "misaligned dV")
 
 
 def test_bwd_deterministic():

@@ -147,6 +147,30 @@ def test_ndh_bwd_shapes(H, D, dtype):
         check_bwd(random_graph(H * 41 + D, 80, 900, H, D, dtype))
 
 
+@pytest.mark.parametrize("dtype", [gtgen.F32, gtgen.BF16])
+def test_ndh_bwd_word_shape_large_graph(dtype):
+    # 8 x 10 heads on 70 K edges, a hub destination split into chunks: the
+    # backward runs on [N][H][D] copies in the word layout, so its gradients
+    # are the [N][H][D] call's, bit for bit, given the same out and lse
+    N, E = 8000, 70000
+    src, dst = gtgen.random_coo(77, N, E)
+    dst = np.where(np.arange(E) < 3000, 11, dst)
+    w = with_grad(custom(N, src, dst, 8, 10, dtype, seed=77))
+    check_bwd(w)
+    t = to_dev(w)
+    d = dev()
+    tip, tix = (torch.from_numpy(x).to(d) for x in (w["t_indptr"], w["t_indices"]))
+    out, lse = gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], ndh(t["Q"]), ndh(t["K"]), ndh(t["V"]),
+                                           layout="ndh", want_lse=True)
+    dO = to_torch(w["dO"])
+    g = gt.gt_sparse_mha_bwd_layout(t["indptr"], t["indices"], tip, tix, None, ndh(t["Q"]), ndh(t["K"]),
+                                    ndh(t["V"]), out, ndh(dO), lse, layout="ndh")
+    ref = gt.gt_sparse_mha_bwd(t["indptr"], t["indices"], tip, tix, t["Q"], t["K"], t["V"], nhd(out), dO, lse)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(nhd(g[i]), ref[i]), "gradient %d" % i
+
+
 def test_ndh_bwd_zero_edges_and_hub_source():
     w = with_grad(custom(20, [], [], 8, 10))
     t = to_dev(w)

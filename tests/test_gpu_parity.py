@@ -234,6 +234,51 @@ def test_shapes(H, D, dtype):
         check_fused_full(random_graph(H * 1000 + D, 70, 900, H, D, dtype))
 
 
+# Heads of whole 8- or 4-byte words but not 16-byte vectors take the word
+# layout (every head of an edge in one lane group): one, three, five, seven,
+# fifteen and thirty-one words per head, lane groups of 1 to 64 lanes.
+WORD_SHAPES = [(8, 10, gtgen.F32), (8, 10, gtgen.BF16), (6, 10, gtgen.F32), (3, 5, gtgen.F32), (1, 1, gtgen.F32),
+               (12, 2, gtgen.F32), (7, 6, gtgen.F32), (4, 14, gtgen.F32), (2, 30, gtgen.F32), (1, 62, gtgen.F32),
+               (1, 2, gtgen.BF16), (8, 4, gtgen.BF16), (64, 2, gtgen.BF16), (5, 6, gtgen.BF16), (3, 12, gtgen.BF16),
+               (4, 30, gtgen.BF16), (2, 62, gtgen.BF16)]
+
+
+def hub_graph(H, D, dtype, seed):
+    # a destination hub of 500 in-edges and a source hub of 400 out-edges
+    N, E = 60, 1500
+    src, dst = gtgen.random_coo(seed, N, E)
+    dst = np.where(np.arange(E) < 500, 5, dst)
+    src = np.where((np.arange(E) >= 500) & (np.arange(E) < 900), 9, src)
+    return custom(N, src, dst, H, D, dtype, seed=seed)
+
+
+@pytest.mark.parametrize("H,D,dtype", WORD_SHAPES)
+@pytest.mark.parametrize("chunk", [512, 37])
+def test_word_layout_shapes(H, D, dtype, chunk):
+    with chunk_edges(chunk):
+        check_fused_full(hub_graph(H, D, dtype, H * 100 + D))
+        check_fused_full(random_graph(H * 1000 + D, 70, 900, H, D, dtype))
+
+
+@pytest.mark.parametrize("H,D,shift", [(2, 64, 2), (4, 10, 1), (8, 10, 1), (8, 10, 2)])
+def test_misaligned_features_take_word_or_scalar_layouts(H, D, shift):
+    # fp32 views `shift` elements into larger buffers: 8-byte aligned rows take
+    # 8-byte words (2 x 64 loses the vector layout), 4-byte aligned ones 4-byte
+    # words where a head's words fit 32 lane slots (4 x 10), else the scalar layout
+    w = hub_graph(H, D, gtgen.F32, 7 * shift + D)
+    t = to_dev(w)
+    n = t["Q"].numel()
+    bufs = {k: torch.empty(n + shift, dtype=torch.float32, device=dev()) for k in ("Q", "K", "V", "out")}
+    views = {k: bufs[k][shift:].view(t["Q"].shape) for k in bufs}
+    for k in ("Q", "K", "V"):
+        views[k].copy_(t[k])
+    with chunk_edges(37):
+        say("fused misaligned by %d elements H=%d D=%d" % (shift, H, D))
+        gt.gt_sparse_mha_fwd(t["indptr"], t["indices"], views["Q"], views["K"], views["V"], out=views["out"])
+        torch.cuda.synchronize()
+    assert_close(host(views["out"]), oracle.fwd(*oracle_inputs(w)), F32_TOL, "misaligned by %d" % shift)
+
+
 def test_misaligned_features_use_the_scalar_layout():
     w = random_graph(8, 40, 300, 8, 64)
     t = to_dev(w)
