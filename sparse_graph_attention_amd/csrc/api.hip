@@ -98,8 +98,9 @@ void size_plan_at(int64_t N, int64_t E, int64_t C, Plan& p) {
     p.max_heavy = std::min<int64_t>(N, E / (C + 1));
     p.max_chunks = p.max_heavy ? E / C + p.max_heavy : 0;
     // the row order by degree bin comes with the plan kernel, which runs when
-    // a row can be split (for smaller graphs rows go in index order)
-    p.n_order = p.max_heavy ? N : 0;
+    // a row can be split, on graphs of more than one plan block of rows (for
+    // other graphs rows go in index order)
+    p.n_order = p.max_heavy && N > kPlanBlockRows ? N : 0;
 }
 
 void size_plan(int64_t N, int64_t E, Plan& p) { size_plan_at(N, E, g_chunk.load(), p); }

@@ -76,6 +76,10 @@ __device__ __forceinline__ int order_bin(int64_t deg) {
     return deg > 256 ? 0 : deg > 64 ? 1 : deg > 16 ? 2 : deg > 4 ? 3 : deg > 0 ? 4 : 5;
 }
 
+// Rows one plan block takes.  Graphs of at most this many rows are planned by
+// a single block and keep their rows in index order.
+constexpr int64_t kPlanBlockRows = 8192;
+
 struct PlanCounters {
     uint32_t nheavy;                  // heavy rows listed
     uint32_t nchunks;                 // chunk items listed

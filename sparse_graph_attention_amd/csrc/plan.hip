@@ -21,11 +21,11 @@ __global__ void reset_kernel(PlanCounters* c) {
 // with a block-wide prefix scan and takes its ranges with one atomic per
 // counter.  The counters are hot words that every block updates at the
 // coherent memory side, so the fewer the atomics the better.  A graph of at
-// most kPlanThreads * kPlanRows rows has one block, which writes the counters
-// and the row order itself, so small graphs need neither a reset launch nor
-// the ordering launch.
+// most kPlanBlockRows rows goes to plan_small_kernel instead: one block, no
+// reset launch, no row order.
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanRows = 8;
+static_assert((int64_t)kPlanThreads * kPlanRows == kPlanBlockRows, "one plan block's rows");
 constexpr int kPlanWaves = kPlanThreads / kWave;
 constexpr int kPlanCounts = 2 + kOrderBins;  // heavy rows, chunks, rows of each bin
 
@@ -95,47 +95,19 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
     }
     uint32_t pre[kPlanCounts], tot[kPlanCounts];
     block_prefix(cnt, pre, tot, s_w);
-    const bool single = gridDim.x == 1;
     if (threadIdx.x < kPlanCounts) {
         const int i = threadIdx.x;
         uint32_t* ctr = i == 0 ? &p.counters->nheavy : i == 1 ? &p.counters->nchunks : &p.counters->bin_total[i - 2];
-        if (single) {  // the only block: it sets the counters (no reset ran)
-            *ctr = tot[i];
-            if (i >= 2) p.counters->bin_cursor[i - 2] = tot[i];
-            s_base[i] = 0u;
-        } else {
-            s_base[i] = tot[i] && i < 2 ? atomicAdd(ctr, tot[i]) : 0u;
-            if (i >= 2 && tot[i]) atomicAdd(ctr, tot[i]);
-        }
+        s_base[i] = tot[i] && i < 2 ? atomicAdd(ctr, tot[i]) : 0u;
+        if (i >= 2 && tot[i]) atomicAdd(ctr, tot[i]);
     }
     __syncthreads();
     uint32_t hs = s_base[0] + pre[0];
     uint32_t cb = s_base[1] + pre[1];
-    // one block: the row order too, each bin's part after the longer bins'
-    uint32_t ob[kOrderBins];
-    if (single && p.order) {
-        uint32_t start = 0;
-#pragma unroll
-        for (int b = 0; b < kOrderBins; ++b) {
-            ob[b] = start + pre[2 + b];
-            start += tot[2 + b];
-        }
-    }
 #pragma unroll
     for (int k = 0; k < kPlanRows; ++k) {
-        if (deg[k] < 0) continue;
+        if (deg[k] < 0 || !nch[k]) continue;
         const int32_t v = (int32_t)(v0 + k);
-        if (!nch[k]) {
-            if (single && p.order) {
-                const int b = order_bin(deg[k]);
-                uint32_t pos = 0;
-#pragma unroll
-                for (int c = 0; c < kOrderBins; ++c)
-                    if (c == b) pos = ob[c]++;
-                if ((int64_t)pos < p.n_order) p.order[pos] = v;
-            }
-            continue;
-        }
         // a valid CSR never trips this (the host sizes both tables for it); a
         // malformed one must not write past them
         if ((int64_t)hs >= p.max_heavy || (int64_t)cb + nch[k] > p.max_chunks) return;
@@ -143,6 +115,46 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(const int64_t* __res
         for (uint32_t i = 0; i < nch[k]; ++i) p.chunks[cb + i] = ChunkRef{v, (int32_t)i, (int32_t)hs, 0};
         ++hs;
         cb += nch[k];
+    }
+}
+
+// Graphs of at most one plan block of rows: one block lists the heavy rows
+// and their chunks, taking slots with LDS atomics, and leaves the rows in
+// index order.  Small graphs gained nothing from the degree order, and the
+// block-wide scan the order needs cost more than the attention it plans for
+// (a 4k-row molecule batch: 8.0 us of plan for 4.4 us of fused kernel).
+// Slot order depends on scheduling; no result does.
+__global__ __launch_bounds__(kPlanThreads) void plan_small_kernel(const int64_t* __restrict__ indptr, int64_t N,
+                                                                  Plan p) {
+    __shared__ uint32_t s_heavy, s_chunks, s_bad;
+    if (threadIdx.x == 0) s_heavy = s_chunks = s_bad = 0u;
+    int64_t deg[kPlanRows];  // rows k * kPlanThreads + thread: coalesced loads, all issued up front
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k) {
+        const int64_t v = (int64_t)k * kPlanThreads + threadIdx.x;
+        deg[k] = v < N ? indptr[v + 1] - indptr[v] : 0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < kPlanRows; ++k) {
+        if (deg[k] <= p.chunk) continue;
+        const int32_t v = (int32_t)(k * kPlanThreads + threadIdx.x);
+        const uint32_t nch = (uint32_t)((deg[k] + p.chunk - 1) / p.chunk);
+        const uint32_t hs = atomicAdd(&s_heavy, 1u);
+        const uint32_t cb = atomicAdd(&s_chunks, nch);
+        // a valid CSR never trips this (the host sizes both tables for it); a
+        // malformed one must not write past them, and then lists nothing
+        if ((int64_t)hs >= p.max_heavy || (int64_t)cb + nch > p.max_chunks) {
+            s_bad = 1u;
+            continue;
+        }
+        p.heavy[hs] = HeavyRow{v, (int32_t)nch, (int64_t)cb};
+        for (uint32_t i = 0; i < nch; ++i) p.chunks[cb + i] = ChunkRef{v, (int32_t)i, (int32_t)hs, 0};
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        p.counters->nheavy = s_bad ? 0u : s_heavy;
+        p.counters->nchunks = s_bad ? 0u : s_chunks;
     }
 }
 
@@ -190,14 +202,17 @@ hipError_t launch_plan(const Args& a, hipStream_t s) {
     if (a.plan.max_heavy == 0) return hipSuccess;  // no row can be split: nothing to list, rows in index order
     const int64_t per_block = (int64_t)kPlanThreads * kPlanRows;
     const unsigned blocks = (unsigned)((a.N + per_block - 1) / per_block);
-    if (blocks > 1) {  // several blocks add to the counters: clear them first
-        reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
-        hipError_t err = hipGetLastError();
-        if (err != hipSuccess) return err;
+    if (blocks == 1) {  // one block sets the counters itself: no reset, no order
+        plan_small_kernel<<<1, kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
+        return hipGetLastError();
     }
-    plan_kernel<<<blocks, kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
+    // several blocks add to the counters: clear them first
+    reset_kernel<<<1, 64, 0, s>>>(a.plan.counters);
     hipError_t err = hipGetLastError();
-    if (err != hipSuccess || blocks == 1 || !a.plan.order) return err;
+    if (err != hipSuccess) return err;
+    plan_kernel<<<blocks, kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
+    err = hipGetLastError();
+    if (err != hipSuccess || !a.plan.order) return err;
     order_kernel<<<blocks, kPlanThreads, 0, s>>>(a.indptr, a.N, a.plan);
     return hipGetLastError();
 }
