@@ -1002,6 +1002,7 @@ int check_graph(int64_t n_dst, int64_t n_src, int64_t E) {
 // sort_scratch_bytes(E, perm != nullptr).
 hipError_t group_by_key(const uint32_t* keys, const uint32_t* vals_src, int64_t E, int64_t nrows, int64_t* offsets,
                         uint32_t* out, uint32_t* perm, void* scratch, hipStream_t s) {
+    if (group_small_fits(E, 0)) return launch_group_small(keys, vals_src, nullptr, 0, E, nrows, offsets, out, perm, s);
     const uint32_t *ks = nullptr, *vs = nullptr, *v2s = nullptr;
     hipError_t e = perm ? radix_sort(keys, nullptr, vals_src, E, key_bits_for(nrows), scratch, perm, out, s, &ks, &vs,
                                      &v2s)
@@ -1013,6 +1014,11 @@ hipError_t group_by_key(const uint32_t* keys, const uint32_t* vals_src, int64_t 
 
 // Source-sorted copy of a destination-sorted graph in the plan.
 int build_transpose(gt_plan_s* P, hipStream_t stream) {
+    if (group_small_fits(P->E, P->n_dst)) {  // one launch: rows of positions, sort and offsets together
+        hipError_t e = launch_group_small((const uint32_t*)P->indices, nullptr, P->indptr, P->n_dst, P->E, P->n_src,
+                                          P->t_indptr, (uint32_t*)P->t_indices, (uint32_t*)P->t_perm, stream);
+        return e == hipSuccess ? GT_OK : hip_fail(e, "transpose launch");
+    }
     void* base = nullptr;
     const size_t rows_bytes = align256(sizeof(uint32_t) * (size_t)P->E);
     int rc = get_scratch(stream, rows_bytes + sort_scratch_bytes(P->E, true), &base);

@@ -24,7 +24,7 @@
 //     write consecutive keys, so each digit's run leaves as one contiguous
 //     stretch instead of one scattered 4-byte store per key.
 // Keys of equal digit keep their input order, so every pass is stable.  At
-// most 16,384 keys take one launch per pass (radix_pass_small_kernel).
+// most 16,384 keys are grouped in one launch instead (group_small_kernel).
 #include "kernels.hpp"
 
 namespace gt {
@@ -155,94 +155,8 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
     }
 }
 
-// A whole pass in one block of kSmallWaves waves for at most kSmallSortKeys
-// keys: a small graph (a batch of molecules) otherwise pays three dependent
-// launches per pass, each a few memory round trips long.  Wave w takes keys
-// [w * kWaveSpan, (w + 1) * kWaveSpan), the same span as in the tiled kernels.
-//  1. every wave ranks its keys within their digit and counts the digits
-//     into cnt[wave][digit];
-//  2. thread t = digit t (the first four waves) turns the counts into first
-//     slots: the counts of the waves before, plus the keys of lower digits;
-//  3. every key takes its output slot: its digit's first slot for its wave
-//     plus its rank among the wave's keys of that digit, which step 1 found
-//     with the tiled kernels' ballot multisplit and kept in registers.  Keys
-//     and values are placed in LDS and leave with coalesced stores (a second
-//     value array, for which LDS has no room, is stored to its slot directly).
-// Equal digits keep their input order: slots grow with (wave, item, lane).
 constexpr int kSmallWaves = 16;
 constexpr int64_t kSmallSortKeys = (int64_t)kSmallWaves * kWaveSpan;
-
-template <bool IOTA, bool TWO>
-__global__ __launch_bounds__(kSmallWaves * kWave) void radix_pass_small_kernel(
-    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, const uint32_t* __restrict__ vals2_in,
-    uint32_t* __restrict__ keys_out, uint32_t* __restrict__ vals_out, uint32_t* __restrict__ vals2_out, int n,
-    int shift, int bits) {
-    __shared__ uint32_t cnt[kSmallWaves][256];
-    __shared__ uint32_t wsum[4];
-    __shared__ uint32_t sk[kSmallSortKeys], sv[kSmallSortKeys];  // the pass's output, in slot order
-    const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
-    const uint32_t mask = (1u << bits) - 1u;
-    for (int k = t; k < kSmallWaves * 256; k += kSmallWaves * kWave) (&cnt[0][0])[k] = 0;
-    const int base = w * kWaveSpan;
-    uint32_t key[kSortItems], val[kSortItems], val2[TWO ? kSortItems : 1];
-#pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
-        const int e = base + i * kWave + lane;
-        const bool valid = e < n;
-        key[i] = valid ? keys_in[e] : 0u;
-        val[i] = valid ? (IOTA ? (uint32_t)e : vals_in[e]) : 0u;
-        if constexpr (TWO) val2[i] = valid ? vals2_in[e] : 0u;
-    }
-    __syncthreads();
-    uint32_t rank[kSortItems];
-#pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
-        const bool valid = base + i * kWave + lane < n;
-        const uint32_t d = (key[i] >> shift) & mask;
-        const uint64_t peers = digit_peers(d, bits, valid);
-        const int leader = valid ? (int)__builtin_ctzll(peers) : lane;
-        uint32_t old = 0;
-        if (valid && leader == lane) old = atomicAdd(&cnt[w][d], (uint32_t)__builtin_popcountll(peers));
-        old = __shfl(old, leader, kWave);
-        rank[i] = old + (uint32_t)__builtin_popcountll(peers & lanes_below(lane));
-    }
-    __syncthreads();
-    uint32_t tot = 0, inc = 0;
-    if (t < 256) {
-        for (int j = 0; j < kSmallWaves; ++j) {
-            const uint32_t c = cnt[j][t];
-            cnt[j][t] = tot;
-            tot += c;
-        }
-        inc = tot;
-        for (int off = 1; off < kWave; off <<= 1) {
-            const uint32_t y = __shfl_up(inc, off, kWave);
-            if (lane >= off) inc += y;
-        }
-        if (lane == kWave - 1) wsum[w] = inc;
-    }
-    __syncthreads();
-    if (t < 256) {
-        uint32_t start = inc - tot;
-        for (int j = 0; j < w; ++j) start += wsum[j];
-        for (int j = 0; j < kSmallWaves; ++j) cnt[j][t] += start;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kSortItems; ++i) {
-        if (base + i * kWave + lane < n) {
-            const uint32_t slot = cnt[w][(key[i] >> shift) & mask] + rank[i];
-            sk[slot] = key[i];
-            sv[slot] = val[i];
-            if constexpr (TWO) vals2_out[slot] = val2[i];
-        }
-    }
-    __syncthreads();
-    for (int j = t; j < n; j += kSmallWaves * kWave) {
-        keys_out[j] = sk[j];
-        vals_out[j] = sv[j];
-    }
-}
 
 // ---------------------------------------------------------------- exclusive scan (uint32)
 
@@ -367,6 +281,128 @@ __global__ __launch_bounds__(256) void fill_rows_kernel(const int64_t* __restric
     }
 }
 
+// Grouping by key in one launch for at most kSmallSortKeys items (a batch of
+// molecules: 8.5k edges), where the tiled sort takes a launch per pass and
+// the row offsets one more, each a few memory round trips long.  One block
+// of kSmallWaves waves keeps every item in registers, wave w holding items
+// [w * kWaveSpan, (w + 1) * kWaveSpan), and runs the LSD passes one after
+// another:
+//  1. every wave ranks its keys within their digit (the tiled kernels' ballot
+//     multisplit) and counts the digits into cnt[wave][digit];
+//  2. thread t = digit t (the first four waves) turns the counts into first
+//     slots: the counts of the waves before, plus the keys of lower digits;
+//  3. each item goes to LDS at its digit's first slot for its wave plus its
+//     rank, and every thread reloads the items of its positions for the next
+//     pass.  Equal digits keep their order: slots grow with (wave, item, lane).
+// The items carry their input position; after the last pass the block writes
+// each item's value, its position (perm) and the row offsets, which it reads
+// off the sorted keys (offsets[v] = first position whose key is >= v).
+// ROWS: the value of item e is the row holding position e of the CSR
+// row_indptr (row_n rows, fewer than 2^18), packed beside the position
+// (e < 2^14) through the passes; the rows come from a fill of LDS from
+// row_indptr, each thread writing whole rows (a wave per 63 rows, as in
+// fill_rows_kernel, was a chain of shuffles per row: 55 us for 4k rows on one
+// block's 16 waves).  Otherwise the value is vals[e], gathered at the end.
+template <bool ROWS, bool PERM>
+__global__ __launch_bounds__(kSmallWaves * kWave) void group_small_kernel(
+    const uint32_t* __restrict__ keys_in, const uint32_t* __restrict__ vals_in, const int64_t* __restrict__ row_indptr,
+    int64_t row_n, int n, int key_bits, int64_t nrows, int64_t* __restrict__ offsets, uint32_t* __restrict__ out,
+    uint32_t* __restrict__ perm) {
+    __shared__ uint32_t cnt[kSmallWaves][256];
+    __shared__ uint32_t wsum[4];
+    __shared__ uint32_t sk[kSmallSortKeys], sv[kSmallSortKeys];  // a pass's output, in slot order
+    const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
+    const int base = w * kWaveSpan;
+    if constexpr (ROWS) {
+        for (int64_t r = t; r < row_n; r += kSmallWaves * kWave) {
+            const int64_t b = row_indptr[r], e = row_indptr[r + 1];
+            for (int64_t q = b; q < e && q < n; ++q) sv[q] = (uint32_t)r;
+        }
+        __syncthreads();
+    }
+    uint32_t key[kSortItems], val[kSortItems], rank[kSortItems];
+#pragma unroll
+    for (int i = 0; i < kSortItems; ++i) {
+        const int e = base + i * kWave + lane;
+        const bool valid = e < n;
+        key[i] = valid ? keys_in[e] : 0u;
+        val[i] = valid ? (ROWS ? (uint32_t)e | (sv[e] << 14) : (uint32_t)e) : 0u;
+    }
+    const int passes = key_bits > 0 ? (key_bits + 7) / 8 : 1;
+    for (int p = 0; p < passes; ++p) {
+        const int shift = 8 * p;
+        const int bits = key_bits - shift < 8 ? (key_bits - shift > 0 ? key_bits - shift : 1) : 8;
+        const uint32_t mask = (1u << bits) - 1u;
+        __syncthreads();  // the last pass's reloads (or the row fill's reads) are done
+        for (int k = t; k < kSmallWaves * 256; k += kSmallWaves * kWave) (&cnt[0][0])[k] = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSortItems; ++i) {
+            const bool valid = base + i * kWave + lane < n;
+            const uint32_t d = (key[i] >> shift) & mask;
+            const uint64_t peers = digit_peers(d, bits, valid);
+            const int leader = valid ? (int)__builtin_ctzll(peers) : lane;
+            uint32_t old = 0;
+            if (valid && leader == lane) old = atomicAdd(&cnt[w][d], (uint32_t)__builtin_popcountll(peers));
+            old = __shfl(old, leader, kWave);
+            rank[i] = old + (uint32_t)__builtin_popcountll(peers & lanes_below(lane));
+        }
+        __syncthreads();
+        uint32_t tot = 0, inc = 0;
+        if (t < 256) {
+            for (int j = 0; j < kSmallWaves; ++j) {
+                const uint32_t c = cnt[j][t];
+                cnt[j][t] = tot;
+                tot += c;
+            }
+            inc = tot;
+            for (int off = 1; off < kWave; off <<= 1) {
+                const uint32_t y = __shfl_up(inc, off, kWave);
+                if (lane >= off) inc += y;
+            }
+            if (lane == kWave - 1) wsum[w] = inc;
+        }
+        __syncthreads();
+        if (t < 256) {
+            uint32_t start = inc - tot;
+            for (int j = 0; j < w; ++j) start += wsum[j];
+            for (int j = 0; j < kSmallWaves; ++j) cnt[j][t] += start;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kSortItems; ++i) {
+            if (base + i * kWave + lane < n) {
+                const uint32_t slot = cnt[w][(key[i] >> shift) & mask] + rank[i];
+                sk[slot] = key[i];
+                sv[slot] = val[i];
+            }
+        }
+        __syncthreads();
+        if (p + 1 < passes) {
+#pragma unroll
+            for (int i = 0; i < kSortItems; ++i) {
+                const int e = base + i * kWave + lane;
+                if (e < n) {
+                    key[i] = sk[e];
+                    val[i] = sv[e];
+                }
+            }
+        }
+    }
+    for (int j = t; j < n; j += kSmallWaves * kWave) {
+        const uint32_t v = sv[j];
+        const uint32_t pos = ROWS ? v & ((1u << 14) - 1u) : v;
+        out[j] = ROWS ? v >> 14 : vals_in[pos];
+        if constexpr (PERM) perm[j] = pos;
+    }
+    // keys >= nrows (a malformed input) are clamped so that nothing lands past offsets[nrows]
+    for (int j = t; j <= n; j += kSmallWaves * kWave) {
+        const int64_t prev = j > 0 ? min((int64_t)sk[j - 1], nrows) : -1;
+        const int64_t cur = j < n ? min((int64_t)sk[j], nrows) : nrows;
+        for (int64_t v = prev + 1; v <= cur; ++v) offsets[v] = j;
+    }
+}
+
 unsigned grid256(int64_t n) { return (unsigned)cdiv(n, 256); }
 
 }  // namespace
@@ -406,22 +442,7 @@ hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const ui
         uint32_t* kout = kb[p & 1];
         uint32_t* vout = (last && vals_final) ? vals_final : vb[p & 1];
         uint32_t* v2out = (last && vals2_final) ? vals2_final : v2b[p & 1];
-        if (n > 0 && n <= kSmallSortKeys) {
-            if (!vin && two)
-                radix_pass_small_kernel<true, true><<<1, kSmallWaves * kWave, 0, s>>>(kin, nullptr, v2in, kout, vout, v2out, (int)n,
-                                                                         shift, bits);
-            else if (!vin)
-                radix_pass_small_kernel<true, false><<<1, kSmallWaves * kWave, 0, s>>>(kin, nullptr, nullptr, kout, vout, nullptr,
-                                                                          (int)n, shift, bits);
-            else if (two)
-                radix_pass_small_kernel<false, true><<<1, kSmallWaves * kWave, 0, s>>>(kin, vin, v2in, kout, vout, v2out, (int)n,
-                                                                          shift, bits);
-            else
-                radix_pass_small_kernel<false, false><<<1, kSmallWaves * kWave, 0, s>>>(kin, vin, nullptr, kout, vout, nullptr,
-                                                                           (int)n, shift, bits);
-            const hipError_t err = hipGetLastError();
-            if (err != hipSuccess) return err;
-        } else if (n > 0) {
+        if (n > 0) {
             radix_count_kernel<<<grid, block, 0, s>>>(kin, n, shift, bits, hist, tiles);
             hipError_t err = hipGetLastError();
             if (err != hipSuccess) return err;
@@ -454,6 +475,26 @@ hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const ui
 
 hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, int64_t* offsets, hipStream_t s) {
     lower_bounds_kernel<<<grid256(nrows + 1), 256, 0, s>>>(keys, n, nrows, offsets);
+    return hipGetLastError();
+}
+
+bool group_small_fits(int64_t n, int64_t row_n) { return n > 0 && n <= kSmallSortKeys && row_n < ((int64_t)1 << 18); }
+
+hipError_t launch_group_small(const uint32_t* keys, const uint32_t* vals, const int64_t* row_indptr, int64_t row_n,
+                              int64_t n, int64_t nrows, int64_t* offsets, uint32_t* out, uint32_t* perm,
+                              hipStream_t s) {
+    if (!group_small_fits(n, row_indptr ? row_n : 0)) return hipErrorInvalidValue;
+    const int bits = key_bits_for(nrows);
+    const dim3 grid(1), block(kSmallWaves * kWave);
+    if (row_indptr)
+        group_small_kernel<true, true><<<grid, block, 0, s>>>(keys, nullptr, row_indptr, row_n, (int)n, bits, nrows,
+                                                              offsets, out, perm);
+    else if (perm)
+        group_small_kernel<false, true><<<grid, block, 0, s>>>(keys, vals, nullptr, 0, (int)n, bits, nrows, offsets,
+                                                               out, perm);
+    else
+        group_small_kernel<false, false><<<grid, block, 0, s>>>(keys, vals, nullptr, 0, (int)n, bits, nrows, offsets,
+                                                                out, nullptr);
     return hipGetLastError();
 }
 

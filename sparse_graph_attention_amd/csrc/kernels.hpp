@@ -219,6 +219,15 @@ hipError_t radix_sort(const uint32_t* keys_in, const uint32_t* vals_in, const ui
 hipError_t launch_lower_bounds(const uint32_t* keys, int64_t n, int64_t nrows, int64_t* offsets, hipStream_t s);
 // rows[p] = the row of CSR position p.
 hipError_t launch_row_of_position(const int64_t* indptr, int64_t nrows, int64_t n, uint32_t* rows, hipStream_t s);
+// Grouping by key in one launch, for n <= 16,384 items (group_small_fits):
+// offsets[nrows + 1] and out[j] = the value of the j-th item in key order
+// (stable); perm[j] = its input position when perm is non-null.  The value of
+// item e is vals[e], or with row_indptr non-null the row holding position e
+// of that CSR of row_n (< 2^18) rows, perm then required.
+bool group_small_fits(int64_t n, int64_t row_n);
+hipError_t launch_group_small(const uint32_t* keys, const uint32_t* vals, const int64_t* row_indptr, int64_t row_n,
+                              int64_t n, int64_t nrows, int64_t* offsets, uint32_t* out, uint32_t* perm,
+                              hipStream_t s);
 // Measurement aid (calib.hip): the K and V rows of every edge, read as the
 // fused kernel reads them, XOR-folded into *sink.  row_bytes 512, 1024 or 2048.
 hipError_t launch_calib_gather(const int32_t* indices, int64_t E, const void* K, const void* V, int64_t n_rows,
