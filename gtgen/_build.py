@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "gtgen.c")
 # GT_SANITIZE=1: an AddressSanitizer + UndefinedBehaviorSanitizer build (a
 # library of its own; the process must preload gcc's libasan).
-SANITIZE = os.environ.get("GT_SANITIZE", "") not in ("", "0")
+SANITIZE = os.environ.get("GT_SANITIZE", "") == "1"
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 LIB = os.path.join(HERE, "libgtgen_san.so" if SANITIZE else "libgtgen.so")
 

@@ -6,8 +6,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(HERE, "oracle.c")
 # GT_SANITIZE=1: an AddressSanitizer + UndefinedBehaviorSanitizer build of the
 # oracle (a library of its own, loaded instead of the plain one).  The process
-# must preload gcc's libasan; see the design doc for the command.
-SANITIZE = os.environ.get("GT_SANITIZE", "") not in ("", "0")
+# must preload gcc's libasan, e.g.
+#   GT_SANITIZE=1 LD_PRELOAD=$(gcc -print-file-name=libasan.so) ASAN_OPTIONS=detect_leaks=0 \
+#   python -m pytest tests -m "not gpu"
+SANITIZE = os.environ.get("GT_SANITIZE", "") == "1"
 SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 LIB = os.path.join(HERE, "liboracle_san.so" if SANITIZE else "liboracle.so")
 

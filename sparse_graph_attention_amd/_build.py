@@ -7,11 +7,15 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
-# GT_SANITIZE=1: the host code built with AddressSanitizer and
+# GT_SANITIZE=lib: the host code built with AddressSanitizer and
 # UndefinedBehaviorSanitizer (device code unchanged), as a library of its own
-# for CPU tests of the argument checks; the process must preload clang's ASan
-# runtime (see the design doc for the command).  Never used on a GPU.
-SANITIZE = os.environ.get("GT_SANITIZE", "") not in ("", "0")
+# for CPU tests of the argument checks.  The process must preload clang's ASan
+# runtime, e.g.
+#   GT_SANITIZE=lib LD_PRELOAD=/opt/rocm/llvm/lib/clang/22/lib/linux/libclang_rt.asan-x86_64.so \
+#   ASAN_OPTIONS=detect_leaks=0 python -m pytest tests/test_abi_cpu.py tests/test_abi_c.py
+# Never used on a GPU.  (GT_SANITIZE=1 instruments the oracle and the
+# generators instead, with gcc's runtime, which cannot load this library.)
+SANITIZE = os.environ.get("GT_SANITIZE", "") == "lib"
 LIB = os.path.join(HERE, "libgtattn_san.so" if SANITIZE else "libgtattn.so")
 OBJDIR = os.path.join(ROOT, "_build_san" if SANITIZE else "_build")
 HOST_SAN_FLAGS = ("-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined "
