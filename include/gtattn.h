@@ -61,6 +61,16 @@
  * threads at once: one call growing the buffer would free it under another
  * call that is still enqueuing work on it.
  *
+ * Graph capture.  The compute calls without a plan (gt_sparse_mha_fwd*,
+ * gt_sparse_mha_bwd*, gt_sddmm, gt_edge_softmax, gt_spmm) enqueue kernels
+ * only: no memset, no host synchronisation, no event.  They may be captured
+ * into a HIP graph once the capturing stream's scratch is large enough, which
+ * one call of the same size on that stream before the capture ensures (else
+ * the capture would record the scratch's allocation).  The graph then replays
+ * with the results of the eager calls, bit for bit.  gt_sparse_mha_fwd_noalloc
+ * needs no warm-up.  Calls on a plan record an event for the plan's release
+ * and are not for capture.
+ *
  * Errors.  Arguments are checked before anything is enqueued; on a non-OK
  * status nothing was launched.  No exception or abort crosses the ABI.
  *  GT_EINVAL       a NULL array with N > 0 (or E > 0 for indices/scores/
