@@ -269,11 +269,14 @@ int gt_sparse_mha_bwd_ex(const int64_t* indptr, const int32_t* indices, const in
  * dweight), kernels of their own serve shapes where H is a multiple of the
  * 16-byte vector (4 fp32 or 8 bf16 elements) with a power-of-two quotient and
  * a row fits 256 vectors (4 KB), when they are the faster route: always when
- * a head of D elements is not a power-of-two number of 16-byte vectors, and
- * for the forward also when a row's gathers are large against the cross-lane
- * sums this layout needs.  Everything else goes through [N][H][D] copies in
- * the per-stream scratch (transposed on the device), with results
- * bit-identical to the [N][H][D] calls.
+ * [N][H][D] rows would take one wave per head (heads neither whole 16-byte
+ * vectors nor whole 8- or 4-byte words of at most 32 per head, 64 per row);
+ * for heads of whole words (fp32 D = 10) the forward always and the backward
+ * below 65,536 edges, where the copies' launches cost more than the
+ * cross-lane sums this layout needs; for heads of 16-byte vectors the forward
+ * when a row's gathers are large against those sums.  Everything else goes
+ * through [N][H][D] copies in the per-stream scratch (transposed on the
+ * device), with results bit-identical to the [N][H][D] calls.
  *
  * (The tutorial also normalises along A[src, dst]'s rows, i.e. over each
  * source's out-edges with the source's query: that is these calls on the
