@@ -157,6 +157,8 @@ __global__ __launch_bounds__(kSortWaves * kWave) void radix_scatter_kernel(
 
 constexpr int kSmallWaves = 16;
 constexpr int64_t kSmallSortKeys = (int64_t)kSmallWaves * kWaveSpan;
+constexpr int kGapList = 2048;  // long runs of rows without keys, filled by the whole block
+constexpr int kLongGap = 64;
 
 // ---------------------------------------------------------------- exclusive scan (uint32)
 
@@ -311,6 +313,7 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void group_small_kernel(
     __shared__ uint32_t cnt[kSmallWaves][256];
     __shared__ uint32_t wsum[4];
     __shared__ uint32_t sk[kSmallSortKeys], sv[kSmallSortKeys];  // a pass's output, in slot order
+    __shared__ uint32_t s_gap[kGapList], s_ngap;                   // positions before long runs of empty rows
     const int t = threadIdx.x, lane = t & (kWave - 1), w = t >> 6;
     const int base = w * kWaveSpan;
     if constexpr (ROWS) {
@@ -395,11 +398,32 @@ __global__ __launch_bounds__(kSmallWaves * kWave) void group_small_kernel(
         out[j] = ROWS ? v >> 14 : vals_in[pos];
         if constexpr (PERM) perm[j] = pos;
     }
-    // keys >= nrows (a malformed input) are clamped so that nothing lands past offsets[nrows]
+    // Position j writes the offsets of the rows after the previous key up to its
+    // own; keys >= nrows (a malformed input) are clamped so that nothing lands
+    // past offsets[nrows].  A long run of rows without keys (a shard whose
+    // sources start far above row 0) is listed and then written by the whole
+    // block, not by one thread; a full list falls back to the thread.
+    if (t == 0) s_ngap = 0u;
+    __syncthreads();
     for (int j = t; j <= n; j += kSmallWaves * kWave) {
         const int64_t prev = j > 0 ? min((int64_t)sk[j - 1], nrows) : -1;
         const int64_t cur = j < n ? min((int64_t)sk[j], nrows) : nrows;
+        if (cur - prev > kLongGap) {
+            const uint32_t k = atomicAdd(&s_ngap, 1u);
+            if (k < kGapList) {
+                s_gap[k] = (uint32_t)j;
+                continue;
+            }
+        }
         for (int64_t v = prev + 1; v <= cur; ++v) offsets[v] = j;
+    }
+    __syncthreads();
+    const uint32_t ng = min(s_ngap, (uint32_t)kGapList);
+    for (uint32_t g = 0; g < ng; ++g) {
+        const int j = (int)s_gap[g];
+        const int64_t prev = j > 0 ? min((int64_t)sk[j - 1], nrows) : -1;
+        const int64_t cur = j < n ? min((int64_t)sk[j], nrows) : nrows;
+        for (int64_t v = prev + 1 + t; v <= cur; v += kSmallWaves * kWave) offsets[v] = j;
     }
 }
 

@@ -159,6 +159,29 @@ def test_plan_arrays_around_the_one_launch_sort(n, E):
     plan.destroy()
 
 
+@pytest.mark.parametrize("lo,hi,n,n_src", [(60000, 61000, 70000, 70000), (0, 100, 70000, 1000),
+                                           (3000, 3500, 4000, 250000), (9000, 9001, 200000, 9500)])
+def test_plan_with_long_runs_of_empty_rows(lo, hi, n, n_src):
+    # destinations and sources confined to narrow ranges, like a row shard of a
+    # batch of small graphs: long runs of rows without keys before, between and
+    # after the keys, in the CSR and in the transpose (one-launch grouping)
+    rng = np.random.default_rng(lo + n)
+    E = 5000
+    dst = rng.integers(lo, hi, E).astype(np.int32)
+    src = rng.integers(max(0, lo - 100), min(n_src, hi + 100), E).astype(np.int32)
+    say("plan with empty runs dst [%d, %d) n=%d n_src=%d" % (lo, hi, n, n_src))
+    d = dev()
+    plan = gt.gt_plan_create_coo(torch.from_numpy(src).to(d), torch.from_numpy(dst).to(d), n, n_src=n_src)
+    p = plan_arrays(plan)
+    rip, rix, _ = oracle.coo_to_csr(n, src, dst, n_src=n_src)
+    assert np.array_equal(p["indptr"], rip) and np.array_equal(p["indices"], rix)
+    tip, tix, tpm = oracle.source_sorted(rip, rix, want_perm=True, n_src=n_src)
+    assert np.array_equal(p["t_indptr"], tip) and np.array_equal(p["t_indices"], tix)
+    assert np.array_equal(p["t_perm"], tpm)
+    plan.destroy()
+    check_coo(src, dst, n, n_src, "empty runs")
+
+
 @pytest.mark.parametrize("name,chunk", [("tiny_random", 3), ("molecules", 2), ("regular16", 5), ("powerlaw", 512),
                                         ("lognormal", 512)])
 def test_plan_attention_is_bitwise_the_plain_call(name, chunk):
