@@ -1205,10 +1205,11 @@ static bool launch_dq_fixed(const Args& a, dim3 grid, dim3 block, hipStream_t s,
         return true;
     return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
+        constexpr int U0 = XL ? (U < GT_PARTIAL_XL_U ? U : GT_PARTIAL_XL_U) : U;  // as in the forward
         if (a.R == a.NC * a.G)  // padded heads filling the lane groups: heads per edge known
             bwd_dq_vec_kernel<DT, nc, U, g, lph, 2, XL><<<grid, block, 0, s>>>(a);
         else
-            bwd_dq_vec_kernel<DT, nc, U, g, lph, 0, XL><<<grid, block, 0, s>>>(a);
+            bwd_dq_vec_kernel<DT, nc, U0, g, lph, 0, XL><<<grid, block, 0, s>>>(a);
     });
 }
 

@@ -38,6 +38,9 @@
 #ifndef GT_SPMM_BF16_U
 #define GT_SPMM_BF16_U 4
 #endif
+#ifndef GT_PARTIAL_XL_U
+#define GT_PARTIAL_XL_U 2  // rows that end before their last lane group, with logit options: edges in flight
+#endif
 #ifndef GT_UNFUSED_NTL
 #define GT_UNFUSED_NTL 0  // fp32 gathers of arrays over 1 GB with the non-temporal hint (measured slower)
 #endif

@@ -103,8 +103,13 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
     const char* Kb = (const char*)a.K;
     const char* Vb = (const char*)a.V;
     DropBatch db;
+    // batches one keep-bit evaluation covers: fixed for the hot instances, else
+    // as many as one round of 64 lanes holds (rows that end before their last
+    // lane group: 8-9% of the forward with dropout, where one round per batch
+    // left most lanes idle; the backward passes measured no gain and keep one)
+    const int dmb = kBatched ? kDropMB : drop_batches_per_eval(epw, U, a.H);
     int dph = 0;  // position of the batch among those its keep bits were drawn for
-    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U, dph = dph + 1 == kDropMB ? 0 : dph + 1) {
+    for (int64_t eb = e0; eb < e1; eb += (int64_t)epw * U, dph = dph + 1 == dmb ? 0 : dph + 1) {
         int32_t u[U];
         bool ok[U];
 #pragma unroll
@@ -150,9 +155,9 @@ __global__ __launch_bounds__(kBlock) void fused_vec_kernel(const Args a) {
         bool bdrop = false;
         if constexpr (XL) {
             bdrop = XL == 2 && (kBatched || drop_batched(a.H, -1, epw * U));
-            // one evaluation covers kDropMB consecutive batches (consecutive edges)
+            // one evaluation covers dmb consecutive batches (consecutive edges)
             if (bdrop && dph == 0)
-                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, kDropMB * epw * U, lane,
+                drop_batch_init(db, a.drop_seed, a.drop_thresh, a.H, -1, dmb * epw * U, lane,
                                 [&](int k) { return eb + k; });
         }
 
@@ -895,10 +900,14 @@ static bool launch_fixed_lph(const Args& a, dim3 grid, dim3 block, hipStream_t s
     // rows with idle lane slots
     return for_fixed_partial_layout(a, [&](auto nc, auto u, auto g, auto lph) {
         constexpr int U = XL ? (decltype(u)::value < 4 ? decltype(u)::value : 4) : decltype(u)::value;
+        // rows that end early with logit options: the run-time head masks and
+        // per-lane dropout state took 141-175 VGPRs at 4 edges in flight (2-3
+        // waves per SIMD); 2 in flight keep more waves resident
+        constexpr int U0 = XL ? (U < GT_PARTIAL_XL_U ? U : GT_PARTIAL_XL_U) : U;
         if (a.R == a.NC * a.G)  // padded heads filling the lane groups: heads per edge known
             fused_vec_kernel<DT, nc, U, g, lph, 2, false, XL><<<grid, block, 0, s>>>(a);
         else
-            fused_vec_kernel<DT, nc, U, g, lph, 0, false, XL><<<grid, block, 0, s>>>(a);
+            fused_vec_kernel<DT, nc, U0, g, lph, 0, false, XL><<<grid, block, 0, s>>>(a);
     });
 }
 
