@@ -69,11 +69,12 @@ def kernel_source_sha(sources=KERNEL_SOURCES):
     return h.hexdigest()
 
 
-def load_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
+def load_traffic(threshold, path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
     """HBM bytes per call of the timed kernels from a committed counter summary
     (rocprofv3 FETCH_SIZE and WRITE_SIZE per dispatch, summed over the call's
     kernels and scaled by what the counters read for a plain copy), or None when
-    the summary is missing or the kernel sources changed since it was taken."""
+    the summary is missing, the kernel sources changed since it was taken, or
+    it was taken at another split threshold than `threshold` (edges)."""
     if not os.path.exists(path):
         return None, "no counter summary"
     kv = {}
@@ -84,6 +85,8 @@ def load_traffic(path=TRAFFIC_FILE, sources=KERNEL_SOURCES):
             kv[k.strip()] = v.strip()
     if kv.get("kernel_source_sha256") != kernel_source_sha(sources):
         return None, "kernel changed since the counters were taken"
+    if kv.get("split_threshold_edges") != str(threshold):
+        return None, "counters taken at another split threshold"
     fetch = float(kv["fetch_kib_per_call"]) * 1024 * float(kv["copy_fetch_scale"])
     write = float(kv["write_kib_per_call"]) * 1024 * float(kv["copy_write_scale"])
     return fetch + write, "stored rocprofv3 FETCH_SIZE + WRITE_SIZE (%s), scaled by a plain copy" % (
@@ -194,7 +197,8 @@ def time_backward(gt, t, w, steps, warmup):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     nbytes = backward_bytes(w)
-    traffic, note = (load_traffic(BWD_TRAFFIC_FILE, BWD_SOURCES) if w.get("name") == "powerlaw"
+    traffic, note = (load_traffic(gt.gt_config_chunk_edges(w["E"]), BWD_TRAFFIC_FILE, BWD_SOURCES)
+                     if w.get("name") == "powerlaw"
                      else (None, "counters are for the power-law workload"))
     res = {"ms": ms, "edge_heads_per_s": w["E"] * w["H"] / (ms * 1e-3),
            # the method's bytes over the call time: can pass the HBM peak, since the
@@ -660,7 +664,8 @@ def main():
     E, H = w["E"], w["H"]
     alg = algorithmic_bytes(w)
     achieved = alg / (kern_avg_ms * 1e-3) / 1e9
-    traffic, traffic_note = load_traffic() if args.workload == "powerlaw" else (None, "counters are for powerlaw")
+    traffic, traffic_note = (load_traffic(gt.gt_config_chunk_edges(E)) if args.workload == "powerlaw"
+                             else (None, "counters are for powerlaw"))
     log("ms/step %.3f (event-timed call %.3f ms, fused kernel + merge %.3f ms); algorithmic %.2f GB -> %.0f GB/s"
         % (ms_per_step, call_ms / calls, kern_avg_ms, alg / 1e9, achieved))
     log("traffic: %s" % traffic_note)
@@ -678,7 +683,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32" if w["dtype"] == 0 else "bf16",
         "data": "synthetic",
-        "config": {"workload": DESCRIPTIONS[args.workload], "N": w["N"], "E": E, "H": H, "D": w["D"]},
+        "config": {"workload": DESCRIPTIONS[args.workload], "N": w["N"], "E": E, "H": H, "D": w["D"],
+                   "split_threshold_edges": gt.gt_config_chunk_edges(E)},
         "roofline": {
             "bound": "hbm",
             "achieved": achieved,

@@ -120,11 +120,11 @@ int gt_sparse_mha_fwd(const int64_t* indptr, const int32_t* indices, const void*
  * other allocating call.  The split-row work lists and partial results go to
  * a file-scope device array of 160 MiB, which every GPU the library runs on
  * holds until the process ends, instead of the per-stream scratch.  The split
- * threshold is the configured one (GT_CFG_CHUNK_EDGES), doubled, up to 64
- * times, until the work lists and partials fit; while it is unchanged, out is
- * bit-identical to gt_sparse_mha_fwd's (at the default 512 and 16 in-edges
- * per node on average: up to about 19M edges for 8 heads of 64 features,
- * 35M for 8 heads of 32; each doubling about doubles that).  Inputs that do not fit
+ * threshold (gt_config_chunk_edges) is doubled, up to 64 times, until the
+ * work lists and partials fit; while it is unchanged, out is bit-identical to
+ * gt_sparse_mha_fwd's (at the automatic threshold and 16 in-edges per node on
+ * average: up to about 70M edges for 8 heads of 64 features, 120M for 8 heads
+ * of 32; each doubling about doubles that).  Inputs that do not fit
  * even at 64 times the threshold return GT_EUNSUPPORTED, before anything is
  * enqueued (gt_last_error() gives the bytes needed).  All calls on one GPU
  * share the array, which keeps the last call's contents; nothing in it needs
@@ -401,12 +401,22 @@ const char* gt_last_error(void);
  * Tuning and testing knobs, process-wide, read at each call.
  *  GT_CFG_CHUNK_EDGES  rows with more in-edges than this are split into
  *                      chunks of this many edges, processed in parallel and
- *                      merged exactly (default 512; valid 1 .. 2^30).
- * gt_config_set returns GT_EINVAL for an unknown key or an invalid value.
+ *                      merged exactly (valid 1 .. 2^30; 0, the default, for
+ *                      automatic: 2,048 edges on graphs of 2^23 edges or
+ *                      more, 512 on smaller graphs and in gt_edge_softmax).
+ * gt_config_set returns GT_EINVAL for an unknown key or an invalid value;
+ * gt_config_get returns the configured value (-1 for an unknown key).
+ * gt_config_chunk_edges returns the threshold a call on a graph of E edges
+ * uses, the configured one or the automatic one (softmax != 0: that of
+ * gt_edge_softmax); -1 for E < 0.  The threshold changes results only in
+ * the order of rounding; since the automatic one depends on E, a shard of a
+ * graph (or a batch of a different size) can take another threshold than the
+ * whole graph: configure one where the two must agree bit for bit.
  */
 typedef enum { GT_CFG_CHUNK_EDGES = 0 } gt_config_key;
 int gt_config_set(int32_t key, int64_t value);
 int64_t gt_config_get(int32_t key);
+int64_t gt_config_chunk_edges(int64_t E, int32_t softmax);
 
 /*
  * The scratch buffer of `stream` on the current device: gt_scratch_release

@@ -33,7 +33,8 @@ The functions have the names of the C entry points declared in
 * ``gt_sparse_mha_fwd_plan(plan, Q, K, V)`` / ``gt_sparse_mha_bwd_plan(plan, ...)``;
 * ``gt_scratch_release(stream=None)`` / ``gt_scratch_bytes(stream=None)`` -- the
   library's per-stream work buffer;
-* ``gt_config_set`` / ``gt_config_get``, ``gt_profile_begin`` / ``gt_profile_end``.
+* ``gt_config_set`` / ``gt_config_get`` / ``gt_config_chunk_edges``, ``gt_profile_begin`` /
+  ``gt_profile_end``.
 
 Every tensor must be contiguous and on the current device; calls are
 asynchronous on ``stream`` (default: torch's current stream).
@@ -81,6 +82,7 @@ EXPORTS = (
     "gt_last_error",
     "gt_config_set",
     "gt_config_get",
+    "gt_config_chunk_edges",
     "gt_scratch_release",
     "gt_scratch_bytes",
     "gt_profile_begin",
@@ -142,6 +144,8 @@ def lib():
         L.gt_config_set.argtypes = [_i32, _i64]
         L.gt_config_get.restype = _i64
         L.gt_config_get.argtypes = [_i32]
+        L.gt_config_chunk_edges.restype = _i64
+        L.gt_config_chunk_edges.argtypes = [_i64, _i32]
         L.gt_scratch_release.argtypes = [_p]
         L.gt_scratch_release.restype = ctypes.c_int
         L.gt_scratch_bytes.argtypes = [_p]
@@ -667,6 +671,12 @@ def gt_config_set(key, value):
 
 def gt_config_get(key):
     return lib().gt_config_get(key)
+
+
+def gt_config_chunk_edges(E, softmax=False):
+    """The split threshold a call on a graph of E edges uses (that of
+    gt_edge_softmax if softmax)."""
+    return lib().gt_config_chunk_edges(E, 1 if softmax else 0)
 
 
 def gt_scratch_release(stream=None):

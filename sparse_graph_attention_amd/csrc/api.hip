@@ -21,7 +21,23 @@ using namespace gt;
 namespace {
 
 thread_local std::string g_err;
-std::atomic<int64_t> g_chunk{512};
+std::atomic<int64_t> g_chunk{0};  // the configured split threshold; 0: automatic
+
+// The automatic split threshold.  Each chunk of a split row is one wave's
+// item, and a wave keeps only a few edges' rows in flight (on its own, some
+// 10-20 GB/s at memory latency), so a chunk must stay short against the call
+// as a whole.  From 2^23 edges up, the 4,096 waves the
+// chip holds at four a SIMD average 2,048 edges each, and 2,048-edge chunks make
+// fewer partials and merges than 512-edge ones; below that, chunks stay at
+// 512 edges.  The unfused softmax keeps a chunk's scores in its lanes (64 a
+// lane: 512 edges of 8 heads) and reads a longer chunk twice, so it keeps 512.
+constexpr int64_t kChunkSmall = 512, kChunkLarge = 2048, kChunkLargeFromEdges = (int64_t)1 << 23;
+
+int64_t chunk_for(int64_t E, bool softmax) {
+    const int64_t c = g_chunk.load();
+    if (c > 0) return c;
+    return !softmax && E >= kChunkLargeFromEdges ? kChunkLarge : kChunkSmall;
+}
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -103,7 +119,7 @@ void size_plan_at(int64_t N, int64_t E, int64_t C, Plan& p) {
     p.n_order = p.max_heavy && N > kPlanBlockRows ? N : 0;
 }
 
-void size_plan(int64_t N, int64_t E, Plan& p) { size_plan_at(N, E, g_chunk.load(), p); }
+void size_plan(int64_t N, int64_t E, Plan& p) { size_plan_at(N, E, chunk_for(E, false), p); }
 
 size_t table_bytes(const Plan& p) {
     return align256(sizeof(PlanCounters)) + align256(sizeof(HeavyRow) * p.max_heavy) +
@@ -140,9 +156,10 @@ int check_plan(const Plan& p) {
 
 // Sizes the plan for (N, E), carves tables and partials out of the stream's
 // scratch and lists the split rows on the device.
-int make_plan(const int64_t* indptr, int64_t N, int64_t E, int H, int D, hipStream_t stream, Args& a) {
+int make_plan(const int64_t* indptr, int64_t N, int64_t E, int H, int D, hipStream_t stream, Args& a,
+              bool softmax = false) {
     (void)indptr;
-    size_plan(N, E, a.plan);
+    size_plan_at(N, E, chunk_for(E, softmax), a.plan);
     int rc = check_plan(a.plan);
     if (rc) return rc;
     const int64_t accw = (int64_t)H * D;
@@ -337,12 +354,14 @@ const char* gt_last_error(void) { return g_err.c_str(); }
 
 int gt_config_set(int32_t key, int64_t value) {
     if (key != GT_CFG_CHUNK_EDGES) return fail(GT_EINVAL, "unknown configuration key %d", key);
-    if (value < 1 || value > ((int64_t)1 << 30)) return fail(GT_EINVAL, "chunk edges %lld out of range", (long long)value);
+    if (value < 0 || value > ((int64_t)1 << 30)) return fail(GT_EINVAL, "chunk edges %lld out of range", (long long)value);
     g_chunk.store(value);
     return GT_OK;
 }
 
 int64_t gt_config_get(int32_t key) { return key == GT_CFG_CHUNK_EDGES ? g_chunk.load() : -1; }
+
+int64_t gt_config_chunk_edges(int64_t E, int32_t softmax) { return E < 0 ? -1 : chunk_for(E, softmax != 0); }
 
 int gt_scratch_release(hipStream_t stream) {
     int dev = 0;
@@ -714,7 +733,7 @@ int gt_edge_softmax(const int64_t* indptr, const float* scores, float* alpha, in
     a.H = H;
     a.D = 1;
     a.dtype = GT_F32;
-    rc = make_plan(indptr, N, E, H, 1, stream, a);
+    rc = make_plan(indptr, N, E, H, 1, stream, a, true);
     if (rc) return rc;
     hipError_t e = launch_softmax(a, stream);
     return e == hipSuccess ? GT_OK : hip_fail(e, "edge softmax launch");
@@ -914,7 +933,7 @@ int gt_sparse_mha_fwd_noalloc(const int64_t* indptr, const int32_t* indices, con
     // the configured split threshold, doubled until the plan's tables and
     // partials fit the static scratch
     const int64_t HD = (int64_t)H * D;
-    const int64_t C0 = g_chunk.load();
+    const int64_t C0 = chunk_for(E, false);
     Plan p{};
     size_t need = 0;
     for (int64_t C = C0;; C *= 2) {

@@ -30,8 +30,11 @@ int main(void) {
         printf("gt_last_error is empty after a rejection\n");
         ++failures;
     }
-    expect(gt_config_set(GT_CFG_CHUNK_EDGES, 0), GT_EINVAL, "chunk of 0 edges");
-    expect((int)gt_config_get(GT_CFG_CHUNK_EDGES), 512, "default chunk");
+    expect(gt_config_set(GT_CFG_CHUNK_EDGES, -1), GT_EINVAL, "chunk of -1 edges");
+    expect((int)gt_config_get(GT_CFG_CHUNK_EDGES), 0, "default chunk (automatic)");
+    expect((int)gt_config_chunk_edges(1000, 0), 512, "automatic chunk, small graph");
+    expect((int)gt_config_chunk_edges((int64_t)1 << 23, 0), 2048, "automatic chunk, large graph");
+    expect((int)gt_config_chunk_edges((int64_t)1 << 23, 1), 512, "automatic chunk, softmax");
     expect((int)gt_config_get(77), -1, "unknown key");
     expect(gt_profile_begin(0), GT_EINVAL, "profile capacity 0");
     expect(strcmp(gt_status_string(GT_OK), "ok"), 0, "status string");

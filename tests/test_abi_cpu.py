@@ -94,12 +94,25 @@ def test_calib_gather_rejects():
 
 def test_config():
     old = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
-    assert old == 512
+    assert old == 0  # automatic
+    # automatic: 512 edges below 2^23 edges and in the softmax, 2,048 from there
+    assert gt.gt_config_chunk_edges(0) == 512
+    assert gt.gt_config_chunk_edges(2 ** 23 - 1) == 512
+    assert gt.gt_config_chunk_edges(2 ** 23) == 2048
+    assert gt.gt_config_chunk_edges(60_000_000) == 2048
+    assert gt.gt_config_chunk_edges(60_000_000, softmax=True) == 512
+    assert gt.gt_config_chunk_edges(-1) == -1
     try:
         gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 7)
         assert gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES) == 7
+        assert gt.gt_config_chunk_edges(60_000_000) == 7
+        assert gt.gt_config_chunk_edges(100, softmax=True) == 7
+        gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 0)
+        assert gt.gt_config_chunk_edges(2 ** 23) == 2048
         with pytest.raises(gt.GtError):
-            gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 0)
+            gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, -1)
+        with pytest.raises(gt.GtError):
+            gt.gt_config_set(gt.GT_CFG_CHUNK_EDGES, 2 ** 30 + 1)
         with pytest.raises(gt.GtError):
             gt.gt_config_set(99, 5)
         assert gt.gt_config_get(99) == -1

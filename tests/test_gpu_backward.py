@@ -107,7 +107,7 @@ def check_lse(g, o, what):
 
 def check_bwd_full(w, tol=None):
     say("bwd %s N=%d E=%d H=%d D=%d dtype=%d chunk=%d" % (w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"],
-                                                          gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+                                                          gt.gt_config_chunk_edges(w["E"])))
     res = run_gpu(w)
     _, lse, dq, dk, dv = res
     rq, rk, rv, rlse, _ = oracle.bwd(*oracle_inputs(w), w["dO"])
@@ -127,7 +127,7 @@ def check_bwd_sampled(w, n_random=800):
     empty rows, random ones), the oracle computing them one by one."""
     say("bwd %s sampled, N=%d E=%d" % (w["name"], w["N"], w["E"]))
     _, lse, dq, dk, dv = (host(x) for x in run_gpu(w))
-    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    chunk = gt.gt_config_chunk_edges(w["E"])
     rlse, rdelta = oracle.row_stats(*oracle_inputs(w), w["dO"])
     check_lse(lse, rlse, "lse " + w["name"])
     tol = btol_of(w)

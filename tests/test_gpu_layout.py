@@ -44,7 +44,7 @@ def takes_kernel(w):
 def check_fwd(w):
     say("ndh fwd %s N=%d E=%d H=%d D=%d dtype=%d kernel=%s chunk=%d" % (
         w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"], takes_kernel(w),
-        gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+        gt.gt_config_chunk_edges(w["E"])))
     t = to_dev(w)
     out, lse = gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], ndh(t["Q"]), ndh(t["K"]), ndh(t["V"]),
                                            layout="ndh", want_lse=True)
@@ -102,7 +102,7 @@ def check_bwd(w):
     w = with_grad(w)
     say("ndh bwd %s N=%d E=%d H=%d D=%d dtype=%d kernel=%s chunk=%d" % (
         w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"], takes_kernel(w),
-        gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+        gt.gt_config_chunk_edges(w["E"])))
     t = to_dev(w)
     d = dev()
     tip, tix = (torch.from_numpy(x).to(d) for x in (w["t_indptr"], w["t_indices"]))
@@ -228,7 +228,7 @@ def test_ndh_large_sampled():
     out, lse = gt.gt_sparse_mha_fwd_layout(t["indptr"], t["indices"], ndh(t["Q"]), ndh(t["K"]), ndh(t["V"]),
                                            want_lse=True)
     torch.cuda.synchronize()
-    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    chunk = gt.gt_config_chunk_edges(w["E"])
     rows = sample_rows(w["indptr"], chunk, n_random=400)
     say_split(w["indptr"], rows, chunk, "ndh powerlaw")
     rows_t = torch.from_numpy(rows).to(dev())

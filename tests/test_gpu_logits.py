@@ -100,7 +100,7 @@ def bound_opts(w, o):
 def check_full(w, o):
     say("ex %s N=%d E=%d H=%d D=%d dtype=%d bias=%s ew=%s p=%g chunk=%d" % (
         w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"], o["bias"] is not None, o["ew"] is not None,
-        o["drop_p"], gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+        o["drop_p"], gt.gt_config_chunk_edges(w["E"])))
     out, lse, dq, dk, dv, dbias, dw = run_ex(w, o)
     ftol, btol = tols(w)
     kw = oracle_opts(o)
@@ -225,7 +225,7 @@ def test_variants_large_sampled(name, p):
     out, lse, dq, dk, dv, dbias, dw = (host(x) for x in run_ex(w, o))
     ftol, btol = tols(w)
     kw = oracle_opts(o)
-    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    chunk = gt.gt_config_chunk_edges(w["E"])
     rows = sample_rows(w["indptr"], chunk, n_random=600)
     say_split(w["indptr"], rows, chunk, "ex destinations " + name)
     rlse, rdelta = oracle.row_stats_ex(*oracle_inputs(w), w["dO"], **kw)

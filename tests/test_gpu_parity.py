@@ -114,7 +114,7 @@ def run_fused(w, t=None):
 
 def check_fused_full(w, tol=None):
     say("fused %s N=%d E=%d H=%d D=%d dtype=%d chunk=%d" % (w["name"], w["N"], w["E"], w["H"], w["D"], w["dtype"],
-                                                            gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)))
+                                                            gt.gt_config_chunk_edges(w["E"])))
     out = run_fused(w)
     ref = oracle.fwd(*oracle_inputs(w))
     assert_close(host(out), ref, tol or tol_of(w), "fused " + w["name"])
@@ -178,7 +178,7 @@ def test_fused_large_sampled(name):
     w = workload(name)
     say("fused %s sampled rows, N=%d E=%d" % (name, w["N"], w["E"]))
     out = host(run_fused(w))
-    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    chunk = gt.gt_config_chunk_edges(w["E"])
     rows = sample_rows(w["indptr"], chunk)
     say_split(w["indptr"], rows, chunk, "fused " + name)
     ref = oracle.fwd_rows(*oracle_inputs(w), rows)
@@ -446,9 +446,12 @@ def test_softmax_in_place_and_odd_heads():
 @pytest.mark.parametrize("name", ["powerlaw", "lognormal"])
 def test_unfused_large_sampled(name):
     w = workload(name)
-    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
-    rows = sample_rows(w["indptr"], chunk, n_random=500)
+    # SDDMM and SpMM split rows at one threshold, the softmax at its own
+    chunk = gt.gt_config_chunk_edges(w["E"])
+    s_chunk = gt.gt_config_chunk_edges(w["E"], softmax=True)
+    rows = np.union1d(sample_rows(w["indptr"], chunk, n_random=500), sample_rows(w["indptr"], s_chunk, n_random=0))
     say_split(w["indptr"], rows, chunk, "unfused " + name)
+    say_split(w["indptr"], rows, s_chunk, "unfused softmax " + name)
     check_stages(w, rows)
 
 

@@ -48,7 +48,7 @@ def test_more_items_than_one_slice():
     E = int(indptr[-1])
     Q, K, V = gtgen.make_features(N, H, D, gtgen.F32, 3, 1.0)
     dO = gtgen.make_grad(N, H, D, gtgen.F32, 11)
-    chunk = gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES)
+    chunk = gt.gt_config_chunk_edges(E)
     # the host's upper bound of chunk items, which precede the rows
     max_heavy = min(N, E // (chunk + 1))
     max_chunks = E // chunk + max_heavy

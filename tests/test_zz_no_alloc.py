@@ -7,8 +7,8 @@ made in a row, each on a smaller input than the one before, so a call that
 wrongly read what the last one left (its counters, chunk lists or partials)
 would show.  While the split threshold needs no raising, out must equal
 gt_sparse_mha_fwd's bit for bit; where it is raised (the log-normal graph
-needs twice the default to fit), it must equal gt_sparse_mha_fwd at that
-threshold bit for bit.  Every case is also held to the oracle (sampled rows,
+needs twice a threshold of 512 edges to fit), it must equal gt_sparse_mha_fwd
+at that threshold bit for bit.  Every case is also held to the oracle (sampled rows,
 every split row included, on the million-node graphs).
 """
 import math
@@ -55,13 +55,19 @@ def check(w, chunk_ref, sampled):
 
 
 def test_noalloc_calls_in_a_row_each_smaller():
-    assert gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES) == 512
-    # the log-normal graph's plan needs 255 MiB of scratch at a split
-    # threshold of 512 edges: the call doubles it to 1024 (128 MiB)
-    check(gtgen.make_workload("lognormal"), 1024, True)
-    # the power-law graph's fits at 512 (129 MiB)
-    check(gtgen.make_workload("powerlaw"), 512, True)
-    # smaller graphs with split rows, then without
+    assert gt.gt_config_get(gt.GT_CFG_CHUNK_EDGES) == 0  # automatic
+    lognormal = gtgen.make_workload("lognormal")
+    # at a configured split threshold of 512 edges the log-normal graph's plan
+    # needs 255 MiB of scratch: the call doubles the threshold to 1024 (128 MiB)
+    with chunk_edges(512):
+        check(lognormal, 1024, True)
+    del lognormal
+    # the power-law graph's fits at the automatic threshold (2,048 edges: 36 MiB)
+    w = gtgen.make_workload("powerlaw")
+    assert gt.gt_config_chunk_edges(w["E"]) == 2048
+    check(w, 2048, True)
+    del w
+    # smaller graphs with split rows (automatic threshold 512), then without
     check(hub_graph(3, 20000, 400000, [5, 77, 19999], gtgen.F32, 8, 64), 512, False)
     check(hub_graph(4, 3000, 40000, [0, 2999], gtgen.BF16, 8, 32), 512, False)
     check(hub_graph(5, 500, 6000, [7], gtgen.F32, 8, 10), 512, False)
