@@ -1265,7 +1265,7 @@ static hipError_t launch_dq_dt(const Args& a0, hipStream_t s) {
             else if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dq_vec_kernel<DT, 2, 4, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dq_vec_kernel<DT, 1, XL == 2 ? GT_BWD_BF16_DQ_XL2_U : XL ? 4 : 8, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dq_vec_kernel<DT, 1, XL == 2 ? GT_BWD_BF16_DQ_XL2_U : XL ? GT_BWD_BF16_DQ_XL1_U : GT_BWD_BF16_DQ_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (launch_dq_fixed<DT, XL>(a, grid, block, s, stream_kv))
                 ;
             else if (a.NC == 1)
@@ -1325,7 +1325,7 @@ static hipError_t launch_dkv_dt(const Args& a0, hipStream_t s) {
             if (DT == kF32 && a.NC == 2 && a.G == 64 && a.lph == 16 && full)
                 bwd_dkv_vec_kernel<DT, 2, XL ? 2 : GT_BWD_F32_DKV_U, 64, 16, true, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
-                bwd_dkv_vec_kernel<DT, 1, XL == 2 ? 2 : XL == 1 ? GT_BWD_BF16_DKV_XL1_U : GT_BWD_BF16_DKV_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
+                bwd_dkv_vec_kernel<DT, 1, XL == 2 ? GT_BWD_BF16_DKV_XL2_U : XL == 1 ? GT_BWD_BF16_DKV_XL1_U : GT_BWD_BF16_DKV_U, 32, 4, true, XL><<<grid, block, 0, s>>>(a);
             else if (launch_dkv_fixed<DT, XL>(a, grid, block, s))
                 ;
             else if (a.NC == 1)

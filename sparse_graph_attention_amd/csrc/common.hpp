@@ -24,7 +24,7 @@
 #define GT_F32_D64_U 4  // edges in flight per wave, fp32 rows of 8 heads x 64
 #endif
 #ifndef GT_BF16_D32_U
-#define GT_BF16_D32_U 8  // edges in flight per half-wave, bf16 rows of 8 heads x 32
+#define GT_BF16_D32_U 2  // edges in flight per half-wave, bf16 rows of 8 heads x 32 (8 waves per SIMD)
 #endif
 #ifndef GT_SDDMM_F32_U
 #define GT_SDDMM_F32_U 4  // unfused stages, fp32 8 x 64 and bf16 8 x 32 rows: edges in flight per group
@@ -50,17 +50,29 @@
 #ifndef GT_BWD_F32_DKV_U
 #define GT_BWD_F32_DKV_U 4  // source pass, plain logits
 #endif
+#ifndef GT_BWD_BF16_DQ_U
+#define GT_BWD_BF16_DQ_U 2  // backward, bf16 8 x 32: destination pass, plain logits (8 waves per SIMD)
+#endif
 #ifndef GT_BWD_BF16_DQ_XL2_U
-#define GT_BWD_BF16_DQ_XL2_U 4  // backward, bf16 8 x 32: destination pass with dropout
+#define GT_BWD_BF16_DQ_XL2_U 2  // backward, bf16 8 x 32: destination pass with dropout
 #endif
 #ifndef GT_BWD_BF16_DKV_U
-#define GT_BWD_BF16_DKV_U 8  // source pass, plain logits
+#define GT_BWD_BF16_DKV_U 2  // source pass, plain logits (6 waves per SIMD)
 #endif
 #ifndef GT_BWD_BF16_DKV_XL1_U
-#define GT_BWD_BF16_DKV_XL1_U 4  // source pass with bias or edge weights
+#define GT_BWD_BF16_DKV_XL1_U 2  // source pass with bias or edge weights
+#endif
+#ifndef GT_BF16_D32_XL2_U
+#define GT_BF16_D32_XL2_U 4  // the same with dropout
+#endif
+#ifndef GT_BWD_BF16_DQ_XL1_U
+#define GT_BWD_BF16_DQ_XL1_U 2  // backward, bf16 8 x 32: destination pass with bias or edge weights
+#endif
+#ifndef GT_BWD_BF16_DKV_XL2_U
+#define GT_BWD_BF16_DKV_XL2_U 2  // source pass with dropout
 #endif
 #ifndef GT_BF16_D32_XL1_U
-#define GT_BF16_D32_XL1_U 4  // the same with bias or edge weights (keeps 4 waves per SIMD)
+#define GT_BF16_D32_XL1_U 2  // the same with bias or edge weights (7 waves per SIMD)
 #endif
 
 namespace gt {
