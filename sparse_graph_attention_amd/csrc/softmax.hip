@@ -27,17 +27,31 @@ __device__ __forceinline__ float wave_sum_stride(float x, int hstride) {
     return x;
 }
 
-// Elements per lane kept in registers when a whole item fits: 64 x 64 scores
-// (a 512-edge chunk of 8 heads) for chunks, 64 x 32 for rows (fewer registers,
-// more waves: row blocks are latency-bound).
-constexpr int kChunkCache = 64;
-constexpr int kRowCache = 32;
+// Elements per lane kept in registers when a whole item fits (0: none).
+// Rows: 16 x 64 scores (128 edges of 8 heads), few registers so that many
+// waves hide the latency of the short rows' loads.  Chunks need only their
+// statistics, which one streaming pass gives: no cache, more waves.
+#ifndef GT_SOFTMAX_ROW_CACHE
+#define GT_SOFTMAX_ROW_CACHE 16
+#endif
+#ifndef GT_SOFTMAX_CHUNK_CACHE
+#define GT_SOFTMAX_CHUNK_CACHE 0
+#endif
+constexpr int kRowCache = GT_SOFTMAX_ROW_CACHE;
+constexpr int kChunkCache = GT_SOFTMAX_CHUNK_CACHE;
 // Loads in flight per lane in the streaming loops.
+#ifndef GT_SOFTMAX_CHUNK_BATCH
+#define GT_SOFTMAX_CHUNK_BATCH 16
+#endif
 constexpr int kBatch = 8;
+constexpr int kChunkBatch = GT_SOFTMAX_CHUNK_BATCH;
 
 // One wave over edges [e0, e1) of one destination: the statistics of a chunk
-// (slot >= 0), or the weights of a whole row (slot < 0).
-template <int kCache>
+// (slot >= 0), or the weights of a whole row (slot < 0).  Items larger than
+// the cache are streamed: one pass for the maximum and the sum together (the
+// sum rescaled whenever the lane's maximum grows), and for a row a second
+// pass that writes the weights.
+template <int kCache, int kB>
 __device__ __forceinline__ void softmax_wave(const Args& a, int64_t e0, int64_t e1, int64_t slot, int lane) {
     const int H = a.H;
     const float* s = a.scores_in;  // may alias alpha_out (in place)
@@ -45,28 +59,29 @@ __device__ __forceinline__ void softmax_wave(const Args& a, int64_t e0, int64_t 
     if ((kWave % H) == 0) {
         // lane j covers flat elements e0*H + j + 64t; its head is j mod H
         const int64_t i0 = e0 * H, i1 = e1 * H;
-        if (i1 - i0 <= (int64_t)kWave * kCache) {
+        if (kCache > 0 && i1 - i0 <= (int64_t)kWave * kCache) {
             // the whole item fits in registers: one read, all loads in flight at once
-            float v[kCache];
+            constexpr int kC = kCache > 0 ? kCache : 1;
+            float v[kC];
 #pragma unroll
-            for (int t = 0; t < kCache; ++t) {
+            for (int t = 0; t < kC; ++t) {
                 const int64_t i = i0 + lane + (int64_t)t * kWave;
                 v[t] = i < i1 ? s[i] : -INFINITY;
             }
             float m = -INFINITY;
 #pragma unroll
-            for (int t = 0; t < kCache; ++t) m = fmaxf(m, v[t]);
+            for (int t = 0; t < kC; ++t) m = fmaxf(m, v[t]);
             m = wave_max_stride(m, H);
             float l = 0.0f;
 #pragma unroll
-            for (int t = 0; t < kCache; ++t) {
+            for (int t = 0; t < kC; ++t) {
                 v[t] = v[t] == -INFINITY ? 0.0f : expd(v[t], m);
                 l += v[t];
             }
             l = wave_sum_stride(l, H);
             if (slot < 0) {
 #pragma unroll
-                for (int t = 0; t < kCache; ++t) {
+                for (int t = 0; t < kC; ++t) {
                     const int64_t i = i0 + lane + (int64_t)t * kWave;
                     if (i < i1) alpha[i] = v[t] / l;
                 }
@@ -76,24 +91,26 @@ __device__ __forceinline__ void softmax_wave(const Args& a, int64_t e0, int64_t 
             }
             return;
         }
-        // larger items: three streaming passes, kBatch loads in flight per lane
-        float m = -INFINITY;
-        for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
-            float v[kBatch];
+        // larger items: the lane's running maximum and its sum of exp(s - max)
+        float m = -INFINITY, l = 0.0f;
+        for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kB) {
+            float v[kB];
 #pragma unroll
-            for (int t = 0; t < kBatch; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : -INFINITY;
+            for (int t = 0; t < kB; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : -INFINITY;
+            float mb = v[0];
 #pragma unroll
-            for (int t = 0; t < kBatch; ++t) m = fmaxf(m, v[t]);
+            for (int t = 1; t < kB; ++t) mb = fmaxf(mb, v[t]);
+            if (mb > m) {
+                l = m == -INFINITY ? 0.0f : l * expd(m, mb);
+                m = mb;
+            }
+#pragma unroll
+            for (int t = 0; t < kB; ++t) l += v[t] == -INFINITY ? 0.0f : expd(v[t], m);
         }
-        m = wave_max_stride(m, H);
-        float l = 0.0f;
-        for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
-            float v[kBatch];
-#pragma unroll
-            for (int t = 0; t < kBatch; ++t) v[t] = ib + t * kWave < i1 ? s[ib + t * kWave] : -INFINITY;
-#pragma unroll
-            for (int t = 0; t < kBatch; ++t) l += v[t] == -INFINITY ? 0.0f : expd(v[t], m);
-        }
+        // the lanes of a head: their sums rescaled to the head's maximum
+        const float M = wave_max_stride(m, H);
+        l = m == -INFINITY ? 0.0f : l * expd(m, M);
+        m = M;
         l = wave_sum_stride(l, H);
         if (slot < 0) {
             for (int64_t ib = i0 + lane; ib < i1; ib += (int64_t)kWave * kBatch) {
@@ -128,7 +145,7 @@ __device__ __forceinline__ void softmax_wave(const Args& a, int64_t e0, int64_t 
 
 // Rows of at most this many in-edges are done by one lane per (row, head).
 #ifndef GT_SOFTMAX_SMALL_DEG
-#define GT_SOFTMAX_SMALL_DEG 32
+#define GT_SOFTMAX_SMALL_DEG 16
 #endif
 constexpr int kSmallDeg = GT_SOFTMAX_SMALL_DEG;
 
@@ -139,7 +156,7 @@ __global__ __launch_bounds__(kBlock) void softmax_chunk_kernel(const Args a) {
     if (item >= a.plan.max_chunks) return;
     Item it;
     if (!resolve_item(a.plan, a.indptr, a.N, item, it)) return;
-    softmax_wave<kChunkCache>(a, uniform64(it.e0), uniform64(it.e1), it.slot, lane);
+    softmax_wave<kChunkCache, kChunkBatch>(a, uniform64(it.e0), uniform64(it.e1), it.slot, lane);
 }
 
 // Rows that are not split.  When H divides 64 an item is a block of 64/H
@@ -154,7 +171,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(const Args a) {
         Item it;
         if (!resolve_item(a.plan, a.indptr, a.N, item + a.plan.max_chunks, it)) return;
         const int64_t e0 = uniform64(it.e0), e1 = uniform64(it.e1);
-        if (e1 > e0) softmax_wave<kRowCache>(a, e0, e1, -1, lane);
+        if (e1 > e0) softmax_wave<kRowCache, kBatch>(a, e0, e1, -1, lane);
         return;
     }
     const int rpw = kWave / H;
@@ -194,7 +211,7 @@ __global__ __launch_bounds__(kBlock) void softmax_kernel(const Args a) {
         const int j = __builtin_ctzll(big);
         big &= big - 1;
         const int64_t row = r0 + j / H;
-        softmax_wave<kRowCache>(a, a.indptr[row], a.indptr[row + 1], -1, lane);
+        softmax_wave<kRowCache, kBatch>(a, a.indptr[row], a.indptr[row + 1], -1, lane);
     }
 }
 

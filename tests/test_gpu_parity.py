@@ -459,10 +459,12 @@ def test_unfused_large_sampled(name):
 @pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("chunk", [512, 20])
 def test_softmax_row_blocks(H, in_place, chunk):
-    # degrees around the lane/wave cut (32) and the split threshold (512 by
-    # default; 20 splits rows that the per-lane path could otherwise take, which
-    # in place must not be overwritten before their chunks are read)
-    degs = [0, 1, 2, 19, 20, 21, 31, 32, 33, 100, 511, 512, 513, 1300, 0, 5, 64, 65, 7]
+    # degrees around the lane/wave cut (16), the rows a wave holds in
+    # registers (16 scores a lane: 1024/H edges) and the split threshold (512
+    # by default; 20 splits rows that the per-lane path could otherwise take,
+    # which in place must not be overwritten before their chunks are read)
+    degs = [0, 1, 2, 15, 16, 17, 19, 20, 21, 31, 32, 33, 100, 511, 512, 513, 1300, 0, 5, 64, 65, 7, 127, 128, 129,
+            255, 256, 257, 1023, 1024, 1025]
     N = len(degs) + 3
     dst = np.concatenate([np.full(d, v) for v, d in enumerate(degs)])
     src = gtgen.random_coo(41, N, len(dst))[0]
