@@ -26,12 +26,12 @@ std::atomic<int64_t> g_chunk{0};  // the configured split threshold; 0: automati
 // The automatic split threshold.  Each chunk of a split row is one wave's
 // item, and a wave keeps only a few edges' rows in flight (on its own, some
 // 10-20 GB/s at memory latency), so a chunk must stay short against the call
-// as a whole.  From 2^23 edges up, the 4,096 waves the
-// chip holds at four a SIMD average 2,048 edges each, and 2,048-edge chunks make
-// fewer partials and merges than 512-edge ones; below that, chunks stay at
-// 512 edges.  The unfused softmax keeps 512: its row kernel gives each row
-// below the threshold to one wave, and rows of a few thousand edges would
-// each hold one wave for their whole length.
+// as a whole.  From 2^23 edges up, the 4,096 waves the chip holds at four a
+// SIMD average 2,048 edges each, and 2,048-edge chunks make fewer partials
+// and merges than 512-edge ones; below that, chunks stay at 512 edges.  The
+// unfused softmax keeps 512: its row kernel gives each row below the
+// threshold to one wave, and rows of a few thousand edges would each hold one
+// wave for their whole length.
 constexpr int64_t kChunkSmall = 512, kChunkLarge = 2048, kChunkLargeFromEdges = (int64_t)1 << 23;
 
 int64_t chunk_for(int64_t E, bool softmax) {
