@@ -944,7 +944,7 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
                 fused_vec_kernel<DT, 2, XL == 2 ? 4 : GT_F32_D64_U, 64, 16, true, false, XL><<<grid, block, 0, s>>>(a);
             else if (DT == kBF16 && a.NC == 1 && a.G == 32 && a.lph == 4 && full)
                 // the extended kernel keeps per-edge inputs live: fewer edges in flight
-                fused_vec_kernel<DT, 1, XL == 2 ? GT_BF16_D32_XL2_U : XL == 1 ? GT_BF16_D32_XL1_U : GT_BF16_D32_U, 32, 4, true, false, XL><<<grid, block, 0, s>>>(a);
+                fused_vec_kernel<DT, 1, XL == 2 ? GT_BF16_D32_XL2_U : XL == 1 ? GT_BF16_D32_XL1_U : GT_BF16_D32_U, 32, 4, true, GT_BF16_NTL != 0, XL><<<grid, block, 0, s>>>(a);
             else if (launch_fixed_lph<DT, XL>(a, grid, block, s, DT == kF32 && stream_kv))
                 ;
             else if (a.NC == 1)
