@@ -62,6 +62,9 @@
 #ifndef GT_BWD_BF16_DKV_XL1_U
 #define GT_BWD_BF16_DKV_XL1_U 2  // source pass with bias or edge weights
 #endif
+#ifndef GT_NDH_F32_U
+#define GT_NDH_F32_U 4  // head-innermost forward, fp32 rows of 65 to 128 vectors: edges in flight
+#endif
 #ifndef GT_BF16_NTL
 #define GT_BF16_NTL 0  // bf16 8 x 32 forward: gathers with the non-temporal hint (measured slower)
 #endif

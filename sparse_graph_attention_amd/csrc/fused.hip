@@ -925,7 +925,7 @@ static hipError_t launch_fused_dt(const Args& a0, hipStream_t s) {
         return for_slices(a0, a0.items, [&](const Args& a, unsigned gx) {
             switch (a.NC) {
                 case 1: fused_ndh_kernel<DT, 4, 1><<<dim3(gx), block, 0, s>>>(a); break;
-                case 2: fused_ndh_kernel<DT, DT == kF32 ? 4 : 2, 2><<<dim3(gx), block, 0, s>>>(a); break;
+                case 2: fused_ndh_kernel<DT, DT == kF32 ? GT_NDH_F32_U : 2, 2><<<dim3(gx), block, 0, s>>>(a); break;
                 case 3: fused_ndh_kernel<DT, 2, 3><<<dim3(gx), block, 0, s>>>(a); break;
                 default: fused_ndh_kernel<DT, 2, 4><<<dim3(gx), block, 0, s>>>(a); break;
             }
